@@ -1,0 +1,32 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def gpu_available() -> bool:
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.fixture(scope="session")
+def lib():
+    """The built HIP library through its Python binding (GPU tests only)."""
+    if not gpu_available():
+        pytest.skip("no GPU")
+    import head_dim_attention_flash_amd as ffpa
+
+    ffpa.load()  # raises if the shared library is missing: no fallback exists
+    return ffpa
