@@ -1,0 +1,175 @@
+"""Benchmark of the large-head-dimension attention forward on one MI355X.
+
+Default workload (the headline metric): self-attention forward, B=1, Hq=Hkv=32,
+Nq=Nkv=8192, D=512, fp16 inputs, N(0, 1) synthetic data, fp32 output
+accumulation. One "step" is one forward call (every kernel of the path).
+
+TFLOPS follow the convention of "FFPA Attention Benchmark" (section "More
+Benchmark"): the forward counts 2 GEMMs = 4 B Hq Nq Nkv D flops, the backward
+the standard 5 = 10 B Hq Nq Nkv D, and a causal pass half of that.
+
+Prints ONE JSON line. ``--suite`` instead times every workload family and
+prints one line per workload (not the headline contract).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6}  # MI355X dense MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def counted_flops(B, Hq, Nq, Nkv, D, causal=False, backward=False) -> float:
+    """Flops credited to one pass: 2 (fwd) or 5 (bwd) GEMMs of 2 B Hq Nq Nkv D, halved if causal."""
+    f = (10.0 if backward else 4.0) * B * Hq * Nq * Nkv * D
+    return f * 0.5 if causal else f
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, inp, heads: int) -> dict:
+    """The float64 oracle timed on the host on `heads` query heads of the workload."""
+    from oracle import attn_fwd
+
+    g = w.Hq // w.Hkv
+    hk = max(1, (heads + g - 1) // g)
+    q = inp["q"][:, :heads].cpu()
+    k = inp["k"][:, :hk].cpu()
+    v = inp["v"][:, :hk].cpu()
+    mask = None if inp.get("mask") is None else inp["mask"].cpu()
+    t0 = time.perf_counter()
+    attn_fwd(q, k, v, w.scale, causal=w.causal, mask=mask)
+    dt = time.perf_counter() - t0
+    fl = counted_flops(1, heads, w.Nq, w.Nkv, w.D, w.causal)
+    return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.Hq} (b, h) heads of the same workload, float64 numpy, "
+                      f"{dt:.2f} s"}
+
+
+def time_forward(ffpa, w, inp, accum, steps, warmup):
+    import torch
+
+    q, k, v, mask = inp["q"], inp["k"], inp["v"], inp.get("mask")
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=q.device)
+
+    def step():
+        ffpa.attention(q, k, v, causal=w.causal, mask=mask, scale=w.scale, accum=accum, out=o,
+                       lse_out=lse)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    return per, wall
+
+
+def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
+    import torch
+
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, device="cuda")
+    per, wall = time_forward(ffpa, w, inp, accum, steps, warmup)
+    mean_ms = sum(per) / len(per)
+    fl = counted_flops(w.B, w.Hq, w.Nq, w.Nkv, w.D, w.causal)
+    tflops = fl / (mean_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    line = {
+        "metric": "attention fwd TFLOPS at N=8192, D=512 fp16; % of MI355X MFMA fp16 peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic N(0,1), seeded",
+        "config": {"workload": f"{name}: self-attention forward" if name == "self" else name,
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nkv": w.Nkv, "D": w.D,
+                   "causal": w.causal, "mask": w.mask, "accum": accum, "parallelism": "none"},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+        "kernel_ms": {"mean": round(mean_ms, 4), "median": round(per[len(per) // 2], 4),
+                      "min": round(per[0], 4)},
+    }
+    if with_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, inp, cpu_heads)
+    del inp
+    torch.cuda.empty_cache()
+    return line
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="self")
+    ap.add_argument("--accum", default="f32", choices=["f32", "f16"])
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="(b, h) heads the oracle CPU baseline runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--suite", action="store_true", help="time every workload family")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import head_dim_attention_flash_amd as ffpa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    ffpa.load()
+    if args.suite:
+        names = ["tiny", "self", "self_bf16", "cross", "gqa", "causal", "nonaligned", "mask"] + \
+                [f"dsweep{d}_f32" for d in (320, 448, 512)]
+        for n in names:
+            for acc in ("f32", "f16"):
+                line = run_one(ffpa, W, n, acc, args.steps, args.warmup, False, 0)
+                print(json.dumps(line), flush=True)
+        return 0
+    line = run_one(ffpa, W, args.workload, args.accum, args.steps, args.warmup,
+                   not args.no_cpu_baseline, args.cpu_heads)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,200 @@
+"""Python binding of libffpa_attn (large-head-dimension fused attention on MI355X).
+
+The entry points ``ffpa_attn_fwd``, ``ffpa_attn_bwd`` and the workspace queries
+have the names and argument order of the C ABI in ``include/ffpa_attn.h`` and
+only marshal arguments (device pointers as integers, sizes, the stream
+handle). ``attention`` and ``attention_backward`` are conveniences that take
+torch tensors, allocate outputs and workspace with torch and pass the current
+HIP stream; every step of the computation runs in the library's kernels.
+
+There is no fallback: if the shared library is missing or fails to load,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = [
+    "load", "FFPAError", "ffpa_attn_fwd", "ffpa_attn_bwd", "ffpa_attn_fwd_workspace_size",
+    "ffpa_attn_bwd_workspace_size", "ffpa_last_error", "ffpa_version", "attention",
+    "attention_backward", "F16", "BF16", "ACC_F32", "ACC_F16", "LIB_PATH", "EXPORTED",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libffpa_attn.so")
+
+F16, BF16 = 0, 1
+ACC_F32, ACC_F16 = 0, 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+_STATUS = {1: "FFPA_ERR_INVALID_ARG", 2: "FFPA_ERR_UNSUPPORTED", 3: "FFPA_ERR_WORKSPACE",
+           4: "FFPA_ERR_HIP"}
+
+# Symbols declared in include/ffpa_attn.h.
+EXPORTED = ("ffpa_attn_fwd", "ffpa_attn_fwd_workspace_size", "ffpa_attn_bwd",
+            "ffpa_attn_bwd_workspace_size", "ffpa_last_error", "ffpa_version")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class FFPAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the shared library once (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FFPAError(-1, f"{path} is missing: build it with "
+                            "`python -m head_dim_attention_flash_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.ffpa_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, i, i, vp, sz, vp]
+    lib.ffpa_attn_fwd.restype = i
+    lib.ffpa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i,
+                                  i, i, vp, sz, vp]
+    lib.ffpa_attn_bwd.restype = i
+    lib.ffpa_attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.ffpa_attn_fwd_workspace_size.restype = sz
+    lib.ffpa_attn_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.ffpa_attn_bwd_workspace_size.restype = sz
+    lib.ffpa_last_error.argtypes = []
+    lib.ffpa_last_error.restype = ctypes.c_char_p
+    lib.ffpa_version.argtypes = []
+    lib.ffpa_version.restype = i
+    _lib = lib
+    return lib
+
+
+def ffpa_last_error() -> str:
+    return load().ffpa_last_error().decode()
+
+
+def ffpa_version() -> int:
+    return load().ffpa_version()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise FFPAError(status, ffpa_last_error())
+
+
+def ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype) -> int:
+    return load().ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype)
+
+
+def ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype) -> int:
+    return load().ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype)
+
+
+def ffpa_attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                  accum_dtype, dtype, workspace, workspace_bytes, stream) -> int:
+    """Raw C call: pointers are integers (0 = NULL); returns the status code."""
+    return load().ffpa_attn_fwd(q, k, v, o, lse or None, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
+                                mask or None, mask_rows, accum_dtype, dtype, workspace or None,
+                                workspace_bytes, stream or None)
+
+
+def ffpa_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask,
+                  mask_rows, accum_dtype, dtype, workspace, workspace_bytes, stream) -> int:
+    """Raw C call: pointers are integers (0 = NULL); returns the status code."""
+    return load().ffpa_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale,
+                                causal, mask or None, mask_rows, accum_dtype, dtype,
+                                workspace or None, workspace_bytes, stream or None)
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences (torch supplies device memory and the stream only)
+# ---------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float16 or bfloat16")
+
+
+def _accum_code(accum: str) -> int:
+    if accum in ("f32", "fp32", "float32"):
+        return ACC_F32
+    if accum in ("f16", "fp16", "float16"):
+        return ACC_F16
+    raise ValueError("accum must be 'f32' or 'f16'")
+
+
+def _dims(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, D]")
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nkv, Dk = k.shape
+    if (Bk, Dk) != (B, D) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, Nkv, D] matching q")
+    for t in (q, k, v):
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("tensors must be contiguous device tensors")
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v must share a dtype")
+    return B, Hq, Hkv, Nq, Nkv, D
+
+
+def _mask_args(mask, q, Nq, Nkv):
+    if mask is None:
+        return 0, 0
+    if mask.dtype != q.dtype or not mask.is_contiguous() or not mask.is_cuda:
+        raise ValueError("mask must be a contiguous device tensor in q's dtype")
+    rows = mask.numel() // Nkv if Nkv else 0
+    if mask.numel() != rows * Nkv or rows not in (1, Nq):
+        raise ValueError("mask must have Nkv columns and 1 or Nq rows ([1,1,1,Nkv] or [1,1,Nq,Nkv])")
+    return mask.data_ptr(), rows
+
+
+def attention(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float] = None,
+              accum: str = "f32", return_lse: bool = False, out=None, lse_out=None):
+    """O = softmax(scale q k^T + mask) v on the current HIP stream (see include/ffpa_attn.h)."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nkv, D = _dims(q, k, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = None
+    if return_lse or lse_out is not None:
+        lse = (torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
+               if lse_out is None else lse_out)
+    mptr, mrows = _mask_args(mask, q, Nq, Nkv)
+    dt = _dtype_code(q)
+    ws_bytes = ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(ffpa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                         lse.data_ptr() if lse is not None else 0, B, Hq, Hkv, Nq, Nkv, D, scale,
+                         int(causal), mptr, mrows, _accum_code(accum), dt,
+                         ws.data_ptr() if ws is not None else 0, ws_bytes, stream))
+    return (o, lse) if return_lse else o
+
+
+def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None,
+                       scale: Optional[float] = None):
+    """(dq, dk, dv) of attention on the current HIP stream; o, lse from ``attention``."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nkv, D = _dims(q, k, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    mptr, mrows = _mask_args(mask, q, Nq, Nkv)
+    dt = _dtype_code(q)
+    ws_bytes = ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(ffpa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv,
+                         Nq, Nkv, D, scale, int(causal), mptr, mrows, ACC_F32, dt, ws.data_ptr(),
+                         ws_bytes, stream))
+    return dq, dk, dv

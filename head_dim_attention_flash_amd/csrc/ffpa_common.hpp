@@ -1,0 +1,198 @@
+// Shared device helpers for the gfx950 (CDNA4) attention kernels:
+// vector types, MFMA wrappers, the LDS swizzle, direct global->LDS copies,
+// explicit wait counters and the XCD-aware workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffpa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FFPA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Element traits: fp16 or bf16 storage, fp32 MFMA accumulation.
+// MFMA v_mfma_f32_32x32x16_{f16,bf16} lane layout (checked on gfx950):
+//   A[m][k]: lane l holds m = l % 32, k = 8 * (l / 32) + e, e = 0..7
+//   B[k][n]: lane l holds k = 8 * (l / 32) + e, n = l % 32
+//   C[m][n]: lane l, reg i holds m = 8 * (i / 4) + 4 * (l / 32) + i % 4, n = l % 32
+// v_mfma_f32_16x16x32_{f16,bf16}:
+//   A[m][k]: m = l % 16, k = 8 * (l / 16) + e;  B[k][n]: k = 8 * (l / 16) + e, n = l % 16
+//   C[m][n]: lane l, reg i holds m = 4 * (l / 16) + i, n = l % 16
+// ---------------------------------------------------------------------------
+template <bool BF16>
+struct Elem;
+
+template <>
+struct Elem<false> {
+  using scalar = _Float16;
+  using vec8 = f16x8;
+  __device__ static inline f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline float to_f32(uint16_t bits) {
+    return (float)__builtin_bit_cast(_Float16, bits);
+  }
+  // Round-to-nearest-even pack of two floats.
+  __device__ static inline uint32_t pack2(float a, float b) {
+    f16x2 h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+};
+
+template <>
+struct Elem<true> {
+  using scalar = __bf16;
+  using vec8 = bf16x8;
+  __device__ static inline f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline float to_f32(uint16_t bits) {
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+  }
+  __device__ static inline uint32_t pack2(float a, float b) {
+    __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  }
+};
+
+// Two fp16 values from their packed bits. Takes the word BY VALUE: this clang
+// mis-lowers __builtin_bit_cast applied directly to an ext_vector element
+// (every element of the vector then reads as element 0).
+__device__ inline f16x2 f16x2_from_bits(uint32_t bits) { return __builtin_bit_cast(f16x2, bits); }
+
+template <class V>
+__device__ inline V as_vec8(u32x4 x) {
+  return __builtin_bit_cast(V, x);
+}
+
+// Eight packed 16-bit values from eight floats (round to nearest even).
+template <bool BF16>
+__device__ inline typename Elem<BF16>::vec8 pack8(float a0, float a1, float a2, float a3, float a4,
+                                                   float a5, float a6, float a7) {
+  u32x4 w = {Elem<BF16>::pack2(a0, a1), Elem<BF16>::pack2(a2, a3), Elem<BF16>::pack2(a4, a5),
+             Elem<BF16>::pack2(a6, a7)};
+  return __builtin_bit_cast(typename Elem<BF16>::vec8, w);
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles. A staged tile is R rows x DC columns of 16-bit values, rows of
+// DC*2 bytes (a multiple of 128 B), split in 16-byte granules. Granule g of
+// row r is stored at granule g ^ swz(r). swz permutes the low three bits so
+// that (a) 8 consecutive rows read at one granule (ds_read_b128, 8 lanes per
+// LDS cycle) hit 8 distinct granule slots, and (b) 4 consecutive rows x 32
+// contiguous bytes (one 16-lane group of ds_read_b64_tr_b16) also hit 8
+// distinct slots.
+// ---------------------------------------------------------------------------
+__device__ __host__ inline int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// ---------------------------------------------------------------------------
+// Wait counters and the workgroup barrier, as inline asm with a "memory"
+// clobber: the compiler must not move any load or store (LDS reads of a
+// chunk, copies into a slot) across them. The clang builtins for these
+// instructions are not memory barriers.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ inline void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0). Loads at or
+// past `bytes` return zero instead of touching memory. 0x00020000 selects the
+// 32-bit data format gfx9 requires of untyped buffer loads.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16-byte direct copy buffer -> LDS: lane t of the wave reads
+// rsrc[voff + soff .. +16) and writes LDS bytes [16 t, 16 t + 16) after
+// `lds_base` (wave-uniform). Out-of-range reads write zeros.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
+                             FFPA_LDS void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_base, 16, voff, soff, 0, 0);
+}
+
+__device__ inline u32x4 lds_read16(const FFPA_LDS char* p) { return *(const FFPA_LDS u32x4*)p; }
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane j receives element (j % 4) of the 4-element chunks addressed by
+// lanes j/4, j/4 + 4, j/4 + 8 and j/4 + 12 (in that order). Checked on gfx950.
+__device__ inline i16x4 lds_read_tr(const FFPA_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FFPA_LDS i16x4*)p);
+}
+
+__device__ inline u32x4 join8(i16x4 lo, i16x4 hi) {
+  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(u32x4, v);
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// acc *= s for a 16-float MFMA accumulator that lives in AGPRs: each value
+// goes AGPR -> VGPR -> multiply -> AGPR through one VGPR temporary, so the
+// accumulator never has to be copied out as a whole. The s_nop padding covers
+// the MFMA-write -> accvgpr-read and accvgpr-write -> MFMA-read hazards, which
+// the compiler cannot see inside inline asm.
+#define FFPA_RESCALE1(i) \
+  "v_accvgpr_read_b32 %[t], %[a" #i "]\n v_mul_f32 %[t], %[s], %[t]\n v_accvgpr_write_b32 %[a" #i "], %[t]\n"
+__device__ inline void scale_agpr16(f32x16& acc, float s) {
+  float x0 = acc[0], x1 = acc[1], x2 = acc[2], x3 = acc[3], x4 = acc[4], x5 = acc[5], x6 = acc[6],
+        x7 = acc[7], x8 = acc[8], x9 = acc[9], x10 = acc[10], x11 = acc[11], x12 = acc[12],
+        x13 = acc[13], x14 = acc[14], x15 = acc[15];
+  float t;
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 4\n" FFPA_RESCALE1(0) FFPA_RESCALE1(1) FFPA_RESCALE1(2)
+                   FFPA_RESCALE1(3) FFPA_RESCALE1(4) FFPA_RESCALE1(5) FFPA_RESCALE1(6)
+                       FFPA_RESCALE1(7) FFPA_RESCALE1(8) FFPA_RESCALE1(9) FFPA_RESCALE1(10)
+                           FFPA_RESCALE1(11) FFPA_RESCALE1(12) FFPA_RESCALE1(13)
+                               FFPA_RESCALE1(14) FFPA_RESCALE1(15) "s_nop 7\n s_nop 7\n"
+               : [a0] "+a"(x0), [a1] "+a"(x1), [a2] "+a"(x2), [a3] "+a"(x3), [a4] "+a"(x4),
+                 [a5] "+a"(x5), [a6] "+a"(x6), [a7] "+a"(x7), [a8] "+a"(x8), [a9] "+a"(x9),
+                 [a10] "+a"(x10), [a11] "+a"(x11), [a12] "+a"(x12), [a13] "+a"(x13),
+                 [a14] "+a"(x14), [a15] "+a"(x15), [t] "=&v"(t)
+               : [s] "v"(s));
+  acc = f32x16{x0, x1, x2, x3, x4, x5, x6, x7, x8, x9, x10, x11, x12, x13, x14, x15};
+}
+#undef FFPA_RESCALE1
+
+// Value of lane (l ^ 32) of x.
+__device__ inline float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// ---------------------------------------------------------------------------
+// Workgroup order. The dispatcher hands workgroup i to XCD i % 8; each XCD has
+// its own L2. Logical tile t is given to workgroup ids so that every XCD works
+// on a contiguous range of logical tiles (tiles of the same head share K/V in
+// that XCD's L2).
+// ---------------------------------------------------------------------------
+__device__ inline int xcd_logical(int bid, int total) {
+  constexpr int kXcd = 8;
+  int x = bid % kXcd, j = bid / kXcd;
+  int per = total / kXcd, rem = total % kXcd;
+  return x * per + (x < rem ? x : rem) + j;
+}
+
+}  // namespace ffpa

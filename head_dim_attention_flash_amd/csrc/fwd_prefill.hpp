@@ -1,0 +1,410 @@
+// Forward attention kernel for 32-query-per-wave tiles (D <= 512 with an fp32
+// output accumulator, D <= 768 with an fp16 one).
+//
+// What it computes: O = softmax(scale * Q K^T + mask) V and lse per row, the
+// "naive_math" definition of section 3 of the attention-kernel-profiler design
+// document, with the additive mask and GQA conventions of "FFPA Attention
+// Benchmark" ("Quick Start") and the profiler's "gqa_4kv" entry. The scores
+// are never materialised in memory: keys are visited in tiles of 64 and the
+// softmax is carried online (running max and sum, output rescaled).
+//
+// Work decomposition (MI355X): one workgroup = 4 waves = 128 query rows of
+// one (batch, head). Wave w owns 32 rows. Every wave computes
+//     S^T (64 keys x 32 queries) = K_tile Q^T       (MFMA 32x32x16, A = K from LDS)
+//     O^T (D x 32 queries)     += V_tile^T P^T      (MFMA 32x32x16, A = V^T from LDS)
+// so that each lane's accumulators all belong to one query row (l % 32): the
+// online-softmax rescale is a per-lane scalar and P goes from the S
+// accumulators into the B operand of the second MFMA without leaving
+// registers. V^T is read from a row-major V tile with ds_read_b64_tr_b16.
+//
+// K and V tiles reach LDS in chunks of 64 rows x 64 columns (8 KiB) by
+// direct global->LDS copies; a ring of 2 * D/64 slots holds one whole tile of
+// K and V, and the copy of chunk u + ring - 1 is issued while chunk u is
+// consumed. Tiles past the last one re-read the last tile, so that every wave
+// always has the same number of copies in flight (the wait counts are
+// compile-time constants).
+#pragma once
+
+#include "ffpa_common.hpp"
+
+namespace ffpa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;         // may be null
+  const void* mask;   // may be null
+  int B, Hq, Hkv, Nq, Nkv;
+  int mask_rows;      // 0 (none) or 1 (key bias, staged in LDS after the ring)
+  int causal;
+  float scale_log2;   // scale * log2(e)
+  int n_qtiles;
+  int total_wg;
+};
+
+constexpr int kFwdWaves = 4;
+constexpr int kFwdRows = 32 * kFwdWaves;  // query rows per workgroup
+constexpr int kFwdBc = 64;                // keys per tile
+constexpr int kFwdDc = 64;                // columns per LDS chunk
+constexpr int kFwdChunkBytes = kFwdBc * kFwdDc * 2;
+
+template <int D>
+constexpr int fwd_ring_bytes() {
+  return 2 * (D / kFwdDc) * kFwdChunkBytes;
+}
+
+// Log2-domain threshold for the conditional rescale: the reference max is
+// moved only when a row max exceeds it by more than this, so P <= 2^8.
+constexpr float kRescaleTau = 8.0f;
+
+template <int D, bool BF16, bool ACC16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void fwd_prefill_kernel(FwdArgs a) {
+  static_assert(D % kFwdDc == 0, "D must be a multiple of 64");
+  using E = Elem<BF16>;
+  using V8 = typename E::vec8;
+  constexpr int NC = D / kFwdDc;       // chunks per tensor per tile
+  constexpr int NBUF = 2 * NC;         // ring slots: one tile of K and V
+  constexpr int LPW = kFwdChunkBytes / 1024 / kFwdWaves;  // copies per wave per chunk
+  constexpr int WAITN = (NBUF - 2) * LPW;
+  static_assert(WAITN < 64, "too many copies in flight");
+  constexpr int ROWB = kFwdDc * 2;     // bytes per LDS row
+  constexpr int NDB = D / 32;          // output d-blocks of 32
+
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // ---- workgroup -> (b, h, q-tile)
+  int t = xcd_logical(blockIdx.x, a.total_wg);
+  int qt = t % a.n_qtiles;
+  const int bh = t / a.n_qtiles;
+  if (a.causal) qt = a.n_qtiles - 1 - qt;  // longest rows first
+  const int h = bh % a.Hq, b = bh / a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int q0 = qt * kFwdRows;              // first row of the workgroup
+  const int qw = q0 + wave * 32;             // first row of this wave
+  const int my_q = qw + l32;                 // the row this lane accumulates
+
+  const typename E::scalar* Q = (const typename E::scalar*)a.q + ((size_t)(b * a.Hq + h) * a.Nq) * D;
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * a.Nkv) * D * 2;
+  const uint32_t kv_bytes = (uint32_t)a.Nkv * D * 2;  // rows >= Nkv read as zeros
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc((const char*)a.k + kv_off, kv_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc((const char*)a.v + kv_off, kv_bytes);
+
+  // ---- key range
+  int kv_end = a.Nkv;
+  if (a.causal) {
+    int last_q = min(q0 + kFwdRows, a.Nq) - 1;
+    kv_end = min(kv_end, last_q + 1);
+  }
+  const int n_tiles = (kv_end + kFwdBc - 1) / kFwdBc;
+
+  // ---- zero the ring once: every value a kernel reads from it is then finite
+  for (int i = threadIdx.x; i < fwd_ring_bytes<D>() / 16; i += 256)
+    *(FFPA_LDS u32x4*)(smem + 16 * i) = u32x4{0, 0, 0, 0};
+
+  // ---- stage the key bias [Nkv] in LDS (once; the host checks it fits)
+  const bool has_mask = a.mask_rows > 0;
+  FFPA_LDS uint16_t* bias_lds = (FFPA_LDS uint16_t*)(smem + fwd_ring_bytes<D>());
+  if (has_mask) {  // zero-padded to whole tiles; keys >= Nkv are masked anyway
+    const uint16_t* mk = (const uint16_t*)a.mask;
+    const int padded = ((a.Nkv + kFwdBc - 1) / kFwdBc) * kFwdBc;
+    for (int i = threadIdx.x; i < padded; i += 256) bias_lds[i] = i < a.Nkv ? mk[i] : (uint16_t)0;
+  }
+
+  // ---- Q^T operand in registers: lane holds Q[my_q][16 s + 8 hi .. +7]
+  V8 qf[D / 16];
+  {
+    const int qrow = min(my_q, a.Nq - 1);
+    const u32x4* qp = (const u32x4*)(Q + (size_t)qrow * D + 8 * hi);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[s] = as_vec8<V8>(qp[2 * s]);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // ---- per-lane constant parts of addresses
+  // Copy: instruction n of a chunk covers rows 8n .. 8n+7; lane -> row 8n + lane/8,
+  // stored granule lane%8, which holds logical granule (lane%8) ^ swz(row).
+  const int dma_row = lane >> 3;
+  const uint32_t dma_voff = (uint32_t)(dma_row * D + 8 * ((lane & 7) ^ swz(dma_row))) * 2;
+  // LDS read addresses are a per-lane base plus a compile-time offset below
+  // 64 KiB (the ds_read immediate): K slots start at 0, V slots at NC chunks.
+  // K fragment (A of S^T): row 32 kb + l32, granule (2 sl + hi) ^ swz(row).
+  uint32_t kaddr[kFwdDc / 16];
+  {
+    const int kswz = swz(l32);
+#pragma unroll
+    for (int sl = 0; sl < kFwdDc / 16; ++sl)
+      kaddr[sl] = (uint32_t)(l32 * ROWB + (((2 * sl + hi) ^ kswz) << 4));
+  }
+  // V^T fragment by transposed reads: group G = lane/16, i = lane%16 reads
+  // row 32 kb + 16 t2 + 8 r + 4 (G/2) + i/4, columns 32 dbl + 16 (G%2) + 4 (i%4).
+  uint32_t vaddr[kFwdDc / 32];
+  {
+    const int G = lane >> 4, gi = lane & 15;
+    const int vrow = 4 * (G >> 1) + (gi >> 2);
+    const int vswz = swz(vrow);
+    const int vgran = 2 * (G & 1) + ((gi & 3) >> 1);
+#pragma unroll
+    for (int dbl = 0; dbl < kFwdDc / 32; ++dbl)
+      vaddr[dbl] = (uint32_t)(NC * kFwdChunkBytes + vrow * ROWB +
+                              (((4 * dbl + vgran) ^ vswz) << 4) + (gi & 1) * 8);
+  }
+
+  auto issue_chunk = [&](int tile, int pos) {
+    tile = min(tile, n_tiles - 1);
+    const int c = pos < NC ? pos : pos - NC;
+#pragma unroll
+    for (int r = 0; r < LPW; ++r) {
+      const int n = wave + kFwdWaves * r;
+      const uint32_t soff = (uint32_t)((tile * kFwdBc + 8 * n) * D + c * kFwdDc) * 2;
+      dma16(pos < NC ? Kr : Vr, dma_voff, soff, smem + pos * kFwdChunkBytes + n * 1024);
+    }
+  };
+
+  // ---- accumulators
+  f32x16 o_acc[ACC16 ? 1 : NDB];
+  u32x4 o16[ACC16 ? NDB * 2 : 1];  // fp16 pairs: d-block db uses o16[2db], o16[2db+1]
+  if constexpr (!ACC16) {
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) o_acc[i] = f32x16{};
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2 * NDB; ++i) o16[i] = u32x4{0, 0, 0, 0};
+  }
+  float m_ref = -INFINITY;  // reference max (log2 domain)
+  float l_run = 0.f;        // ACC32: this lane's partial row sum; ACC16: full row sum
+
+  // ---- prologue: chunks 0 .. NBUF-2 of tile 0
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p) issue_chunk(0, p);
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int j0 = j * kFwdBc;
+    f32x16 s_acc[2] = {f32x16{}, f32x16{}};
+    // Opaque per iteration: keeps base + offset sums inside the loop, where
+    // they fold into the ds_read offset field instead of each holding a VGPR.
+#pragma unroll
+    for (int sl = 0; sl < kFwdDc / 16; ++sl) asm volatile("" : "+v"(kaddr[sl]));
+#pragma unroll
+    for (int dbl = 0; dbl < kFwdDc / 32; ++dbl) asm volatile("" : "+v"(vaddr[dbl]));
+    // The fp32 output accumulators live in AGPRs for the whole loop; the score
+    // accumulators and everything else use VGPRs.
+    if constexpr (!ACC16) {
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) asm volatile("" : "+a"(o_acc[d]));
+    }
+
+    // ===== S^T = K Q^T over the NC chunks of K
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      wait_vmcnt<WAITN>();
+      wait_lgkm0();
+      barrier();
+      if (c == 0) issue_chunk(j, NBUF - 1);
+      else issue_chunk(j + 1, c - 1);
+#pragma unroll
+      for (int sl = 0; sl < kFwdDc / 16; ++sl) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 kv = lds_read16(smem + kaddr[sl] + c * kFwdChunkBytes + 32 * kb * ROWB);
+          s_acc[kb] = E::mfma32(as_vec8<V8>(kv), qf[c * (kFwdDc / 16) + sl], s_acc[kb]);
+        }
+      }
+    }
+
+    // ===== online softmax on the tile (log2 domain)
+    const bool need_mask = has_mask || (j0 + kFwdBc > a.Nkv) ||
+                           (a.causal && j0 + kFwdBc - 1 > qw);
+    float tv[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tv[kb][i] = s_acc[kb][i] * a.scale_log2;
+    if (need_mask) {
+      // lane's keys: j0 + 4 hi + c, c = 32 kb + 8 (i / 4) + i % 4
+      const int kb0 = j0 + 4 * hi;
+      if (has_mask) {
+        // additive bias, four consecutive keys per 8-byte LDS read
+        const FFPA_LDS char* bp = (const FFPA_LDS char*)bias_lds + 2 * kb0;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const u32x2 w = *(const FFPA_LDS u32x2*)(bp + 2 * (32 * kb + 8 * g4));
+            tv[kb][4 * g4 + 0] += E::to_f32((uint16_t)(w[0] & 0xffff)) * kLog2e;
+            tv[kb][4 * g4 + 1] += E::to_f32((uint16_t)(w[0] >> 16)) * kLog2e;
+            tv[kb][4 * g4 + 2] += E::to_f32((uint16_t)(w[1] & 0xffff)) * kLog2e;
+            tv[kb][4 * g4 + 3] += E::to_f32((uint16_t)(w[1] >> 16)) * kLog2e;
+          }
+      }
+      // keys at or past the limit are dead: past Nkv, or after this row (causal)
+      int klim = a.Nkv - kb0;
+      if (a.causal) klim = min(klim, my_q + 1 - kb0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = 32 * kb + 8 * (i >> 2) + (i & 3);
+          tv[kb][i] = c >= klim ? -INFINITY : tv[kb][i];
+        }
+    }
+    float mx = tv[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, tv[kb][i]);
+    mx = fmaxf(mx, swap_halves(mx));
+
+    float alpha = 1.f;
+    const bool need = mx > m_ref + kRescaleTau;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {  // wave-uniform branch
+      const float m_new = fmaxf(m_ref, mx);
+      alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_ref - m_new);
+      m_ref = m_new;
+      if constexpr (!ACC16) {
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) scale_agpr16(o_acc[d], alpha);
+      }
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        tv[kb][i] = exp2_fast(tv[kb][i] - m_use);
+        psum += tv[kb][i];
+      }
+    float pscale = 1.f, oscale = 1.f;
+    if constexpr (!ACC16) {
+      l_run += psum;
+    } else {
+      // normalised fp16 accumulator: O <- O * (alpha l_old / l_new) + (P / l_new) V
+      const float l_old = l_run;
+      const float l_new = alpha * l_old + psum + swap_halves(psum);
+      l_run = l_new;
+      pscale = l_new > 0.f ? 1.f / l_new : 0.f;
+      oscale = alpha * l_old * pscale;
+    }
+    V8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const float* x = &tv[kb][8 * t2];
+        if constexpr (ACC16) {
+          pf[kb][t2] = pack8<BF16>(x[0] * pscale, x[1] * pscale, x[2] * pscale, x[3] * pscale,
+                                   x[4] * pscale, x[5] * pscale, x[6] * pscale, x[7] * pscale);
+        } else {
+          pf[kb][t2] = pack8<BF16>(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+        }
+      }
+
+    // ===== O^T += V^T P^T over the NC chunks of V
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      wait_vmcnt<WAITN>();
+      wait_lgkm0();
+      barrier();
+      issue_chunk(j + 1, NC + c - 1);
+#pragma unroll
+      for (int dbl = 0; dbl < kFwdDc / 32; ++dbl) {
+        const int db = c * (kFwdDc / 32) + dbl;
+        f32x16 acc;
+        if constexpr (ACC16) acc = f32x16{};
+        else acc = o_acc[db];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) {
+            const FFPA_LDS char* p = smem + vaddr[dbl] + c * kFwdChunkBytes + (32 * kb + 16 * t2) * ROWB;
+            const i16x4 lo = lds_read_tr(p);
+            const i16x4 hi8 = lds_read_tr(p + 8 * ROWB);
+            acc = E::mfma32(as_vec8<V8>(join8(lo, hi8)), pf[kb][t2], acc);
+          }
+        if constexpr (ACC16) {
+          // o16 <- o16 * oscale + acc, in packed fp16
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            u32x4 w = o16[2 * db + hh];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              f16x2 cur = f16x2_from_bits(w[e]);
+              f16x2 add = {(_Float16)acc[8 * hh + 2 * e], (_Float16)acc[8 * hh + 2 * e + 1]};
+              f16x2 sc = {(_Float16)oscale, (_Float16)oscale};
+              cur = cur * sc + add;
+              w[e] = __builtin_bit_cast(uint32_t, cur);
+            }
+            o16[2 * db + hh] = w;
+          }
+        } else {
+          o_acc[db] = acc;
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no copy may still target this workgroup's LDS when it ends
+
+  // ===== epilogue: normalise, store O and lse
+  float l_tot, inv;
+  if constexpr (!ACC16) {
+    l_tot = l_run + swap_halves(l_run);
+    inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  } else {
+    l_tot = l_run;
+    inv = 1.f;
+  }
+  if (my_q < a.Nq) {
+    typename E::scalar* O = (typename E::scalar*)a.o + ((size_t)(b * a.Hq + h) * a.Nq + my_q) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float x0, x1, x2, x3;
+        if constexpr (!ACC16) {
+          x0 = o_acc[db][4 * g4 + 0] * inv;
+          x1 = o_acc[db][4 * g4 + 1] * inv;
+          x2 = o_acc[db][4 * g4 + 2] * inv;
+          x3 = o_acc[db][4 * g4 + 3] * inv;
+        } else {
+          const u32x4 w = o16[2 * db + (g4 >> 1)];
+          const f16x2 p0 = f16x2_from_bits(w[2 * (g4 & 1)]);
+          const f16x2 p1 = f16x2_from_bits(w[2 * (g4 & 1) + 1]);
+          x0 = (float)p0[0];
+          x1 = (float)p0[1];
+          x2 = (float)p1[0];
+          x3 = (float)p1[1];
+        }
+        u32x2 st = {E::pack2(x0, x1), E::pack2(x2, x3)};
+        const int d = 32 * db + 8 * g4 + 4 * hi;
+        *(u32x2*)(O + d) = st;
+      }
+    }
+    if (a.lse != nullptr && hi == 0) {
+      float* L = a.lse + (size_t)(b * a.Hq + h) * a.Nq + my_q;
+      *L = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// Host launcher. lds_bytes = ring + key-bias bytes (the caller checks <= 160 KiB).
+template <int D, bool BF16, bool ACC16>
+hipError_t launch_fwd_prefill(const FwdArgs& a, size_t lds_bytes, hipStream_t stream) {
+  auto kern = fwd_prefill_kernel<D, BF16, ACC16>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(a.total_wg), dim3(256), lds_bytes, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ffpa

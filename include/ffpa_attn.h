@@ -1,0 +1,139 @@
+/*
+ * ffpa_attn.h - C ABI of the large-head-dimension fused attention library
+ * (libffpa_attn.so, hand-written HIP kernels for AMD MI355X / gfx950).
+ *
+ * Operation. The forward computes, for every batch b and query head h,
+ *     O[b,h] = softmax(scale * Q[b,h] K[b,hk]^T + mask) V[b,hk],   hk = h / (Hq / Hkv)
+ * and the natural-log log-sum-exp of each row of the scaled, masked scores.
+ *  - The definition is the materialised attention listed as "naive_math" in
+ *    section "3. Attention Variants" of the attention-kernel-profiler design
+ *    document (scores = Q K^T / sqrt(d_head), mask, softmax, attn V); the
+ *    scale is an argument here (callers normally pass 1/sqrt(D)).
+ *  - The additive mask is the one of "FFPA Attention Benchmark"
+ *    (ffpa-attn.readthedocs.io), section "Quick Start": a compact key-position
+ *    bias of shape [1,1,1,Nkv] (mask_rows = 1), or a per-query bias
+ *    [1,1,Nq,Nkv] (mask_rows = Nq). It is added to the scaled scores.
+ *  - Grouped-query attention maps query head h to K/V head h / (Hq/Hkv), the
+ *    repeat_interleave convention of "gqa_4kv" in the same section 3.
+ *  - The cases served are those of the benchmark tables in section "More
+ *    Benchmark" of "FFPA Attention Benchmark": self-attn, cross-attn
+ *    (Nq != Nkv), decode-attn (Nq = 1), gqa, causal, attn-mask and
+ *    non-aligned lengths, at head dimensions well above 256 (D = 320 ... 1024,
+ *    "FFPA-Attn Performance Benchmarks on Lambda.ai", sections 1-3).
+ *  - The backward returns dQ, dK, dV: the "standard 5 GEMMs" backward named in
+ *    "More Benchmark" (P recomputed from Q, K and the forward's lse).
+ *
+ * Readings taken where the pages say nothing:
+ *  - causal masking is top-left aligned: query i sees keys j <= i, also when
+ *    Nq != Nkv (so a lone decode query sees key 0 only);
+ *  - a query row whose every score is -inf gets O = 0 and lse = -inf;
+ *  - lse is natural-log and includes scale and mask;
+ *  - "fp16 accumulation" (FFPA_ACC_F16): gfx950 has no MFMA with an fp16
+ *    result, so scores and every MFMA partial stay fp32; the running output
+ *    accumulator is held in fp16, kept normalised so it cannot overflow.
+ *
+ * Layout. All tensors are dense, row-major and contiguous:
+ *   q, o, dout, dq : [B, Hq,  Nq,  D]  (element type = dtype)
+ *   k, v, dk, dv   : [B, Hkv, Nkv, D]  (element type = dtype)
+ *   lse            : [B, Hq,  Nq]      float32
+ *   mask           : [mask_rows, Nkv]  (element type = dtype, -inf allowed)
+ * Element type: FFPA_F16 = IEEE binary16, FFPA_BF16 = bfloat16.
+ * Outputs are rounded to nearest even.
+ *
+ * Ownership and memory. Every tensor pointer is a DEVICE pointer owned by the
+ * caller; the library never allocates or frees device memory. Pointers must
+ * be 16-byte aligned. Scratch space, when an entry point needs it, is passed
+ * by the caller as (workspace, workspace_bytes); its size comes from the
+ * matching *_workspace_size query. It need not be initialised.
+ *
+ * Execution. Entry points validate their arguments, then only enqueue kernels
+ * on `stream` (a hipStream_t; NULL = the default stream) and return. FFPA_OK
+ * means "launched"; faults on the device surface at the caller's next
+ * synchronisation. Calls that share a workspace must be ordered on one stream.
+ *
+ * Errors. On any non-OK status nothing has been enqueued and no output has
+ * been written; ffpa_last_error() returns a thread-local message. Arguments
+ * are checked in this order: null required pointer, sizes < 1,
+ * Hq % Hkv != 0, causal not 0/1, mask_rows not in {1, Nq} with a mask present
+ * (FFPA_ERR_INVALID_ARG); dtype, accumulator or D not supported
+ * (FFPA_ERR_UNSUPPORTED); a pointer not 16-byte aligned or a NaN scale
+ * (FFPA_ERR_INVALID_ARG); workspace too small (FFPA_ERR_WORKSPACE); a shape
+ * the built kernels do not cover (FFPA_ERR_UNSUPPORTED); a HIP launch error
+ * (FFPA_ERR_HIP).
+ *
+ * Threading. The library holds no mutable global state besides the
+ * thread-local error message; all entry points are reentrant.
+ */
+#ifndef FFPA_ATTN_H_
+#define FFPA_ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FFPA_F16 = 0, FFPA_BF16 = 1 } ffpa_dtype_t;
+typedef enum { FFPA_ACC_F32 = 0, FFPA_ACC_F16 = 1 } ffpa_accum_t;
+typedef enum {
+  FFPA_OK = 0,
+  FFPA_ERR_INVALID_ARG = 1,
+  FFPA_ERR_UNSUPPORTED = 2,
+  FFPA_ERR_WORKSPACE = 3,
+  FFPA_ERR_HIP = 4
+} ffpa_status_t;
+
+/* Largest supported head dimension; D must be a multiple of 32 in [32, 1024]. */
+#define FFPA_MAX_HEAD_DIM 1024
+
+/*
+ * Forward attention.
+ *   q, k, v   : inputs (layout above).
+ *   o         : output [B, Hq, Nq, D], written in full.
+ *   lse       : output [B, Hq, Nq] float32, or NULL to skip it.
+ *   scale     : multiplies Q K^T before the mask is added (usually 1/sqrt(D)).
+ *   causal    : 0 or 1 (top-left aligned).
+ *   mask      : NULL, or an additive mask [mask_rows, Nkv] with mask_rows 1 or Nq.
+ *   accum_dtype : FFPA_ACC_F32 or FFPA_ACC_F16 (see the reading above).
+ *   dtype     : FFPA_F16 or FFPA_BF16, for q, k, v, mask and o.
+ *   workspace : device scratch of at least ffpa_attn_fwd_workspace_size(...)
+ *               bytes (NULL allowed when that size is 0). Used by the
+ *               split-KV decode path for partial outputs.
+ *   stream    : hipStream_t to enqueue on.
+ */
+int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
+                  const void* mask, int mask_rows, int accum_dtype, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace ffpa_attn_fwd needs for these sizes (0 if none). */
+size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
+
+/*
+ * Backward attention: given dout = dL/dO, writes dq, dk, dv (same dtype and
+ * layout as q, k, v). o and lse must be the forward's outputs for the same
+ * q, k, v, scale, causal and mask. dk and dv of a K/V head sum the
+ * contributions of all query heads that share it. accum_dtype must be
+ * FFPA_ACC_F32. workspace: at least ffpa_attn_bwd_workspace_size(...) bytes
+ * (holds delta_i = sum_d dO_id O_id and float32 partial gradients).
+ */
+int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv,
+                  int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
+                  const void* mask, int mask_rows, int accum_dtype, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace ffpa_attn_bwd needs for these sizes. */
+size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
+
+/* Thread-local message describing the last non-OK status ("" if none). */
+const char* ffpa_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int ffpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFPA_ATTN_H_ */

