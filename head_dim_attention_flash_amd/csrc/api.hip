@@ -104,13 +104,13 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   size_t ring = 0;
   FwdLauncher launch = fwd_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, &ring);
   if (launch == nullptr) return fail(FFPA_ERR_UNSUPPORTED, "this head dimension is not built yet");
-  size_t lds = ring;
+  size_t lds = ring + ffpa::kFwdFlagBytes;
   if (mask != nullptr) {
     if (mask_rows != 1)
       return fail(FFPA_ERR_UNSUPPORTED, "per-query masks [Nq, Nkv] are not supported yet");
-    lds += ((size_t)(Nkv + ffpa::kFwdBc - 1) / ffpa::kFwdBc) * ffpa::kFwdBc * 2;
+    lds += (size_t)ffpa::fwd_bias_bytes(Nkv);
     if (lds > kLdsLimit)
-      return fail(FFPA_ERR_UNSUPPORTED, "key bias does not fit in LDS beside the K/V ring");
+      return fail(FFPA_ERR_UNSUPPORTED, "key bias does not fit in LDS beside the K/V tiles");
   }
 
   ffpa::FwdArgs a{};

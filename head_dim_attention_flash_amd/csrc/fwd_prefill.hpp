@@ -1,5 +1,5 @@
-// Forward attention kernel for 32-query-per-wave tiles (D <= 512 with an fp32
-// output accumulator, D <= 768 with an fp16 one).
+// Forward attention kernel, 32 query rows per wave (head dimensions that are
+// multiples of 64, up to 512).
 //
 // What it computes: O = softmax(scale * Q K^T + mask) V and lse per row, the
 // "naive_math" definition of section 3 of the attention-kernel-profiler design
@@ -15,14 +15,14 @@
 // so that each lane's accumulators all belong to one query row (l % 32): the
 // online-softmax rescale is a per-lane scalar and P goes from the S
 // accumulators into the B operand of the second MFMA without leaving
-// registers. V^T is read from a row-major V tile with ds_read_b64_tr_b16.
+// registers. V^T is read from the row-major V tile with ds_read_b64_tr_b16.
 //
-// K and V tiles reach LDS in chunks of 64 rows x 64 columns (8 KiB) by
-// direct global->LDS copies; a ring of 2 * D/64 slots holds one whole tile of
-// K and V, and the copy of chunk u + ring - 1 is issued while chunk u is
-// consumed. Tiles past the last one re-read the last tile, so that every wave
-// always has the same number of copies in flight (the wait counts are
-// compile-time constants).
+// Staging: one LDS buffer holds the K tile (64 x D), another the V tile, both
+// swizzled. The copy of V(j) is issued when the K(j) phase starts and the copy
+// of K(j+1) when the V(j) phase starts, so each copy has one phase of MFMA
+// work to land, and a tile costs two workgroup barriers. Copies go straight
+// from global memory to LDS (buffer_load ... lds) through a buffer resource
+// whose range ends at row Nkv, so rows past the end read as zeros.
 #pragma once
 
 #include "ffpa_common.hpp"
@@ -37,7 +37,7 @@ struct FwdArgs {
   float* lse;         // may be null
   const void* mask;   // may be null
   int B, Hq, Hkv, Nq, Nkv;
-  int mask_rows;      // 0 (none) or 1 (key bias, staged in LDS after the ring)
+  int mask_rows;      // 0 (none) or 1 (key bias, staged in LDS after the tiles)
   int causal;
   float scale_log2;   // scale * log2(e)
   int n_qtiles;
@@ -47,31 +47,45 @@ struct FwdArgs {
 constexpr int kFwdWaves = 4;
 constexpr int kFwdRows = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBc = 64;                // keys per tile
-constexpr int kFwdDc = 64;                // columns per LDS chunk
-constexpr int kFwdChunkBytes = kFwdBc * kFwdDc * 2;
 
+// LDS bytes of the K and V tile buffers.
 template <int D>
 constexpr int fwd_ring_bytes() {
-  return 2 * (D / kFwdDc) * kFwdChunkBytes;
+  return 2 * kFwdBc * D * 2;
 }
+// LDS bytes of the staged key bias (zero-padded to whole tiles).
+__host__ __device__ inline int fwd_bias_bytes(int nkv) { return ((nkv + kFwdBc - 1) / kFwdBc) * kFwdBc * 2; }
+// LDS bytes after the buffers and the bias: four restart flags.
+constexpr int kFwdFlagBytes = 16;
 
-// Log2-domain threshold for the conditional rescale: the reference max is
-// moved only when a row max exceeds it by more than this, so P <= 2^8.
-constexpr float kRescaleTau = 8.0f;
+// Online softmax without rescaling the fp32 output accumulators.
+// Each row keeps a reference max m_ref (log2 domain) and accumulates
+// P = 2^(t - m_ref). m_ref is set from the first tile in which the row sees an
+// unmasked key. As long as every later score stays below m_ref + tau, P stays
+// within 2^tau (representable in the MFMA operand type) and no accumulator
+// ever needs a rescale. A tile that breaks the bound makes the whole
+// workgroup restart its key loop with O and l zeroed and the raised m_ref;
+// every restart lifts a row's reference by more than tau, so there are at most
+// (range of the scores) / tau of them (none on typical data). The fp16
+// accumulator path instead renormalises every tile (its scale is a VGPR op).
+template <bool BF16>
+constexpr float fwd_tau() {
+  return BF16 ? 60.0f : 15.0f;  // P <= 2^15 < 65504 (fp16); bf16 has fp32's range
+}
+constexpr float kRescaleTau = 8.0f;  // fp16-accumulator path: move m_ref past this
 
 template <int D, bool BF16, bool ACC16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fwd_prefill_kernel(FwdArgs a) {
-  static_assert(D % kFwdDc == 0, "D must be a multiple of 64");
+  static_assert(D % 64 == 0 && D <= 512, "D must be a multiple of 64, at most 512");
   using E = Elem<BF16>;
   using V8 = typename E::vec8;
-  constexpr int NC = D / kFwdDc;       // chunks per tensor per tile
-  constexpr int NBUF = 2 * NC;         // ring slots: one tile of K and V
-  constexpr int LPW = kFwdChunkBytes / 1024 / kFwdWaves;  // copies per wave per chunk
-  constexpr int WAITN = (NBUF - 2) * LPW;
-  static_assert(WAITN < 64, "too many copies in flight");
-  constexpr int ROWB = kFwdDc * 2;     // bytes per LDS row
-  constexpr int NDB = D / 32;          // output d-blocks of 32
+  constexpr int ROWB = D * 2;             // bytes per LDS row
+  constexpr int GPR = D / 8;              // 16-byte granules per row
+  constexpr int TILEB = kFwdBc * ROWB;    // bytes per tile buffer
+  constexpr int NDMA = TILEB / 1024 / kFwdWaves;  // copies per wave per tile
+  constexpr int NDB = D / 32;             // output d-blocks of 32
+  constexpr int KB = 0, VB = TILEB;       // buffer offsets
 
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
@@ -105,14 +119,11 @@ void fwd_prefill_kernel(FwdArgs a) {
   }
   const int n_tiles = (kv_end + kFwdBc - 1) / kFwdBc;
 
-  // ---- zero the ring once: every value a kernel reads from it is then finite
-  for (int i = threadIdx.x; i < fwd_ring_bytes<D>() / 16; i += 256)
-    *(FFPA_LDS u32x4*)(smem + 16 * i) = u32x4{0, 0, 0, 0};
-
-  // ---- stage the key bias [Nkv] in LDS (once; the host checks it fits)
+  // ---- stage the key bias [Nkv] in LDS (once; the host checks it fits),
+  // zero-padded to whole tiles: keys >= Nkv are masked anyway
   const bool has_mask = a.mask_rows > 0;
   FFPA_LDS uint16_t* bias_lds = (FFPA_LDS uint16_t*)(smem + fwd_ring_bytes<D>());
-  if (has_mask) {  // zero-padded to whole tiles; keys >= Nkv are masked anyway
+  if (has_mask) {
     const uint16_t* mk = (const uint16_t*)a.mask;
     const int padded = ((a.Nkv + kFwdBc - 1) / kFwdBc) * kFwdBc;
     for (int i = threadIdx.x; i < padded; i += 256) bias_lds[i] = i < a.Nkv ? mk[i] : (uint16_t)0;
@@ -129,45 +140,44 @@ void fwd_prefill_kernel(FwdArgs a) {
   wait_vmcnt<0>();
   __syncthreads();
 
-  // ---- per-lane constant parts of addresses
-  // Copy: instruction n of a chunk covers rows 8n .. 8n+7; lane -> row 8n + lane/8,
-  // stored granule lane%8, which holds logical granule (lane%8) ^ swz(row).
-  const int dma_row = lane >> 3;
-  const uint32_t dma_voff = (uint32_t)(dma_row * D + 8 * ((lane & 7) ^ swz(dma_row))) * 2;
-  // LDS read addresses are a per-lane base plus a compile-time offset below
-  // 64 KiB (the ds_read immediate): K slots start at 0, V slots at NC chunks.
-  // K fragment (A of S^T): row 32 kb + l32, granule (2 sl + hi) ^ swz(row).
-  uint32_t kaddr[kFwdDc / 16];
-  {
-    const int kswz = swz(l32);
+  // ---- copy of one tile of K or V into its buffer. Copy instruction n of a
+  // tile (n = wave + 4 r) fills LDS bytes [1024 n, 1024 n + 1024) of the
+  // buffer: 16-byte granule L = 64 n + lane, stored at row L / GPR, slot
+  // L % GPR, holding the logical granule (slot ^ swz(row)) of that row.
+  auto issue_tile = [&](__amdgpu_buffer_rsrc_t rs, int buf, int tile) {
+    const uint32_t soff = (uint32_t)tile * kFwdBc * ROWB;
+    // recomputed at each call (a few VALU ops per copy) rather than held in
+    // NDMA live registers across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int sl = 0; sl < kFwdDc / 16; ++sl)
-      kaddr[sl] = (uint32_t)(l32 * ROWB + (((2 * sl + hi) ^ kswz) << 4));
-  }
-  // V^T fragment by transposed reads: group G = lane/16, i = lane%16 reads
-  // row 32 kb + 16 t2 + 8 r + 4 (G/2) + i/4, columns 32 dbl + 16 (G%2) + 4 (i%4).
-  uint32_t vaddr[kFwdDc / 32];
+    for (int r = 0; r < NDMA; ++r) {
+      const int n = wave + kFwdWaves * r;
+      const int L = 64 * n + ln;
+      const int row = L / GPR, slot = L % GPR;
+      const uint32_t voff = (uint32_t)(row * ROWB + ((slot ^ swz(row)) << 4));
+      dma16(rs, voff, soff, smem + buf + n * 1024);
+    }
+  };
+
+  // ---- LDS read addresses: a per-lane base plus compile-time offsets < 64 KiB
+  // K fragment (A of S^T) for d-step s = 4 a + c: row 32 kb + l32, granule
+  // 8 a + ((2 c + hi) ^ swz(row)).
+  uint32_t kaddr[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) kaddr[c] = (uint32_t)(KB + l32 * ROWB + (((2 * c + hi) ^ swz(l32)) << 4));
+  // V^T fragment by transposed reads: group G = lane/16, i = lane%16 reads row
+  // 32 kb + 16 t2 + 8 r + 4 (G/2) + i/4 at columns 32 db + 16 (G%2) + 4 (i%4),
+  // i.e. granule 8 (db/2) + ((4 (db%2) + y) ^ swz(row)) with y = 2 (G%2) + (i%4)/2.
+  uint32_t vaddr[2];
   {
     const int G = lane >> 4, gi = lane & 15;
     const int vrow = 4 * (G >> 1) + (gi >> 2);
-    const int vswz = swz(vrow);
-    const int vgran = 2 * (G & 1) + ((gi & 3) >> 1);
+    const int y = 2 * (G & 1) + ((gi & 3) >> 1);
 #pragma unroll
-    for (int dbl = 0; dbl < kFwdDc / 32; ++dbl)
-      vaddr[dbl] = (uint32_t)(NC * kFwdChunkBytes + vrow * ROWB +
-                              (((4 * dbl + vgran) ^ vswz) << 4) + (gi & 1) * 8);
+    for (int e = 0; e < 2; ++e)
+      vaddr[e] = (uint32_t)(VB + vrow * ROWB + (((4 * e + y) ^ swz(vrow)) << 4) + (gi & 1) * 8);
   }
-
-  auto issue_chunk = [&](int tile, int pos) {
-    tile = min(tile, n_tiles - 1);
-    const int c = pos < NC ? pos : pos - NC;
-#pragma unroll
-    for (int r = 0; r < LPW; ++r) {
-      const int n = wave + kFwdWaves * r;
-      const uint32_t soff = (uint32_t)((tile * kFwdBc + 8 * n) * D + c * kFwdDc) * 2;
-      dma16(pos < NC ? Kr : Vr, dma_voff, soff, smem + pos * kFwdChunkBytes + n * 1024);
-    }
-  };
 
   // ---- accumulators
   f32x16 o_acc[ACC16 ? 1 : NDB];
@@ -181,20 +191,26 @@ void fwd_prefill_kernel(FwdArgs a) {
   }
   float m_ref = -INFINITY;  // reference max (log2 domain)
   float l_run = 0.f;        // ACC32: this lane's partial row sum; ACC16: full row sum
+  bool fresh = true;        // ACC32: no PV product accumulated yet in this attempt
+  // one word per wave: did a row of that wave break m_ref + tau in this tile
+  FFPA_LDS uint32_t* restart_flag = (FFPA_LDS uint32_t*)(smem + fwd_ring_bytes<D>() +
+                                                         (has_mask ? fwd_bias_bytes(a.Nkv) : 0));
 
-  // ---- prologue: chunks 0 .. NBUF-2 of tile 0
-#pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p) issue_chunk(0, p);
+  issue_tile(Kr, KB, 0);
 
   for (int j = 0; j < n_tiles; ++j) {
     const int j0 = j * kFwdBc;
-    f32x16 s_acc[2] = {f32x16{}, f32x16{}};
+    // per-lane values are re-derived from the lane id in each iteration (one
+    // live VGPR instead of several across the loop)
+    int lj = lane;
+    asm volatile("" : "+v"(lj));
+    const int hij = lj >> 5;
+    const int my_qj = qw + (lj & 31);
     // Opaque per iteration: keeps base + offset sums inside the loop, where
     // they fold into the ds_read offset field instead of each holding a VGPR.
 #pragma unroll
-    for (int sl = 0; sl < kFwdDc / 16; ++sl) asm volatile("" : "+v"(kaddr[sl]));
-#pragma unroll
-    for (int dbl = 0; dbl < kFwdDc / 32; ++dbl) asm volatile("" : "+v"(vaddr[dbl]));
+    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(kaddr[c]));
+    asm volatile("" : "+v"(vaddr[0]), "+v"(vaddr[1]));
     // The fp32 output accumulators live in AGPRs for the whole loop; the score
     // accumulators and everything else use VGPRs.
     if constexpr (!ACC16) {
@@ -202,21 +218,18 @@ void fwd_prefill_kernel(FwdArgs a) {
       for (int d = 0; d < NDB; ++d) asm volatile("" : "+a"(o_acc[d]));
     }
 
-    // ===== S^T = K Q^T over the NC chunks of K
+    // ===== K phase: S^T = K Q^T
+    wait_vmcnt<0>();  // K(j) landed (this wave's copies) ...
+    wait_lgkm0();
+    barrier();        // ... and everyone's; everyone is done with V(j-1)
+    issue_tile(Vr, VB, j);
+    f32x16 s_acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      wait_vmcnt<WAITN>();
-      wait_lgkm0();
-      barrier();
-      if (c == 0) issue_chunk(j, NBUF - 1);
-      else issue_chunk(j + 1, c - 1);
+    for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
-      for (int sl = 0; sl < kFwdDc / 16; ++sl) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 kv = lds_read16(smem + kaddr[sl] + c * kFwdChunkBytes + 32 * kb * ROWB);
-          s_acc[kb] = E::mfma32(as_vec8<V8>(kv), qf[c * (kFwdDc / 16) + sl], s_acc[kb]);
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 kv = lds_read16(smem + kaddr[s & 3] + 128 * (s >> 2) + 32 * kb * ROWB);
+        s_acc[kb] = E::mfma32(as_vec8<V8>(kv), qf[s], s_acc[kb]);
       }
     }
 
@@ -230,7 +243,7 @@ void fwd_prefill_kernel(FwdArgs a) {
       for (int i = 0; i < 16; ++i) tv[kb][i] = s_acc[kb][i] * a.scale_log2;
     if (need_mask) {
       // lane's keys: j0 + 4 hi + c, c = 32 kb + 8 (i / 4) + i % 4
-      const int kb0 = j0 + 4 * hi;
+      const int kb0 = j0 + 4 * hij;
       if (has_mask) {
         // additive bias, four consecutive keys per 8-byte LDS read
         const FFPA_LDS char* bp = (const FFPA_LDS char*)bias_lds + 2 * kb0;
@@ -247,7 +260,7 @@ void fwd_prefill_kernel(FwdArgs a) {
       }
       // keys at or past the limit are dead: past Nkv, or after this row (causal)
       int klim = a.Nkv - kb0;
-      if (a.causal) klim = min(klim, my_q + 1 - kb0);
+      if (a.causal) klim = min(klim, my_qj + 1 - kb0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -264,15 +277,19 @@ void fwd_prefill_kernel(FwdArgs a) {
     mx = fmaxf(mx, swap_halves(mx));
 
     float alpha = 1.f;
-    const bool need = mx > m_ref + kRescaleTau;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {  // wave-uniform branch
-      const float m_new = fmaxf(m_ref, mx);
-      alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_ref - m_new);
-      m_ref = m_new;
-      if constexpr (!ACC16) {
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) scale_agpr16(o_acc[d], alpha);
+    if constexpr (!ACC16) {
+      // first unmasked keys of this row: adopt their max (O and l are still 0)
+      if (m_ref == -INFINITY) m_ref = mx;
+      const bool broke = mx > m_ref + fwd_tau<BF16>();
+      // the ballot runs with the whole wave active; only the store is lane 0's
+      const uint32_t any_broke = __builtin_amdgcn_ballot_w64(broke) != 0 ? 1u : 0u;
+      if (lane == 0) restart_flag[wave] = any_broke;
+    } else {
+      const bool need = mx > m_ref + kRescaleTau;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {  // wave-uniform branch
+        const float m_new = fmaxf(m_ref, mx);
+        alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_ref - m_new);
+        m_ref = m_new;
       }
     }
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
@@ -309,52 +326,74 @@ void fwd_prefill_kernel(FwdArgs a) {
         }
       }
 
-    // ===== O^T += V^T P^T over the NC chunks of V
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      wait_vmcnt<WAITN>();
-      wait_lgkm0();
-      barrier();
-      issue_chunk(j + 1, NC + c - 1);
-#pragma unroll
-      for (int dbl = 0; dbl < kFwdDc / 32; ++dbl) {
-        const int db = c * (kFwdDc / 32) + dbl;
-        f32x16 acc;
-        if constexpr (ACC16) acc = f32x16{};
-        else acc = o_acc[db];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int t2 = 0; t2 < 2; ++t2) {
-            const FFPA_LDS char* p = smem + vaddr[dbl] + c * kFwdChunkBytes + (32 * kb + 16 * t2) * ROWB;
-            const i16x4 lo = lds_read_tr(p);
-            const i16x4 hi8 = lds_read_tr(p + 8 * ROWB);
-            acc = E::mfma32(as_vec8<V8>(join8(lo, hi8)), pf[kb][t2], acc);
-          }
-        if constexpr (ACC16) {
-          // o16 <- o16 * oscale + acc, in packed fp16
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            u32x4 w = o16[2 * db + hh];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              f16x2 cur = f16x2_from_bits(w[e]);
-              f16x2 add = {(_Float16)acc[8 * hh + 2 * e], (_Float16)acc[8 * hh + 2 * e + 1]};
-              f16x2 sc = {(_Float16)oscale, (_Float16)oscale};
-              cur = cur * sc + add;
-              w[e] = __builtin_bit_cast(uint32_t, cur);
-            }
-            o16[2 * db + hh] = w;
-          }
-        } else {
-          o_acc[db] = acc;
-        }
+    // ===== V phase: O^T += V^T P^T
+    wait_vmcnt<0>();  // V(j) landed ...
+    wait_lgkm0();
+    barrier();        // ... everywhere; everyone is done with K(j)
+    if constexpr (!ACC16) {
+      const u32x4 f = *(const FFPA_LDS u32x4*)restart_flag;
+      if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // workgroup-uniform
+        // restart with the raised reference; O restarts from zero through
+        // `fresh` (the next PV product ignores the old accumulators), which
+        // avoids writing 256 accumulator registers here
+        m_ref = fmaxf(m_ref, mx);
+        l_run = 0.f;
+        fresh = true;
+        issue_tile(Kr, KB, 0);
+        j = -1;
+        continue;
       }
     }
+    if (j + 1 < n_tiles) issue_tile(Kr, KB, j + 1);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      f32x16 acc;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const FFPA_LDS char* p = smem + vaddr[db & 1] + 128 * (db >> 1) + (32 * kb + 16 * t2) * ROWB;
+          const i16x4 lo = lds_read_tr(p);
+          const i16x4 hi8 = lds_read_tr(p + 8 * ROWB);
+          const V8 va = as_vec8<V8>(join8(lo, hi8));
+          if (kb == 0 && t2 == 0) {
+            if constexpr (ACC16) {
+              acc = E::mfma32(va, pf[0][0], f32x16{});
+            } else {
+              // two MFMAs on a uniform branch, both writing the accumulators:
+              // no select or copy of the AGPR tuple is needed
+              if (fresh) acc = E::mfma32(va, pf[0][0], f32x16{});
+              else acc = E::mfma32(va, pf[0][0], o_acc[db]);
+            }
+          } else {
+            acc = E::mfma32(va, pf[kb][t2], acc);
+          }
+        }
+      if constexpr (ACC16) {
+        // o16 <- o16 * oscale + acc, in packed fp16
+        const f16x2 sc = {(_Float16)oscale, (_Float16)oscale};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4 w = o16[2 * db + hh];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            f16x2 cur = f16x2_from_bits(w[e]);
+            const f16x2 add = {(_Float16)acc[8 * hh + 2 * e], (_Float16)acc[8 * hh + 2 * e + 1]};
+            cur = cur * sc + add;
+            w[e] = __builtin_bit_cast(uint32_t, cur);
+          }
+          o16[2 * db + hh] = w;
+        }
+      } else {
+        o_acc[db] = acc;
+      }
+    }
+    fresh = false;
   }
   wait_vmcnt<0>();  // no copy may still target this workgroup's LDS when it ends
 
   // ===== epilogue: normalise, store O and lse
+  const int le = threadIdx.x & 63, hie = le >> 5, my_qe = qw + (le & 31);
   float l_tot, inv;
   if constexpr (!ACC16) {
     l_tot = l_run + swap_halves(l_run);
@@ -363,8 +402,8 @@ void fwd_prefill_kernel(FwdArgs a) {
     l_tot = l_run;
     inv = 1.f;
   }
-  if (my_q < a.Nq) {
-    typename E::scalar* O = (typename E::scalar*)a.o + ((size_t)(b * a.Hq + h) * a.Nq + my_q) * D;
+  if (my_qe < a.Nq) {
+    typename E::scalar* O = (typename E::scalar*)a.o + ((size_t)(b * a.Hq + h) * a.Nq + my_qe) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -385,18 +424,19 @@ void fwd_prefill_kernel(FwdArgs a) {
           x3 = (float)p1[1];
         }
         u32x2 st = {E::pack2(x0, x1), E::pack2(x2, x3)};
-        const int d = 32 * db + 8 * g4 + 4 * hi;
+        const int d = 32 * db + 8 * g4 + 4 * hie;
         *(u32x2*)(O + d) = st;
       }
     }
-    if (a.lse != nullptr && hi == 0) {
-      float* L = a.lse + (size_t)(b * a.Hq + h) * a.Nq + my_q;
+    if (a.lse != nullptr && hie == 0) {
+      float* L = a.lse + (size_t)(b * a.Hq + h) * a.Nq + my_qe;
       *L = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }
 
-// Host launcher. lds_bytes = ring + key-bias bytes (the caller checks <= 160 KiB).
+// Host launcher. lds_bytes = tile buffers + key-bias bytes (the caller checks
+// <= 160 KiB).
 template <int D, bool BF16, bool ACC16>
 hipError_t launch_fwd_prefill(const FwdArgs& a, size_t lds_bytes, hipStream_t stream) {
   auto kern = fwd_prefill_kernel<D, BF16, ACC16>;

@@ -176,3 +176,21 @@ def test_deterministic(lib):
     o1, l1 = _run(lib, q, k, v, causal=True)
     o2, l2 = _run(lib, q, k, v, causal=True)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("slope", [0.05, 0.5])
+@pytest.mark.parametrize("D", [128, 512])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("accum", ["f32", "f16"])
+def test_growing_row_max(lib, slope, D, dtype, accum):
+    """A key-bias ramp raises every row's running max tile after tile (by up to
+    46 in log2 units per 64-key tile at slope 0.5), which forces the online
+    softmax off its first reference max again and again."""
+    q, k, v, _ = _inputs(13, 1, 2, 2, 200, 512, D, dtype)
+    ramp = (slope * torch.arange(512, dtype=torch.float32)).to(W.DTYPES[dtype])[None]
+    scale = 1.0 / math.sqrt(D)
+    for causal in (False, True):
+        o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), causal=causal, mask=ramp.cuda(),
+                      accum=accum, scale=scale)
+        _compare(o, lse, q, k, v, scale, causal, ramp, dtype, accum,
+                 f"ramp{slope}-D{D}-{dtype}-{accum}-causal{causal}")
