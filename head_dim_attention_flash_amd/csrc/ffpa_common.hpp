@@ -83,6 +83,77 @@ struct Elem<true> {
 // (every element of the vector then reads as element 0).
 __device__ inline f16x2 f16x2_from_bits(uint32_t bits) { return __builtin_bit_cast(f16x2, bits); }
 
+// ---------------------------------------------------------------------------
+// MFMA 32x32x16 issued as inline asm so that operand register files can be
+// chosen (the compiler will not feed an MFMA source from AGPRs by itself):
+// A in VGPRs, B in AGPRs (B_A) or VGPRs (B_V), C/D in AGPRs (C_A) or VGPRs
+// (C_V). The compiler does not know these are MFMAs, so hazards it would
+// otherwise pad are handled here:
+//  - an MFMA result read by a VALU or accvgpr instruction needs up to 19 wait
+//    states: the last MFMA of a chain is issued with mfma_last=true (pads 21);
+//  - a VALU write of an MFMA source needs a few wait states: a chain whose B
+//    operand was just written by VALU code starts with mfma_first=true (pads 4).
+// Back-to-back MFMAs whose C is exactly the previous D are interlocked by the
+// hardware. `zero` replaces C by the inline constant 0.
+// ---------------------------------------------------------------------------
+#define FFPA_MFMA_ASM(OPC, CA, BA, ZERO, PRE, POST)                                            \
+  if constexpr (ZERO)                                                                           \
+    asm volatile(PRE OPC " %0, %1, %2, 0" POST : "=&" CA(acc) : "v"(a), BA(b));                 \
+  else                                                                                          \
+    asm volatile(PRE OPC " %0, %1, %2, %0" POST : "+" CA(acc) : "v"(a), BA(b));
+template <bool BF16, bool B_AGPR, bool C_AGPR, bool ZERO = false, bool FIRST = false, bool LAST = false>
+__device__ inline void mfma32_asm(f32x16& acc, u32x4 a, u32x4 b) {
+#define FFPA_PRE (FIRST ? "s_nop 4\n" : "")
+  // PRE/POST must be string literals: select with constexpr branches
+  if constexpr (!BF16) {
+    if constexpr (FIRST && LAST) {
+      if constexpr (B_AGPR && C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "a", "a", ZERO, "s_nop 4\n", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else if constexpr (B_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "v", "a", ZERO, "s_nop 4\n", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else if constexpr (C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "a", "v", ZERO, "s_nop 4\n", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "v", "v", ZERO, "s_nop 4\n", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+    } else if constexpr (FIRST) {
+      if constexpr (B_AGPR && C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "a", "a", ZERO, "s_nop 4\n", "") }
+      else if constexpr (B_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "v", "a", ZERO, "s_nop 4\n", "") }
+      else if constexpr (C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "a", "v", ZERO, "s_nop 4\n", "") }
+      else { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "v", "v", ZERO, "s_nop 4\n", "") }
+    } else if constexpr (LAST) {
+      if constexpr (B_AGPR && C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "a", "a", ZERO, "", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else if constexpr (B_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "v", "a", ZERO, "", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else if constexpr (C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "a", "v", ZERO, "", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "v", "v", ZERO, "", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+    } else {
+      if constexpr (B_AGPR && C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "a", "a", ZERO, "", "") }
+      else if constexpr (B_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "v", "a", ZERO, "", "") }
+      else if constexpr (C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "a", "v", ZERO, "", "") }
+      else { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_f16", "v", "v", ZERO, "", "") }
+    }
+  } else {
+    if constexpr (FIRST && LAST) {
+      if constexpr (B_AGPR && C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "a", "a", ZERO, "s_nop 4\n", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else if constexpr (B_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "v", "a", ZERO, "s_nop 4\n", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else if constexpr (C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "a", "v", ZERO, "s_nop 4\n", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "v", "v", ZERO, "s_nop 4\n", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+    } else if constexpr (FIRST) {
+      if constexpr (B_AGPR && C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "a", "a", ZERO, "s_nop 4\n", "") }
+      else if constexpr (B_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "v", "a", ZERO, "s_nop 4\n", "") }
+      else if constexpr (C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "a", "v", ZERO, "s_nop 4\n", "") }
+      else { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "v", "v", ZERO, "s_nop 4\n", "") }
+    } else if constexpr (LAST) {
+      if constexpr (B_AGPR && C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "a", "a", ZERO, "", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else if constexpr (B_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "v", "a", ZERO, "", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else if constexpr (C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "a", "v", ZERO, "", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+      else { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "v", "v", ZERO, "", "\n s_nop 7\n s_nop 7\n s_nop 4") }
+    } else {
+      if constexpr (B_AGPR && C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "a", "a", ZERO, "", "") }
+      else if constexpr (B_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "v", "a", ZERO, "", "") }
+      else if constexpr (C_AGPR) { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "a", "v", ZERO, "", "") }
+      else { FFPA_MFMA_ASM("v_mfma_f32_32x32x16_bf16", "v", "v", ZERO, "", "") }
+    }
+  }
+#undef FFPA_PRE
+}
+#undef FFPA_MFMA_ASM
+
 template <class V>
 __device__ inline V as_vec8(u32x4 x) {
   return __builtin_bit_cast(V, x);

@@ -86,6 +86,10 @@ void fwd_prefill_kernel(FwdArgs a) {
   constexpr int NDMA = TILEB / 1024 / kFwdWaves;  // copies per wave per tile
   constexpr int NDB = D / 32;             // output d-blocks of 32
   constexpr int KB = 0, VB = TILEB;       // buffer offsets
+  constexpr int kKAhead = 3;              // K-fragment read-ahead, in d-steps
+  // fp32 accumulator d-blocks that share the AGPRs with the Q fragments; the
+  // remaining blocks live in VGPRs
+  constexpr int kOAgpr = (256 - D / 4) / 16 < NDB ? (256 - D / 4) / 16 : NDB;
 
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
@@ -130,12 +134,12 @@ void fwd_prefill_kernel(FwdArgs a) {
   }
 
   // ---- Q^T operand in registers: lane holds Q[my_q][16 s + 8 hi .. +7]
-  V8 qf[D / 16];
+  u32x4 qf[D / 16];  // raw bits; kept in AGPRs as the B operand of the K-phase MFMAs
   {
     const int qrow = min(my_q, a.Nq - 1);
     const u32x4* qp = (const u32x4*)(Q + (size_t)qrow * D + 8 * hi);
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = as_vec8<V8>(qp[2 * s]);
+    for (int s = 0; s < D / 16; ++s) qf[s] = qp[2 * s];
   }
   wait_vmcnt<0>();
   __syncthreads();
@@ -211,11 +215,16 @@ void fwd_prefill_kernel(FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(kaddr[c]));
     asm volatile("" : "+v"(vaddr[0]), "+v"(vaddr[1]));
-    // The fp32 output accumulators live in AGPRs for the whole loop; the score
-    // accumulators and everything else use VGPRs.
+    // Register placement for the whole loop. The Q fragments (read-only MFMA
+    // operands) live in AGPRs; the fp32 output accumulators fill the rest of
+    // the AGPRs and spill over into VGPRs. VGPRs then keep room for the score
+    // accumulators and for K/V fragments read ahead from LDS.
     if constexpr (!ACC16) {
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) asm volatile("" : "+a"(o_acc[d]));
+      for (int d = 0; d < NDB; ++d) {
+        if (d < kOAgpr) asm volatile("" : "+a"(o_acc[d]));
+        else asm volatile("" : "+v"(o_acc[d]));
+      }
     }
 
     // ===== K phase: S^T = K Q^T
@@ -223,13 +232,38 @@ void fwd_prefill_kernel(FwdArgs a) {
     wait_lgkm0();
     barrier();        // ... and everyone's; everyone is done with V(j-1)
     issue_tile(Vr, VB, j);
-    f32x16 s_acc[2] = {f32x16{}, f32x16{}};
+    f32x16 s_acc[2];
+    {
+      // K fragments are read kKAhead d-steps ahead of the MFMAs that use them
+      constexpr int NS = D / 16;
+      u32x4 kf[kKAhead][2];
+      auto kread = [&](int st, int kb) {
+        return lds_read16(smem + kaddr[st & 3] + 128 * (st >> 2) + 32 * kb * ROWB);
+      };
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
+      for (int st = 0; st < kKAhead; ++st) {
+        kf[st][0] = kread(st, 0);
+        kf[st][1] = kread(st, 1);
+      }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 kv = lds_read16(smem + kaddr[s & 3] + 128 * (s >> 2) + 32 * kb * ROWB);
-        s_acc[kb] = E::mfma32(as_vec8<V8>(kv), qf[s], s_acc[kb]);
+      for (int st = 0; st < NS; ++st) {
+        const u32x4 a0 = kf[st % kKAhead][0], a1 = kf[st % kKAhead][1];
+        if (st + kKAhead < NS) {
+          kf[st % kKAhead][0] = kread(st + kKAhead, 0);
+          kf[st % kKAhead][1] = kread(st + kKAhead, 1);
+        }
+        // S^T chains in VGPRs, Q operand from AGPRs; the last pair pads for the
+        // softmax VALU that reads the scores next
+        if (st == 0) {
+          mfma32_asm<BF16, true, false, true>(s_acc[0], a0, qf[st]);
+          mfma32_asm<BF16, true, false, true>(s_acc[1], a1, qf[st]);
+        } else if (st == NS - 1) {
+          mfma32_asm<BF16, true, false, false>(s_acc[0], a0, qf[st]);
+          mfma32_asm<BF16, true, false, false, false, true>(s_acc[1], a1, qf[st]);
+        } else {
+          mfma32_asm<BF16, true, false>(s_acc[0], a0, qf[st]);
+          mfma32_asm<BF16, true, false>(s_acc[1], a1, qf[st]);
+        }
       }
     }
 
@@ -355,18 +389,38 @@ void fwd_prefill_kernel(FwdArgs a) {
           const FFPA_LDS char* p = smem + vaddr[db & 1] + 128 * (db >> 1) + (32 * kb + 16 * t2) * ROWB;
           const i16x4 lo = lds_read_tr(p);
           const i16x4 hi8 = lds_read_tr(p + 8 * ROWB);
-          const V8 va = as_vec8<V8>(join8(lo, hi8));
-          if (kb == 0 && t2 == 0) {
-            if constexpr (ACC16) {
-              acc = E::mfma32(va, pf[0][0], f32x16{});
-            } else {
-              // two MFMAs on a uniform branch, both writing the accumulators:
-              // no select or copy of the AGPR tuple is needed
-              if (fresh) acc = E::mfma32(va, pf[0][0], f32x16{});
-              else acc = E::mfma32(va, pf[0][0], o_acc[db]);
-            }
+          const u32x4 vbits = join8(lo, hi8);
+          if constexpr (ACC16) {
+            if (kb == 0 && t2 == 0) acc = E::mfma32(as_vec8<V8>(vbits), pf[0][0], f32x16{});
+            else acc = E::mfma32(as_vec8<V8>(vbits), pf[kb][t2], acc);
           } else {
-            acc = E::mfma32(va, pf[kb][t2], acc);
+            const u32x4 pb = __builtin_bit_cast(u32x4, pf[kb][t2]);
+            if (kb == 0 && t2 == 0) {
+              acc = o_acc[db];
+              // two MFMAs on a uniform branch, both writing the accumulators:
+              // no select or copy of the tuple is needed. The first MFMA of
+              // the phase pads for the VALU that wrote P.
+              if (db < kOAgpr) {
+                if (db == 0) {
+                  if (fresh) mfma32_asm<BF16, false, true, true, true>(acc, vbits, pb);
+                  else mfma32_asm<BF16, false, true, false, true>(acc, vbits, pb);
+                } else {
+                  if (fresh) mfma32_asm<BF16, false, true, true>(acc, vbits, pb);
+                  else mfma32_asm<BF16, false, true>(acc, vbits, pb);
+                }
+              } else {
+                if (db == 0) {
+                  if (fresh) mfma32_asm<BF16, false, false, true, true>(acc, vbits, pb);
+                  else mfma32_asm<BF16, false, false, false, true>(acc, vbits, pb);
+                } else {
+                  if (fresh) mfma32_asm<BF16, false, false, true>(acc, vbits, pb);
+                  else mfma32_asm<BF16, false, false>(acc, vbits, pb);
+                }
+              }
+            } else {
+              if (db < kOAgpr) mfma32_asm<BF16, false, true>(acc, vbits, pb);
+              else mfma32_asm<BF16, false, false>(acc, vbits, pb);
+            }
           }
         }
       if constexpr (ACC16) {
@@ -391,6 +445,16 @@ void fwd_prefill_kernel(FwdArgs a) {
     fresh = false;
   }
   wait_vmcnt<0>();  // no copy may still target this workgroup's LDS when it ends
+  if constexpr (!ACC16) {
+    // the accumulators were last written by MFMAs issued as inline asm: pad
+    // before the epilogue reads them (the padding is tied to every block)
+    asm volatile("s_nop 7\n s_nop 7\n s_nop 4" ::: "memory");
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      if (d < kOAgpr) asm volatile("" : "+a"(o_acc[d]));
+      else asm volatile("" : "+v"(o_acc[d]));
+    }
+  }
 
   // ===== epilogue: normalise, store O and lse
   const int le = threadIdx.x & 63, hie = le >> 5, my_qe = qw + (le & 31);
