@@ -87,6 +87,7 @@ void fwd_prefill_kernel(FwdArgs a) {
   constexpr int NDB = D / 32;             // output d-blocks of 32
   constexpr int KB = 0, VB = TILEB;       // buffer offsets
   constexpr int kKAhead = 3;              // K-fragment read-ahead, in d-steps
+  constexpr int kVAhead = 6;              // V-fragment read-ahead, in MFMAs
   // fp32 accumulator d-blocks that share the AGPRs with the Q fragments; the
   // remaining blocks live in VGPRs
   constexpr int kOAgpr = (256 - D / 4) / 16 < NDB ? (256 - D / 4) / 16 : NDB;
@@ -379,67 +380,82 @@ void fwd_prefill_kernel(FwdArgs a) {
       }
     }
     if (j + 1 < n_tiles) issue_tile(Kr, KB, j + 1);
+    {
+      // 4 MFMAs per output d-block (2 key blocks x 2 k-steps); V^T fragments
+      // are read kVAhead MFMAs ahead of their use
+      constexpr int NSV = 4 * NDB;
+      auto vread = [&](int st) {
+        const int db = st >> 2, kb = (st >> 1) & 1, t2 = st & 1;
+        const FFPA_LDS char* p = smem + vaddr[db & 1] + 128 * (db >> 1) + (32 * kb + 16 * t2) * ROWB;
+        return join8(lds_read_tr(p), lds_read_tr(p + 8 * ROWB));
+      };
+      u32x4 vf[kVAhead];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+      for (int st = 0; st < kVAhead; ++st) vf[st] = vread(st);
       f32x16 acc;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const FFPA_LDS char* p = smem + vaddr[db & 1] + 128 * (db >> 1) + (32 * kb + 16 * t2) * ROWB;
-          const i16x4 lo = lds_read_tr(p);
-          const i16x4 hi8 = lds_read_tr(p + 8 * ROWB);
-          const u32x4 vbits = join8(lo, hi8);
-          if constexpr (ACC16) {
-            if (kb == 0 && t2 == 0) acc = E::mfma32(as_vec8<V8>(vbits), pf[0][0], f32x16{});
-            else acc = E::mfma32(as_vec8<V8>(vbits), pf[kb][t2], acc);
+      for (int st = 0; st < NSV; ++st) {
+        const int db = st >> 2, kb = (st >> 1) & 1, t2 = st & 1;
+        const u32x4 vbits = vf[st % kVAhead];
+        if (st + kVAhead < NSV) vf[st % kVAhead] = vread(st + kVAhead);
+        const u32x4 pb = __builtin_bit_cast(u32x4, pf[kb][t2]);
+        const bool first = kb == 0 && t2 == 0, last = kb == 1 && t2 == 1;
+        if constexpr (ACC16) {
+          // per-tile product in VGPRs; the last MFMA of a d-block pads for the
+          // VALU that folds it into the fp16 accumulator
+          if (first) {
+            if (st == 0) mfma32_asm<BF16, false, false, true, true>(acc, vbits, pb);
+            else mfma32_asm<BF16, false, false, true>(acc, vbits, pb);
+          } else if (last) {
+            mfma32_asm<BF16, false, false, false, false, true>(acc, vbits, pb);
           } else {
-            const u32x4 pb = __builtin_bit_cast(u32x4, pf[kb][t2]);
-            if (kb == 0 && t2 == 0) {
-              acc = o_acc[db];
-              // two MFMAs on a uniform branch, both writing the accumulators:
-              // no select or copy of the tuple is needed. The first MFMA of
-              // the phase pads for the VALU that wrote P.
-              if (db < kOAgpr) {
-                if (db == 0) {
-                  if (fresh) mfma32_asm<BF16, false, true, true, true>(acc, vbits, pb);
-                  else mfma32_asm<BF16, false, true, false, true>(acc, vbits, pb);
-                } else {
-                  if (fresh) mfma32_asm<BF16, false, true, true>(acc, vbits, pb);
-                  else mfma32_asm<BF16, false, true>(acc, vbits, pb);
-                }
-              } else {
-                if (db == 0) {
-                  if (fresh) mfma32_asm<BF16, false, false, true, true>(acc, vbits, pb);
-                  else mfma32_asm<BF16, false, false, false, true>(acc, vbits, pb);
-                } else {
-                  if (fresh) mfma32_asm<BF16, false, false, true>(acc, vbits, pb);
-                  else mfma32_asm<BF16, false, false>(acc, vbits, pb);
-                }
+            mfma32_asm<BF16, false, false>(acc, vbits, pb);
+          }
+          if (last) {
+            // o16 <- o16 * oscale + acc, in packed fp16
+            const f16x2 sc = {(_Float16)oscale, (_Float16)oscale};
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              u32x4 w = o16[2 * db + hh];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                f16x2 cur = f16x2_from_bits(w[e]);
+                const f16x2 add = {(_Float16)acc[8 * hh + 2 * e], (_Float16)acc[8 * hh + 2 * e + 1]};
+                cur = cur * sc + add;
+                w[e] = __builtin_bit_cast(uint32_t, cur);
               }
-            } else {
-              if (db < kOAgpr) mfma32_asm<BF16, false, true>(acc, vbits, pb);
-              else mfma32_asm<BF16, false, false>(acc, vbits, pb);
+              o16[2 * db + hh] = w;
             }
           }
-        }
-      if constexpr (ACC16) {
-        // o16 <- o16 * oscale + acc, in packed fp16
-        const f16x2 sc = {(_Float16)oscale, (_Float16)oscale};
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 w = o16[2 * db + hh];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            f16x2 cur = f16x2_from_bits(w[e]);
-            const f16x2 add = {(_Float16)acc[8 * hh + 2 * e], (_Float16)acc[8 * hh + 2 * e + 1]};
-            cur = cur * sc + add;
-            w[e] = __builtin_bit_cast(uint32_t, cur);
+        } else {
+          if (first) {
+            acc = o_acc[db];
+            // two MFMAs on a uniform branch, both writing the accumulators:
+            // no select or copy of the tuple is needed. The first MFMA of the
+            // phase pads for the VALU that wrote P.
+            if (db < kOAgpr) {
+              if (st == 0) {
+                if (fresh) mfma32_asm<BF16, false, true, true, true>(acc, vbits, pb);
+                else mfma32_asm<BF16, false, true, false, true>(acc, vbits, pb);
+              } else {
+                if (fresh) mfma32_asm<BF16, false, true, true>(acc, vbits, pb);
+                else mfma32_asm<BF16, false, true>(acc, vbits, pb);
+              }
+            } else {
+              if (st == 0) {
+                if (fresh) mfma32_asm<BF16, false, false, true, true>(acc, vbits, pb);
+                else mfma32_asm<BF16, false, false, false, true>(acc, vbits, pb);
+              } else {
+                if (fresh) mfma32_asm<BF16, false, false, true>(acc, vbits, pb);
+                else mfma32_asm<BF16, false, false>(acc, vbits, pb);
+              }
+            }
+          } else {
+            if (db < kOAgpr) mfma32_asm<BF16, false, true>(acc, vbits, pb);
+            else mfma32_asm<BF16, false, false>(acc, vbits, pb);
           }
-          o16[2 * db + hh] = w;
+          if (last) o_acc[db] = acc;
         }
-      } else {
-        o_acc[db] = acc;
       }
     }
     fresh = false;
