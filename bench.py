@@ -26,6 +26,33 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6}  # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("head_dim_attention_flash_amd/csrc/fwd_prefill.hpp",
+                  "head_dim_attention_flash_amd/csrc/ffpa_common.hpp")
+COPY_BYTES = 1 << 30  # the calibration copy moves 1 GiB in and 1 GiB out
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch recorded by rocprofv3 counters for `key`, or None if
+    the record is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_hash():
+        return None
+    return int(rec["hbm_bytes"])
 
 
 def counted_flops(B, Hq, Nq, Nkv, D, causal=False, backward=False) -> float:
@@ -120,7 +147,8 @@ def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
                    "causal": w.causal, "mask": w.mask, "accum": accum, "parallelism": "none"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": measured_traffic(f"{name}:{accum}")},
         "kernel_ms": {"mean": round(mean_ms, 4), "median": round(per[len(per) // 2], 4),
                       "min": round(per[0], 4)},
     }
@@ -142,6 +170,8 @@ def main(argv=None) -> int:
                     help="(b, h) heads the oracle CPU baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true", help="time every workload family")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of 1 GiB (for HBM counter scaling)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -168,6 +198,13 @@ def main(argv=None) -> int:
     line = run_one(ffpa, W, args.workload, args.accum, args.steps, args.warmup,
                    not args.no_cpu_baseline, args.cpu_heads)
     print(json.dumps(line), flush=True)
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": COPY_BYTES}), flush=True)
     return 0
 
 

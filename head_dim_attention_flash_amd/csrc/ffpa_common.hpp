@@ -169,15 +169,27 @@ __device__ inline typename Elem<BF16>::vec8 pack8(float a0, float a1, float a2, 
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles. A staged tile is R rows x DC columns of 16-bit values, rows of
-// DC*2 bytes (a multiple of 128 B), split in 16-byte granules. Granule g of
-// row r is stored at granule g ^ swz(r). swz permutes the low three bits so
-// that (a) 8 consecutive rows read at one granule (ds_read_b128, 8 lanes per
-// LDS cycle) hit 8 distinct granule slots, and (b) 4 consecutive rows x 32
-// contiguous bytes (one 16-lane group of ds_read_b64_tr_b16) also hit 8
-// distinct slots.
+// LDS tiles. A staged tile is R rows of D 16-bit values (rows of 2D bytes,
+// 16-byte granules). The LDS serves 64 banks of 4 bytes: a 16-byte read is
+// conflict-free when the 16 lanes served together hit 16 distinct 16-byte
+// slots modulo 256 bytes, an 8-byte read when 32 lanes hit distinct 8-byte
+// slots. Within every complete group of 16 granules of a row, granule g of
+// row r is stored at g ^ swz4(r); a trailing group of 8 granules (D % 128 ==
+// 64) uses the low three bits of swz4(r). This makes both access patterns of
+// the attention kernels conflict-free for D % 128 == 0 (and leaves at most
+// two-way conflicts in the trailing group otherwise):
+//  - 16 consecutive rows reading the same granule (K fragments, b128), and
+//  - 4 consecutive rows x 4 consecutive granules (one half-wave of transposed
+//    V^T reads, ds_read_b64_tr_b16).
 // ---------------------------------------------------------------------------
-__device__ __host__ inline int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __host__ inline int swz4(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+
+// Stored granule of logical granule g of row `row` (and, the map being an
+// involution within each group, the logical granule of stored granule g).
+template <int GPR>
+__device__ __host__ inline int swz_granule(int row, int g) {
+  return ((g & ~15) + 16 <= GPR) ? (g ^ swz4(row)) : (g ^ (swz4(row) & 7));
+}
 
 // ---------------------------------------------------------------------------
 // Wait counters and the workgroup barrier, as inline asm with a "memory"

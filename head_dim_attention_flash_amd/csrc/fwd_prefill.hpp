@@ -48,10 +48,15 @@ constexpr int kFwdWaves = 4;
 constexpr int kFwdRows = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBc = 64;                // keys per tile
 
+// Every staged row takes 1 KiB of LDS whatever D is (up to 512): one copy
+// instruction fills one row, the swizzle groups are all complete, and two
+// 64-row tiles still fit.
+constexpr int kFwdRowBytes = 1024;
+
 // LDS bytes of the K and V tile buffers.
 template <int D>
 constexpr int fwd_ring_bytes() {
-  return 2 * kFwdBc * D * 2;
+  return 2 * kFwdBc * kFwdRowBytes;
 }
 // LDS bytes of the staged key bias (zero-padded to whole tiles).
 __host__ __device__ inline int fwd_bias_bytes(int nkv) { return ((nkv + kFwdBc - 1) / kFwdBc) * kFwdBc * 2; }
@@ -80,14 +85,14 @@ void fwd_prefill_kernel(FwdArgs a) {
   static_assert(D % 64 == 0 && D <= 512, "D must be a multiple of 64, at most 512");
   using E = Elem<BF16>;
   using V8 = typename E::vec8;
-  constexpr int ROWB = D * 2;             // bytes per LDS row
-  constexpr int GPR = D / 8;              // 16-byte granules per row
+  constexpr int ROWB = kFwdRowBytes;      // bytes per LDS row (D * 2 used)
+  constexpr int GPR = D / 8;              // 16-byte granules of data per row
   constexpr int TILEB = kFwdBc * ROWB;    // bytes per tile buffer
-  constexpr int NDMA = TILEB / 1024 / kFwdWaves;  // copies per wave per tile
+  constexpr int NDMA = kFwdBc / kFwdWaves;  // copies per wave per tile (one per row)
   constexpr int NDB = D / 32;             // output d-blocks of 32
   constexpr int KB = 0, VB = TILEB;       // buffer offsets
   constexpr int kKAhead = 3;              // K-fragment read-ahead, in d-steps
-  constexpr int kVAhead = 6;              // V-fragment read-ahead, in MFMAs
+  constexpr int kVAhead = ACC16 ? 6 : 12; // V-fragment read-ahead, in MFMAs
   // fp32 accumulator d-blocks that share the AGPRs with the Q fragments; the
   // remaining blocks live in VGPRs
   constexpr int kOAgpr = (256 - D / 4) / 16 < NDB ? (256 - D / 4) / 16 : NDB;
@@ -146,43 +151,53 @@ void fwd_prefill_kernel(FwdArgs a) {
   __syncthreads();
 
   // ---- copy of one tile of K or V into its buffer. Copy instruction n of a
-  // tile (n = wave + 4 r) fills LDS bytes [1024 n, 1024 n + 1024) of the
-  // buffer: 16-byte granule L = 64 n + lane, stored at row L / GPR, slot
-  // L % GPR, holding the logical granule (slot ^ swz(row)) of that row.
+  // tile (n = wave + 4 r) fills LDS row n: lane i writes slot i, which holds
+  // the logical granule i ^ swz4(n) of key row (64 tile + n). Granules past D
+  // get an out-of-range offset and cost no memory traffic.
+  auto issue_copy = [&](__amdgpu_buffer_rsrc_t rs, int buf, int tile, int r, int ln) {
+    const int n = wave + kFwdWaves * r;
+    const int lg = ln ^ swz4(n);
+    const uint32_t voff = (GPR == 64 || lg < GPR) ? (uint32_t)lg << 4 : 0x80000000u;
+    const uint32_t soff = (uint32_t)(tile * kFwdBc + n) * (D * 2);
+    dma16(rs, voff, soff, smem + buf + n * ROWB);
+  };
   auto issue_tile = [&](__amdgpu_buffer_rsrc_t rs, int buf, int tile) {
-    const uint32_t soff = (uint32_t)tile * kFwdBc * ROWB;
-    // recomputed at each call (a few VALU ops per copy) rather than held in
-    // NDMA live registers across the loop
-    int ln = lane;
+    int ln = lane;  // recomputed at each call rather than held across the loop
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int r = 0; r < NDMA; ++r) {
-      const int n = wave + kFwdWaves * r;
-      const int L = 64 * n + ln;
-      const int row = L / GPR, slot = L % GPR;
-      const uint32_t voff = (uint32_t)(row * ROWB + ((slot ^ swz(row)) << 4));
-      dma16(rs, voff, soff, smem + buf + n * 1024);
-    }
+    for (int r = 0; r < NDMA; ++r) issue_copy(rs, buf, tile, r, ln);
   };
 
-  // ---- LDS read addresses: a per-lane base plus compile-time offsets < 64 KiB
-  // K fragment (A of S^T) for d-step s = 4 a + c: row 32 kb + l32, granule
-  // 8 a + ((2 c + hi) ^ swz(row)).
-  uint32_t kaddr[4];
+  // ---- LDS read addresses: per-lane bases (recomputed at the start of each
+  // phase, so they are live only there) plus compile-time offsets < 64 KiB.
+  // K fragment (A of S^T) for d-step s = 8 a + c: row 32 kb + l32, logical
+  // granule 16 a + 2 c + hi, stored at 16 a + ((2 c + hi) ^ swz4(row)).
+  auto k_bases = [&](int ln, uint32_t* kx) {
+    const int r = ln & 31, h = ln >> 5, x = swz4(r);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) kaddr[c] = (uint32_t)(KB + l32 * ROWB + (((2 * c + hi) ^ swz(l32)) << 4));
+    for (int c = 0; c < 8; ++c) kx[c] = (uint32_t)(KB + r * ROWB + (((2 * c + h) ^ x) << 4));
+  };
+  auto k_addr = [&](const uint32_t* kx, int st, int kb) -> uint32_t {
+    return kx[st & 7] + 256 * (st >> 3) + 32 * kb * ROWB;
+  };
   // V^T fragment by transposed reads: group G = lane/16, i = lane%16 reads row
-  // 32 kb + 16 t2 + 8 r + 4 (G/2) + i/4 at columns 32 db + 16 (G%2) + 4 (i%4),
-  // i.e. granule 8 (db/2) + ((4 (db%2) + y) ^ swz(row)) with y = 2 (G%2) + (i%4)/2.
-  uint32_t vaddr[2];
-  {
-    const int G = lane >> 4, gi = lane & 15;
+  // 32 kb + 16 t2 + 8 r8 + 4 (G/2) + i/4 at columns 32 db + 16 (G%2) + 4 (i%4),
+  // i.e. logical granule 4 db + y with y = 2 (G%2) + (i%4)/2.
+  auto v_bases = [&](int ln, uint32_t* vx) {
+    const int G = ln >> 4, gi = ln & 15;
     const int vrow = 4 * (G >> 1) + (gi >> 2);
     const int y = 2 * (G & 1) + ((gi & 3) >> 1);
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-      vaddr[e] = (uint32_t)(VB + vrow * ROWB + (((4 * e + y) ^ swz(vrow)) << 4) + (gi & 1) * 8);
-  }
+    for (int r8 = 0; r8 < 2; ++r8) {
+      const int row = vrow + 8 * r8, x = swz4(row);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vx[4 * r8 + e] = (uint32_t)(VB + row * ROWB + (((4 * e + y) ^ x) << 4) + (gi & 1) * 8);
+    }
+  };
+  auto v_addr = [&](const uint32_t* vx, int db, int kb, int t2, int r8) -> uint32_t {
+    return vx[4 * r8 + (db & 3)] + 256 * (db >> 2) + (32 * kb + 16 * t2) * ROWB;
+  };
 
   // ---- accumulators
   f32x16 o_acc[ACC16 ? 1 : NDB];
@@ -211,11 +226,6 @@ void fwd_prefill_kernel(FwdArgs a) {
     asm volatile("" : "+v"(lj));
     const int hij = lj >> 5;
     const int my_qj = qw + (lj & 31);
-    // Opaque per iteration: keeps base + offset sums inside the loop, where
-    // they fold into the ds_read offset field instead of each holding a VGPR.
-#pragma unroll
-    for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(kaddr[c]));
-    asm volatile("" : "+v"(vaddr[0]), "+v"(vaddr[1]));
     // Register placement for the whole loop. The Q fragments (read-only MFMA
     // operands) live in AGPRs; the fp32 output accumulators fill the rest of
     // the AGPRs and spill over into VGPRs. VGPRs then keep room for the score
@@ -232,15 +242,17 @@ void fwd_prefill_kernel(FwdArgs a) {
     wait_vmcnt<0>();  // K(j) landed (this wave's copies) ...
     wait_lgkm0();
     barrier();        // ... and everyone's; everyone is done with V(j-1)
+    // Copies are issued in one burst right after the barrier: spreading them
+    // between the MFMAs of the phase measured markedly slower.
     issue_tile(Vr, VB, j);
     f32x16 s_acc[2];
     {
       // K fragments are read kKAhead d-steps ahead of the MFMAs that use them
       constexpr int NS = D / 16;
       u32x4 kf[kKAhead][2];
-      auto kread = [&](int st, int kb) {
-        return lds_read16(smem + kaddr[st & 3] + 128 * (st >> 2) + 32 * kb * ROWB);
-      };
+      uint32_t kx[8];
+      k_bases(lj, kx);
+      auto kread = [&](int st, int kb) { return lds_read16(smem + k_addr(kx, st, kb)); };
 #pragma unroll
       for (int st = 0; st < kKAhead; ++st) {
         kf[st][0] = kread(st, 0);
@@ -361,6 +373,14 @@ void fwd_prefill_kernel(FwdArgs a) {
         }
       }
 
+    // P is the B operand of MFMAs issued as inline asm, which the compiler
+    // does not pad for hazards: force every VALU write of P to happen here,
+    // before the barrier (the first MFMA of the phase also pads).
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[kb][t2]));
+
     // ===== V phase: O^T += V^T P^T
     wait_vmcnt<0>();  // V(j) landed ...
     wait_lgkm0();
@@ -379,15 +399,22 @@ void fwd_prefill_kernel(FwdArgs a) {
         continue;
       }
     }
-    if (j + 1 < n_tiles) issue_tile(Kr, KB, j + 1);
+    const bool next_k = j + 1 < n_tiles;
+    if (next_k) issue_tile(Kr, KB, j + 1);
     {
       // 4 MFMAs per output d-block (2 key blocks x 2 k-steps); V^T fragments
       // are read kVAhead MFMAs ahead of their use
       constexpr int NSV = 4 * NDB;
+      uint32_t vx[8];
+      {
+        int lv = lane;
+        asm volatile("" : "+v"(lv));
+        v_bases(lv, vx);
+      }
       auto vread = [&](int st) {
         const int db = st >> 2, kb = (st >> 1) & 1, t2 = st & 1;
-        const FFPA_LDS char* p = smem + vaddr[db & 1] + 128 * (db >> 1) + (32 * kb + 16 * t2) * ROWB;
-        return join8(lds_read_tr(p), lds_read_tr(p + 8 * ROWB));
+        return join8(lds_read_tr(smem + v_addr(vx, db, kb, t2, 0)),
+                     lds_read_tr(smem + v_addr(vx, db, kb, t2, 1)));
       };
       u32x4 vf[kVAhead];
 #pragma unroll
