@@ -500,6 +500,12 @@ void fwd_prefill_kernel(FwdArgs a) {
   }
 
   // ===== epilogue: normalise, store O and lse
+  // The accumulators hold O transposed (a lane has 4-element pieces of one
+  // row), so the rows go through LDS first: each wave writes its 32 rows to a
+  // 32 KiB slice of the (now idle) tile buffers, then stores them as whole
+  // contiguous 1 KiB pieces. Written straight from the accumulators, a cache
+  // line of O would be filled by many partial writes and leave the L2 several
+  // times.
   const int le = threadIdx.x & 63, hie = le >> 5, my_qe = qw + (le & 31);
   float l_tot, inv;
   if constexpr (!ACC16) {
@@ -509,8 +515,13 @@ void fwd_prefill_kernel(FwdArgs a) {
     l_tot = l_run;
     inv = 1.f;
   }
-  if (my_qe < a.Nq) {
-    typename E::scalar* O = (typename E::scalar*)a.o + ((size_t)(b * a.Hq + h) * a.Nq + my_qe) * D;
+  wait_lgkm0();
+  barrier();  // every wave is done reading the tile buffers
+  FFPA_LDS char* ostage = smem + wave * 32 * ROWB;
+  {
+    // row r = lane % 32 of the wave; granule g (8 elements) sits in slot
+    // g ^ (r % 16), which puts 16 consecutive rows on distinct banks
+    const int r = le & 31;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -530,15 +541,28 @@ void fwd_prefill_kernel(FwdArgs a) {
           x2 = (float)p1[0];
           x3 = (float)p1[1];
         }
-        u32x2 st = {E::pack2(x0, x1), E::pack2(x2, x3)};
-        const int d = 32 * db + 8 * g4 + 4 * hie;
-        *(u32x2*)(O + d) = st;
+        const u32x2 st = {E::pack2(x0, x1), E::pack2(x2, x3)};
+        const int g = 4 * db + g4;  // elements 32 db + 8 g4 + 4 hi .. +3
+        *(FFPA_LDS u32x2*)(ostage + r * ROWB + ((g ^ (r & 15)) << 4) + 8 * hie) = st;
       }
     }
-    if (a.lse != nullptr && hie == 0) {
-      float* L = a.lse + (size_t)(b * a.Hq + h) * a.Nq + my_qe;
-      *L = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  }
+  // a wave's LDS accesses complete in order: its own rows can be read back
+  // without a barrier. The wave's 32 rows are one contiguous run of O.
+  {
+    typename E::scalar* O = (typename E::scalar*)a.o + ((size_t)(b * a.Hq + h) * a.Nq + qw) * D;
+    const int rows = min(32, a.Nq - qw);
+#pragma unroll
+    for (int it = 0; it < GPR / 2; ++it) {
+      const int c = it * 64 + le;  // granule index within the wave's rows
+      const int r = c / GPR, g = c % GPR;
+      const u32x4 x = *(const FFPA_LDS u32x4*)(ostage + r * ROWB + ((g ^ (r & 15)) << 4));
+      if (r < rows) *(u32x4*)(O + (size_t)c * 8) = x;
     }
+  }
+  if (my_qe < a.Nq && a.lse != nullptr && hie == 0) {
+    float* L = a.lse + (size_t)(b * a.Hq + h) * a.Nq + my_qe;
+    *L = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
