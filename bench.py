@@ -8,7 +8,12 @@ TFLOPS follow the convention of "FFPA Attention Benchmark" (section "More
 Benchmark"): the forward counts 2 GEMMs = 4 B Hq Nq Nkv D flops, the backward
 the standard 5 = 10 B Hq Nq Nkv D, and a causal pass half of that.
 
-Prints ONE JSON line. ``--suite`` instead times every workload family and
+Prints ONE JSON line. Besides the headline forward it carries, under
+"paths", the other two parts of the hot path measured in the same run:
+the backward (B=1, H=32, N=8192, D=512, bf16, dQ/dK/dV after this library's
+forward; TFLOPS counted as 5 GEMMs) and the decode forward (B=16, H=32,
+Nq=1, Nkv=8192, D=512, fp16; HBM GB/s of its algorithmic bytes against the
+8 TB/s HBM3E peak). ``--suite`` instead times every workload family and
 prints one line per workload (not the headline contract).
 """
 from __future__ import annotations
@@ -119,6 +124,100 @@ def time_forward(ffpa, w, inp, accum, steps, warmup):
     return per, wall
 
 
+def _time_calls(call, steps, warmup):
+    """Per-call durations (ms, sorted) of `call` with HIP events on the current
+    stream, the stream every library call is launched on."""
+    import torch
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
+
+
+def run_backward(ffpa, W, name, steps, warmup):
+    """dQ, dK, dV at the backward workload; O and lse from this library's forward."""
+    import torch
+
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, device="cuda")
+    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["dout"]
+    o, lse = ffpa.attention(q, k, v, causal=w.causal, scale=w.scale, return_lse=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dt = ffpa.BF16 if w.dtype == "bf16" else ffpa.F16
+    ws_bytes = ffpa.ffpa_attn_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call():
+        st = ffpa.ffpa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.scale,
+                                int(w.causal), 0, 0, ffpa.ACC_F32, dt, ws.data_ptr(), ws_bytes,
+                                stream)
+        if st != 0:
+            raise ffpa.FFPAError(st, ffpa.ffpa_last_error())
+
+    per = _time_calls(call, steps, warmup)
+    mean_ms = sum(per) / len(per)
+    tflops = counted_flops(w.B, w.Hq, w.Nq, w.Nkv, w.D, w.causal, backward=True) / (mean_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    del inp, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{name}: B={w.B} H={w.Hq} N={w.Nq} D={w.D} {w.dtype} causal={w.causal}",
+            "value": round(tflops, 2), "unit": "TFLOPS (5 GEMMs counted)",
+            "ms_per_call": round(mean_ms, 4), "kernels": "prep + dK/dV + dQ",
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4)}}
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic HBM bytes of one decode call: q, K, V read once, O and lse written."""
+    e = 2
+    return (w.B * w.Hq * w.D * e * 2 + 2 * w.B * w.Hkv * w.Nkv * w.D * e + w.B * w.Hq * 4)
+
+
+def run_decode(ffpa, W, steps, warmup):
+    import torch
+
+    w = W.WORKLOADS["decode"]
+    inp = W.make_inputs(w, device="cuda")
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, 1, dtype=torch.float32, device="cuda")
+    dt = ffpa.BF16 if w.dtype == "bf16" else ffpa.F16
+    ws_bytes = ffpa.ffpa_attn_fwd_workspace_size(w.B, w.Hq, w.Hkv, 1, w.Nkv, w.D, dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call():
+        st = ffpa.ffpa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), w.B, w.Hq, w.Hkv, 1, w.Nkv, w.D, w.scale, 0, 0, 0,
+                                ffpa.ACC_F32, dt, ws.data_ptr(), ws_bytes, stream)
+        if st != 0:
+            raise ffpa.FFPAError(st, ffpa.ffpa_last_error())
+
+    per = _time_calls(call, steps, warmup)
+    mean_ms = sum(per) / len(per)
+    gbs = decode_bytes(w) / (mean_ms * 1e-3) / 1e9
+    del inp, o, lse, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"decode: B={w.B} H={w.Hq} Nq=1 Nkv={w.Nkv} D={w.D} {w.dtype}",
+            "value": round(gbs, 1), "unit": "GB/s", "ms_per_call": round(mean_ms, 4),
+            "kernels": "split-KV + combine",
+            "tflops": round(counted_flops(w.B, w.Hq, 1, w.Nkv, w.D) / (mean_ms * 1e-3) / 1e12, 3),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
     import torch
 
@@ -170,6 +269,8 @@ def main(argv=None) -> int:
                     help="(b, h) heads the oracle CPU baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true", help="time every workload family")
+    ap.add_argument("--no-paths", action="store_true",
+                    help="headline forward only (skip the backward and decode measurements)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of 1 GiB (for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -195,8 +296,20 @@ def main(argv=None) -> int:
                 line = run_one(ffpa, W, n, acc, args.steps, args.warmup, False, 0)
                 print(json.dumps(line), flush=True)
         return 0
+    if args.workload in ("bwd", "bwd_causal"):
+        print(json.dumps(run_backward(ffpa, W, args.workload, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.workload == "decode":
+        print(json.dumps(run_decode(ffpa, W, args.steps, args.warmup)), flush=True)
+        return 0
     line = run_one(ffpa, W, args.workload, args.accum, args.steps, args.warmup,
                    not args.no_cpu_baseline, args.cpu_heads)
+    if not args.no_paths:
+        line["paths"] = {
+            "backward": run_backward(ffpa, W, "bwd", max(3, args.steps // 2), 2),
+            "backward_causal": run_backward(ffpa, W, "bwd_causal", max(3, args.steps // 2), 2),
+            "decode": run_decode(ffpa, W, args.steps, args.warmup),
+        }
     print(json.dumps(line), flush=True)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device="cuda").normal_()

@@ -6,6 +6,8 @@
 #include <string>
 
 #include "ffpa_attn.h"
+#include "bwd.hpp"
+#include "decode.hpp"
 #include "fwd_prefill.hpp"
 
 namespace {
@@ -49,6 +51,51 @@ FwdLauncher fwd_launcher(int D, int bf16, int acc16, size_t* ring_bytes) {
   }
 }
 
+using DecLauncher = hipError_t (*)(const ffpa::DecArgs&, hipStream_t);
+
+DecLauncher dec_launcher(int D, int bf16) {
+  switch (D) {
+#define FFPA_CASE(DD) \
+  case DD:            \
+    return bf16 ? ffpa::launch_decode<DD, true> : ffpa::launch_decode<DD, false>;
+    FFPA_CASE(32) FFPA_CASE(64) FFPA_CASE(96) FFPA_CASE(128) FFPA_CASE(160) FFPA_CASE(192)
+    FFPA_CASE(224) FFPA_CASE(256) FFPA_CASE(288) FFPA_CASE(320) FFPA_CASE(352) FFPA_CASE(384)
+    FFPA_CASE(416) FFPA_CASE(448) FFPA_CASE(480) FFPA_CASE(512) FFPA_CASE(544) FFPA_CASE(576)
+    FFPA_CASE(608) FFPA_CASE(640) FFPA_CASE(672) FFPA_CASE(704) FFPA_CASE(736) FFPA_CASE(768)
+    FFPA_CASE(800) FFPA_CASE(832) FFPA_CASE(864) FFPA_CASE(896) FFPA_CASE(928) FFPA_CASE(960)
+    FFPA_CASE(992) FFPA_CASE(1024)
+#undef FFPA_CASE
+    default:
+      return nullptr;
+  }
+}
+
+// Keys a decode row sees: top-left causal leaves row 0 only key 0.
+int dec_kv_end(int Nkv, int causal) { return causal ? 1 : Nkv; }
+
+using BwdLauncher = hipError_t (*)(const ffpa::BwdArgs&, hipStream_t);
+
+BwdLauncher bwd_launcher(int D, int bf16) {
+  switch (D) {
+#define FFPA_CASE(DD) \
+  case DD:            \
+    return bf16 ? ffpa::launch_bwd<DD, true> : ffpa::launch_bwd<DD, false>;
+    FFPA_CASE(64)
+    FFPA_CASE(128)
+    FFPA_CASE(192)
+    FFPA_CASE(256)
+    FFPA_CASE(320)
+    FFPA_CASE(384)
+    FFPA_CASE(448)
+    FFPA_CASE(512)
+#undef FFPA_CASE
+    default:
+      return nullptr;
+  }
+}
+
+int64_t bwd_nq_pad(int Nq) { return ((int64_t)Nq + ffpa::kBwdPad - 1) / ffpa::kBwdPad * ffpa::kBwdPad; }
+
 // Checks shared by forward and backward; returns FFPA_OK or an error code.
 int check_common(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, const void* mask,
                  int mask_rows, int accum_dtype, int dtype) {
@@ -81,8 +128,12 @@ int ffpa_version(void) { return 100; }
 const char* ffpa_last_error(void) { return g_err.c_str(); }
 
 size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {
-  (void)B; (void)Hq; (void)Hkv; (void)Nq; (void)Nkv; (void)D; (void)dtype;
-  return 0;
+  (void)Hkv; (void)dtype;
+  if (Nq != 1 || B < 1 || Hq < 1 || Nkv < 1 || D < 1) return 0;
+  // decode: per key range, o (D fp32) and a log-sum-exp (fp32); the causal
+  // variant uses fewer ranges, so the non-causal count bounds both
+  const size_t s = (size_t)ffpa::dec_splits(B, Hq, Nkv);
+  return (size_t)B * Hq * s * ((size_t)D + 1) * sizeof(float);
 }
 
 int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
@@ -100,6 +151,28 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_fwd_workspace_size()");
   if (!(scale == scale)) return fail(FFPA_ERR_INVALID_ARG, "scale is NaN");
+
+  if (Nq == 1) {
+    // one query row per head: split-KV decode kernels
+    DecLauncher launch = dec_launcher(D, dtype == FFPA_BF16);
+    if (launch == nullptr) return fail(FFPA_ERR_UNSUPPORTED, "this head dimension is not built yet");
+    if (!aligned16(workspace)) return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    ffpa::DecArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.mask = mask;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nkv = Nkv;
+    a.kv_end = dec_kv_end(Nkv, causal);
+    a.splits = ffpa::dec_splits(B, Hq, a.kv_end);
+    a.keys_per_split = ffpa::dec_keys_per_split(a.kv_end, a.splits);
+    a.scale_log2 = scale * ffpa::kLog2e;
+    const int64_t waves = (int64_t)B * Hq * a.splits;
+    if (waves >= (int64_t(1) << 31)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
+    a.n_waves = (int)waves;
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)workspace + (size_t)waves * D;
+    hipError_t e = launch(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    return FFPA_OK;
+  }
 
   size_t ring = 0;
   FwdLauncher launch = fwd_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, &ring);
@@ -131,7 +204,9 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
 
 size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {
   (void)Hkv; (void)Nkv; (void)D; (void)dtype;
-  return (size_t)B * Hq * Nq * sizeof(float);
+  if (B < 1 || Hq < 1 || Nq < 1) return 0;
+  // delta and lse * log2(e) per query row, rows padded to a multiple of 64
+  return 2 * (size_t)B * Hq * (size_t)bwd_nq_pad(Nq) * sizeof(float);
 }
 
 int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -145,8 +220,41 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   if (st != FFPA_OK) return st;
   if (accum_dtype != FFPA_ACC_F32)
     return fail(FFPA_ERR_UNSUPPORTED, "the backward accumulates in fp32 only (FFPA_ACC_F32)");
-  (void)scale; (void)workspace; (void)workspace_bytes; (void)stream;
-  return fail(FFPA_ERR_UNSUPPORTED, "backward kernels are not built yet");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(mask) ||
+      !aligned16(workspace))
+    return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t need = ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_bwd_workspace_size()");
+  if (!(scale == scale)) return fail(FFPA_ERR_INVALID_ARG, "scale is NaN");
+  if (mask != nullptr && mask_rows != 1)
+    return fail(FFPA_ERR_UNSUPPORTED, "per-query masks [Nq, Nkv] are not supported yet");
+  BwdLauncher launch = bwd_launcher(D, dtype == FFPA_BF16);
+  if (launch == nullptr)
+    return fail(FFPA_ERR_UNSUPPORTED, "the backward is built for D = 64, 128, ..., 512");
+
+  ffpa::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.mask = mask;
+  const int64_t nq_pad = bwd_nq_pad(Nq);
+  a.delta = (float*)workspace;
+  a.lse2 = (float*)workspace + (size_t)B * Hq * nq_pad;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv;
+  a.nq_pad = (int)nq_pad;
+  a.causal = causal;
+  a.scale = scale;
+  a.scale_log2 = scale * ffpa::kLog2e;
+  const int64_t wg_dkdv = (int64_t)B * Hkv * ((Nkv + 63) / 64);
+  const int64_t wg_dq = (int64_t)B * Hq * ((Nq + 63) / 64);
+  if (wg_dkdv >= (int64_t(1) << 31) || wg_dq >= (int64_t(1) << 31) ||
+      (int64_t)B * Hq * nq_pad / 4 >= (int64_t(1) << 31))
+    return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
+  a.wg_dkdv = (int)wg_dkdv;
+  a.wg_dq = (int)wg_dq;
+  hipError_t e = launch(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return FFPA_OK;
 }
 
 }  // extern "C"

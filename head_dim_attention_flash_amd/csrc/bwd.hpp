@@ -1,0 +1,637 @@
+// Backward attention kernels (head dimensions that are multiples of 64, up to
+// 512): dQ, dK and dV of O = softmax(scale * Q K^T + mask) V, given dO and
+// the forward's per-row logsumexp.
+//
+// The gradients are those of the "naive_math" definition (section 3 of the
+// attention-kernel-profiler design document), in the standard flash form
+// that the "FFPA Attention Benchmark" backward counts as 5 GEMMs:
+//     P  = exp(scale S + mask - lse),  S = Q K^T        (recomputed, never stored)
+//     dV = P^T dO,   dP = dO V^T,   delta_i = sum_d dO_id O_id
+//     dS = P o (dP - delta),   dK = scale dS^T Q,   dQ = scale dS K
+// with GQA gradients summed over the query heads of a group. Three launches:
+//  1. bwd_prep_kernel: delta and lse * log2(e) per row into the workspace
+//     (padded rows get delta = 0 and +inf, which makes their P zero);
+//  2. bwd_dkdv_kernel: one workgroup per 64 keys of a (batch, kv head),
+//     looping over every query tile of every query head of the group;
+//  3. bwd_dq_kernel: one workgroup per 64 queries of a (batch, head),
+//     looping over the key tiles.
+//
+// Register budget at D = 512. A workgroup is 4 waves = 2 row blocks of 32
+// (keys for dK/dV, queries for dQ) x 2 halves of D. A wave holds the
+// operands of its rows for its half of D (K and V, or Q and dO: 128 AGPRs)
+// and the fp32 gradient accumulators of its rows for that half (256
+// registers). Each score-like product (S and dP) is a contraction over all
+// of D: a wave computes the partial sum over its half, the two waves of a
+// row block swap partial sums through LDS, and both then hold the full S and
+// dP tile (the sum a + b is the same in either order, so both see identical
+// values). Every product is an MFMA 32x32x16 with one operand streamed from
+// LDS: per wave and 32 x 32 tile, 4 products of D/2 = 64 MFMAs.
+//
+// Staged tiles (Q and dO, or K and V): 32 rows, double-buffered, copied
+// straight from global memory into LDS. Every row takes 1 KiB: the two
+// 512-byte halves hold the two halves of D, and granule g (8 elements) of a
+// half is stored at g ^ swz4(row), which keeps both the 16-byte row reads
+// and the transposed 8-byte reads conflict-free.
+#pragma once
+
+#include "ffpa_common.hpp"
+
+namespace ffpa {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // [B, Hq, Nq] natural log, from the forward
+  void* dq;
+  void* dk;
+  void* dv;
+  const void* mask;  // key bias [Nkv] in the input dtype, or null
+  float* delta;      // workspace [B * Hq * nq_pad]
+  float* lse2;       // workspace [B * Hq * nq_pad]: lse * log2(e), +inf for dead and padded rows
+  int B, Hq, Hkv, Nq, Nkv;
+  int nq_pad;        // Nq rounded up to 64
+  int causal;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  int wg_dkdv;       // B * Hkv * ceil(Nkv / 64)
+  int wg_dq;         // B * Hq * ceil(Nq / 64)
+};
+
+constexpr int kBwdRows = 32;                       // rows per staged tile
+constexpr int kBwdRowBytes = 1024;                 // LDS row pitch
+constexpr int kBwdHalfBytes = 512;                 // one half of D
+constexpr int kBwdTile = kBwdRows * kBwdRowBytes;  // 32 KiB
+constexpr int kBwdXchg = 8 * 1024;                 // per wave: partial S and dP tiles, fp32
+constexpr int kBwdLds = 4 * kBwdTile + 4 * kBwdXchg;  // 160 KiB
+constexpr int kBwdPad = 64;                        // workspace row padding
+
+// ---------------------------------------------------------------------------
+// Shared pieces of the two main kernels.
+// ---------------------------------------------------------------------------
+
+// Copy rows row0 .. row0 + 31 of a [rows, D] tensor (buffer resource `rs`)
+// into a staged tile at `dst`. Wave w issues rows w, w + 4, ...; lane t of a
+// row writes slot t % 32 of half t / 32, which holds the logical granule
+// (t % 32) ^ swz4(row) of that half. The whole offset sits in the range-
+// checked per-lane offset: rows past the end and granules past D/2 read as
+// zeros (the latter without memory traffic).
+template <int D>
+__device__ inline void bwd_copy_tile(__amdgpu_buffer_rsrc_t rs, FFPA_LDS char* dst, int row0,
+                                     int wave, int lane) {
+  constexpr int SG = D / 16;  // granules per half
+  const int u = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < kBwdRows / 4; ++r) {
+    const int n = wave + 4 * r;
+    const int gl = u ^ swz4(n);
+    const uint32_t lanepart = gl < SG ? (uint32_t)(half * SG + gl) << 4 : 0x80000000u;
+    dma16(rs, lanepart + (uint32_t)(row0 + n) * (D * 2), 0, dst + n * kBwdRowBytes);
+  }
+}
+
+// 16-byte row reads (MFMA A operand, m = row): lane l reads row l % 32,
+// granule 2 st + l / 32 of half `hf`, st = 8 a + c. Per-lane bases for c.
+__device__ inline void bwd_row_bases(int ln, int hf, uint32_t* ax) {
+  const int r = ln & 31, h = ln >> 5, x = swz4(r);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    ax[c] = (uint32_t)(r * kBwdRowBytes + hf * kBwdHalfBytes + (((2 * c + h) ^ x) << 4));
+}
+__device__ inline uint32_t bwd_row_addr(const uint32_t* ax, int st) { return ax[st & 7] + 256 * (st >> 3); }
+
+// Transposed reads (MFMA A operand, m = column d, k = row): for d-block db
+// of half `hf` and row group t2, lane l gets column 32 db + l % 32 of rows
+// 16 t2 + 8 (e / 4) + 4 (l / 32) + e % 4, e = 0..7 (two ds_read_b64_tr_b16).
+// That row order matches the C layout of a 32x32 MFMA result whose m index
+// is the row, so a P or dS tile feeds the B operand straight from registers.
+__device__ inline void bwd_tr_bases(int ln, int hf, uint32_t* tx) {
+  const int G = ln >> 4, gi = ln & 15;
+  const int vrow = 4 * (G >> 1) + (gi >> 2);
+  const int y = 2 * (G & 1) + ((gi & 3) >> 1);
+#pragma unroll
+  for (int r8 = 0; r8 < 2; ++r8) {
+    const int row = vrow + 8 * r8, x = swz4(row);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      tx[4 * r8 + e] = (uint32_t)(row * kBwdRowBytes + hf * kBwdHalfBytes + (((4 * e + y) ^ x) << 4) +
+                                  (gi & 1) * 8);
+  }
+}
+__device__ inline u32x4 bwd_tr_read(const FFPA_LDS char* tile, const uint32_t* tx, int db, int t2) {
+  const uint32_t off = 256 * (db >> 2) + 16 * t2 * kBwdRowBytes;
+  return join8(lds_read_tr(tile + tx[db & 3] + off), lds_read_tr(tile + tx[4 + (db & 3)] + off));
+}
+
+// Swap partial products with the partner wave (same rows, other half of D)
+// and add its part: afterwards s and p hold the full contractions. Contains
+// a workgroup barrier (every wave calls it).
+__device__ inline void bwd_exchange(FFPA_LDS char* xbase, int wave, int lane, f32x16& s, f32x16& p) {
+  FFPA_LDS f32x4* mine = (FFPA_LDS f32x4*)(xbase + wave * kBwdXchg) + lane;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mine[64 * j] = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+    mine[64 * (4 + j)] = f32x4{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+  }
+  wait_lgkm0();
+  barrier();
+  const FFPA_LDS f32x4* other = (const FFPA_LDS f32x4*)(xbase + (wave ^ 1) * kBwdXchg) + lane;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 x = other[64 * j], y = other[64 * (4 + j)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[4 * j + e] += x[e];
+      p[4 * j + e] += y[e];
+    }
+  }
+}
+
+// Partial products S (or S^T) and dP (or dP^T) over one half of D: A
+// fragments are rows of the staged tiles `ta` and `tb`, B fragments the
+// register operands `fa` and `fb` (AGPRs). The chains end padded for the
+// VALU/LDS reads of their results.
+template <bool BF16, int NS>
+__device__ inline void bwd_partials(const FFPA_LDS char* ta, const FFPA_LDS char* tb, const uint32_t* ax,
+                                    const u32x4* fa, const u32x4* fb, f32x16& s, f32x16& p) {
+  constexpr int kAhead = NS < 3 ? NS : 3;
+  u32x4 xa[kAhead], xb[kAhead];
+#pragma unroll
+  for (int st = 0; st < kAhead; ++st) {
+    xa[st] = lds_read16(ta + bwd_row_addr(ax, st));
+    xb[st] = lds_read16(tb + bwd_row_addr(ax, st));
+  }
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const u32x4 x = xa[st % kAhead], y = xb[st % kAhead];
+    if (st + kAhead < NS) {
+      xa[st % kAhead] = lds_read16(ta + bwd_row_addr(ax, st + kAhead));
+      xb[st % kAhead] = lds_read16(tb + bwd_row_addr(ax, st + kAhead));
+    }
+    if (st == 0) {
+      mfma32_asm<BF16, true, false, true>(s, x, fa[st]);
+      mfma32_asm<BF16, true, false, true>(p, y, fb[st]);
+    } else if (st == NS - 1) {
+      mfma32_asm<BF16, true, false>(s, x, fa[st]);
+      mfma32_asm<BF16, true, false, false, false, true>(p, y, fb[st]);
+    } else {
+      mfma32_asm<BF16, true, false>(s, x, fa[st]);
+      mfma32_asm<BF16, true, false>(p, y, fb[st]);
+    }
+  }
+}
+
+// Rows r = lane % 32 of a [32, D/2] fp32 result held transposed in MFMA
+// accumulators (acc[db][4 g4 + e] = element (r, 32 db + 8 g4 + 4 (lane/32) + e)),
+// scaled by `mul`, converted and written to a 512-byte-pitch LDS staging area
+// (granule g of row r at g ^ (r % 16)).
+template <bool BF16, int NDB>
+__device__ inline void bwd_stage_rows(FFPA_LDS char* st, const f32x16* acc, float mul, int lane) {
+  const int r = lane & 31, hie = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const u32x2 w = {Elem<BF16>::pack2(acc[db][4 * g4] * mul, acc[db][4 * g4 + 1] * mul),
+                       Elem<BF16>::pack2(acc[db][4 * g4 + 2] * mul, acc[db][4 * g4 + 3] * mul)};
+      const int g = 4 * db + g4;
+      *(FFPA_LDS u32x2*)(st + r * 512 + ((g ^ (r & 15)) << 4) + 8 * hie) = w;
+    }
+}
+
+// Store `rows` (<= 32) staged rows to dst (row pitch D elements), 16 bytes
+// per lane and instruction.
+template <int D, class T>
+__device__ inline void bwd_store_rows(T* dst, const FFPA_LDS char* st, int rows, int lane) {
+  constexpr int SG = D / 16;
+#pragma unroll
+  for (int it = 0; it < SG / 2; ++it) {
+    const int c = it * 64 + lane;
+    const int r = c / SG, g = c % SG;
+    const u32x4 x = *(const FFPA_LDS u32x4*)(st + r * 512 + ((g ^ (r & 15)) << 4));
+    if (r < rows) *(u32x4*)(dst + (size_t)r * D + 8 * g) = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1. delta_i = sum_d dO_id O_id and lse_i * log2(e), one wave per row.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  using T = typename Elem<BF16>::scalar;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.B * a.Hq * a.nq_pad) return;
+  const int64_t bh = row / a.nq_pad;
+  const int qi = (int)(row % a.nq_pad);
+  float dsum = 0.f, l2 = INFINITY;
+  if (qi < a.Nq) {
+    const size_t base = ((size_t)bh * a.Nq + qi) * D;
+    const T* O = (const T*)a.o + base;
+    const T* dO = (const T*)a.dout + base;
+    float acc = 0.f;
+    for (int gi = lane; gi < D / 8; gi += 64) {
+      const u32x4 x = *(const u32x4*)(O + 8 * gi), y = *(const u32x4*)(dO + 8 * gi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc += Elem<BF16>::to_f32((uint16_t)(x[e] & 0xffff)) * Elem<BF16>::to_f32((uint16_t)(y[e] & 0xffff));
+        acc += Elem<BF16>::to_f32((uint16_t)(x[e] >> 16)) * Elem<BF16>::to_f32((uint16_t)(y[e] >> 16));
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    dsum = acc;
+    const float l = a.lse[(size_t)bh * a.Nq + qi];
+    l2 = l == -INFINITY ? INFINITY : l * kLog2e;  // a dead row has P = 0
+  }
+  if (lane == 0) {
+    a.delta[row] = dsum;
+    a.lse2[row] = l2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK and dV. Wave (kb, hf) owns keys kw = 64 kt + 32 kb .. +31 and half hf
+// of D. Per query tile (32 rows of one query head):
+//    S, dP (32 q x 32 keys) partial over the half, swapped, summed;
+//    P = 2^(scale_log2 S + bias_log2 - lse2), dS = P (dP - delta);
+//    dV^T[half] += dO^T P,  dK^T[half] += Q^T dS.
+// Accumulators: dV^T in AGPRs, dK^T in VGPRs (m = d, n = key).
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdArgs a) {
+  static_assert(D % 64 == 0 && D <= 512, "D must be a multiple of 64, at most 512");
+  using E = Elem<BF16>;
+  using T = typename E::scalar;
+  using V8 = typename E::vec8;
+  constexpr int DW = D / 2, NS = DW / 16, NDB = DW / 32;
+  constexpr int QB = 0, OB = 2 * kBwdTile, XB = 4 * kBwdTile;
+  constexpr int NT = 2 * NDB;                   // phase-2 steps per accumulator set
+  constexpr int kTAhead = NT < 4 ? NT : 4;      // transposed-read lookahead
+
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = wave >> 1, hf = wave & 1;
+
+  const int n_kt = (a.Nkv + 63) / 64;
+  const int t = xcd_logical(blockIdx.x, a.wg_dkdv);
+  const int kt = t % n_kt, bhk = t / n_kt;
+  const int hk = bhk % a.Hkv, b = bhk / a.Hkv;
+  const int g = a.Hq / a.Hkv;
+  const int kw = kt * 64 + 32 * kb;
+
+  // K and V of the wave's keys, its half of D: B operands (k = d, n = key)
+  u32x4 kf[NS], vf[NS];
+  {
+    const int key = min(kw + (lane & 31), a.Nkv - 1);  // keys past the end: never stored
+    const size_t off = ((size_t)(b * a.Hkv + hk) * a.Nkv + key) * D + hf * DW + 8 * (lane >> 5);
+    const u32x4* kp = (const u32x4*)((const T*)a.k + off);
+    const u32x4* vp = (const u32x4*)((const T*)a.v + off);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      kf[st] = kp[2 * st];
+      vf[st] = vp[2 * st];
+    }
+  }
+  float bias2 = 0.f;  // this lane's key bias, log2 domain
+  if (a.mask != nullptr) {
+    const int key = kw + (lane & 31);
+    bias2 = key < a.Nkv ? E::to_f32(((const uint16_t*)a.mask)[key]) * kLog2e : -INFINITY;
+  }
+
+  const int n_qt = (a.Nq + kBwdRows - 1) / kBwdRows;
+  const int qt0 = a.causal ? min(kt * 2, n_qt) : 0;  // earlier query tiles see none of these keys
+  const int per_head = n_qt - qt0;
+  const int n_it = g * per_head;
+  const uint32_t q_bytes = (uint32_t)a.Nq * D * 2;
+
+  auto issue = [&](int it) {
+    const int hh = hk * g + it / per_head;
+    const int qt = qt0 + it % per_head;
+    const size_t hoff = (size_t)(b * a.Hq + hh) * a.Nq * D * 2;
+    const int s = it & 1;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    bwd_copy_tile<D>(make_rsrc((const char*)a.q + hoff, q_bytes), smem + QB + s * kBwdTile, qt * kBwdRows, wave, ln);
+    bwd_copy_tile<D>(make_rsrc((const char*)a.dout + hoff, q_bytes), smem + OB + s * kBwdTile, qt * kBwdRows, wave, ln);
+  };
+
+  f32x16 dv[NDB], dk[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    dv[i] = f32x16{};
+    dk[i] = f32x16{};
+  }
+  if (n_it > 0) issue(0);
+
+  for (int it = 0; it < n_it; ++it) {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      asm volatile("" : "+a"(dv[d]));
+      asm volatile("" : "+v"(dk[d]));
+    }
+    const int hh = hk * g + it / per_head;
+    const int qt = qt0 + it % per_head;
+    const int s = it & 1;
+    const FFPA_LDS char* qtile = smem + QB + s * kBwdTile;
+    const FFPA_LDS char* otile = smem + OB + s * kBwdTile;
+    int lj = lane;
+    asm volatile("" : "+v"(lj));
+    const int hij = lj >> 5;
+    const int my_k = kw + (lj & 31);
+
+    wait_vmcnt<0>();  // this wave's copies of tile `it` landed ...
+    wait_lgkm0();
+    barrier();        // ... everyone's; tile it - 1 and the swap area are free
+
+    // lse2 and delta of rows 8 j + 4 hi + 0..3 of the tile
+    f32x4 l2[4], dl[4];
+    {
+      const size_t rb = (size_t)(b * a.Hq + hh) * a.nq_pad + qt * kBwdRows + 4 * hij;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        l2[j] = *(const f32x4*)(a.lse2 + rb + 8 * j);
+        dl[j] = *(const f32x4*)(a.delta + rb + 8 * j);
+      }
+    }
+    if (it + 1 < n_it) issue(it + 1);
+
+    // S = Q K^T and dP = dO V^T (32 q x 32 keys), partial over this half of D
+    f32x16 sacc, pacc;
+    {
+      uint32_t ax[8];
+      bwd_row_bases(lj, hf, ax);
+      bwd_partials<BF16, NS>(qtile, otile, ax, kf, vf, sacc, pacc);
+    }
+    bwd_exchange(smem + XB, wave, lj, sacc, pacc);
+
+    // P and dS; register i holds query 8 (i / 4) + 4 hi + i % 4 of the tile
+    float pv[16], dsv[16];
+    const int qg0 = qt * kBwdRows + 4 * hij;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = i >> 2, e = i & 3;
+      float x = fmaf(sacc[i], a.scale_log2, bias2) - l2[j][e];
+      if (a.causal && my_k > qg0 + 8 * j + e) x = -INFINITY;
+      const float p = exp2_fast(x);
+      pv[i] = p;
+      dsv[i] = p * (pacc[i] - dl[j][e]);
+    }
+    V8 pf[2], sf[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const float* x = &pv[8 * t2];
+      const float* y = &dsv[8 * t2];
+      pf[t2] = pack8<BF16>(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+      sf[t2] = pack8<BF16>(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
+    }
+    // every VALU write of the MFMA B operands happens before this point; the
+    // first MFMA below pads for the last of them
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[t2]), "+v"(sf[t2]));
+
+    // dV^T += dO^T P and dK^T += Q^T dS over the half's d-blocks; step
+    // st = NDB t2 + db, so consecutive MFMAs use different accumulators
+    {
+      uint32_t tx[8];
+      {
+        int lv = lane;
+        asm volatile("" : "+v"(lv));
+        bwd_tr_bases(lv, hf, tx);
+      }
+      u32x4 fo[kTAhead], fq[kTAhead];
+#pragma unroll
+      for (int st = 0; st < kTAhead; ++st) {
+        fo[st] = bwd_tr_read(otile, tx, st % NDB, st / NDB);
+        fq[st] = bwd_tr_read(qtile, tx, st % NDB, st / NDB);
+      }
+#pragma unroll
+      for (int st = 0; st < NT; ++st) {
+        const int db = st % NDB, t2 = st / NDB;
+        const u32x4 x = fo[st % kTAhead], y = fq[st % kTAhead];
+        if (st + kTAhead < NT) {
+          fo[st % kTAhead] = bwd_tr_read(otile, tx, (st + kTAhead) % NDB, (st + kTAhead) / NDB);
+          fq[st % kTAhead] = bwd_tr_read(qtile, tx, (st + kTAhead) % NDB, (st + kTAhead) / NDB);
+        }
+        const u32x4 pb = __builtin_bit_cast(u32x4, pf[t2]), sb = __builtin_bit_cast(u32x4, sf[t2]);
+        if (st == 0) mfma32_asm<BF16, false, true, false, true>(dv[db], x, pb);
+        else mfma32_asm<BF16, false, true>(dv[db], x, pb);
+        mfma32_asm<BF16, false, false>(dk[db], y, sb);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  // the accumulators were last written by MFMAs issued as inline asm: pad
+  // before the epilogue reads them
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 4" ::: "memory");
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    asm volatile("" : "+a"(dv[d]));
+    asm volatile("" : "+v"(dk[d]));
+  }
+
+  // ---- epilogue: each wave stages its 32 keys x D/2 of dV and dK (16 KiB
+  // each) in LDS, then stores them as contiguous 16-byte pieces
+  wait_lgkm0();
+  barrier();
+  FFPA_LDS char* stg = smem + wave * 2 * 16384;
+  bwd_stage_rows<BF16, NDB>(stg, dv, 1.f, lane);
+  bwd_stage_rows<BF16, NDB>(stg + 16384, dk, a.scale, lane);
+  {
+    const size_t row0 = ((size_t)(b * a.Hkv + hk) * a.Nkv + kw) * D + hf * DW;
+    const int rows = min(kBwdRows, a.Nkv - kw);
+    bwd_store_rows<D>((T*)a.dv + row0, stg, rows, lane);
+    bwd_store_rows<D>((T*)a.dk + row0, stg + 16384, rows, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ. Wave (qb, hf) owns queries qw = 64 qblk + 32 qb .. +31 and half hf
+// of D. Per key tile (32 keys):
+//    S^T, dP^T (32 keys x 32 q) partial over the half, swapped, summed;
+//    P = 2^(scale_log2 S + bias_log2 - lse2), dS = P (dP - delta);
+//    dQ^T[half] += K^T dS^T   (accumulators in AGPRs, m = d, n = query).
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdArgs a) {
+  static_assert(D % 64 == 0 && D <= 512, "D must be a multiple of 64, at most 512");
+  using E = Elem<BF16>;
+  using T = typename E::scalar;
+  using V8 = typename E::vec8;
+  constexpr int DW = D / 2, NS = DW / 16, NDB = DW / 32;
+  constexpr int KB = 0, VB = 2 * kBwdTile, XB = 4 * kBwdTile;
+  constexpr int NT = 2 * NDB;
+  constexpr int kTAhead = NT < 6 ? NT : 6;
+
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qb = wave >> 1, hf = wave & 1;
+
+  const int n_qb = (a.Nq + 63) / 64;
+  const int t = xcd_logical(blockIdx.x, a.wg_dq);
+  int qblk = t % n_qb;
+  const int bh = t / n_qb;
+  if (a.causal) qblk = n_qb - 1 - qblk;  // longest rows first
+  const int h = bh % a.Hq, b = bh / a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int qw = qblk * 64 + 32 * qb;
+
+  // Q and dO of the wave's rows, its half of D: B operands (k = d, n = query)
+  u32x4 qf[NS], of[NS];
+  {
+    const int qr = min(qw + (lane & 31), a.Nq - 1);  // rows past the end: never stored
+    const size_t off = ((size_t)(b * a.Hq + h) * a.Nq + qr) * D + hf * DW + 8 * (lane >> 5);
+    const u32x4* qp = (const u32x4*)((const T*)a.q + off);
+    const u32x4* op = (const u32x4*)((const T*)a.dout + off);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      qf[st] = qp[2 * st];
+      of[st] = op[2 * st];
+    }
+  }
+  // this lane's row: lse2 (+inf past Nq) and delta, from the padded workspace
+  const size_t wrow = (size_t)(b * a.Hq + h) * a.nq_pad + qw + (lane & 31);
+  const float lse2_me = a.lse2[wrow];
+  const float dl_me = a.delta[wrow];
+
+  int kv_end = a.Nkv;
+  if (a.causal) kv_end = min(kv_end, min(qblk * 64 + 64, a.Nq));  // keys <= last row of the block
+  const int n_kt = (kv_end + kBwdRows - 1) / kBwdRows;
+  const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Nkv * D * 2;
+  const uint32_t kv_bytes = (uint32_t)a.Nkv * D * 2;
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc((const char*)a.k + kvoff, kv_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc((const char*)a.v + kvoff, kv_bytes);
+  const uint16_t* mk = (const uint16_t*)a.mask;
+
+  auto issue = [&](int j) {
+    const int s = j & 1;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    bwd_copy_tile<D>(Kr, smem + KB + s * kBwdTile, j * kBwdRows, wave, ln);
+    bwd_copy_tile<D>(Vr, smem + VB + s * kBwdTile, j * kBwdRows, wave, ln);
+  };
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
+  if (n_kt > 0) issue(0);
+
+  for (int j = 0; j < n_kt; ++j) {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) asm volatile("" : "+a"(dq[d]));
+    const int s = j & 1;
+    const FFPA_LDS char* ktile = smem + KB + s * kBwdTile;
+    const FFPA_LDS char* vtile = smem + VB + s * kBwdTile;
+    int lj = lane;
+    asm volatile("" : "+v"(lj));
+    const int hij = lj >> 5;
+    const int my_q = qw + (lj & 31);
+    const int kg0 = j * kBwdRows + 4 * hij;  // register i holds key kg0 + 8 (i / 4) + i % 4
+
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    barrier();
+
+    float bias2[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kg0 + 8 * (i >> 2) + (i & 3);
+      if (mk != nullptr) {
+        const float bv = E::to_f32(mk[min(key, a.Nkv - 1)]) * kLog2e;
+        bias2[i] = key < a.Nkv ? bv : -INFINITY;
+      } else {
+        bias2[i] = key < a.Nkv ? 0.f : -INFINITY;
+      }
+    }
+    if (j + 1 < n_kt) issue(j + 1);
+
+    // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 q), partial over the half
+    f32x16 sacc, pacc;
+    {
+      uint32_t ax[8];
+      bwd_row_bases(lj, hf, ax);
+      bwd_partials<BF16, NS>(ktile, vtile, ax, qf, of, sacc, pacc);
+    }
+    bwd_exchange(smem + XB, wave, lj, sacc, pacc);
+
+    float dsv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = fmaf(sacc[i], a.scale_log2, bias2[i]) - lse2_me;
+      if (a.causal && kg0 + 8 * (i >> 2) + (i & 3) > my_q) x = -INFINITY;
+      const float p = exp2_fast(x);
+      dsv[i] = p * (pacc[i] - dl_me);
+    }
+    V8 sf[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const float* y = &dsv[8 * t2];
+      sf[t2] = pack8<BF16>(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(sf[t2]));
+
+    // dQ^T += K^T dS^T over the half's d-blocks
+    {
+      uint32_t tx[8];
+      {
+        int lv = lane;
+        asm volatile("" : "+v"(lv));
+        bwd_tr_bases(lv, hf, tx);
+      }
+      u32x4 fk[kTAhead];
+#pragma unroll
+      for (int st = 0; st < kTAhead; ++st) fk[st] = bwd_tr_read(ktile, tx, st % NDB, st / NDB);
+#pragma unroll
+      for (int st = 0; st < NT; ++st) {
+        const int db = st % NDB, t2 = st / NDB;
+        const u32x4 x = fk[st % kTAhead];
+        if (st + kTAhead < NT) fk[st % kTAhead] = bwd_tr_read(ktile, tx, (st + kTAhead) % NDB, (st + kTAhead) / NDB);
+        const u32x4 sb = __builtin_bit_cast(u32x4, sf[t2]);
+        if (st == 0) mfma32_asm<BF16, false, true, false, true>(dq[db], x, sb);
+        else mfma32_asm<BF16, false, true>(dq[db], x, sb);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 4" ::: "memory");
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) asm volatile("" : "+a"(dq[d]));
+
+  wait_lgkm0();
+  barrier();
+  FFPA_LDS char* stg = smem + wave * 16384;
+  bwd_stage_rows<BF16, NDB>(stg, dq, a.scale, lane);
+  {
+    const size_t row0 = ((size_t)(b * a.Hq + h) * a.Nq + qw) * D + hf * DW;
+    bwd_store_rows<D>((T*)a.dq + row0, stg, min(kBwdRows, a.Nq - qw), lane);
+  }
+}
+
+// Host launcher: the three kernels in order on `stream`.
+template <int D, bool BF16>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  auto kdkdv = bwd_dkdv_kernel<D, BF16>;
+  auto kdq = bwd_dq_kernel<D, BF16>;
+  static const hipError_t attr1 =
+      hipFuncSetAttribute((const void*)kdkdv, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
+  static const hipError_t attr2 =
+      hipFuncSetAttribute((const void*)kdq, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
+  if (attr1 != hipSuccess) return attr1;
+  if (attr2 != hipSuccess) return attr2;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.nq_pad;
+  hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kdkdv, dim3(a.wg_dkdv), dim3(256), kBwdLds, stream, a);
+  hipLaunchKernelGGL(kdq, dim3(a.wg_dq), dim3(256), kBwdLds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ffpa

@@ -1,0 +1,7 @@
+// Instances of the backward kernels for head dimension 128.
+#include "bwd.hpp"
+
+namespace ffpa {
+template hipError_t launch_bwd<128, false>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd<128, true>(const BwdArgs&, hipStream_t);
+}  // namespace ffpa

@@ -214,7 +214,8 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 
 // 16-byte direct copy buffer -> LDS: lane t of the wave reads
 // rsrc[voff + soff .. +16) and writes LDS bytes [16 t, 16 t + 16) after
-// `lds_base` (wave-uniform). Out-of-range reads write zeros.
+// `lds_base` (wave-uniform). The range check applies to voff only (the scalar
+// offset is not checked): reads with voff at or past the range write zeros.
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
                              FFPA_LDS void* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_base, 16, voff, soff, 0, 0);

@@ -153,13 +153,15 @@ void fwd_prefill_kernel(FwdArgs a) {
   // ---- copy of one tile of K or V into its buffer. Copy instruction n of a
   // tile (n = wave + 4 r) fills LDS row n: lane i writes slot i, which holds
   // the logical granule i ^ swz4(n) of key row (64 tile + n). Granules past D
-  // get an out-of-range offset and cost no memory traffic.
+  // get an out-of-range offset and cost no memory traffic. The whole byte
+  // offset goes in the per-lane offset, the part the buffer range check
+  // covers, so that rows at or past Nkv read as zeros.
   auto issue_copy = [&](__amdgpu_buffer_rsrc_t rs, int buf, int tile, int r, int ln) {
     const int n = wave + kFwdWaves * r;
     const int lg = ln ^ swz4(n);
-    const uint32_t voff = (GPR == 64 || lg < GPR) ? (uint32_t)lg << 4 : 0x80000000u;
-    const uint32_t soff = (uint32_t)(tile * kFwdBc + n) * (D * 2);
-    dma16(rs, voff, soff, smem + buf + n * ROWB);
+    const uint32_t lanepart = (GPR == 64 || lg < GPR) ? (uint32_t)lg << 4 : 0x80000000u;
+    const uint32_t voff = lanepart + (uint32_t)(tile * kFwdBc + n) * (D * 2);
+    dma16(rs, voff, 0, smem + buf + n * ROWB);
   };
   auto issue_tile = [&](__amdgpu_buffer_rsrc_t rs, int buf, int tile) {
     int ln = lane;  // recomputed at each call rather than held across the loop

@@ -37,7 +37,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attn_fwd", "attn_bwd", "to_f64"]
+__all__ = ["attn_fwd", "attn_bwd", "attn_probs", "to_f64"]
 
 
 def to_f64(x) -> np.ndarray:
@@ -151,3 +151,22 @@ def attn_bwd(q, k, v, dout, scale, causal=False, mask=None, row_block=1024):
                 dq[b, h, r0:r1] = scale * (ds @ k[b, hk])
                 dk[b, hk] += scale * (ds.T @ q[b, h, r0:r1])
     return dq, dk, dv
+
+
+def attn_probs(q, k, scale, causal=False, mask=None):
+    """The materialised softmax P [B, Hq, Nq, Nkv] (float64) of attn_fwd.
+
+    For small shapes only (P is held whole). Tests use it to size rounding
+    bounds; it is the same _scores/_softmax_rows path attn_fwd takes.
+    """
+    q, k, mask = to_f64(q), to_f64(k), to_f64(mask)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    pos = np.arange(Nq)
+    p = np.zeros((B, Hq, Nq, Nkv))
+    for b in range(B):
+        for h in range(Hq):
+            s = _scores(q[b, h], k[b, h // g], float(scale), mask, causal, pos)
+            p[b, h], _ = _softmax_rows(s)
+    return p

@@ -90,6 +90,12 @@ def test_forward_validation(kw, code):
     (dict(Hq=4, Hkv=3), ffpa.ERR_INVALID_ARG),
     (dict(D=1100), ffpa.ERR_UNSUPPORTED),
     (dict(accum_dtype=1), ffpa.ERR_UNSUPPORTED),
+    (dict(dv=P + 8), ffpa.ERR_INVALID_ARG),
+    (dict(workspace=0, workspace_bytes=1 << 20), ffpa.ERR_WORKSPACE),
+    (dict(workspace=P, workspace_bytes=16), ffpa.ERR_WORKSPACE),
+    (dict(workspace=P, workspace_bytes=1 << 30, mask=P, mask_rows=8), ffpa.ERR_UNSUPPORTED),
+    (dict(workspace=P, workspace_bytes=1 << 30, D=576), ffpa.ERR_UNSUPPORTED),
+    (dict(workspace=P, workspace_bytes=1 << 30, D=96), ffpa.ERR_UNSUPPORTED),
 ])
 def test_backward_validation(kw, code):
     assert bwd(**kw) == code

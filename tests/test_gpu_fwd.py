@@ -194,3 +194,40 @@ def test_growing_row_max(lib, slope, D, dtype, accum):
                       accum=accum, scale=scale)
         _compare(o, lse, q, k, v, scale, causal, ramp, dtype, accum,
                  f"ramp{slope}-D{D}-{dtype}-{accum}-causal{causal}")
+
+
+DECODE_CASES = [
+    # (B, Hq, Hkv, 1, Nkv, D): the split-KV decode kernels
+    (2, 8, 2, 1, 1000, 1024),   # GQA g = 4, D = 1024 (two granules per lane)
+    (1, 4, 4, 1, 3, 96),        # fewer keys than one step
+    (3, 2, 1, 1, 4097, 576),    # ragged last range
+    (1, 1, 1, 1, 1, 64),        # one key
+    (2, 16, 16, 1, 8192, 512),  # the decode shape, fewer heads
+    (1, 2, 2, 1, 300, 320),     # D / 8 not a multiple of 64 lanes
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_CASES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("variant", ["plain", "causal", "mask"])
+def test_decode_matches_oracle(lib, shape, dtype, variant):
+    B, Hq, Hkv, Nq, Nkv, D = shape
+    causal = variant == "causal"
+    mk = "key" if variant == "mask" else None
+    q, k, v, mask = _inputs(500 + sum(shape), B, Hq, Hkv, Nq, Nkv, D, dtype, mk)
+    if mask is not None:
+        mask[0, 0] = 0.0
+    scale = 1.0 / math.sqrt(D)
+    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), causal=causal,
+                  mask=None if mask is None else mask.cuda(), scale=scale)
+    _compare(o, lse, q, k, v, scale, causal, mask, dtype, "f32", f"decode-{shape}-{dtype}-{variant}")
+
+
+def test_decode_fully_masked_row(lib):
+    # every key masked: O = 0 and lse = -inf (the oracle's reading of a dead row)
+    B, Hq, Hkv, Nq, Nkv, D = 1, 2, 2, 1, 700, 512
+    q, k, v, _ = _inputs(600, B, Hq, Hkv, Nq, Nkv, D, "fp16")
+    mask = torch.full((1, Nkv), float("-inf"), dtype=torch.float16)
+    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), mask=mask.cuda())
+    assert torch.count_nonzero(o).item() == 0
+    assert torch.isneginf(lse).all()

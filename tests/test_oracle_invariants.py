@@ -162,3 +162,21 @@ def test_backward_zero_query_dv_is_mean_of_dout():
     _, _, dv = attn_bwd(q, k, v, do, 0.4)
     np.testing.assert_allclose(dv, np.broadcast_to(do.sum(axis=2, keepdims=True) / 25, dv.shape),
                                atol=1e-14)
+
+
+def test_attn_probs_rows_and_product():
+    # the materialised softmax: rows sum to 1 (0 for a dead row) and P V is attn_fwd's O
+    from oracle import attn_probs
+
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, 2, 9, 16))
+    k = rng.standard_normal((1, 1, 7, 16))
+    v = rng.standard_normal((1, 1, 7, 16))
+    mask = rng.standard_normal((1, 7))
+    mask[0, 0] = -np.inf
+    p = attn_probs(q, k, 0.25, causal=True, mask=mask)
+    o, _ = attn_fwd(q, k, v, 0.25, causal=True, mask=mask)
+    sums = p.sum(axis=-1)
+    assert np.allclose(sums[:, :, 1:], 1.0, atol=1e-12)
+    assert np.all(sums[:, :, 0] == 0.0)  # row 0 sees only key 0, which is masked
+    assert np.allclose(p @ v[0, 0], o, atol=1e-12)
