@@ -97,9 +97,14 @@ typedef enum {
  *   accum_dtype : FFPA_ACC_F32 or FFPA_ACC_F16 (see the reading above).
  *   dtype     : FFPA_F16 or FFPA_BF16, for q, k, v, mask and o.
  *   workspace : device scratch of at least ffpa_attn_fwd_workspace_size(...)
- *               bytes (NULL allowed when that size is 0). Used by the
- *               split-KV decode path for partial outputs.
+ *               bytes (NULL allowed when that size is 0). Nq = 1 takes the
+ *               split-KV decode path, which keeps per-key-range partial
+ *               outputs (fp32 o and log-sum-exp) there; other shapes need none.
  *   stream    : hipStream_t to enqueue on.
+ * Built today: every D (multiple of 32, <= 1024) for Nq = 1; D a multiple of
+ * 64 up to 512 for Nq > 1; the mask as a key bias (mask_rows = 1). Other
+ * valid shapes return FFPA_ERR_UNSUPPORTED before any launch. With Nq = 1
+ * the accumulation is fp32 whatever accum_dtype asks for.
  */
 int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
@@ -114,8 +119,13 @@ size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
  * layout as q, k, v). o and lse must be the forward's outputs for the same
  * q, k, v, scale, causal and mask. dk and dv of a K/V head sum the
  * contributions of all query heads that share it. accum_dtype must be
- * FFPA_ACC_F32. workspace: at least ffpa_attn_bwd_workspace_size(...) bytes
- * (holds delta_i = sum_d dO_id O_id and float32 partial gradients).
+ * FFPA_ACC_F32. workspace: at least ffpa_attn_bwd_workspace_size(...) bytes,
+ * 16-byte aligned (holds delta_i = sum_d dO_id O_id and lse_i log2(e) per
+ * query row, rows padded to a multiple of 64). Three kernels are enqueued:
+ * the delta pass, then dK/dV, then dQ. Built for D a multiple of 64 up to 512
+ * and the key-bias mask; other valid shapes return FFPA_ERR_UNSUPPORTED.
+ * The gradients are those of sum(dout * O) ("FFPA Attention Benchmark",
+ * "More Benchmark": the backward counted as 5 GEMMs).
  */
 int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv,
