@@ -10,8 +10,11 @@ instruction counted as one wait state, ``s_nop N`` as N + 1) and reports:
 * a VALU/accvgpr/LDS/VMEM instruction that reads or overwrites an MFMA
   result fewer than ``MFMA_TO_VALU`` wait states after that MFMA.
 
-Branches are ignored (the scan follows the text), which is conservative for
-fall-through code. Usage: ``python -m head_dim_attention_flash_amd.check_hazards``.
+The scan follows the control flow: basic blocks split at labels and
+branches, and the pending distances (registers still inside a hazard window)
+flow along every edge, loop back-edges included, taking at each block entry
+the worst case over its predecessors until nothing changes.
+Usage: ``python -m head_dim_attention_flash_amd.check_hazards``.
 """
 from __future__ import annotations
 
@@ -41,7 +44,7 @@ def regs(text: str) -> set[tuple[str, int]]:
 
 
 def kernels(asm: str):
-    """Yield (name, [instruction lines]) for every kernel in an assembly file."""
+    """Yield (name, [instruction or 'label:' lines]) for every kernel in an assembly file."""
     name, body = None, []
     for line in asm.splitlines():
         m = re.match(r"^(_Z\w+):", line)
@@ -51,10 +54,12 @@ def kernels(asm: str):
         if name is None:
             continue
         t = line.split(";")[0].strip()
-        if not t or t.startswith(".") or t.endswith(":"):
-            if "s_endpgm" in t:
-                yield name, body
-                name = None
+        if not t or t.startswith("."):
+            if t.startswith(".L") and t.endswith(":"):
+                body.append(t)  # a local label (branch target)
+            continue
+        if t.endswith(":"):
+            body.append(t)
             continue
         body.append(t)
         if t.startswith("s_endpgm"):
@@ -62,40 +67,99 @@ def kernels(asm: str):
             name = None
 
 
-def check_kernel(lines):
-    issues = []
-    clock = 0
-    last_valu_write = {}   # reg -> clock
-    last_mfma_write = {}   # reg -> (clock, index)
+def _effects(ins):
+    """(wait states, kind, written regs, read regs) of one instruction."""
+    op = ins.split()[0]
+    if op == "s_nop":
+        return int(ins.split()[1], 0) + 1, "nop", set(), set()
+    operands = ins[len(op):]
+    parts = [p.strip() for p in operands.split(",")]
+    if op.startswith("v_mfma"):
+        return 1, "mfma", regs(parts[0]), regs(",".join(parts[1:4]))
+    if op.startswith(("v_", "ds_", "buffer_", "global_", "scratch_")):
+        written = regs(parts[0]) if op.startswith("v_") and parts and parts[0] else set()
+        return 1, "vec", written, regs(operands)
+    return 1, "other", set(), set()
+
+
+def _blocks(lines):
+    """Basic blocks: list of (label or None, [instruction indices]) and the successor map."""
+    blocks, cur, label = [], [], None
     for i, ins in enumerate(lines):
+        if ins.endswith(":"):
+            if cur or label is not None:
+                blocks.append((label, cur))
+            label, cur = ins[:-1], []
+            continue
+        cur.append(i)
         op = ins.split()[0]
-        if op == "s_nop":
-            clock += int(ins.split()[1], 0) + 1
-            continue
-        clock += 1
-        operands = ins[len(op):]
-        parts = [p.strip() for p in operands.split(",")]
-        if op.startswith("v_mfma"):
-            dst, srcs = regs(parts[0]), regs(",".join(parts[1:4]))
-            for r in srcs:
-                t = last_valu_write.get(r)
-                if t is not None and clock - t < VALU_TO_MFMA:
-                    issues.append((i, f"VALU write of {r} read by MFMA after {clock - t} wait states: {ins}"))
-            for r in dst:
-                last_mfma_write[r] = (clock, i)
-            continue
-        if not (op.startswith("v_") or op.startswith("ds_") or op.startswith("buffer_")
-                or op.startswith("global_") or op.startswith("scratch_")):
-            continue
-        touched = regs(operands)
-        for r in touched:
-            w = last_mfma_write.get(r)
-            if w is not None and clock - w[0] < MFMA_TO_VALU:
-                issues.append((i, f"{op} touches MFMA result {r} after {clock - w[0]} wait states: {ins}"))
-        if op.startswith("v_") and parts and parts[0]:
-            for r in regs(parts[0]):
-                last_valu_write[r] = clock
-    return issues
+        if op.startswith("s_branch") or op.startswith("s_cbranch") or op == "s_endpgm" or op.startswith("s_setpc"):
+            blocks.append((label, cur))
+            label, cur = None, []
+    if cur or label is not None:
+        blocks.append((label, cur))
+    index = {lab: k for k, (lab, _) in enumerate(blocks) if lab is not None}
+    succ = []
+    for k, (_, idx) in enumerate(blocks):
+        last = lines[idx[-1]].split() if idx else [""]
+        op = last[0]
+        nxt = [k + 1] if k + 1 < len(blocks) else []
+        if op == "s_branch":
+            succ.append([index[last[1]]] if last[1] in index else [])
+        elif op.startswith("s_cbranch"):
+            tgt = [index[last[1]]] if len(last) > 1 and last[1] in index else []
+            succ.append(tgt + nxt)
+        elif op == "s_endpgm" or op.startswith("s_setpc"):
+            succ.append([])
+        else:
+            succ.append(nxt)
+    return blocks, succ
+
+
+def check_kernel(lines):
+    """Hazards in one kernel's instruction list (labels as 'name:' lines)."""
+    blocks, succ = _blocks(lines)
+    # state: (mfma_pending, valu_pending): reg -> wait states still required
+    entry = {0: ({}, {})} if blocks else {}
+    issues = {}
+    work = [0] if blocks else []
+    while work:
+        k = work.pop()
+        mp, vp = (dict(d) for d in entry[k])
+        for i in blocks[k][1]:
+            w, kind, written, read = _effects(lines[i])
+            if kind == "other" and w == 1 and not written and not read:
+                pass
+            mp = {r: c - w for r, c in mp.items() if c - w > 0}
+            vp = {r: c - w for r, c in vp.items() if c - w > 0}
+            if kind == "mfma":
+                for r in read:
+                    if r in vp:
+                        issues.setdefault(i, f"VALU write of {r} read by MFMA {VALU_TO_MFMA - vp[r]} wait states later: {lines[i]}")
+                for r in written:
+                    mp[r] = MFMA_TO_VALU
+            elif kind == "vec":
+                for r in read | written:
+                    if r in mp:
+                        issues.setdefault(i, f"{lines[i].split()[0]} touches MFMA result {r} "
+                                             f"{MFMA_TO_VALU - mp[r]} wait states after it: {lines[i]}")
+                for r in written:
+                    vp[r] = VALU_TO_MFMA
+        for n in succ[k]:
+            old = entry.get(n)
+            if old is None:
+                entry[n] = (dict(mp), dict(vp))
+                work.append(n)
+                continue
+            changed = False
+            for o, x in ((old[0], mp), (old[1], vp)):
+                for r, c in x.items():
+                    if o.get(r, 0) < c:
+                        o[r] = c
+                        changed = True
+            if changed:
+                work.append(n)
+    return sorted(issues.items())
 
 
 def check_file(src: str) -> list[str]:

@@ -9,6 +9,7 @@
 #include "bwd.hpp"
 #include "decode.hpp"
 #include "fwd_prefill.hpp"
+#include "fwd_wide.hpp"
 
 namespace {
 
@@ -45,6 +46,21 @@ FwdLauncher fwd_launcher(int D, int bf16, int acc16, size_t* ring_bytes) {
     FFPA_CASE(384)
     FFPA_CASE(448)
     FFPA_CASE(512)
+#undef FFPA_CASE
+    default:
+      return nullptr;
+  }
+}
+
+using WideLauncher = hipError_t (*)(const ffpa::FwdArgs&, hipStream_t);
+
+WideLauncher wide_launcher(int D, int bf16) {
+  switch (D) {
+#define FFPA_CASE(DD) \
+  case DD:            \
+    return bf16 ? ffpa::launch_fwd_wide<DD, true> : ffpa::launch_fwd_wide<DD, false>;
+    FFPA_CASE(576) FFPA_CASE(640) FFPA_CASE(704) FFPA_CASE(768)
+    FFPA_CASE(832) FFPA_CASE(896) FFPA_CASE(960) FFPA_CASE(1024)
 #undef FFPA_CASE
     default:
       return nullptr;
@@ -169,6 +185,28 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     a.n_waves = (int)waves;
     a.part_o = (float*)workspace;
     a.part_lse = (float*)workspace + (size_t)waves * D;
+    hipError_t e = launch(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    return FFPA_OK;
+  }
+
+  if (D > 512) {
+    // head dimensions above 512: D split across wave pairs
+    WideLauncher launch = wide_launcher(D, dtype == FFPA_BF16);
+    if (launch == nullptr)
+      return fail(FFPA_ERR_UNSUPPORTED, "for Nq > 1, D above 512 must be a multiple of 64");
+    if (mask != nullptr && mask_rows != 1)
+      return fail(FFPA_ERR_UNSUPPORTED, "per-query masks [Nq, Nkv] are not supported yet");
+    ffpa::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.mask = mask;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv;
+    a.mask_rows = mask ? 1 : 0;
+    a.causal = causal;
+    a.scale_log2 = scale * ffpa::kLog2e;
+    a.n_qtiles = (Nq + 63) / 64;
+    const int64_t total = (int64_t)B * Hq * a.n_qtiles;
+    if (total >= (int64_t(1) << 31)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
+    a.total_wg = (int)total;
     hipError_t e = launch(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return FFPA_OK;

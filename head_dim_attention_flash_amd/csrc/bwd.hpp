@@ -421,7 +421,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const u32x4 pb = __builtin_bit_cast(u32x4, pf[t2]), sb = __builtin_bit_cast(u32x4, sf[t2]);
         if (st == 0) mfma32_asm<BF16, false, true, false, true>(dv[db], x, pb);
         else mfma32_asm<BF16, false, true>(dv[db], x, pb);
-        mfma32_asm<BF16, false, false>(dk[db], y, sb);
+        // the iteration's last MFMA pads: the compiler may copy accumulators
+        // on the loop's exit or back edge right after it
+        if (st == NT - 1) mfma32_asm<BF16, false, false, false, false, true>(dk[db], y, sb);
+        else mfma32_asm<BF16, false, false>(dk[db], y, sb);
       }
     }
   }
@@ -596,7 +599,11 @@ void bwd_dq_kernel(BwdArgs a) {
         const u32x4 x = fk[st % kTAhead];
         if (st + kTAhead < NT) fk[st % kTAhead] = bwd_tr_read(ktile, tx, (st + kTAhead) % NDB, (st + kTAhead) / NDB);
         const u32x4 sb = __builtin_bit_cast(u32x4, sf[t2]);
-        if (st == 0) mfma32_asm<BF16, false, true, false, true>(dq[db], x, sb);
+        // first MFMA pads for the VALU writes of dS; the last for accumulator
+        // copies the compiler may place on the loop's exit or back edge
+        if (st == 0 && NT == 1) mfma32_asm<BF16, false, true, false, true, true>(dq[db], x, sb);
+        else if (st == 0) mfma32_asm<BF16, false, true, false, true>(dq[db], x, sb);
+        else if (st == NT - 1) mfma32_asm<BF16, false, true, false, false, true>(dq[db], x, sb);
         else mfma32_asm<BF16, false, true>(dq[db], x, sb);
       }
     }

@@ -1,0 +1,7 @@
+// Instances of the wide forward kernel (D split across wave pairs) for head dimension 576.
+#include "fwd_wide.hpp"
+
+namespace ffpa {
+template hipError_t launch_fwd_wide<576, false>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd_wide<576, true>(const FwdArgs&, hipStream_t);
+}  // namespace ffpa

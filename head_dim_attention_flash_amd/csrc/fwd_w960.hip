@@ -1,0 +1,7 @@
+// Instances of the wide forward kernel (D split across wave pairs) for head dimension 960.
+#include "fwd_wide.hpp"
+
+namespace ffpa {
+template hipError_t launch_fwd_wide<960, false>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd_wide<960, true>(const FwdArgs&, hipStream_t);
+}  // namespace ffpa

@@ -1,0 +1,366 @@
+// Forward attention for head dimensions above 512 (multiples of 64 up to 1024).
+//
+// Same operation as fwd_prefill.hpp: O = softmax(scale * Q K^T + mask) V and
+// lse per row (the "naive_math" definition of section 3 of the
+// attention-kernel-profiler design document; mask and GQA conventions of
+// "FFPA Attention Benchmark", "Quick Start", and the profiler's "gqa_4kv").
+// The D sweep of that benchmark page runs to D = 1024.
+//
+// At D = 1024 one wave cannot hold both the Q fragments and the fp32 output
+// accumulators of 32 rows (256 + 512 registers). So D is split in two halves
+// inside the workgroup: 4 waves = 2 row blocks of 32 queries x 2 halves of D.
+// A wave keeps Q and O of its 32 rows for its half only (D/8 + D/4
+// registers, at most 384), and per key tile
+//   1. computes the partial S^T = K_half Q_half^T (32 keys x 32 queries);
+//   2. swaps it with the wave holding the other half of the same rows through
+//      LDS and adds (a + b is the same in either order, so both waves hold
+//      identical scores and take identical softmax decisions);
+//   3. runs the online softmax (restart-based reference max, as in the
+//      prefill kernel with fp32 accumulation);
+//   4. accumulates O^T_half += V_half^T P^T.
+// Tiles are 32 keys; a staged K or V tile holds both halves, each half row
+// in its own 1 KiB LDS row (granules XOR-swizzled by swz4(row)), so a tile is
+// 64 KiB and K plus V fill 128 KiB. As in the prefill kernel the copy of V(j)
+// is issued when the K(j) phase starts and the copy of K(j+1) when the V(j)
+// phase starts.
+//
+// Accumulation is fp32 (the fp16-accumulator request maps to this kernel too:
+// it is at least as accurate).
+#pragma once
+
+#include "ffpa_common.hpp"
+#include "fwd_prefill.hpp"
+
+namespace ffpa {
+
+constexpr int kWideBc = 32;                      // keys per tile
+constexpr int kWideHalfTile = kWideBc * 1024;    // one half of a staged tile
+constexpr int kWideTile = 2 * kWideHalfTile;     // 64 KiB
+constexpr int kWideXchg = 4096;                  // per wave: a 32 x 32 fp32 tile
+constexpr int kWideLds = 2 * kWideTile + 4 * kWideXchg + 16;
+
+template <int D, bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void fwd_wide_kernel(FwdArgs a) {
+  static_assert(D % 64 == 0 && D > 512 && D <= 1024, "D must be a multiple of 64 in (512, 1024]");
+  using E = Elem<BF16>;
+  using V8 = typename E::vec8;
+  constexpr int W = D / 2;              // elements per half
+  constexpr int SG = W / 8;             // granules per half row (36 .. 64)
+  constexpr int NS = W / 16;            // k-steps of the partial product
+  constexpr int NDB = W / 32;           // output d-blocks of the half
+  constexpr int KB = 0, VB = kWideTile, XB = 2 * kWideTile, FB = 2 * kWideTile + 4 * kWideXchg;
+  constexpr int kKAhead = 3;
+  constexpr int kVAhead = 8;
+  // fp32 accumulator d-blocks in AGPRs (beside the W/4 Q registers); the rest in VGPRs
+  constexpr int kOAgpr = (256 - W / 4) / 16 < NDB ? (256 - W / 4) / 16 : NDB;
+
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = wave >> 1, hf = wave & 1;
+
+  // ---- workgroup -> (b, h, block of 64 rows)
+  const int n_qb = (a.Nq + 63) / 64;
+  const int t = xcd_logical(blockIdx.x, a.total_wg);
+  int qb = t % n_qb;
+  const int bh = t / n_qb;
+  if (a.causal) qb = n_qb - 1 - qb;  // longest rows first
+  const int h = bh % a.Hq, b = bh / a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int q0 = qb * 64;
+  const int qw = q0 + 32 * rb;        // first row of this wave
+
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * a.Nkv) * D * 2;
+  const uint32_t kv_bytes = (uint32_t)a.Nkv * D * 2;  // rows >= Nkv read as zeros
+  const __amdgpu_buffer_rsrc_t Kr = make_rsrc((const char*)a.k + kv_off, kv_bytes);
+  const __amdgpu_buffer_rsrc_t Vr = make_rsrc((const char*)a.v + kv_off, kv_bytes);
+
+  int kv_end = a.Nkv;
+  if (a.causal) kv_end = min(kv_end, min(q0 + 64, a.Nq));  // keys <= last row of the block
+  const int n_tiles = (kv_end + kWideBc - 1) / kWideBc;
+  const bool has_mask = a.mask_rows > 0;
+  const uint16_t* mk = (const uint16_t*)a.mask;
+
+  // ---- Q^T half in registers: lane holds Q[qw + l % 32][W hf + 16 s + 8 (l / 32) .. +7]
+  u32x4 qf[NS];
+  {
+    const typename E::scalar* Q = (const typename E::scalar*)a.q + ((size_t)(b * a.Hq + h) * a.Nq) * D;
+    const int qrow = min(qw + (lane & 31), a.Nq - 1);
+    const u32x4* qp = (const u32x4*)(Q + (size_t)qrow * D + W * hf + 8 * (lane >> 5));
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = qp[2 * s];
+  }
+
+  // ---- copies: instruction n of a tile (n = wave + 4 r, r < 16) fills half
+  // n / 32 of key row n % 32; lane i writes slot i = logical granule i ^ swz4(row)
+  auto issue_tile = [&](__amdgpu_buffer_rsrc_t rs, int buf, int tile) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = wave + 4 * r;
+      const int row = n & 31, half = n >> 5;
+      const int lg = ln ^ swz4(row);
+      const uint32_t lanepart = lg < SG ? (uint32_t)(half * SG + lg) << 4 : 0x80000000u;
+      const uint32_t voff = lanepart + (uint32_t)(tile * kWideBc + row) * (D * 2);
+      dma16(rs, voff, 0, smem + buf + half * kWideHalfTile + row * 1024);
+    }
+  };
+
+  // K fragment (A of S^T) for k-step st = 8 a + c: key row l % 32, granule 2 st + l / 32
+  auto k_bases = [&](int ln, uint32_t* kx) {
+    const int r = ln & 31, hh = ln >> 5, x = swz4(r);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      kx[c] = (uint32_t)(KB + hf * kWideHalfTile + r * 1024 + (((2 * c + hh) ^ x) << 4));
+  };
+  // V^T fragment by transposed reads: rows 16 t2 + 8 r8 + 4 (G / 2) + i / 4,
+  // columns 32 db + 16 (G % 2) + 4 (i % 4) of the half (G = lane / 16, i = lane % 16)
+  auto v_bases = [&](int ln, uint32_t* vx) {
+    const int G = ln >> 4, gi = ln & 15;
+    const int vrow = 4 * (G >> 1) + (gi >> 2);
+    const int y = 2 * (G & 1) + ((gi & 3) >> 1);
+#pragma unroll
+    for (int r8 = 0; r8 < 2; ++r8) {
+      const int row = vrow + 8 * r8, x = swz4(row);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vx[4 * r8 + e] = (uint32_t)(VB + hf * kWideHalfTile + row * 1024 + (((4 * e + y) ^ x) << 4) + (gi & 1) * 8);
+    }
+  };
+
+  f32x16 o_acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o_acc[i] = f32x16{};
+  float m_ref = -INFINITY;  // reference max (log2 domain)
+  float l_run = 0.f;        // this lane's partial row sum
+  bool fresh = true;        // no PV product accumulated yet in this attempt
+  FFPA_LDS uint32_t* restart_flag = (FFPA_LDS uint32_t*)(smem + FB);
+
+  if (n_tiles > 0) issue_tile(Kr, KB, 0);
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int j0 = j * kWideBc;
+    int lj = lane;
+    asm volatile("" : "+v"(lj));
+    const int hij = lj >> 5;
+    const int my_qj = qw + (lj & 31);
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      if (d < kOAgpr) asm volatile("" : "+a"(o_acc[d]));
+      else asm volatile("" : "+v"(o_acc[d]));
+    }
+
+    // ===== K phase: partial S^T over this half, two chains (even / odd k-steps)
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    barrier();
+    issue_tile(Vr, VB, j);
+    f32x16 s_acc, s_odd;
+    {
+      u32x4 kf[kKAhead];
+      uint32_t kx[8];
+      k_bases(lj, kx);
+      auto kread = [&](int st) { return lds_read16(smem + kx[st & 7] + 256 * (st >> 3)); };
+#pragma unroll
+      for (int st = 0; st < kKAhead; ++st) kf[st] = kread(st);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const u32x4 a0 = kf[st % kKAhead];
+        if (st + kKAhead < NS) kf[st % kKAhead] = kread(st + kKAhead);
+        f32x16& acc = (st & 1) ? s_odd : s_acc;
+        if (st < 2) mfma32_asm<BF16, true, false, true>(acc, a0, qf[st]);
+        else if (st == NS - 1) mfma32_asm<BF16, true, false, false, false, true>(acc, a0, qf[st]);
+        else mfma32_asm<BF16, true, false>(acc, a0, qf[st]);
+      }
+    }
+    // both chains end at least 19 wait states before this VALU (the last MFMA pads)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_acc[i] += s_odd[i];
+
+    // ===== swap partial scores with the other half's wave; add
+    {
+      FFPA_LDS f32x4* mine = (FFPA_LDS f32x4*)(smem + XB + wave * kWideXchg) + lj;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        mine[64 * jj] = f32x4{s_acc[4 * jj], s_acc[4 * jj + 1], s_acc[4 * jj + 2], s_acc[4 * jj + 3]};
+      wait_lgkm0();
+      barrier();
+      const FFPA_LDS f32x4* other = (const FFPA_LDS f32x4*)(smem + XB + (wave ^ 1) * kWideXchg) + lj;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 x = other[64 * jj];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_acc[4 * jj + e] += x[e];
+      }
+    }
+
+    // ===== online softmax (log2 domain); register i holds key j0 + 8 (i/4) + 4 hi + i%4
+    const int kb0 = j0 + 4 * hij;
+    const bool need_mask = has_mask || (j0 + kWideBc > a.Nkv) || (a.causal && j0 + kWideBc - 1 > qw);
+    float tv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tv[i] = s_acc[i] * a.scale_log2;
+    if (need_mask) {
+      int klim = a.Nkv - kb0;
+      if (a.causal) klim = min(klim, my_qj + 1 - kb0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = 8 * (i >> 2) + (i & 3);
+        if (has_mask) tv[i] += E::to_f32(mk[min(kb0 + c, a.Nkv - 1)]) * kLog2e;
+        tv[i] = c >= klim ? -INFINITY : tv[i];
+      }
+    }
+    float mx = tv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, tv[i]);
+    mx = fmaxf(mx, swap_halves(mx));
+    if (m_ref == -INFINITY) m_ref = mx;
+    {
+      const bool broke = mx > m_ref + fwd_tau<BF16>();
+      const uint32_t any_broke = __builtin_amdgcn_ballot_w64(broke) != 0 ? 1u : 0u;
+      if (lane == 0) restart_flag[wave] = any_broke;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      tv[i] = exp2_fast(tv[i] - m_use);
+      psum += tv[i];
+    }
+    l_run += psum;
+    V8 pf[2];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const float* x = &tv[8 * t2];
+      pf[t2] = pack8<BF16>(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[t2]));
+
+    // ===== V phase: O^T_half += V_half^T P^T
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    barrier();
+    {
+      const u32x4 f = *(const FFPA_LDS u32x4*)restart_flag;
+      if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // workgroup-uniform: restart the key loop
+        m_ref = fmaxf(m_ref, mx);
+        l_run = 0.f;
+        fresh = true;
+        issue_tile(Kr, KB, 0);
+        j = -1;
+        continue;
+      }
+    }
+    if (j + 1 < n_tiles) issue_tile(Kr, KB, j + 1);
+    {
+      constexpr int NSV = 2 * NDB;  // steps st = NDB t2 + db
+      uint32_t vx[8];
+      {
+        int lv = lane;
+        asm volatile("" : "+v"(lv));
+        v_bases(lv, vx);
+      }
+      auto vread = [&](int st) {
+        const int db = st % NDB, t2 = st / NDB;
+        const uint32_t off = 256 * (db >> 2) + 16 * t2 * 1024;
+        return join8(lds_read_tr(smem + vx[db & 3] + off), lds_read_tr(smem + vx[4 + (db & 3)] + off));
+      };
+      u32x4 vf[kVAhead];
+#pragma unroll
+      for (int st = 0; st < kVAhead; ++st) vf[st] = vread(st);
+#pragma unroll
+      for (int st = 0; st < NSV; ++st) {
+        const int db = st % NDB, t2 = st / NDB;
+        const u32x4 vbits = vf[st % kVAhead];
+        if (st + kVAhead < NSV) vf[st % kVAhead] = vread(st + kVAhead);
+        const u32x4 pb = __builtin_bit_cast(u32x4, pf[t2]);
+        // the t2 = 0 MFMA of a block starts its chain: zero C on a fresh attempt
+        if (t2 == 0) {
+          if (db < kOAgpr) {
+            if (st == 0) {
+              if (fresh) mfma32_asm<BF16, false, true, true, true>(o_acc[db], vbits, pb);
+              else mfma32_asm<BF16, false, true, false, true>(o_acc[db], vbits, pb);
+            } else {
+              if (fresh) mfma32_asm<BF16, false, true, true>(o_acc[db], vbits, pb);
+              else mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
+            }
+          } else {
+            if (st == 0) {
+              if (fresh) mfma32_asm<BF16, false, false, true, true>(o_acc[db], vbits, pb);
+              else mfma32_asm<BF16, false, false, false, true>(o_acc[db], vbits, pb);
+            } else {
+              if (fresh) mfma32_asm<BF16, false, false, true>(o_acc[db], vbits, pb);
+              else mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
+            }
+          }
+        } else {
+          if (db < kOAgpr) mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
+          else mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
+        }
+      }
+    }
+    fresh = false;
+  }
+  wait_vmcnt<0>();
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 4" ::: "memory");
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    if (d < kOAgpr) asm volatile("" : "+a"(o_acc[d]));
+    else asm volatile("" : "+v"(o_acc[d]));
+  }
+
+  // ===== epilogue: rows of the half through LDS (32 rows x 1 KiB per wave),
+  // then stored as contiguous pieces of W elements per row
+  const float l_tot = l_run + swap_halves(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  wait_lgkm0();
+  barrier();
+  FFPA_LDS char* ostage = smem + wave * 32 * 1024;
+  {
+    const int r = lane & 31, hie = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const u32x2 st = {E::pack2(o_acc[db][4 * g4] * inv, o_acc[db][4 * g4 + 1] * inv),
+                          E::pack2(o_acc[db][4 * g4 + 2] * inv, o_acc[db][4 * g4 + 3] * inv)};
+        const int g = 4 * db + g4;
+        *(FFPA_LDS u32x2*)(ostage + r * 1024 + ((g ^ (r & 15)) << 4) + 8 * hie) = st;
+      }
+  }
+  {
+    typename E::scalar* O = (typename E::scalar*)a.o + ((size_t)(b * a.Hq + h) * a.Nq + qw) * D + W * hf;
+    const int rows = min(32, a.Nq - qw);
+    constexpr int NIT = (32 * SG + 63) / 64;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int c = it * 64 + lane;
+      const int r = c / SG, g = c % SG;
+      if (r < rows) {
+        const u32x4 x = *(const FFPA_LDS u32x4*)(ostage + r * 1024 + ((g ^ (r & 15)) << 4));
+        *(u32x4*)(O + (size_t)r * D + 8 * g) = x;
+      }
+    }
+  }
+  if (hf == 0 && a.lse != nullptr && (lane >> 5) == 0 && qw + lane < a.Nq) {
+    float* L = a.lse + (size_t)(b * a.Hq + h) * a.Nq + qw + lane;
+    *L = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, bool BF16>
+hipError_t launch_fwd_wide(const FwdArgs& a, hipStream_t stream) {
+  auto kern = fwd_wide_kernel<D, BF16>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(a.total_wg), dim3(256), kWideLds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ffpa

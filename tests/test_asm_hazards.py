@@ -29,3 +29,29 @@ def test_checker_flags_a_planted_hazard():
              "v_add_f32 v3, v3, v3"]
     issues = H.check_kernel(lines)
     assert len(issues) == 2  # VALU -> MFMA operand, MFMA result -> VALU
+
+
+def test_checker_follows_loop_back_edges():
+    # the MFMA at the end of the loop body reaches the VALU at the loop top
+    lines = [".LBB0_1:", "v_add_f32 v3, v3, v3", "s_nop 7",
+             "v_mfma_f32_32x32x16_f16 v[2:17], v[46:49], v[42:45], v[2:17]",
+             "s_cbranch_scc1 .LBB0_1", "s_endpgm"]
+    issues = H.check_kernel(lines)
+    assert any("touches MFMA result" in m for _, m in issues)
+
+
+def test_checker_skips_code_after_an_unconditional_branch():
+    # the instruction after s_branch is reached only from .LBB0_9 (no MFMA there)
+    lines = ["v_mfma_f32_32x32x16_f16 v[2:17], v[46:49], v[42:45], v[2:17]",
+             "s_nop 7", "s_nop 7", "s_nop 4", "s_branch .LBB0_9",
+             "v_mov_b32 v3, 0", ".LBB0_9:", "v_add_f32 v3, v3, v3", "s_endpgm"]
+    assert H.check_kernel(lines) == []
+
+
+def test_checker_merges_predecessors_at_a_join():
+    # one predecessor pads, the other does not: the join must be flagged
+    lines = ["v_mfma_f32_32x32x16_f16 v[2:17], v[46:49], v[42:45], v[2:17]",
+             "s_cbranch_scc1 .LBB0_5", "s_nop 7", "s_nop 7", "s_nop 4",
+             ".LBB0_5:", "v_add_f32 v3, v3, v3", "s_endpgm"]
+    issues = H.check_kernel(lines)
+    assert any("touches MFMA result" in m for _, m in issues)

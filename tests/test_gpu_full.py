@@ -68,8 +68,6 @@ def test_full_size_forward(lib, name, accum):
 @pytest.mark.parametrize("D", [320, 448, 512, 576, 768, 1024])
 @pytest.mark.parametrize("accum", ["f32", "f16"])
 def test_head_dim_sweep(lib, D, accum):
-    if D > 512:
-        pytest.skip("D > 512 forward kernels are not built yet")
     _check(lib, f"dsweep{D}_{accum}")
 
 

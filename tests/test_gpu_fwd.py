@@ -99,6 +99,10 @@ CASES = [
     (1, 2, 1, 129, 1, 128),     # single key
     (1, 1, 1, 77, 700, 64),
     (1, 2, 2, 100, 100, 192),
+    (1, 2, 2, 200, 333, 576),   # D above 512: D split across wave pairs
+    (2, 4, 2, 130, 77, 768),    # GQA, Nq > Nkv
+    (1, 2, 2, 64, 300, 1024),
+    (1, 3, 1, 100, 100, 640),   # GQA g = 3
 ]
 
 
@@ -179,7 +183,7 @@ def test_deterministic(lib):
 
 
 @pytest.mark.parametrize("slope", [0.05, 0.5])
-@pytest.mark.parametrize("D", [128, 512])
+@pytest.mark.parametrize("D", [128, 512, 1024])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("accum", ["f32", "f16"])
 def test_growing_row_max(lib, slope, D, dtype, accum):
