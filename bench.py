@@ -290,7 +290,7 @@ def main(argv=None) -> int:
     ffpa.load()
     if args.suite:
         names = ["tiny", "self", "self_bf16", "cross", "gqa", "causal", "nonaligned", "mask"] + \
-                [f"dsweep{d}_f32" for d in (320, 448, 512)]
+                [f"dsweep{d}_f32" for d in (320, 448, 512, 576, 768, 1024)]
         for n in names:
             for acc in ("f32", "f16"):
                 line = run_one(ffpa, W, n, acc, args.steps, args.warmup, False, 0)

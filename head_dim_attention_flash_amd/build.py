@@ -25,9 +25,13 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
+# -pragma-unroll-threshold: the kernels' `#pragma unroll` loops must unroll in
+# full (their register arrays are indexed by the loop counter); the default
+# size limit gives up on the longest ones and falls back to indexed registers.
 FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-pragma-unroll-threshold=200000",
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]

@@ -176,6 +176,7 @@ __device__ inline void bwd_partials(const FFPA_LDS char* ta, const FFPA_LDS char
     } else if (st == NS - 1) {
       mfma32_asm<BF16, true, false>(s, x, fa[st]);
       mfma32_asm<BF16, true, false, false, false, true>(p, y, fb[st]);
+      pin_after_pad(s);
     } else {
       mfma32_asm<BF16, true, false>(s, x, fa[st]);
       mfma32_asm<BF16, true, false>(p, y, fb[st]);

@@ -154,6 +154,12 @@ __device__ inline void mfma32_asm(f32x16& acc, u32x4 a, u32x4 b) {
 }
 #undef FFPA_MFMA_ASM
 
+// Orders every later read of `acc` after this point. Used after an MFMA chain
+// that ends padded (LAST) on a sibling accumulator: the compiler would
+// otherwise be free to move a VALU read of `acc`, whose own last MFMA is
+// earlier, above that padding.
+__device__ inline void pin_after_pad(f32x16& acc) { asm volatile("" : "+v"(acc)); }
+
 template <class V>
 __device__ inline V as_vec8(u32x4 x) {
   return __builtin_bit_cast(V, x);
@@ -214,11 +220,25 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 
 // 16-byte direct copy buffer -> LDS: lane t of the wave reads
 // rsrc[voff + soff .. +16) and writes LDS bytes [16 t, 16 t + 16) after
-// `lds_base` (wave-uniform). The range check applies to voff only (the scalar
-// offset is not checked): reads with voff at or past the range write zeros.
+// `lds_base` (wave-uniform, passed in M0). The range check applies to voff
+// only (the scalar offset is not checked): reads with voff at or past the
+// range write zeros.
+//
+// Issued as inline asm on purpose. The compiler's wait-count pass treats a
+// copy into LDS it knows about as a pending LDS write, and when it cannot
+// prove that a later LDS read touches another buffer it waits for every
+// outstanding copy (s_waitcnt vmcnt(0)) before that read: a full memory
+// latency per tile. The kernels order copies and reads themselves
+// (wait_vmcnt before the barrier that publishes a tile), so the copy is kept
+// out of the compiler's tracking. s_nop 0 covers the M0 write -> LDS-copy
+// hazard.
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
                              FFPA_LDS void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_base, 16, voff, soff, 0, 0);
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds_base;
+  asm volatile("s_nop 0\n buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+               : "memory");
 }
 
 __device__ inline u32x4 lds_read16(const FFPA_LDS char* p) { return *(const FFPA_LDS u32x4*)p; }

@@ -169,6 +169,13 @@ void fwd_prefill_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < NDMA; ++r) issue_copy(rs, buf, tile, r, ln);
   };
+  // the copies of step st when a tile's NDMA copies are spread over the first
+  // `span` steps of a phase
+  auto issue_spread = [&](__amdgpu_buffer_rsrc_t rs, int buf, int tile, int st, int span, int ln) {
+#pragma unroll
+    for (int r = 0; r < NDMA; ++r)
+      if ((r * span) / NDMA == st) issue_copy(rs, buf, tile, r, ln);
+  };
 
   // ---- LDS read addresses: per-lane bases (recomputed at the start of each
   // phase, so they are live only there) plus compile-time offsets < 64 KiB.
@@ -244,9 +251,8 @@ void fwd_prefill_kernel(FwdArgs a) {
     wait_vmcnt<0>();  // K(j) landed (this wave's copies) ...
     wait_lgkm0();
     barrier();        // ... and everyone's; everyone is done with V(j-1)
-    // Copies are issued in one burst right after the barrier: spreading them
-    // between the MFMAs of the phase measured markedly slower.
-    issue_tile(Vr, VB, j);
+    // The copies of V(j) are spread over the first half of the phase's MFMAs
+    // (issue_spread), which keeps their LDS writes from piling up at once.
     f32x16 s_acc[2];
     {
       // K fragments are read kKAhead d-steps ahead of the MFMAs that use them
@@ -260,8 +266,11 @@ void fwd_prefill_kernel(FwdArgs a) {
         kf[st][0] = kread(st, 0);
         kf[st][1] = kread(st, 1);
       }
+      int lnc = lane;
+      asm volatile("" : "+v"(lnc));
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
+        issue_spread(Vr, VB, j, st, NS > 1 ? NS / 2 : 1, lnc);
         const u32x4 a0 = kf[st % kKAhead][0], a1 = kf[st % kKAhead][1];
         if (st + kKAhead < NS) {
           kf[st % kKAhead][0] = kread(st + kKAhead, 0);
@@ -275,6 +284,7 @@ void fwd_prefill_kernel(FwdArgs a) {
         } else if (st == NS - 1) {
           mfma32_asm<BF16, true, false, false>(s_acc[0], a0, qf[st]);
           mfma32_asm<BF16, true, false, false, false, true>(s_acc[1], a1, qf[st]);
+          pin_after_pad(s_acc[0]);
         } else {
           mfma32_asm<BF16, true, false>(s_acc[0], a0, qf[st]);
           mfma32_asm<BF16, true, false>(s_acc[1], a1, qf[st]);
@@ -401,12 +411,26 @@ void fwd_prefill_kernel(FwdArgs a) {
         continue;
       }
     }
-    const bool next_k = j + 1 < n_tiles;
-    if (next_k) issue_tile(Kr, KB, j + 1);
     {
-      // 4 MFMAs per output d-block (2 key blocks x 2 k-steps); V^T fragments
-      // are read kVAhead MFMAs ahead of their use
+      // Step order: consecutive MFMAs write different accumulators (a
+      // dependent MFMA waits for its predecessor's result). fp32
+      // accumulators: step st = NDB p + db, p = 2 kb + t2 the (key block,
+      // k-step) pair. fp16 accumulator: d-blocks go in pairs, each with a
+      // per-tile product in VGPRs: st = 8 q + 2 p + side, db = 2 q + side.
+      // V^T fragments are read kVAhead MFMAs ahead of their use.
       constexpr int NSV = 4 * NDB;
+      auto step = [](int st, int& db, int& kb, int& t2) {
+        int p;
+        if constexpr (ACC16) {
+          p = (st & 7) >> 1;
+          db = 2 * (st >> 3) + (st & 1);
+        } else {
+          p = st / NDB;
+          db = st % NDB;
+        }
+        kb = p >> 1;
+        t2 = p & 1;
+      };
       uint32_t vx[8];
       {
         int lv = lane;
@@ -414,76 +438,98 @@ void fwd_prefill_kernel(FwdArgs a) {
         v_bases(lv, vx);
       }
       auto vread = [&](int st) {
-        const int db = st >> 2, kb = (st >> 1) & 1, t2 = st & 1;
+        int db, kb, t2;
+        step(st, db, kb, t2);
         return join8(lds_read_tr(smem + v_addr(vx, db, kb, t2, 0)),
                      lds_read_tr(smem + v_addr(vx, db, kb, t2, 1)));
       };
       u32x4 vf[kVAhead];
 #pragma unroll
       for (int st = 0; st < kVAhead; ++st) vf[st] = vread(st);
-      f32x16 acc;
+      f32x16 acc_e, acc_o;  // fp16 path: per-tile products of the pair's even / odd block
+      auto fold = [&](const f32x16& acc, int d2) {
+        // o16 <- o16 * oscale + acc, in packed fp16
+        const f16x2 sc = {(_Float16)oscale, (_Float16)oscale};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4 w = o16[2 * d2 + hh];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            f16x2 cur = f16x2_from_bits(w[e]);
+            const f16x2 add = {(_Float16)acc[8 * hh + 2 * e], (_Float16)acc[8 * hh + 2 * e + 1]};
+            cur = cur * sc + add;
+            w[e] = __builtin_bit_cast(uint32_t, cur);
+          }
+          o16[2 * d2 + hh] = w;
+        }
+      };
+      int lnc = lane;
+      asm volatile("" : "+v"(lnc));
 #pragma unroll
       for (int st = 0; st < NSV; ++st) {
-        const int db = st >> 2, kb = (st >> 1) & 1, t2 = st & 1;
+        // on the last tile this copies rows past the key range (range-checked
+        // zeros) or, causal, rows nobody reads: harmless, and branch-free
+        issue_spread(Kr, KB, j + 1, st, NSV / 2, lnc);
+        int db, kb, t2;
+        step(st, db, kb, t2);
         const u32x4 vbits = vf[st % kVAhead];
         if (st + kVAhead < NSV) vf[st % kVAhead] = vread(st + kVAhead);
         const u32x4 pb = __builtin_bit_cast(u32x4, pf[kb][t2]);
         const bool first = kb == 0 && t2 == 0, last = kb == 1 && t2 == 1;
         if constexpr (ACC16) {
-          // per-tile product in VGPRs; the last MFMA of a d-block pads for the
-          // VALU that folds it into the fp16 accumulator
-          if (first) {
-            if (st == 0) mfma32_asm<BF16, false, false, true, true>(acc, vbits, pb);
-            else mfma32_asm<BF16, false, false, true>(acc, vbits, pb);
-          } else if (last) {
-            mfma32_asm<BF16, false, false, false, false, true>(acc, vbits, pb);
-          } else {
-            mfma32_asm<BF16, false, false>(acc, vbits, pb);
-          }
-          if (last) {
-            // o16 <- o16 * oscale + acc, in packed fp16
-            const f16x2 sc = {(_Float16)oscale, (_Float16)oscale};
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              u32x4 w = o16[2 * db + hh];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                f16x2 cur = f16x2_from_bits(w[e]);
-                const f16x2 add = {(_Float16)acc[8 * hh + 2 * e], (_Float16)acc[8 * hh + 2 * e + 1]};
-                cur = cur * sc + add;
-                w[e] = __builtin_bit_cast(uint32_t, cur);
-              }
-              o16[2 * db + hh] = w;
+          // per-tile products in VGPRs; the pair's last MFMA pads for the
+          // VALU that folds both into the fp16 accumulator
+          if ((st & 1) == 0) {
+            if (first) {
+              if (st == 0) mfma32_asm<BF16, false, false, true, true>(acc_e, vbits, pb);
+              else mfma32_asm<BF16, false, false, true>(acc_e, vbits, pb);
+            } else {
+              mfma32_asm<BF16, false, false>(acc_e, vbits, pb);
             }
+          } else {
+            if (first) mfma32_asm<BF16, false, false, true>(acc_o, vbits, pb);
+            else if (last) mfma32_asm<BF16, false, false, false, false, true>(acc_o, vbits, pb);
+            else mfma32_asm<BF16, false, false>(acc_o, vbits, pb);
+          }
+          if (last && (st & 1)) {
+            pin_after_pad(acc_e);
+            fold(acc_e, db - 1);
+            fold(acc_o, db);
           }
         } else {
-          if (first) {
-            acc = o_acc[db];
-            // two MFMAs on a uniform branch, both writing the accumulators:
-            // no select or copy of the tuple is needed. The first MFMA of the
-            // phase pads for the VALU that wrote P.
-            if (db < kOAgpr) {
+          // the first pair starts every block's chain (C = 0 on a fresh
+          // attempt); the first MFMA of the phase pads for the VALU that wrote
+          // P, the last one for accumulator copies on the loop's edges
+          const bool pad_after = st == NSV - 1;
+          if (db < kOAgpr) {
+            if (first) {
               if (st == 0) {
-                if (fresh) mfma32_asm<BF16, false, true, true, true>(acc, vbits, pb);
-                else mfma32_asm<BF16, false, true, false, true>(acc, vbits, pb);
+                if (fresh) mfma32_asm<BF16, false, true, true, true>(o_acc[db], vbits, pb);
+                else mfma32_asm<BF16, false, true, false, true>(o_acc[db], vbits, pb);
               } else {
-                if (fresh) mfma32_asm<BF16, false, true, true>(acc, vbits, pb);
-                else mfma32_asm<BF16, false, true>(acc, vbits, pb);
+                if (fresh) mfma32_asm<BF16, false, true, true>(o_acc[db], vbits, pb);
+                else mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
               }
+            } else if (pad_after) {
+              mfma32_asm<BF16, false, true, false, false, true>(o_acc[db], vbits, pb);
             } else {
-              if (st == 0) {
-                if (fresh) mfma32_asm<BF16, false, false, true, true>(acc, vbits, pb);
-                else mfma32_asm<BF16, false, false, false, true>(acc, vbits, pb);
-              } else {
-                if (fresh) mfma32_asm<BF16, false, false, true>(acc, vbits, pb);
-                else mfma32_asm<BF16, false, false>(acc, vbits, pb);
-              }
+              mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
             }
           } else {
-            if (db < kOAgpr) mfma32_asm<BF16, false, true>(acc, vbits, pb);
-            else mfma32_asm<BF16, false, false>(acc, vbits, pb);
+            if (first) {
+              if (st == 0) {
+                if (fresh) mfma32_asm<BF16, false, false, true, true>(o_acc[db], vbits, pb);
+                else mfma32_asm<BF16, false, false, false, true>(o_acc[db], vbits, pb);
+              } else {
+                if (fresh) mfma32_asm<BF16, false, false, true>(o_acc[db], vbits, pb);
+                else mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
+              }
+            } else if (pad_after) {
+              mfma32_asm<BF16, false, false, false, false, true>(o_acc[db], vbits, pb);
+            } else {
+              mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
+            }
           }
-          if (last) o_acc[db] = acc;
         }
       }
     }

@@ -178,6 +178,8 @@ void fwd_wide_kernel(FwdArgs a) {
       }
     }
     // both chains end at least 19 wait states before this VALU (the last MFMA pads)
+    pin_after_pad(s_acc);
+    pin_after_pad(s_odd);
 #pragma unroll
     for (int i = 0; i < 16; ++i) s_acc[i] += s_odd[i];
 
