@@ -79,17 +79,34 @@ constexpr int kBwdPad = 64;                        // workspace row padding
 // checked per-lane offset: rows past the end and granules past D/2 read as
 // zeros (the latter without memory traffic).
 template <int D>
-__device__ inline void bwd_copy_tile(__amdgpu_buffer_rsrc_t rs, FFPA_LDS char* dst, int row0,
-                                     int wave, int lane) {
+__device__ inline void bwd_copy_row(__amdgpu_buffer_rsrc_t rs, FFPA_LDS char* dst, int row0,
+                                    int wave, int lane, int r) {
   constexpr int SG = D / 16;  // granules per half
   const int u = lane & 31, half = lane >> 5;
+  const int n = wave + 4 * r;
+  const int gl = u ^ swz4(n);
+  const uint32_t lanepart = gl < SG ? (uint32_t)(half * SG + gl) << 4 : 0x80000000u;
+  dma16(rs, lanepart + (uint32_t)(row0 + n) * (D * 2), 0, dst + n * kBwdRowBytes);
+}
+template <int D>
+__device__ inline void bwd_copy_tile(__amdgpu_buffer_rsrc_t rs, FFPA_LDS char* dst, int row0,
+                                     int wave, int lane) {
 #pragma unroll
-  for (int r = 0; r < kBwdRows / 4; ++r) {
-    const int n = wave + 4 * r;
-    const int gl = u ^ swz4(n);
-    const uint32_t lanepart = gl < SG ? (uint32_t)(half * SG + gl) << 4 : 0x80000000u;
-    dma16(rs, lanepart + (uint32_t)(row0 + n) * (D * 2), 0, dst + n * kBwdRowBytes);
-  }
+  for (int r = 0; r < kBwdRows / 4; ++r) bwd_copy_row<D>(rs, dst, row0, wave, lane, r);
+}
+
+// The 16 copies of a wave for the next pair of tiles (8 rows of each),
+// spread over the first `span` steps of a phase: copy c goes at step c span / 16.
+template <int D>
+__device__ inline void bwd_copy_spread(__amdgpu_buffer_rsrc_t ra, FFPA_LDS char* da,
+                                       __amdgpu_buffer_rsrc_t rb, FFPA_LDS char* db, int row0,
+                                       int wave, int lane, int st, int span) {
+#pragma unroll
+  for (int c = 0; c < 2 * kBwdRows / 4; ++c)
+    if ((c * span) / (2 * kBwdRows / 4) == st) {
+      if (c & 1) bwd_copy_row<D>(rb, db, row0, wave, lane, c >> 1);
+      else bwd_copy_row<D>(ra, da, row0, wave, lane, c >> 1);
+    }
 }
 
 // 16-byte row reads (MFMA A operand, m = row): lane l reads row l % 32,
@@ -153,9 +170,10 @@ __device__ inline void bwd_exchange(FFPA_LDS char* xbase, int wave, int lane, f3
 // fragments are rows of the staged tiles `ta` and `tb`, B fragments the
 // register operands `fa` and `fb` (AGPRs). The chains end padded for the
 // VALU/LDS reads of their results.
-template <bool BF16, int NS>
+template <bool BF16, int NS, class StepFn>
 __device__ inline void bwd_partials(const FFPA_LDS char* ta, const FFPA_LDS char* tb, const uint32_t* ax,
-                                    const u32x4* fa, const u32x4* fb, f32x16& s, f32x16& p) {
+                                    const u32x4* fa, const u32x4* fb, f32x16& s, f32x16& p,
+                                    StepFn&& at_step) {
   constexpr int kAhead = NS < 3 ? NS : 3;
   u32x4 xa[kAhead], xb[kAhead];
 #pragma unroll
@@ -165,6 +183,7 @@ __device__ inline void bwd_partials(const FFPA_LDS char* ta, const FFPA_LDS char
   }
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
+    at_step(st);
     const u32x4 x = xa[st % kAhead], y = xb[st % kAhead];
     if (st + kAhead < NS) {
       xa[st % kAhead] = lds_read16(ta + bwd_row_addr(ax, st + kAhead));
@@ -360,14 +379,25 @@ void bwd_dkdv_kernel(BwdArgs a) {
         dl[j] = *(const f32x4*)(a.delta + rb + 8 * j);
       }
     }
-    if (it + 1 < n_it) issue(it + 1);
-
-    // S = Q K^T and dP = dO V^T (32 q x 32 keys), partial over this half of D
+    // S = Q K^T and dP = dO V^T (32 q x 32 keys), partial over this half of
+    // D; the copies of the next tile go out during its first half
     f32x16 sacc, pacc;
     {
+      const bool has_next = it + 1 < n_it;
+      const int hn = hk * g + (it + 1) / per_head;
+      const int qn = qt0 + (it + 1) % per_head;
+      const size_t hoff = (size_t)(b * a.Hq + hn) * a.Nq * D * 2;
+      const __amdgpu_buffer_rsrc_t Qn = make_rsrc((const char*)a.q + hoff, q_bytes);
+      const __amdgpu_buffer_rsrc_t On = make_rsrc((const char*)a.dout + hoff, q_bytes);
+      FFPA_LDS char* qd = smem + QB + (s ^ 1) * kBwdTile;
+      FFPA_LDS char* od = smem + OB + (s ^ 1) * kBwdTile;
+      int lc = lane;
+      asm volatile("" : "+v"(lc));
       uint32_t ax[8];
       bwd_row_bases(lj, hf, ax);
-      bwd_partials<BF16, NS>(qtile, otile, ax, kf, vf, sacc, pacc);
+      bwd_partials<BF16, NS>(qtile, otile, ax, kf, vf, sacc, pacc, [&](int st) {
+        if (has_next) bwd_copy_spread<D>(Qn, qd, On, od, qn * kBwdRows, wave, lc, st, NS > 1 ? NS / 2 : 1);
+      });
     }
     bwd_exchange(smem + XB, wave, lj, sacc, pacc);
 
@@ -555,14 +585,20 @@ void bwd_dq_kernel(BwdArgs a) {
         bias2[i] = key < a.Nkv ? 0.f : -INFINITY;
       }
     }
-    if (j + 1 < n_kt) issue(j + 1);
-
-    // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 q), partial over the half
+    // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 q), partial over the
+    // half; the copies of the next tile go out during its first half
     f32x16 sacc, pacc;
     {
+      const bool has_next = j + 1 < n_kt;
+      FFPA_LDS char* kd = smem + KB + (s ^ 1) * kBwdTile;
+      FFPA_LDS char* vd = smem + VB + (s ^ 1) * kBwdTile;
+      int lc = lane;
+      asm volatile("" : "+v"(lc));
       uint32_t ax[8];
       bwd_row_bases(lj, hf, ax);
-      bwd_partials<BF16, NS>(ktile, vtile, ax, qf, of, sacc, pacc);
+      bwd_partials<BF16, NS>(ktile, vtile, ax, qf, of, sacc, pacc, [&](int st) {
+        if (has_next) bwd_copy_spread<D>(Kr, kd, Vr, vd, (j + 1) * kBwdRows, wave, lc, st, NS > 1 ? NS / 2 : 1);
+      });
     }
     bwd_exchange(smem + XB, wave, lj, sacc, pacc);
 
