@@ -8,7 +8,8 @@ instruction counted as one wait state, ``s_nop N`` as N + 1) and reports:
 * a VALU/accvgpr write of a register that an MFMA reads (A, B or C) fewer
   than ``VALU_TO_MFMA`` wait states later;
 * a VALU/accvgpr/LDS/VMEM instruction that reads or overwrites an MFMA
-  result fewer than ``MFMA_TO_VALU`` wait states after that MFMA.
+  result fewer than ``MFMA_TO_VALU`` wait states after that MFMA;
+* any kernel that uses scratch memory (spilled registers).
 
 The scan follows the control flow: basic blocks split at labels and
 branches, and the pending distances (registers still inside a hazard window)
@@ -162,6 +163,24 @@ def check_kernel(lines):
     return sorted(issues.items())
 
 
+def scratch_users(asm: str) -> list[str]:
+    """Kernels that spill VGPRs or use scratch memory at all.
+
+    A spill reloads MFMA operands and accumulators from scratch around the
+    inline-asm MFMAs; besides the cost, such a kernel gave wrong results once.
+    The kernels are written to fit their registers, so any scratch use is
+    reported as an error."""
+    out = []
+    for block in asm.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block)
+        priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
+        vsp = re.search(r"\.vgpr_spill_count:\s+(\d+)", block)
+        if name and ((priv and int(priv.group(1))) or (vsp and int(vsp.group(1)))):
+            out.append(f"{name.group(1)[:60]}: scratch {priv.group(1) if priv else '?'} bytes, "
+                       f"{vsp.group(1) if vsp else '?'} VGPRs spilled")
+    return out
+
+
 def check_file(src: str) -> list[str]:
     cmd = [B.HIPCC, *B.FLAGS, "-S", "--cuda-device-only", src, "-o", "-"]
     asm = subprocess.run(cmd, capture_output=True, text=True, check=True).stdout
@@ -169,6 +188,8 @@ def check_file(src: str) -> list[str]:
     for name, lines in kernels(asm):
         for i, msg in check_kernel(lines):
             report.append(f"{os.path.basename(src)} {name[:60]} #{i}: {msg}")
+    for msg in scratch_users(asm):
+        report.append(f"{os.path.basename(src)} {msg}")
     return report
 
 

@@ -195,12 +195,12 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     WideLauncher launch = wide_launcher(D, dtype == FFPA_BF16);
     if (launch == nullptr)
       return fail(FFPA_ERR_UNSUPPORTED, "for Nq > 1, D above 512 must be a multiple of 64");
-    if (mask != nullptr && mask_rows != 1)
-      return fail(FFPA_ERR_UNSUPPORTED, "per-query masks [Nq, Nkv] are not supported yet");
     ffpa::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.mask = mask;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv;
-    a.mask_rows = mask ? 1 : 0;
+    a.mask_rows = mask ? mask_rows : 0;
+    a.mask_stride = (mask && mask_rows > 1) ? Nkv : 0;
+    a.bias_lds = 0;
     a.causal = causal;
     a.scale_log2 = scale * ffpa::kLog2e;
     a.n_qtiles = (Nq + 63) / 64;
@@ -216,18 +216,18 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   FwdLauncher launch = fwd_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, &ring);
   if (launch == nullptr) return fail(FFPA_ERR_UNSUPPORTED, "this head dimension is not built yet");
   size_t lds = ring + ffpa::kFwdFlagBytes;
-  if (mask != nullptr) {
-    if (mask_rows != 1)
-      return fail(FFPA_ERR_UNSUPPORTED, "per-query masks [Nq, Nkv] are not supported yet");
-    lds += (size_t)ffpa::fwd_bias_bytes(Nkv);
-    if (lds > kLdsLimit)
-      return fail(FFPA_ERR_UNSUPPORTED, "key bias does not fit in LDS beside the K/V tiles");
-  }
+  // a key bias is staged in LDS when it fits beside the tiles; otherwise the
+  // kernel reads it (like a per-query mask) from global memory
+  const bool bias_lds = mask != nullptr && mask_rows == 1 &&
+                        lds + (size_t)ffpa::fwd_bias_bytes(Nkv) <= kLdsLimit;
+  if (bias_lds) lds += (size_t)ffpa::fwd_bias_bytes(Nkv);
 
   ffpa::FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.mask = mask;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv;
-  a.mask_rows = mask ? 1 : 0;
+  a.mask_rows = mask ? mask_rows : 0;
+  a.mask_stride = (mask && mask_rows > 1) ? Nkv : 0;
+  a.bias_lds = bias_lds ? 1 : 0;
   a.causal = causal;
   a.scale_log2 = scale * ffpa::kLog2e;
   a.n_qtiles = (Nq + ffpa::kFwdRows - 1) / ffpa::kFwdRows;
@@ -266,8 +266,6 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   if (workspace == nullptr || workspace_bytes < need)
     return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_bwd_workspace_size()");
   if (!(scale == scale)) return fail(FFPA_ERR_INVALID_ARG, "scale is NaN");
-  if (mask != nullptr && mask_rows != 1)
-    return fail(FFPA_ERR_UNSUPPORTED, "per-query masks [Nq, Nkv] are not supported yet");
   BwdLauncher launch = bwd_launcher(D, dtype == FFPA_BF16);
   if (launch == nullptr)
     return fail(FFPA_ERR_UNSUPPORTED, "the backward is built for D = 64, 128, ..., 512");
@@ -275,6 +273,7 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   ffpa::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv; a.mask = mask;
+  a.mask_rows = mask ? mask_rows : 0;
   const int64_t nq_pad = bwd_nq_pad(Nq);
   a.delta = (float*)workspace;
   a.lse2 = (float*)workspace + (size_t)B * Hq * nq_pad;

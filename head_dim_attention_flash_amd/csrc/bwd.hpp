@@ -48,7 +48,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  const void* mask;  // key bias [Nkv] in the input dtype, or null
+  const void* mask;  // key bias [Nkv] or per-query mask [Nq, Nkv] in the input dtype, or null
+  int mask_rows;     // 0, 1 or Nq
   float* delta;      // workspace [B * Hq * nq_pad]
   float* lse2;       // workspace [B * Hq * nq_pad]: lse * log2(e), +inf for dead and padded rows
   int B, Hq, Hkv, Nq, Nkv;
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 //    dV^T[half] += dO^T P,  dK^T[half] += Q^T dS.
 // Accumulators: dV^T in AGPRs, dK^T in VGPRs (m = d, n = key).
 // ---------------------------------------------------------------------------
-template <int D, bool BF16>
+template <int D, bool BF16, bool ROWMASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(D % 64 == 0 && D <= 512, "D must be a multiple of 64, at most 512");
@@ -319,7 +320,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
   float bias2 = 0.f;  // this lane's key bias, log2 domain
-  if (a.mask != nullptr) {
+  // per-query mask: a separate instance, so the common one keeps its registers
+  constexpr bool row_mask = ROWMASK;
+  if (a.mask != nullptr && !row_mask) {
     const int key = kw + (lane & 31);
     bias2 = key < a.Nkv ? E::to_f32(((const uint16_t*)a.mask)[key]) * kLog2e : -INFINITY;
   }
@@ -407,7 +410,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = i >> 2, e = i & 3;
-      float x = fmaf(sacc[i], a.scale_log2, bias2) - l2[j][e];
+      float bias_i = bias2;
+      if constexpr (row_mask) {
+        // per-query mask: entry (row, my_k), rows clamped to the last one
+        const int qr = min(qg0 + 8 * j + e, a.Nq - 1);
+        const float bv = E::to_f32(((const uint16_t*)a.mask)[(size_t)qr * a.Nkv + min(my_k, a.Nkv - 1)]);
+        bias_i = my_k < a.Nkv ? bv * kLog2e : -INFINITY;
+      }
+      float x = fmaf(sacc[i], a.scale_log2, bias_i) - l2[j][e];
       if (a.causal && my_k > qg0 + 8 * j + e) x = -INFINITY;
       const float p = exp2_fast(x);
       pv[i] = p;
@@ -575,11 +585,14 @@ void bwd_dq_kernel(BwdArgs a) {
     barrier();
 
     float bias2[16];
+    // key bias, or row my_q of a per-query mask (clamped to the last row)
+    const uint16_t* mrow = mk == nullptr ? nullptr
+                           : mk + (a.mask_rows > 1 ? (size_t)min(my_q, a.Nq - 1) * a.Nkv : 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = kg0 + 8 * (i >> 2) + (i & 3);
       if (mk != nullptr) {
-        const float bv = E::to_f32(mk[min(key, a.Nkv - 1)]) * kLog2e;
+        const float bv = E::to_f32(mrow[min(key, a.Nkv - 1)]) * kLog2e;
         bias2[i] = key < a.Nkv ? bv : -INFINITY;
       } else {
         bias2[i] = key < a.Nkv ? 0.f : -INFINITY;
@@ -663,13 +676,17 @@ void bwd_dq_kernel(BwdArgs a) {
 // Host launcher: the three kernels in order on `stream`.
 template <int D, bool BF16>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
-  auto kdkdv = bwd_dkdv_kernel<D, BF16>;
+  const bool rowmask = a.mask != nullptr && a.mask_rows > 1;
+  auto kdkdv = rowmask ? bwd_dkdv_kernel<D, BF16, true> : bwd_dkdv_kernel<D, BF16, false>;
   auto kdq = bwd_dq_kernel<D, BF16>;
-  static const hipError_t attr1 =
-      hipFuncSetAttribute((const void*)kdkdv, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
+  static const hipError_t attr1 = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, BF16, false>,
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
+  static const hipError_t attr1m = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, BF16, true>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
   static const hipError_t attr2 =
       hipFuncSetAttribute((const void*)kdq, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
   if (attr1 != hipSuccess) return attr1;
+  if (attr1m != hipSuccess) return attr1m;
   if (attr2 != hipSuccess) return attr2;
   const int64_t rows = (int64_t)a.B * a.Hq * a.nq_pad;
   hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);

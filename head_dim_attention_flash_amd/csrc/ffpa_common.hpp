@@ -243,6 +243,31 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_
 
 __device__ inline u32x4 lds_read16(const FFPA_LDS char* p) { return *(const FFPA_LDS u32x4*)p; }
 
+// Four consecutive entries k4 .. k4 + 3 (k4 a multiple of 4) of one row of an
+// additive mask in the 16-bit input type, as floats; entries at or past Nkv
+// read as 0 (the callers mask those keys anyway) and are never loaded. With
+// Nkv % 4 == 0 a group is wholly inside or outside the row and is one 8-byte
+// load; otherwise each entry is loaded on its own, clamped.
+template <bool BF16>
+__device__ inline f32x4 mask_row4(const uint16_t* row, int k4, int nkv, bool by8) {
+  f32x4 r = {0.f, 0.f, 0.f, 0.f};
+  if (by8) {
+    if (k4 < nkv) {
+      const u32x2 w = *(const u32x2*)(row + k4);
+      r = f32x4{Elem<BF16>::to_f32((uint16_t)(w[0] & 0xffff)), Elem<BF16>::to_f32((uint16_t)(w[0] >> 16)),
+                Elem<BF16>::to_f32((uint16_t)(w[1] & 0xffff)), Elem<BF16>::to_f32((uint16_t)(w[1] >> 16))};
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = k4 + e;
+      const float x = Elem<BF16>::to_f32(row[min(k, nkv - 1)]);
+      r[e] = k < nkv ? x : 0.f;
+    }
+  }
+  return r;
+}
+
 // Transposing 8-byte LDS read (ds_read_b64_tr_b16). Within each group of 16
 // lanes, lane j receives element (j % 4) of the 4-element chunks addressed by
 // lanes j/4, j/4 + 4, j/4 + 8 and j/4 + 12 (in that order). Checked on gfx950.

@@ -37,7 +37,9 @@ struct FwdArgs {
   float* lse;         // may be null
   const void* mask;   // may be null
   int B, Hq, Hkv, Nq, Nkv;
-  int mask_rows;      // 0 (none) or 1 (key bias, staged in LDS after the tiles)
+  int mask_rows;      // 0 (none), 1 (key bias) or Nq (per-query mask)
+  int mask_stride;    // elements between mask rows read from global memory: 0 (key bias) or Nkv
+  int bias_lds;       // 1: the key bias is staged in LDS after the tiles
   int causal;
   float scale_log2;   // scale * log2(e)
   int n_qtiles;
@@ -130,10 +132,12 @@ void fwd_prefill_kernel(FwdArgs a) {
   const int n_tiles = (kv_end + kFwdBc - 1) / kFwdBc;
 
   // ---- stage the key bias [Nkv] in LDS (once; the host checks it fits),
-  // zero-padded to whole tiles: keys >= Nkv are masked anyway
+  // zero-padded to whole tiles: keys >= Nkv are masked anyway. A per-query
+  // mask [Nq, Nkv] is read from global memory, row by row, in the softmax.
   const bool has_mask = a.mask_rows > 0;
+  const bool key_bias = a.bias_lds != 0;
   FFPA_LDS uint16_t* bias_lds = (FFPA_LDS uint16_t*)(smem + fwd_ring_bytes<D>());
-  if (has_mask) {
+  if (key_bias) {
     const uint16_t* mk = (const uint16_t*)a.mask;
     const int padded = ((a.Nkv + kFwdBc - 1) / kFwdBc) * kFwdBc;
     for (int i = threadIdx.x; i < padded; i += 256) bias_lds[i] = i < a.Nkv ? mk[i] : (uint16_t)0;
@@ -223,7 +227,7 @@ void fwd_prefill_kernel(FwdArgs a) {
   bool fresh = true;        // ACC32: no PV product accumulated yet in this attempt
   // one word per wave: did a row of that wave break m_ref + tau in this tile
   FFPA_LDS uint32_t* restart_flag = (FFPA_LDS uint32_t*)(smem + fwd_ring_bytes<D>() +
-                                                         (has_mask ? fwd_bias_bytes(a.Nkv) : 0));
+                                                         (key_bias ? fwd_bias_bytes(a.Nkv) : 0));
 
   issue_tile(Kr, KB, 0);
 
@@ -303,7 +307,22 @@ void fwd_prefill_kernel(FwdArgs a) {
     if (need_mask) {
       // lane's keys: j0 + 4 hi + c, c = 32 kb + 8 (i / 4) + i % 4
       const int kb0 = j0 + 4 * hij;
-      if (has_mask) {
+      if (has_mask && !key_bias) {
+        // mask from global memory: row my_q (clamped to the last row) of a
+        // per-query mask, or the key bias when it is not staged; four
+        // consecutive keys per group
+        const uint16_t* mrow = (const uint16_t*)a.mask + (size_t)min(my_qj, a.Nq - 1) * a.mask_stride;
+        const bool by8 = (a.Nkv & 3) == 0;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 bv = mask_row4<BF16>(mrow, kb0 + 32 * kb + 8 * g4, a.Nkv, by8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tv[kb][4 * g4 + e] += bv[e] * kLog2e;
+          }
+      }
+      if (key_bias) {
         // additive bias, four consecutive keys per 8-byte LDS read
         const FFPA_LDS char* bp = (const FFPA_LDS char*)bias_lds + 2 * kb0;
 #pragma unroll

@@ -207,12 +207,14 @@ void fwd_wide_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) tv[i] = s_acc[i] * a.scale_log2;
     if (need_mask) {
+      // key bias, or row my_q of a per-query mask (clamped to the last row)
+      const uint16_t* mrow = mk + (size_t)min(my_qj, a.Nq - 1) * a.mask_stride;
       int klim = a.Nkv - kb0;
       if (a.causal) klim = min(klim, my_qj + 1 - kb0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int c = 8 * (i >> 2) + (i & 3);
-        if (has_mask) tv[i] += E::to_f32(mk[min(kb0 + c, a.Nkv - 1)]) * kLog2e;
+        if (has_mask) tv[i] += E::to_f32(mrow[min(kb0 + c, a.Nkv - 1)]) * kLog2e;
         tv[i] = c >= klim ? -INFINITY : tv[i];
       }
     }

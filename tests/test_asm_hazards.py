@@ -55,3 +55,12 @@ def test_checker_merges_predecessors_at_a_join():
              ".LBB0_5:", "v_add_f32 v3, v3, v3", "s_endpgm"]
     issues = H.check_kernel(lines)
     assert any("touches MFMA result" in m for _, m in issues)
+
+
+def test_checker_flags_scratch_use():
+    meta = ("  - .agpr_count:     256\n    .name:           _ZN4ffpa3fooEv\n"
+            "    .private_segment_fixed_size: 104\n    .vgpr_spill_count: 25\n"
+            "  - .agpr_count:     0\n    .name:           _ZN4ffpa3barEv\n"
+            "    .private_segment_fixed_size: 0\n    .vgpr_spill_count: 0\n")
+    found = H.scratch_users(meta)
+    assert len(found) == 1 and "foo" in found[0]

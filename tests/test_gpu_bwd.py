@@ -35,12 +35,12 @@ REL = {"fp16": 4e-3, "bf16": 2.5e-2}
 DT = {"fp16": torch.float16, "bf16": torch.bfloat16}
 
 
-def _inputs(seed, B, Hq, Hkv, Nq, Nkv, D, dtype, with_mask):
+def _inputs(seed, B, Hq, Hkv, Nq, Nkv, D, dtype, with_mask, mask_rows=1):
     q = W.draw(seed, W.T_Q, B, Hq, Nq, D, dtype)
     k = W.draw(seed, W.T_K, B, Hkv, Nkv, D, dtype)
     v = W.draw(seed, W.T_V, B, Hkv, Nkv, D, dtype)
     do = W.draw(seed, W.T_DO, B, Hq, Nq, D, dtype)
-    mask = W.draw_key_bias(seed, Nkv, dtype, 0.1, rows=1) if with_mask else None
+    mask = W.draw_key_bias(seed, Nkv, dtype, 0.1, rows=mask_rows) if with_mask else None
     return q, k, v, do, mask
 
 
@@ -91,11 +91,12 @@ def _compare(name, got, ref, dtype, label, bound=None):
         assert rel <= REL[dtype], f"{label}: {name} rel L2 {rel}"
 
 
-def _run_case(lib, shape, dtype, causal, with_mask, seed):
+def _run_case(lib, shape, dtype, causal, with_mask, seed, mask_rows=1):
     B, Hq, Hkv, Nq, Nkv, D = shape
-    q, k, v, do, mask = _inputs(seed, B, Hq, Hkv, Nq, Nkv, D, dtype, with_mask)
+    q, k, v, do, mask = _inputs(seed, B, Hq, Hkv, Nq, Nkv, D, dtype, with_mask,
+                                mask_rows=Nq if mask_rows != 1 else 1)
     scale = 1.0 / math.sqrt(D)
-    m2 = None if mask is None else mask.view(1, Nkv)
+    m2 = None if mask is None else mask.view(-1, Nkv)
     o_ref, lse_ref = attn_fwd(q, k, v, scale, causal=causal, mask=m2)
     o_in = torch.from_numpy(o_ref).to(DT[dtype]).cuda()
     lse_in = torch.from_numpy(lse_ref).to(torch.float32).cuda()
@@ -129,9 +130,10 @@ CASES = [
 
 @pytest.mark.parametrize("shape", CASES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("variant", ["plain", "causal", "mask", "causal_mask"])
+@pytest.mark.parametrize("variant", ["plain", "causal", "mask", "causal_mask", "qmask", "causal_qmask"])
 def test_backward_matches_oracle(lib, shape, dtype, variant):
-    _run_case(lib, shape, dtype, "causal" in variant, "mask" in variant, 300 + sum(shape))
+    _run_case(lib, shape, dtype, "causal" in variant, "mask" in variant, 300 + sum(shape),
+              mask_rows="q" if "qmask" in variant else 1)
 
 
 def test_backward_deterministic(lib):

@@ -76,6 +76,8 @@ def _inputs(seed, B, Hq, Hkv, Nq, Nkv, D, dtype, mask_kind=None):
     mask = None
     if mask_kind == "key":
         mask = W.draw_key_bias(seed, Nkv, dtype, 0.1, rows=1)
+    elif mask_kind == "query":
+        mask = W.draw_key_bias(seed, Nkv, dtype, 0.1, rows=Nq)
     return q, k, v, mask
 
 
@@ -109,15 +111,15 @@ CASES = [
 @pytest.mark.parametrize("shape", CASES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("accum", ["f32", "f16"])
-@pytest.mark.parametrize("variant", ["plain", "causal", "mask", "causal_mask"])
+@pytest.mark.parametrize("variant", ["plain", "causal", "mask", "causal_mask", "qmask", "causal_qmask"])
 def test_forward_matches_oracle(lib, shape, dtype, accum, variant):
     B, Hq, Hkv, Nq, Nkv, D = shape
     causal = "causal" in variant
-    mk = "key" if "mask" in variant else None
+    mk = "query" if "qmask" in variant else "key" if "mask" in variant else None
     seed = 100 + sum(shape)
     q, k, v, mask = _inputs(seed, B, Hq, Hkv, Nq, Nkv, D, dtype, mk)
     if mask is not None:
-        mask[0, 0] = 0.0  # key 0 stays visible: a causal row 0 is then never empty
+        mask[:, 0] = 0.0  # key 0 stays visible: a causal row 0 is then never empty
     scale = 1.0 / math.sqrt(D)
     o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), causal=causal,
                   mask=None if mask is None else mask.cuda(), accum=accum, scale=scale)
@@ -235,3 +237,34 @@ def test_decode_fully_masked_row(lib):
     o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), mask=mask.cuda())
     assert torch.count_nonzero(o).item() == 0
     assert torch.isneginf(lse).all()
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_key_bias_too_long_for_lds(lib, dtype):
+    # 20000 keys: the bias (40000 B) does not fit beside the 128 KiB of tiles,
+    # so the kernel reads it from global memory like a per-query mask
+    B, Hq, Hkv, Nq, Nkv, D = 1, 2, 2, 70, 20000, 512
+    q, k, v, mask = _inputs(700, B, Hq, Hkv, Nq, Nkv, D, dtype, "key")
+    scale = 1.0 / math.sqrt(D)
+    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), causal=False, mask=mask.cuda(), scale=scale)
+    _compare(o, lse, q, k, v, scale, False, mask, dtype, "f32", f"longbias-{dtype}")
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 2, 130, 300, 512), (1, 2, 1, 100, 77, 1024), (2, 2, 2, 64, 64, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_query_mask_equals_deleting_keys_per_row(lib, shape):
+    # a per-query mask of 0 / -inf equals running each row with its own key set:
+    # checked against the oracle on rows whose masks differ
+    B, Hq, Hkv, Nq, Nkv, D = shape
+    q, k, v, _ = _inputs(710 + sum(shape), B, Hq, Hkv, Nq, Nkv, D, "fp16")
+    g = torch.Generator().manual_seed(711)
+    keep = torch.rand(Nq, Nkv, generator=g) > 0.5
+    keep[:, 0] = True
+    mask = torch.where(keep, torch.zeros(()), torch.full((), float("-inf"))).to(torch.float16)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), mask=mask.cuda(), scale=scale)
+    for r in (0, Nq // 2, Nq - 1):
+        ks = keep[r].nonzero().flatten()
+        oo, lo = attn_fwd(q[:, :, r:r + 1], k[:, :, ks], v[:, :, ks], scale)
+        assert np.abs(to_f64(o[:, :, r:r + 1]) - oo).max() <= 1e-2
+        assert np.abs(to_f64(lse[:, :, r:r + 1]) - lo).max() <= 2e-3
