@@ -319,6 +319,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
       vf[st] = vp[2 * st];
     }
   }
+  wait_vmcnt0_visible();
   float bias2 = 0.f;  // this lane's key bias, log2 domain
   // per-query mask: a separate instance, so the common one keeps its registers
   constexpr bool row_mask = ROWMASK;
@@ -350,7 +351,22 @@ void bwd_dkdv_kernel(BwdArgs a) {
     dv[i] = f32x16{};
     dk[i] = f32x16{};
   }
-  if (n_it > 0) issue(0);
+  // lse2 and delta of iteration `it`, rows 8 j + 4 hi + 0..3 of its tile
+  f32x4 l2n[4], dln[4];
+  auto load_rows = [&](int it) {
+    const int hh = hk * g + it / per_head;
+    const int qt = qt0 + it % per_head;
+    const size_t rb = (size_t)(b * a.Hq + hh) * a.nq_pad + qt * kBwdRows + 4 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      l2n[j] = *(const f32x4*)(a.lse2 + rb + 8 * j);
+      dln[j] = *(const f32x4*)(a.delta + rb + 8 * j);
+    }
+  };
+  if (n_it > 0) {
+    if constexpr (!ROWMASK) load_rows(0);
+    issue(0);
+  }
 
   for (int it = 0; it < n_it; ++it) {
 #pragma unroll
@@ -372,15 +388,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
     wait_lgkm0();
     barrier();        // ... everyone's; tile it - 1 and the swap area are free
 
-    // lse2 and delta of rows 8 j + 4 hi + 0..3 of the tile
+    // lse2 and delta of rows 8 j + 4 hi + 0..3 of the tile: loaded during
+    // the previous tile (see load_rows), complete since the wait above; the
+    // empty asm makes the compiler's own wait for them fall here, before
+    // this tile's copies are issued (a wait after them would hold for them).
+    // (The per-query-mask instance has no registers to spare for the
+    // prefetch: it loads them here.)
+    if constexpr (ROWMASK) load_rows(it);
     f32x4 l2[4], dl[4];
-    {
-      const size_t rb = (size_t)(b * a.Hq + hh) * a.nq_pad + qt * kBwdRows + 4 * hij;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        l2[j] = *(const f32x4*)(a.lse2 + rb + 8 * j);
-        dl[j] = *(const f32x4*)(a.delta + rb + 8 * j);
-      }
+    for (int j = 0; j < 4; ++j) {
+      l2[j] = l2n[j];
+      dl[j] = dln[j];
+      if constexpr (!ROWMASK) asm volatile("" ::"v"(l2[j]), "v"(dl[j]));
     }
     // S = Q K^T and dP = dO V^T (32 q x 32 keys), partial over this half of
     // D; the copies of the next tile go out during its first half
@@ -407,22 +427,31 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // P and dS; register i holds query 8 (i / 4) + 4 hi + i % 4 of the tile
     float pv[16], dsv[16];
     const int qg0 = qt * kBwdRows + 4 * hij;
+    // the causal test is a separate instance of the loop (uniform branch),
+    // so that non-causal tiles run no compares
+    auto p_ds = [&](auto causal_tag) {
+      constexpr bool CAUSAL = decltype(causal_tag)::value;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = i >> 2, e = i & 3;
-      float bias_i = bias2;
-      if constexpr (row_mask) {
-        // per-query mask: entry (row, my_k), rows clamped to the last one
-        const int qr = min(qg0 + 8 * j + e, a.Nq - 1);
-        const float bv = E::to_f32(((const uint16_t*)a.mask)[(size_t)qr * a.Nkv + min(my_k, a.Nkv - 1)]);
-        bias_i = my_k < a.Nkv ? bv * kLog2e : -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const int j = i >> 2, e = i & 3;
+        float x;
+        if constexpr (row_mask) {
+          // per-query mask: entry (row, my_k), rows clamped to the last one
+          const int qr = min(qg0 + 8 * j + e, a.Nq - 1);
+          const float bv = E::to_f32(((const uint16_t*)a.mask)[(size_t)qr * a.Nkv + min(my_k, a.Nkv - 1)]);
+          const float bias_i = my_k < a.Nkv ? bv * kLog2e : -INFINITY;
+          x = fmaf(sacc[i], a.scale_log2, bias_i) - l2[j][e];
+        } else {
+          x = fmaf(sacc[i], a.scale_log2, bias2 - l2[j][e]);
+        }
+        if constexpr (CAUSAL) x = my_k > qg0 + 8 * j + e ? -INFINITY : x;
+        const float p = exp2_fast(x);
+        pv[i] = p;
+        dsv[i] = p * (pacc[i] - dl[j][e]);
       }
-      float x = fmaf(sacc[i], a.scale_log2, bias_i) - l2[j][e];
-      if (a.causal && my_k > qg0 + 8 * j + e) x = -INFINITY;
-      const float p = exp2_fast(x);
-      pv[i] = p;
-      dsv[i] = p * (pacc[i] - dl[j][e]);
-    }
+    };
+    if (a.causal && kw + 31 > qt * kBwdRows) p_ds(BoolTag<true>{});
+    else p_ds(BoolTag<false>{});
     V8 pf[2], sf[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
@@ -435,6 +464,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // first MFMA below pads for the last of them
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[t2]), "+v"(sf[t2]));
+
+    // the next tile's lse2 and delta, waited for at its barrier
+    if constexpr (!ROWMASK) {
+      if (it + 1 < n_it) load_rows(it + 1);
+    }
 
     // dV^T += dO^T P and dK^T += Q^T dS over the half's d-blocks; step
     // st = NDB t2 + db, so consecutive MFMAs use different accumulators
@@ -545,6 +579,7 @@ void bwd_dq_kernel(BwdArgs a) {
   const size_t wrow = (size_t)(b * a.Hq + h) * a.nq_pad + qw + (lane & 31);
   const float lse2_me = a.lse2[wrow];
   const float dl_me = a.delta[wrow];
+  wait_vmcnt0_visible();
 
   int kv_end = a.Nkv;
   if (a.causal) kv_end = min(kv_end, min(qblk * 64 + 64, a.Nq));  // keys <= last row of the block
@@ -566,7 +601,22 @@ void bwd_dq_kernel(BwdArgs a) {
   f32x16 dq[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
-  if (n_kt > 0) issue(0);
+  // mask entries of key tile jt for this lane's keys (register i: key
+  // 32 jt + 4 hi + 8 (i / 4) + i % 4): key bias, or row my_q of a per-query
+  // mask (clamped to the last row). Loaded one tile ahead, during the
+  // previous tile's dQ products, so that the wait for them comes before the
+  // tile's copies are in flight.
+  float bn[16];
+  auto load_bias = [&](int jt) {
+    const int kgb = jt * kBwdRows + 4 * (lane >> 5);
+    const uint16_t* mrow = mk + (a.mask_rows > 1 ? (size_t)min(qw + (lane & 31), a.Nq - 1) * a.Nkv : 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bn[i] = E::to_f32(mrow[min(kgb + 8 * (i >> 2) + (i & 3), a.Nkv - 1)]);
+  };
+  if (n_kt > 0) {
+    if (mk != nullptr) load_bias(0);
+    issue(0);
+  }
 
   for (int j = 0; j < n_kt; ++j) {
 #pragma unroll
@@ -585,18 +635,17 @@ void bwd_dq_kernel(BwdArgs a) {
     barrier();
 
     float bias2[16];
-    // key bias, or row my_q of a per-query mask (clamped to the last row)
-    const uint16_t* mrow = mk == nullptr ? nullptr
-                           : mk + (a.mask_rows > 1 ? (size_t)min(my_q, a.Nq - 1) * a.Nkv : 0);
+    if (mk != nullptr) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kg0 + 8 * (i >> 2) + (i & 3);
-      if (mk != nullptr) {
-        const float bv = E::to_f32(mrow[min(key, a.Nkv - 1)]) * kLog2e;
-        bias2[i] = key < a.Nkv ? bv : -INFINITY;
-      } else {
-        bias2[i] = key < a.Nkv ? 0.f : -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const int key = kg0 + 8 * (i >> 2) + (i & 3);
+        float bv = bn[i];
+        asm volatile("" : "+v"(bv));  // the compiler's wait for the load falls here
+        bias2[i] = key < a.Nkv ? bv * kLog2e : -INFINITY;
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bias2[i] = kg0 + 8 * (i >> 2) + (i & 3) < a.Nkv ? 0.f : -INFINITY;
     }
     // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 q), partial over the
     // half; the copies of the next tile go out during its first half
@@ -631,6 +680,8 @@ void bwd_dq_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(sf[t2]));
+
+    if (mk != nullptr && j + 1 < n_kt) load_bias(j + 1);
 
     // dQ^T += K^T dS^T over the half's d-blocks
     {

@@ -160,6 +160,12 @@ __device__ inline void mfma32_asm(f32x16& acc, u32x4 a, u32x4 b) {
 // earlier, above that padding.
 __device__ inline void pin_after_pad(f32x16& acc) { asm volatile("" : "+v"(acc)); }
 
+// A compile-time boolean as a type, to instantiate a generic lambda twice.
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 template <class V>
 __device__ inline V as_vec8(u32x4 x) {
   return __builtin_bit_cast(V, x);
@@ -209,6 +215,14 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ inline void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// vmcnt(0) that the compiler's wait-count pass sees (the builtin, not asm):
+// after it the pass knows every earlier vector-memory load has landed and
+// inserts no further waits for them. Used after a kernel's prologue loads of
+// registers that the main loop only reads; without it the pass keeps waiting
+// for them inside the loop, where its counts cannot see the asm copies, and
+// those waits then also hold for the copies in flight.
+__device__ inline void wait_vmcnt0_visible() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Buffer resource over `bytes` bytes at `base` (raw, stride 0). Loads at or
