@@ -151,7 +151,9 @@ void fwd_prefill_kernel(FwdArgs a) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = qp[2 * s];
   }
-  wait_vmcnt<0>();
+  // compiler-visible: without it the K-phase MFMAs of every tile would wait
+  // for the Q loads again, and those waits also hold for the copies in flight
+  wait_vmcnt0_visible();
   __syncthreads();
 
   // ---- copy of one tile of K or V into its buffer. Copy instruction n of a
