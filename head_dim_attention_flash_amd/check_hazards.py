@@ -9,6 +9,9 @@ instruction counted as one wait state, ``s_nop N`` as N + 1) and reports:
   than ``VALU_TO_MFMA`` wait states later;
 * a VALU/accvgpr/LDS/VMEM instruction that reads or overwrites an MFMA
   result fewer than ``MFMA_TO_VALU`` wait states after that MFMA;
+* an SGPR written by a VALU instruction (v_readlane, v_readfirstlane, ...)
+  and read by a vector-memory instruction fewer than ``VALU_SGPR_TO_VMEM``
+  wait states later;
 * any kernel that uses scratch memory (spilled registers).
 
 The scan follows the control flow: basic blocks split at labels and
@@ -28,6 +31,19 @@ from . import build as B
 
 VALU_TO_MFMA = 4   # wait states required between a VALU write and an MFMA read
 MFMA_TO_VALU = 19  # wait states required between an MFMA write and any other read
+VALU_SGPR_TO_VMEM = 5  # VALU write of an SGPR -> vector-memory instruction reading it
+
+SREG = re.compile(r"\bs(?:\[(\d+):(\d+)\]|(\d+)\b)")
+
+
+def sregs(text: str) -> set[int]:
+    out = set()
+    for m in SREG.finditer(text):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
 
 REG = re.compile(r"\b([va])(?:\[(\d+):(\d+)\]|(\d+)\b)")
 
@@ -69,18 +85,21 @@ def kernels(asm: str):
 
 
 def _effects(ins):
-    """(wait states, kind, written regs, read regs) of one instruction."""
+    """(wait states, kind, written regs, read regs, SGPRs written by VALU,
+    SGPRs read by vector memory) of one instruction."""
     op = ins.split()[0]
     if op == "s_nop":
-        return int(ins.split()[1], 0) + 1, "nop", set(), set()
+        return int(ins.split()[1], 0) + 1, "nop", set(), set(), set(), set()
     operands = ins[len(op):]
     parts = [p.strip() for p in operands.split(",")]
     if op.startswith("v_mfma"):
-        return 1, "mfma", regs(parts[0]), regs(",".join(parts[1:4]))
+        return 1, "mfma", regs(parts[0]), regs(",".join(parts[1:4])), set(), set()
     if op.startswith(("v_", "ds_", "buffer_", "global_", "scratch_")):
         written = regs(parts[0]) if op.startswith("v_") and parts and parts[0] else set()
-        return 1, "vec", written, regs(operands)
-    return 1, "other", set(), set()
+        s_written = sregs(parts[0]) if op.startswith("v_") and parts and parts[0] else set()
+        s_read = sregs(operands) if op.startswith(("buffer_", "global_", "scratch_")) else set()
+        return 1, "vec", written, regs(operands), s_written, s_read
+    return 1, "other", set(), set(), set(), set()
 
 
 def _blocks(lines):
@@ -120,19 +139,24 @@ def _blocks(lines):
 def check_kernel(lines):
     """Hazards in one kernel's instruction list (labels as 'name:' lines)."""
     blocks, succ = _blocks(lines)
-    # state: (mfma_pending, valu_pending): reg -> wait states still required
-    entry = {0: ({}, {})} if blocks else {}
+    # state: (mfma_pending, valu_pending, sgpr_pending): reg -> wait states still required
+    entry = {0: ({}, {}, {})} if blocks else {}
     issues = {}
     work = [0] if blocks else []
     while work:
         k = work.pop()
-        mp, vp = (dict(d) for d in entry[k])
+        mp, vp, sp = (dict(d) for d in entry[k])
         for i in blocks[k][1]:
-            w, kind, written, read = _effects(lines[i])
-            if kind == "other" and w == 1 and not written and not read:
-                pass
+            w, kind, written, read, s_written, s_read = _effects(lines[i])
             mp = {r: c - w for r, c in mp.items() if c - w > 0}
             vp = {r: c - w for r, c in vp.items() if c - w > 0}
+            sp = {r: c - w for r, c in sp.items() if c - w > 0}
+            for r in s_read:
+                if r in sp:
+                    issues.setdefault(i, f"SGPR s{r} written by VALU read by vector memory "
+                                         f"{VALU_SGPR_TO_VMEM - sp[r]} wait states later: {lines[i]}")
+            for r in s_written:
+                sp[r] = VALU_SGPR_TO_VMEM
             if kind == "mfma":
                 for r in read:
                     if r in vp:
@@ -149,11 +173,11 @@ def check_kernel(lines):
         for n in succ[k]:
             old = entry.get(n)
             if old is None:
-                entry[n] = (dict(mp), dict(vp))
+                entry[n] = (dict(mp), dict(vp), dict(sp))
                 work.append(n)
                 continue
             changed = False
-            for o, x in ((old[0], mp), (old[1], vp)):
+            for o, x in ((old[0], mp), (old[1], vp), (old[2], sp)):
                 for r, c in x.items():
                     if o.get(r, 0) < c:
                         o[r] = c

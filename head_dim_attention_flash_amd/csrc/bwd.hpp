@@ -87,7 +87,7 @@ __device__ inline void bwd_copy_row(__amdgpu_buffer_rsrc_t rs, FFPA_LDS char* ds
   const int n = wave + 4 * r;
   const int gl = u ^ swz4(n);
   const uint32_t lanepart = gl < SG ? (uint32_t)(half * SG + gl) << 4 : 0x80000000u;
-  dma16(rs, lanepart + (uint32_t)(row0 + n) * (D * 2), 0, dst + n * kBwdRowBytes);
+  dma16(rs, lanepart + (uint32_t)(row0 + n) * (D * 2), dst + n * kBwdRowBytes);
 }
 template <int D>
 __device__ inline void bwd_copy_tile(__amdgpu_buffer_rsrc_t rs, FFPA_LDS char* dst, int row0,

@@ -233,10 +233,9 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 }
 
 // 16-byte direct copy buffer -> LDS: lane t of the wave reads
-// rsrc[voff + soff .. +16) and writes LDS bytes [16 t, 16 t + 16) after
-// `lds_base` (wave-uniform, passed in M0). The range check applies to voff
-// only (the scalar offset is not checked): reads with voff at or past the
-// range write zeros.
+// rsrc[voff .. +16) and writes LDS bytes [16 t, 16 t + 16) after `lds_base`
+// (wave-uniform, passed in M0). The range check applies to voff: reads with
+// voff at or past the range write zeros.
 //
 // Issued as inline asm on purpose. The compiler's wait-count pass treats a
 // copy into LDS it knows about as a pending LDS write, and when it cannot
@@ -244,14 +243,21 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 // outstanding copy (s_waitcnt vmcnt(0)) before that read: a full memory
 // latency per tile. The kernels order copies and reads themselves
 // (wait_vmcnt before the barrier that publishes a tile), so the copy is kept
-// out of the compiler's tracking. s_nop 0 covers the M0 write -> LDS-copy
-// hazard.
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff,
-                             FFPA_LDS void* lds_base) {
+// out of the compiler's tracking.
+//
+// The compiler does not pad hazards for inline asm either. s_nop 0 covers
+// the M0 write -> LDS copy hazard. The scalar offset is the constant 0, so the
+// only SGPRs read are the resource and M0; a VALU write of one of them (a
+// v_readlane restoring a spilled SGPR) would need 5 wait states before the
+// copy. The compiler has no reason to place one there, and the static hazard
+// check of the built kernels (check_hazards.py, run by the CPU test suite)
+// rejects a build where it does: copies issue every few MFMAs, so a longer
+// fixed pad would cost throughput for nothing.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, FFPA_LDS void* lds_base) {
   const uint32_t m0 = (uint32_t)(uintptr_t)lds_base;
-  asm volatile("s_nop 0\n buffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_nop 0\n buffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+               : "v"(voff), "s"(rsrc), "{m0}"(m0)
                : "memory");
 }
 

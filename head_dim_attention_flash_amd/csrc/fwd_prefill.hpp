@@ -167,7 +167,7 @@ void fwd_prefill_kernel(FwdArgs a) {
     const int lg = ln ^ swz4(n);
     const uint32_t lanepart = (GPR == 64 || lg < GPR) ? (uint32_t)lg << 4 : 0x80000000u;
     const uint32_t voff = lanepart + (uint32_t)(tile * kFwdBc + n) * (D * 2);
-    dma16(rs, voff, 0, smem + buf + n * ROWB);
+    dma16(rs, voff, smem + buf + n * ROWB);
   };
   auto issue_tile = [&](__amdgpu_buffer_rsrc_t rs, int buf, int tile) {
     int ln = lane;  // recomputed at each call rather than held across the loop

@@ -93,6 +93,9 @@ void fwd_wide_kernel(FwdArgs a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = qp[2 * s];
   }
+  // compiler-visible: without it the K-phase MFMAs of every tile would wait
+  // for the Q loads again, and those waits also hold for the copies in flight
+  wait_vmcnt0_visible();
 
   // ---- copies: instruction n of a tile (n = wave + 4 r, r < 16) fills half
   // n / 32 of key row n % 32; lane i writes slot i = logical granule i ^ swz4(row)
@@ -106,7 +109,7 @@ void fwd_wide_kernel(FwdArgs a) {
       const int lg = ln ^ swz4(row);
       const uint32_t lanepart = lg < SG ? (uint32_t)(half * SG + lg) << 4 : 0x80000000u;
       const uint32_t voff = lanepart + (uint32_t)(tile * kWideBc + row) * (D * 2);
-      dma16(rs, voff, 0, smem + buf + half * kWideHalfTile + row * 1024);
+      dma16(rs, voff, smem + buf + half * kWideHalfTile + row * 1024);
     }
   };
 

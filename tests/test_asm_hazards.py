@@ -64,3 +64,13 @@ def test_checker_flags_scratch_use():
             "    .private_segment_fixed_size: 0\n    .vgpr_spill_count: 0\n")
     found = H.scratch_users(meta)
     assert len(found) == 1 and "foo" in found[0]
+
+
+def test_checker_flags_valu_sgpr_write_before_vector_memory():
+    # a spilled SGPR restored by v_readlane right before a copy that reads it
+    bad = ["v_readlane_b32 s1, v82, 3", "s_nop 0",
+           "buffer_load_dwordx4 v2, s[36:39], s1 offen lds", "s_endpgm"]
+    assert any("SGPR s1" in m for _, m in H.check_kernel(bad))
+    ok = ["v_readlane_b32 s1, v82, 3", "s_nop 4",
+          "buffer_load_dwordx4 v2, s[36:39], s1 offen lds", "s_endpgm"]
+    assert H.check_kernel(ok) == []
