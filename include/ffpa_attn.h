@@ -101,10 +101,11 @@ typedef enum {
  *               split-KV decode path, which keeps per-key-range partial
  *               outputs (fp32 o and log-sum-exp) there; other shapes need none.
  *   stream    : hipStream_t to enqueue on.
- * Built today: every D (multiple of 32, <= 1024) for Nq = 1; D a multiple of
- * 64 up to 512 for Nq > 1; the mask as a key bias (mask_rows = 1). Other
- * valid shapes return FFPA_ERR_UNSUPPORTED before any launch. With Nq = 1
- * the accumulation is fp32 whatever accum_dtype asks for.
+ * Built today: every D (multiple of 32, <= 1024) for Nq = 1; for Nq > 1, D a
+ * multiple of 64 up to 1024 (D > 512 runs a kernel that splits D across wave
+ * pairs). Both mask shapes are built on every path. Other valid shapes (Nq > 1
+ * with D not a multiple of 64) return FFPA_ERR_UNSUPPORTED before any launch.
+ * With Nq = 1 the accumulation is fp32 whatever accum_dtype asks for.
  */
 int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
@@ -122,8 +123,8 @@ size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
  * FFPA_ACC_F32. workspace: at least ffpa_attn_bwd_workspace_size(...) bytes,
  * 16-byte aligned (holds delta_i = sum_d dO_id O_id and lse_i log2(e) per
  * query row, rows padded to a multiple of 64). Three kernels are enqueued:
- * the delta pass, then dK/dV, then dQ. Built for D a multiple of 64 up to 512
- * and the key-bias mask; other valid shapes return FFPA_ERR_UNSUPPORTED.
+ * the delta pass, then dK/dV, then dQ. Built for D a multiple of 64 up to 512,
+ * with either mask shape; other valid shapes return FFPA_ERR_UNSUPPORTED.
  * The gradients are those of sum(dout * O) ("FFPA Attention Benchmark",
  * "More Benchmark": the backward counted as 5 GEMMs).
  */
