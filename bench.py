@@ -101,10 +101,14 @@ def time_forward(ffpa, w, inp, accum, steps, warmup):
     q, k, v, mask = inp["q"], inp["k"], inp["v"], inp.get("mask")
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=q.device)
+    # caller-owned workspace, allocated once (the transposed V of the prefill path)
+    ws_bytes = ffpa.ffpa_attn_fwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                                                 ffpa.BF16 if w.dtype == "bf16" else ffpa.F16)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
 
     def step():
         ffpa.attention(q, k, v, causal=w.causal, mask=mask, scale=w.scale, accum=accum, out=o,
-                       lse_out=lse)
+                       lse_out=lse, workspace=ws)
 
     for _ in range(warmup):
         step()

@@ -157,7 +157,8 @@ def _mask_args(mask, q, Nq, Nkv):
 
 
 def attention(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float] = None,
-              accum: str = "f32", return_lse: bool = False, out=None, lse_out=None):
+              accum: str = "f32", return_lse: bool = False, out=None, lse_out=None,
+              workspace=None):
     """O = softmax(scale q k^T + mask) v on the current HIP stream (see include/ffpa_attn.h)."""
     import torch
 
@@ -171,7 +172,12 @@ def attention(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float
     mptr, mrows = _mask_args(mask, q, Nq, Nkv)
     dt = _dtype_code(q)
     ws_bytes = ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    if workspace is not None and ws_bytes:
+        if workspace.numel() * workspace.element_size() < ws_bytes:
+            raise FFPAError(ERR_WORKSPACE, "workspace smaller than ffpa_attn_fwd_workspace_size()")
+        ws = workspace
+    else:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(ffpa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                          lse.data_ptr() if lse is not None else 0, B, Hq, Hkv, Nq, Nkv, D, scale,

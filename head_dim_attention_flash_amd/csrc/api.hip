@@ -9,6 +9,7 @@
 #include "bwd.hpp"
 #include "decode.hpp"
 #include "fwd_prefill.hpp"
+#include "fwd_vt.hpp"
 #include "fwd_wide.hpp"
 
 namespace {
@@ -144,12 +145,17 @@ int ffpa_version(void) { return 100; }
 const char* ffpa_last_error(void) { return g_err.c_str(); }
 
 size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {
-  (void)Hkv; (void)dtype;
-  if (Nq != 1 || B < 1 || Hq < 1 || Nkv < 1 || D < 1) return 0;
-  // decode: per key range, o (D fp32) and a log-sum-exp (fp32); the causal
-  // variant uses fewer ranges, so the non-causal count bounds both
-  const size_t s = (size_t)ffpa::dec_splits(B, Hq, Nkv);
-  return (size_t)B * Hq * s * ((size_t)D + 1) * sizeof(float);
+  (void)dtype;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1) return 0;
+  if (Nq == 1) {
+    // decode: per key range, o (D fp32) and a log-sum-exp (fp32); the causal
+    // variant uses fewer ranges, so the non-causal count bounds both
+    const size_t s = (size_t)ffpa::dec_splits(B, Hq, Nkv);
+    return (size_t)B * Hq * s * ((size_t)D + 1) * sizeof(float);
+  }
+  // prefill up to D = 512: the transposed copy of V
+  if (D <= 512 && D % 64 == 0) return ffpa::fwd_vt_bytes(B, Hkv, Nkv, D);
+  return 0;
 }
 
 int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
@@ -161,18 +167,17 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   int st = check_common(B, Hq, Hkv, Nq, Nkv, D, causal, mask, mask_rows, accum_dtype, dtype);
   if (st != FFPA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(mask))
+      !aligned16(mask) || !aligned16(workspace))
     return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (!(scale == scale)) return fail(FFPA_ERR_INVALID_ARG, "scale is NaN");
   const size_t need = ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_fwd_workspace_size()");
-  if (!(scale == scale)) return fail(FFPA_ERR_INVALID_ARG, "scale is NaN");
 
   if (Nq == 1) {
     // one query row per head: split-KV decode kernels
     DecLauncher launch = dec_launcher(D, dtype == FFPA_BF16);
     if (launch == nullptr) return fail(FFPA_ERR_UNSUPPORTED, "this head dimension is not built yet");
-    if (!aligned16(workspace)) return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
     ffpa::DecArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.mask = mask;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nkv = Nkv;
@@ -234,9 +239,11 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   const int64_t total = (int64_t)B * Hq * a.n_qtiles;
   if (total >= (int64_t(1) << 31)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
   a.total_wg = (int)total;
-  hipError_t e = launch(a, lds, (hipStream_t)stream);
+  a.vt = workspace;
+  a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
+  hipError_t e = ffpa::launch_fwd_vt(v, workspace, B * Hkv, Nkv, D, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch(a, lds, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
-  (void)workspace;
   return FFPA_OK;
 }
 

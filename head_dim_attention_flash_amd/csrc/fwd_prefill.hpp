@@ -15,17 +15,21 @@
 // so that each lane's accumulators all belong to one query row (l % 32): the
 // online-softmax rescale is a per-lane scalar and P goes from the S
 // accumulators into the B operand of the second MFMA without leaving
-// registers. V^T is read from the row-major V tile with ds_read_b64_tr_b16.
+// registers. V is staged from its transposed copy (fwd_vt.hpp), so both
+// operands read from LDS are plain 16-byte reads.
 //
-// Staging: one LDS buffer holds the K tile (64 x D), another the V tile, both
-// swizzled. The copy of V(j) is issued when the K(j) phase starts and the copy
-// of K(j+1) when the V(j) phase starts, so each copy has one phase of MFMA
-// work to land, and a tile costs two workgroup barriers. Copies go straight
-// from global memory to LDS (buffer_load ... lds) through a buffer resource
-// whose range ends at row Nkv, so rows past the end read as zeros.
+// Staging: one LDS buffer holds the K tile (64 keys x D, one 1 KiB row per
+// key), another the V^T tile (D rows x 64 keys, 128 bytes per row), both
+// swizzled. The copy of V(j) is spread over the K(j) phase and the copy of
+// K(j+1) over the V(j) phase, so each copy has one phase of MFMA work to
+// land, and a tile costs two workgroup barriers. Copies go straight from
+// global memory to LDS (buffer_load ... lds); the K buffer resource's range
+// ends at row Nkv, so rows past the end read as zeros, and V^T is zero past
+// Nkv by construction.
 #pragma once
 
 #include "ffpa_common.hpp"
+#include "fwd_vt.hpp"
 
 namespace ffpa {
 
@@ -33,6 +37,8 @@ struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
+  const void* vt;     // V transposed, [B, Hkv, D, nkv_pad] (fwd_vt.hpp); prefill kernel only
+  int nkv_pad;        // Nkv rounded up to a multiple of 64
   void* o;
   float* lse;         // may be null
   const void* mask;   // may be null
@@ -90,7 +96,8 @@ void fwd_prefill_kernel(FwdArgs a) {
   constexpr int ROWB = kFwdRowBytes;      // bytes per LDS row (D * 2 used)
   constexpr int GPR = D / 8;              // 16-byte granules of data per row
   constexpr int TILEB = kFwdBc * ROWB;    // bytes per tile buffer
-  constexpr int NDMA = kFwdBc / kFwdWaves;  // copies per wave per tile (one per row)
+  constexpr int NDMA = kFwdBc / kFwdWaves;  // K copies per wave per tile (one per row)
+  constexpr int NDMAV = D / (8 * kFwdWaves);  // V^T copies per wave per tile (8 rows each)
   constexpr int NDB = D / 32;             // output d-blocks of 32
   constexpr int KB = 0, VB = TILEB;       // buffer offsets
   constexpr int kKAhead = 3;              // K-fragment read-ahead, in d-steps
@@ -121,7 +128,9 @@ void fwd_prefill_kernel(FwdArgs a) {
   const size_t kv_off = ((size_t)(b * a.Hkv + hk) * a.Nkv) * D * 2;
   const uint32_t kv_bytes = (uint32_t)a.Nkv * D * 2;  // rows >= Nkv read as zeros
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc((const char*)a.k + kv_off, kv_bytes);
-  const __amdgpu_buffer_rsrc_t Vr = make_rsrc((const char*)a.v + kv_off, kv_bytes);
+  const uint32_t vt_row = (uint32_t)a.nkv_pad * 2;  // bytes per row of V^T
+  const __amdgpu_buffer_rsrc_t Vr =
+      make_rsrc((const char*)a.vt + (size_t)(b * a.Hkv + hk) * D * vt_row, (uint32_t)D * vt_row);
 
   // ---- key range
   int kv_end = a.Nkv;
@@ -182,6 +191,28 @@ void fwd_prefill_kernel(FwdArgs a) {
     for (int r = 0; r < NDMA; ++r)
       if ((r * span) / NDMA == st) issue_copy(rs, buf, tile, r, ln);
   };
+  // ---- copy of one V^T tile (D rows of 64 keys = 128 bytes). Copy
+  // instruction n (n = wave + 4 r) fills LDS rows 8 n .. 8 n + 7: lane i
+  // writes slot i % 8 of row 8 n + i / 8, which holds the logical granule
+  // (positions 8 g .. 8 g + 7) g = (i % 8) ^ vt_swz(row), vt_swz(row) =
+  // (row / 2) % 8. Within the 8 rows of one instruction vt_swz = 4 (n % 2) +
+  // (i / 8) / 2, so the per-lane part of the offset takes one of two values,
+  // by n's parity.
+  auto vt_lane_offsets = [&](int ln, uint32_t* lo) {
+    const int rl = ln >> 3;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      lo[par] = (uint32_t)rl * vt_row + (uint32_t)(((ln & 7) ^ (rl >> 1) ^ (4 * par)) << 4);
+  };
+  auto issue_spread_v = [&](int tile, int st, int span, const uint32_t* lo) {
+#pragma unroll
+    for (int r = 0; r < NDMAV; ++r)
+      if ((r * span) / NDMAV == st) {
+        const int n = wave + kFwdWaves * r;
+        const uint32_t voff = lo[n & 1] + (uint32_t)(8 * n) * vt_row + (uint32_t)tile * (kFwdBc * 2);
+        dma16(Vr, voff, smem + VB + n * 1024);
+      }
+  };
 
   // ---- LDS read addresses: per-lane bases (recomputed at the start of each
   // phase, so they are live only there) plus compile-time offsets < 64 KiB.
@@ -195,23 +226,18 @@ void fwd_prefill_kernel(FwdArgs a) {
   auto k_addr = [&](const uint32_t* kx, int st, int kb) -> uint32_t {
     return kx[st & 7] + 256 * (st >> 3) + 32 * kb * ROWB;
   };
-  // V^T fragment by transposed reads: group G = lane/16, i = lane%16 reads row
-  // 32 kb + 16 t2 + 8 r8 + 4 (G/2) + i/4 at columns 32 db + 16 (G%2) + 4 (i%4),
-  // i.e. logical granule 4 db + y with y = 2 (G%2) + (i%4)/2.
+  // V^T fragment (A of O^T) for d-block db and the 16-key step (kb, t2):
+  // row 32 db + l32 of the V^T tile, logical granule 4 kb + 2 t2 + hi, whose
+  // 8 positions hold the keys the lane's P operand pairs with (vt_key).
+  // Sixteen consecutive lanes read sixteen consecutive rows: two rows share a
+  // 256-byte bank window, and (row / 2) % 8 spreads the pairs over it.
   auto v_bases = [&](int ln, uint32_t* vx) {
-    const int G = ln >> 4, gi = ln & 15;
-    const int vrow = 4 * (G >> 1) + (gi >> 2);
-    const int y = 2 * (G & 1) + ((gi & 3) >> 1);
+    const int r = ln & 31, h = ln >> 5, x = (r >> 1) & 7;
 #pragma unroll
-    for (int r8 = 0; r8 < 2; ++r8) {
-      const int row = vrow + 8 * r8, x = swz4(row);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vx[4 * r8 + e] = (uint32_t)(VB + row * ROWB + (((4 * e + y) ^ x) << 4) + (gi & 1) * 8);
-    }
+    for (int p = 0; p < 4; ++p) vx[p] = (uint32_t)(VB + r * 128 + (((2 * p + h) ^ x) << 4));
   };
-  auto v_addr = [&](const uint32_t* vx, int db, int kb, int t2, int r8) -> uint32_t {
-    return vx[4 * r8 + (db & 3)] + 256 * (db >> 2) + (32 * kb + 16 * t2) * ROWB;
+  auto v_addr = [&](const uint32_t* vx, int db, int kb, int t2) -> uint32_t {
+    return vx[2 * kb + t2] + 4096 * db;
   };
 
   // ---- accumulators
@@ -272,11 +298,15 @@ void fwd_prefill_kernel(FwdArgs a) {
         kf[st][0] = kread(st, 0);
         kf[st][1] = kread(st, 1);
       }
-      int lnc = lane;
-      asm volatile("" : "+v"(lnc));
+      uint32_t vlo[2];
+      {
+        int lnc = lane;
+        asm volatile("" : "+v"(lnc));
+        vt_lane_offsets(lnc, vlo);
+      }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        issue_spread(Vr, VB, j, st, NS > 1 ? NS / 2 : 1, lnc);
+        issue_spread_v(j, st, NS > 1 ? NS / 2 : 1, vlo);
         const u32x4 a0 = kf[st % kKAhead][0], a1 = kf[st % kKAhead][1];
         if (st + kKAhead < NS) {
           kf[st % kKAhead][0] = kread(st + kKAhead, 0);
@@ -452,7 +482,7 @@ void fwd_prefill_kernel(FwdArgs a) {
         kb = p >> 1;
         t2 = p & 1;
       };
-      uint32_t vx[8];
+      uint32_t vx[4];
       {
         int lv = lane;
         asm volatile("" : "+v"(lv));
@@ -461,8 +491,7 @@ void fwd_prefill_kernel(FwdArgs a) {
       auto vread = [&](int st) {
         int db, kb, t2;
         step(st, db, kb, t2);
-        return join8(lds_read_tr(smem + v_addr(vx, db, kb, t2, 0)),
-                     lds_read_tr(smem + v_addr(vx, db, kb, t2, 1)));
+        return lds_read16(smem + v_addr(vx, db, kb, t2));
       };
       u32x4 vf[kVAhead];
 #pragma unroll

@@ -78,6 +78,10 @@ def bwd(**kw):
     (dict(k=P + 8), ffpa.ERR_INVALID_ARG),
     (dict(lse=P + 4), ffpa.ERR_INVALID_ARG),
     (dict(scale=float("nan")), ffpa.ERR_INVALID_ARG),
+    # Nq > 1, D <= 512: the transposed copy of V lives in the workspace
+    (dict(workspace=0, workspace_bytes=0), ffpa.ERR_WORKSPACE),
+    (dict(workspace=P, workspace_bytes=64 * 64 * 2 * 2 - 1), ffpa.ERR_WORKSPACE),
+    (dict(workspace=P + 8, workspace_bytes=1 << 20), ffpa.ERR_INVALID_ARG),
 ])
 def test_forward_validation(kw, code):
     assert fwd(**kw) == code
@@ -100,6 +104,15 @@ def test_forward_validation(kw, code):
 def test_backward_validation(kw, code):
     assert bwd(**kw) == code
     assert ffpa.ffpa_last_error() != ""
+
+
+def test_forward_workspace_holds_transposed_v():
+    # [B, Hkv, D, Nkv rounded up to 64] in the 16-bit input type
+    assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 8, 8, 64, 0) == 2 * 64 * 64 * 2
+    assert ffpa.ffpa_attn_fwd_workspace_size(2, 32, 8, 8192, 8191, 512, 1) == 2 * 8 * 512 * 8192 * 2
+    assert ffpa.ffpa_attn_fwd_workspace_size(1, 4, 1, 100, 65, 320, 0) == 320 * 128 * 2
+    # the wide path (D > 512) needs none
+    assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 100, 300, 1024, 0) == 0
 
 
 def test_workspace_queries_are_pure_functions():
