@@ -462,7 +462,11 @@ void fwd_prefill_kernel(FwdArgs a) {
         continue;
       }
     }
-    {
+    // The PV products, as a lambda instantiated for the first tile of an
+    // attempt (FRESH: the first product of each block starts from C = 0) and
+    // for the others, so that no MFMA of the hot loop sits behind a branch.
+    auto v_phase = [&](auto fresh_tag) {
+      constexpr bool FRESH = decltype(fresh_tag)::value;
       // Step order: consecutive MFMAs write different accumulators (a
       // dependent MFMA waits for its predecessor's result). fp32
       // accumulators: step st = NDB p + db, p = 2 kb + t2 the (key block,
@@ -554,10 +558,10 @@ void fwd_prefill_kernel(FwdArgs a) {
           if (db < kOAgpr) {
             if (first) {
               if (st == 0) {
-                if (fresh) mfma32_asm<BF16, false, true, true, true>(o_acc[db], vbits, pb);
+                if constexpr (FRESH) mfma32_asm<BF16, false, true, true, true>(o_acc[db], vbits, pb);
                 else mfma32_asm<BF16, false, true, false, true>(o_acc[db], vbits, pb);
               } else {
-                if (fresh) mfma32_asm<BF16, false, true, true>(o_acc[db], vbits, pb);
+                if constexpr (FRESH) mfma32_asm<BF16, false, true, true>(o_acc[db], vbits, pb);
                 else mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
               }
             } else if (pad_after) {
@@ -568,10 +572,10 @@ void fwd_prefill_kernel(FwdArgs a) {
           } else {
             if (first) {
               if (st == 0) {
-                if (fresh) mfma32_asm<BF16, false, false, true, true>(o_acc[db], vbits, pb);
+                if constexpr (FRESH) mfma32_asm<BF16, false, false, true, true>(o_acc[db], vbits, pb);
                 else mfma32_asm<BF16, false, false, false, true>(o_acc[db], vbits, pb);
               } else {
-                if (fresh) mfma32_asm<BF16, false, false, true>(o_acc[db], vbits, pb);
+                if constexpr (FRESH) mfma32_asm<BF16, false, false, true>(o_acc[db], vbits, pb);
                 else mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
               }
             } else if (pad_after) {
@@ -582,7 +586,9 @@ void fwd_prefill_kernel(FwdArgs a) {
           }
         }
       }
-    }
+    };
+    if (!ACC16 && fresh) v_phase(BoolTag<true>{});
+    else v_phase(BoolTag<false>{});
     fresh = false;
   }
   wait_vmcnt<0>();  // no copy may still target this workgroup's LDS when it ends
