@@ -101,7 +101,7 @@ void fwd_prefill_kernel(FwdArgs a) {
   constexpr int NDB = D / 32;             // output d-blocks of 32
   constexpr int KB = 0, VB = TILEB;       // buffer offsets
   constexpr int kKAhead = 3;              // K-fragment read-ahead, in d-steps
-  constexpr int kVAhead = ACC16 ? 6 : 12; // V-fragment read-ahead, in MFMAs
+  constexpr int kVAhead = ACC16 ? 6 : 8;  // V-fragment read-ahead, in MFMAs
   // fp32 accumulator d-blocks that share the AGPRs with the Q fragments; the
   // remaining blocks live in VGPRs
   constexpr int kOAgpr = (256 - D / 4) / 16 < NDB ? (256 - D / 4) / 16 : NDB;
@@ -257,6 +257,245 @@ void fwd_prefill_kernel(FwdArgs a) {
   FFPA_LDS uint32_t* restart_flag = (FFPA_LDS uint32_t*)(smem + fwd_ring_bytes<D>() +
                                                          (key_bias ? fwd_bias_bytes(a.Nkv) : 0));
 
+  if constexpr (!ACC16) {
+    // ---- fp32 accumulation. A tile's scores are two 32-key halves, each one
+    // MFMA chain over D. The softmax of half 0 runs beside the chain of half
+    // 1, and the softmax of half 1 beside the P V products of half 0, so the
+    // matrix cores do not wait for the exponentials. The restart test of a
+    // tile (some row above m_ref + tau) is read after the next tile's first
+    // barrier: the tile that broke the bound has been accumulated by then,
+    // which the restart discards with everything else.
+    constexpr int NS = D / 16;        // d-steps of one chain
+    constexpr int kKA = 6;            // K fragments read ahead
+    float mx_prev = -INFINITY;        // the previous tile's row max (log2 domain)
+    issue_tile(Kr, KB, 0);
+    for (int j = 0; j <= n_tiles; ++j) {
+      const int j0 = j * kFwdBc;
+      int lj = lane;
+      asm volatile("" : "+v"(lj));
+      const int hij = lj >> 5;
+      const int my_qj = qw + (lj & 31);
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        if (d < kOAgpr) asm volatile("" : "+a"(o_acc[d]));
+        else asm volatile("" : "+v"(o_acc[d]));
+      }
+      wait_vmcnt<0>();  // K(j) landed (this wave's copies) ...
+      wait_lgkm0();
+      barrier();        // ... and everyone's; everyone is done with V(j-1)
+      if (j > 0) {
+        const u32x4 f = *(const FFPA_LDS u32x4*)restart_flag;
+        if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // workgroup-uniform
+          // restart with the raised reference; O restarts from zero through
+          // `fresh` (the next P V products ignore the old accumulators)
+          m_ref = fmaxf(m_ref, mx_prev);
+          l_run = 0.f;
+          fresh = true;
+          issue_tile(Kr, KB, 0);
+          j = -1;
+          continue;
+        }
+      }
+      if (j == n_tiles) break;
+
+      const bool need_mask = has_mask || (j0 + kFwdBc > a.Nkv) || (a.causal && j0 + kFwdBc - 1 > qw);
+      const int kb0 = j0 + 4 * hij;  // lane's keys: kb0 + 32 kb + 8 (i / 4) + i % 4
+      // scaled (and masked) scores of half kb in the log2 domain, and their
+      // row max over the half
+      auto half_scores = [&](const f32x16& s, int kb, float* tv) -> float {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tv[i] = s[i] * a.scale_log2;
+        if (need_mask) {
+          if (has_mask && !key_bias) {
+            const uint16_t* mrow = (const uint16_t*)a.mask + (size_t)min(my_qj, a.Nq - 1) * a.mask_stride;
+            const bool by8 = (a.Nkv & 3) == 0;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const f32x4 bv = mask_row4<BF16>(mrow, kb0 + 32 * kb + 8 * g4, a.Nkv, by8);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) tv[4 * g4 + e] += bv[e] * kLog2e;
+            }
+          }
+          if (key_bias) {
+            const FFPA_LDS char* bp = (const FFPA_LDS char*)bias_lds + 2 * (kb0 + 32 * kb);
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const u32x2 w = *(const FFPA_LDS u32x2*)(bp + 16 * g4);
+              tv[4 * g4 + 0] += E::to_f32((uint16_t)(w[0] & 0xffff)) * kLog2e;
+              tv[4 * g4 + 1] += E::to_f32((uint16_t)(w[0] >> 16)) * kLog2e;
+              tv[4 * g4 + 2] += E::to_f32((uint16_t)(w[1] & 0xffff)) * kLog2e;
+              tv[4 * g4 + 3] += E::to_f32((uint16_t)(w[1] >> 16)) * kLog2e;
+            }
+          }
+          int klim = a.Nkv - kb0 - 32 * kb;
+          if (a.causal) klim = min(klim, my_qj + 1 - kb0 - 32 * kb);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) tv[i] = (8 * (i >> 2) + (i & 3)) >= klim ? -INFINITY : tv[i];
+        }
+        float mh = tv[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mh = fmaxf(mh, tv[i]);
+        mh = fmaxf(mh, swap_halves(mh));
+        // first unmasked keys of this row: adopt their max (O and l are still 0)
+        if (m_ref == -INFINITY) m_ref = mh;
+        return mh;
+      };
+      // P = 2^(t - m_ref) of elements [i0, i1) of a half, summed into l_run
+      auto half_exp = [&](float* tv, int i0, int i1) {
+        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+#pragma unroll
+        for (int i = i0; i < i1; ++i) {
+          tv[i] = exp2_fast(tv[i] - m_use);
+          l_run += tv[i];
+        }
+      };
+      auto half_pack = [&](const float* tv, V8* pf) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const float* x = &tv[8 * t2];
+          pf[t2] = pack8<BF16>(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+        }
+      };
+      // softmax work of a half spread over the NS MFMA slots q = 0 .. NS - 1
+      // beside it: the scores at slot 0, the exponentials of element i at
+      // slot 1 + i (NS - 2) / 16, the packing after the last one. Each
+      // element is pinned at its slot, so the compiler keeps the order.
+      auto half_slot = [&](const f32x16& s, int kb, int q, float* tv, float& mh, V8* pf) {
+        if (q == 0) mh = half_scores(s, kb, tv);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int slot = NS > 2 ? 1 + (i * (NS - 2)) / 16 : NS - 1;
+          if (slot == q) {
+            asm volatile("" : "+v"(tv[i]));
+            half_exp(tv, i, i + 1);
+          }
+        }
+        if (q == NS - 1) {
+          half_pack(tv, pf);
+#pragma unroll
+          for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[t2]));
+        }
+      };
+
+      // ===== K phase: S^T = K Q^T, half 0 then half 1, with the softmax of
+      // half 0 beside the chain of half 1. The copies of V(j) are spread over
+      // the chain of half 0.
+      f32x16 s_acc[2];
+      float tv0[16], tv1[16];
+      float mh0 = -INFINITY, mh1 = -INFINITY;
+      V8 pf0[2], pf1[2];
+      {
+        u32x4 kf[kKA];
+        uint32_t kx[8];
+        k_bases(lj, kx);
+        auto kread = [&](int c) { return lds_read16(smem + k_addr(kx, c % NS, c / NS)); };
+#pragma unroll
+        for (int c = 0; c < kKA; ++c) kf[c] = kread(c);
+        uint32_t vlo[2];
+        {
+          int lnc = lane;
+          asm volatile("" : "+v"(lnc));
+          vt_lane_offsets(lnc, vlo);
+        }
+#pragma unroll
+        for (int c = 0; c < 2 * NS; ++c) {
+          issue_spread_v(j, c, NS, vlo);
+          const u32x4 a0 = kf[c % kKA];
+          if (c + kKA < 2 * NS) kf[c % kKA] = kread(c + kKA);
+          const int st = c % NS;
+          f32x16& acc = s_acc[c / NS];
+          // each chain ends padded for the VALU that reads its scores next
+          if (st == 0) mfma32_asm<BF16, true, false, true>(acc, a0, qf[st]);
+          else if (st == NS - 1) mfma32_asm<BF16, true, false, false, false, true>(acc, a0, qf[st]);
+          else mfma32_asm<BF16, true, false>(acc, a0, qf[st]);
+          if (c == NS - 1) pin_after_pad(s_acc[0]);
+          if (c >= NS) half_slot(s_acc[0], 0, c - NS, tv0, mh0, pf0);
+        }
+        pin_after_pad(s_acc[1]);
+      }
+
+      // ===== V phase: O^T += V^T P^T
+      wait_vmcnt<0>();  // V(j) landed ...
+      wait_lgkm0();
+      barrier();        // ... everywhere; everyone is done with K(j)
+      // The P V products, as a lambda instantiated for the first tile of an
+      // attempt (FRESH: the first product of each block starts from C = 0) and
+      // for the others, so that no MFMA of the hot loop sits behind a branch.
+      // Step st = NDB p + db, p = 2 kb + t2: the products of half 0 come
+      // first, and the softmax of half 1 runs beside them.
+      auto v_phase = [&](auto fresh_tag) {
+        constexpr bool FRESH = decltype(fresh_tag)::value;
+        constexpr int NSV = 4 * NDB;
+        uint32_t vx[4];
+        {
+          int lv = lane;
+          asm volatile("" : "+v"(lv));
+          v_bases(lv, vx);
+        }
+        auto vread = [&](int st) {
+          const int p = st / NDB, db = st % NDB;
+          return lds_read16(smem + v_addr(vx, db, p >> 1, p & 1));
+        };
+        u32x4 vf[kVAhead];
+#pragma unroll
+        for (int st = 0; st < kVAhead; ++st) vf[st] = vread(st);
+        int lnc = lane;
+        asm volatile("" : "+v"(lnc));
+#pragma unroll
+        for (int st = 0; st < NSV; ++st) {
+          // on the last tile this copies rows past the key range (range-checked
+          // zeros) or, causal, rows nobody reads: harmless, and branch-free
+          issue_spread(Kr, KB, j + 1, st, NSV / 2, lnc);
+          const int p = st / NDB, db = st % NDB;
+          const int kb = p >> 1, t2 = p & 1;
+          const u32x4 vbits = vf[st % kVAhead];
+          if (st + kVAhead < NSV) vf[st % kVAhead] = vread(st + kVAhead);
+          const u32x4 pb = __builtin_bit_cast(u32x4, kb == 0 ? pf0[t2] : pf1[t2]);
+          // the first MFMA of each half pads for the VALU that wrote its P;
+          // the last one pads for accumulator copies on the loop's edges
+          const bool first = st == 0 || st == 2 * NDB;
+          const bool zero = FRESH && p == 0;
+          const bool pad_after = st == NSV - 1;
+          if (db < kOAgpr) {
+            if (zero) {
+              if (first) mfma32_asm<BF16, false, true, true, true>(o_acc[db], vbits, pb);
+              else mfma32_asm<BF16, false, true, true>(o_acc[db], vbits, pb);
+            } else if (first) {
+              mfma32_asm<BF16, false, true, false, true>(o_acc[db], vbits, pb);
+            } else if (pad_after) {
+              mfma32_asm<BF16, false, true, false, false, true>(o_acc[db], vbits, pb);
+            } else {
+              mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
+            }
+          } else {
+            if (zero) {
+              if (first) mfma32_asm<BF16, false, false, true, true>(o_acc[db], vbits, pb);
+              else mfma32_asm<BF16, false, false, true>(o_acc[db], vbits, pb);
+            } else if (first) {
+              mfma32_asm<BF16, false, false, false, true>(o_acc[db], vbits, pb);
+            } else if (pad_after) {
+              mfma32_asm<BF16, false, false, false, false, true>(o_acc[db], vbits, pb);
+            } else {
+              mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
+            }
+          }
+          // softmax of half 1 over the first NS products (2 NDB >= NS)
+          if (st < NS) half_slot(s_acc[1], 1, st, tv1, mh1, pf1);
+          if (st == NS - 1) {
+            // restart test of the tile, read after the next tile's first barrier
+            float mx = fmaxf(mh0, mh1);
+            mx_prev = mx;
+            const bool broke = mx > m_ref + fwd_tau<BF16>();
+            const uint32_t any_broke = __builtin_amdgcn_ballot_w64(broke) != 0 ? 1u : 0u;
+            if (lane == 0) restart_flag[wave] = any_broke;
+          }
+        }
+      };
+      if (fresh) v_phase(BoolTag<true>{});
+      else v_phase(BoolTag<false>{});
+      fresh = false;
+    }
+  } else {
   issue_tile(Kr, KB, 0);
 
   for (int j = 0; j < n_tiles; ++j) {
@@ -591,6 +830,7 @@ void fwd_prefill_kernel(FwdArgs a) {
     else v_phase(BoolTag<false>{});
     fresh = false;
   }
+  }
   wait_vmcnt<0>();  // no copy may still target this workgroup's LDS when it ends
   if constexpr (!ACC16) {
     // the accumulators were last written by MFMAs issued as inline asm: pad
@@ -610,7 +850,9 @@ void fwd_prefill_kernel(FwdArgs a) {
   // contiguous 1 KiB pieces. Written straight from the accumulators, a cache
   // line of O would be filled by many partial writes and leave the L2 several
   // times.
-  const int le = threadIdx.x & 63, hie = le >> 5, my_qe = qw + (le & 31);
+  int le = threadIdx.x & 63;
+  asm volatile("" : "+v"(le));  // derived afresh: no lane value lives across the loop
+  const int hie = le >> 5, my_qe = qw + (le & 31);
   float l_tot, inv;
   if constexpr (!ACC16) {
     l_tot = l_run + swap_halves(l_run);
