@@ -218,7 +218,7 @@ def check_file(src: str) -> list[str]:
 
 
 def main(argv=None) -> int:
-    srcs = argv or [s for s in B.sources() if os.path.basename(s).startswith(("fwd_d", "bwd_d"))]
+    srcs = argv or [s for s in B.sources() if os.path.basename(s).startswith(("fwd_d", "fwd_w", "bwd_d"))]
     bad = []
     for s in srcs:
         bad += check_file(s)

@@ -153,8 +153,8 @@ size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
     const size_t s = (size_t)ffpa::dec_splits(B, Hq, Nkv);
     return (size_t)B * Hq * s * ((size_t)D + 1) * sizeof(float);
   }
-  // prefill up to D = 512: the transposed copy of V
-  if (D <= 512 && D % 64 == 0) return ffpa::fwd_vt_bytes(B, Hkv, Nkv, D);
+  // the transposed copy of V the attention kernels read
+  if (D % 64 == 0) return ffpa::fwd_vt_bytes(B, Hkv, Nkv, D);
   return 0;
 }
 
@@ -212,7 +212,10 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     const int64_t total = (int64_t)B * Hq * a.n_qtiles;
     if (total >= (int64_t(1) << 31)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
     a.total_wg = (int)total;
-    hipError_t e = launch(a, (hipStream_t)stream);
+    a.vt = workspace;
+    a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
+    hipError_t e = ffpa::launch_fwd_vt(v, workspace, B * Hkv, Nkv, D, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return FFPA_OK;
   }

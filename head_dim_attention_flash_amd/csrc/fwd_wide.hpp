@@ -18,11 +18,12 @@
 //   3. runs the online softmax (restart-based reference max, as in the
 //      prefill kernel with fp32 accumulation);
 //   4. accumulates O^T_half += V_half^T P^T.
-// Tiles are 32 keys; a staged K or V tile holds both halves, each half row
-// in its own 1 KiB LDS row (granules XOR-swizzled by swz4(row)), so a tile is
-// 64 KiB and K plus V fill 128 KiB. As in the prefill kernel the copy of V(j)
-// is issued when the K(j) phase starts and the copy of K(j+1) when the V(j)
-// phase starts.
+// Tiles are 32 keys. A staged K tile holds both halves, each half row in its
+// own 1 KiB LDS row (granules XOR-swizzled by swz4(row)): 64 KiB. V is staged
+// from its transposed copy (fwd_vt.hpp): D rows of 32 keys, 64 bytes each,
+// also 64 KiB, read with plain 16-byte reads. As in the prefill kernel the
+// copy of V(j) is issued when the K(j) phase starts and the copy of K(j+1)
+// when the V(j) phase starts.
 //
 // Accumulation is fp32 (the fp16-accumulator request maps to this kernel too:
 // it is at least as accurate).
@@ -76,7 +77,9 @@ void fwd_wide_kernel(FwdArgs a) {
   const size_t kv_off = ((size_t)(b * a.Hkv + hk) * a.Nkv) * D * 2;
   const uint32_t kv_bytes = (uint32_t)a.Nkv * D * 2;  // rows >= Nkv read as zeros
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc((const char*)a.k + kv_off, kv_bytes);
-  const __amdgpu_buffer_rsrc_t Vr = make_rsrc((const char*)a.v + kv_off, kv_bytes);
+  const uint32_t vt_row = (uint32_t)a.nkv_pad * 2;  // bytes per row of V^T
+  const __amdgpu_buffer_rsrc_t Vr =
+      make_rsrc((const char*)a.vt + (size_t)(b * a.Hkv + hk) * D * vt_row, (uint32_t)D * vt_row);
 
   int kv_end = a.Nkv;
   if (a.causal) kv_end = min(kv_end, min(q0 + 64, a.Nq));  // keys <= last row of the block
@@ -113,6 +116,22 @@ void fwd_wide_kernel(FwdArgs a) {
     }
   };
 
+  // ---- copy of one V^T tile (D rows of 32 keys = 64 bytes). Copy
+  // instruction n (n = wave + 4 r, r < D / 64) fills LDS rows 16 n .. 16 n +
+  // 15: lane i writes slot i % 4 of row 16 n + i / 4, which holds the logical
+  // granule (positions 8 g .. 8 g + 7) g = (i % 4) ^ ((row / 4) % 4), and
+  // (row / 4) % 4 = (i / 16) % 4 whatever n is.
+  auto issue_vt_tile = [&](int tile) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const uint32_t lo = (uint32_t)(ln >> 2) * vt_row + (uint32_t)(((ln & 3) ^ ((ln >> 4) & 3)) << 4);
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r) {
+      const int n = wave + 4 * r;
+      dma16(Vr, lo + (uint32_t)(16 * n) * vt_row + (uint32_t)tile * (kWideBc * 2), smem + VB + n * 1024);
+    }
+  };
+
   // K fragment (A of S^T) for k-step st = 8 a + c: key row l % 32, granule 2 st + l / 32
   auto k_bases = [&](int ln, uint32_t* kx) {
     const int r = ln & 31, hh = ln >> 5, x = swz4(r);
@@ -120,19 +139,16 @@ void fwd_wide_kernel(FwdArgs a) {
     for (int c = 0; c < 8; ++c)
       kx[c] = (uint32_t)(KB + hf * kWideHalfTile + r * 1024 + (((2 * c + hh) ^ x) << 4));
   };
-  // V^T fragment by transposed reads: rows 16 t2 + 8 r8 + 4 (G / 2) + i / 4,
-  // columns 32 db + 16 (G % 2) + 4 (i % 4) of the half (G = lane / 16, i = lane % 16)
+  // V^T fragment (A of O^T_half) for d-block db and the 16-key step t2: row
+  // W hf + 32 db + l % 32 of the V^T tile, logical granule 2 t2 + l / 32,
+  // whose positions hold the keys the lane's P operand pairs with (vt_key).
+  // Sixteen consecutive lanes read sixteen consecutive 64-byte rows: four
+  // share a bank window, and (row / 4) % 4 spreads them over it.
   auto v_bases = [&](int ln, uint32_t* vx) {
-    const int G = ln >> 4, gi = ln & 15;
-    const int vrow = 4 * (G >> 1) + (gi >> 2);
-    const int y = 2 * (G & 1) + ((gi & 3) >> 1);
+    const int r = ln & 31, h = ln >> 5;
 #pragma unroll
-    for (int r8 = 0; r8 < 2; ++r8) {
-      const int row = vrow + 8 * r8, x = swz4(row);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        vx[4 * r8 + e] = (uint32_t)(VB + hf * kWideHalfTile + row * 1024 + (((4 * e + y) ^ x) << 4) + (gi & 1) * 8);
-    }
+    for (int t2 = 0; t2 < 2; ++t2)
+      vx[t2] = (uint32_t)(VB + (W * hf + r) * 64 + (((2 * t2 + h) ^ ((r >> 2) & 3)) << 4));
   };
 
   f32x16 o_acc[NDB];
@@ -161,7 +177,7 @@ void fwd_wide_kernel(FwdArgs a) {
     wait_vmcnt<0>();
     wait_lgkm0();
     barrier();
-    issue_tile(Vr, VB, j);
+    issue_vt_tile(j);
     f32x16 s_acc, s_odd;
     {
       u32x4 kf[kKAhead];
@@ -264,9 +280,13 @@ void fwd_wide_kernel(FwdArgs a) {
       }
     }
     if (j + 1 < n_tiles) issue_tile(Kr, KB, j + 1);
-    {
+    // The PV products, as a lambda instantiated for the first tile of an
+    // attempt (FRESH: the t2 = 0 product of each block starts from C = 0) and
+    // for the others, so that no MFMA of the hot loop sits behind a branch.
+    auto v_phase = [&](auto fresh_tag) {
+      constexpr bool FRESH = decltype(fresh_tag)::value;
       constexpr int NSV = 2 * NDB;  // steps st = NDB t2 + db
-      uint32_t vx[8];
+      uint32_t vx[2];
       {
         int lv = lane;
         asm volatile("" : "+v"(lv));
@@ -274,8 +294,7 @@ void fwd_wide_kernel(FwdArgs a) {
       }
       auto vread = [&](int st) {
         const int db = st % NDB, t2 = st / NDB;
-        const uint32_t off = 256 * (db >> 2) + 16 * t2 * 1024;
-        return join8(lds_read_tr(smem + vx[db & 3] + off), lds_read_tr(smem + vx[4 + (db & 3)] + off));
+        return lds_read16(smem + vx[t2] + 2048 * db);
       };
       u32x4 vf[kVAhead];
 #pragma unroll
@@ -286,31 +305,37 @@ void fwd_wide_kernel(FwdArgs a) {
         const u32x4 vbits = vf[st % kVAhead];
         if (st + kVAhead < NSV) vf[st % kVAhead] = vread(st + kVAhead);
         const u32x4 pb = __builtin_bit_cast(u32x4, pf[t2]);
-        // the t2 = 0 MFMA of a block starts its chain: zero C on a fresh attempt
-        if (t2 == 0) {
-          if (db < kOAgpr) {
-            if (st == 0) {
-              if (fresh) mfma32_asm<BF16, false, true, true, true>(o_acc[db], vbits, pb);
-              else mfma32_asm<BF16, false, true, false, true>(o_acc[db], vbits, pb);
-            } else {
-              if (fresh) mfma32_asm<BF16, false, true, true>(o_acc[db], vbits, pb);
-              else mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
-            }
+        // the first MFMA pads for the VALU that wrote P, the last one for
+        // whatever the compiler places after the phase on any path
+        const bool zero = FRESH && t2 == 0;
+        const bool pad_after = st == NSV - 1;
+        if (db < kOAgpr) {
+          if (zero) {
+            if (st == 0) mfma32_asm<BF16, false, true, true, true>(o_acc[db], vbits, pb);
+            else mfma32_asm<BF16, false, true, true>(o_acc[db], vbits, pb);
+          } else if (st == 0) {
+            mfma32_asm<BF16, false, true, false, true>(o_acc[db], vbits, pb);
+          } else if (pad_after) {
+            mfma32_asm<BF16, false, true, false, false, true>(o_acc[db], vbits, pb);
           } else {
-            if (st == 0) {
-              if (fresh) mfma32_asm<BF16, false, false, true, true>(o_acc[db], vbits, pb);
-              else mfma32_asm<BF16, false, false, false, true>(o_acc[db], vbits, pb);
-            } else {
-              if (fresh) mfma32_asm<BF16, false, false, true>(o_acc[db], vbits, pb);
-              else mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
-            }
+            mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
           }
         } else {
-          if (db < kOAgpr) mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
-          else mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
+          if (zero) {
+            if (st == 0) mfma32_asm<BF16, false, false, true, true>(o_acc[db], vbits, pb);
+            else mfma32_asm<BF16, false, false, true>(o_acc[db], vbits, pb);
+          } else if (st == 0) {
+            mfma32_asm<BF16, false, false, false, true>(o_acc[db], vbits, pb);
+          } else if (pad_after) {
+            mfma32_asm<BF16, false, false, false, false, true>(o_acc[db], vbits, pb);
+          } else {
+            mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
+          }
         }
       }
-    }
+    };
+    if (fresh) v_phase(BoolTag<true>{});
+    else v_phase(BoolTag<false>{});
     fresh = false;
   }
   wait_vmcnt<0>();

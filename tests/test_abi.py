@@ -111,8 +111,7 @@ def test_forward_workspace_holds_transposed_v():
     assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 8, 8, 64, 0) == 2 * 64 * 64 * 2
     assert ffpa.ffpa_attn_fwd_workspace_size(2, 32, 8, 8192, 8191, 512, 1) == 2 * 8 * 512 * 8192 * 2
     assert ffpa.ffpa_attn_fwd_workspace_size(1, 4, 1, 100, 65, 320, 0) == 320 * 128 * 2
-    # the wide path (D > 512) needs none
-    assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 100, 300, 1024, 0) == 0
+    assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 100, 300, 1024, 0) == 2 * 1024 * 320 * 2
 
 
 def test_workspace_queries_are_pure_functions():
