@@ -51,8 +51,8 @@ void fwd_wide_kernel(FwdArgs a) {
   constexpr int NS = W / 16;            // k-steps of the partial product
   constexpr int NDB = W / 32;           // output d-blocks of the half
   constexpr int KB = 0, VB = kWideTile, XB = 2 * kWideTile, FB = 2 * kWideTile + 4 * kWideXchg;
-  constexpr int kKAhead = 3;
-  constexpr int kVAhead = 8;
+  constexpr int kKAhead = 8;
+  constexpr int kVAhead = 12;
   // fp32 accumulator d-blocks in AGPRs (beside the W/4 Q registers); the rest in VGPRs
   constexpr int kOAgpr = (256 - W / 4) / 16 < NDB ? (256 - W / 4) / 16 : NDB;
 
@@ -102,18 +102,19 @@ void fwd_wide_kernel(FwdArgs a) {
 
   // ---- copies: instruction n of a tile (n = wave + 4 r, r < 16) fills half
   // n / 32 of key row n % 32; lane i writes slot i = logical granule i ^ swz4(row)
-  auto issue_tile = [&](__amdgpu_buffer_rsrc_t rs, int buf, int tile) {
+  auto k_copy = [&](int tile, int r, int ln) {
+    const int n = wave + 4 * r;
+    const int row = n & 31, half = n >> 5;
+    const int lg = ln ^ swz4(row);
+    const uint32_t lanepart = lg < SG ? (uint32_t)(half * SG + lg) << 4 : 0x80000000u;
+    const uint32_t voff = lanepart + (uint32_t)(tile * kWideBc + row) * (D * 2);
+    dma16(Kr, voff, smem + KB + half * kWideHalfTile + row * 1024);
+  };
+  auto issue_k_tile = [&](int tile) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = wave + 4 * r;
-      const int row = n & 31, half = n >> 5;
-      const int lg = ln ^ swz4(row);
-      const uint32_t lanepart = lg < SG ? (uint32_t)(half * SG + lg) << 4 : 0x80000000u;
-      const uint32_t voff = lanepart + (uint32_t)(tile * kWideBc + row) * (D * 2);
-      dma16(rs, voff, smem + buf + half * kWideHalfTile + row * 1024);
-    }
+    for (int r = 0; r < 16; ++r) k_copy(tile, r, ln);
   };
 
   // ---- copy of one V^T tile (D rows of 32 keys = 64 bytes). Copy
@@ -121,16 +122,18 @@ void fwd_wide_kernel(FwdArgs a) {
   // 15: lane i writes slot i % 4 of row 16 n + i / 4, which holds the logical
   // granule (positions 8 g .. 8 g + 7) g = (i % 4) ^ ((row / 4) % 4), and
   // (row / 4) % 4 = (i / 16) % 4 whatever n is.
-  auto issue_vt_tile = [&](int tile) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const uint32_t lo = (uint32_t)(ln >> 2) * vt_row + (uint32_t)(((ln & 3) ^ ((ln >> 4) & 3)) << 4);
-#pragma unroll
-    for (int r = 0; r < D / 64; ++r) {
-      const int n = wave + 4 * r;
-      dma16(Vr, lo + (uint32_t)(16 * n) * vt_row + (uint32_t)tile * (kWideBc * 2), smem + VB + n * 1024);
-    }
+  auto vt_lane_offset = [&](int ln) {
+    return (uint32_t)(ln >> 2) * vt_row + (uint32_t)(((ln & 3) ^ ((ln >> 4) & 3)) << 4);
   };
+  auto vt_copy = [&](int tile, int r, uint32_t lo) {
+    const int n = wave + 4 * r;
+    dma16(Vr, lo + (uint32_t)(16 * n) * vt_row + (uint32_t)tile * (kWideBc * 2), smem + VB + n * 1024);
+  };
+  // The copies of a tile are spread over the first `span` MFMA steps of the
+  // phase before the one that reads them (copy r at step r span / count):
+  // issued in one burst, they held the wave's MFMAs back while the copy
+  // instructions queued.
+  constexpr int NKC = 16, NVC = D / 64;  // copies per wave per tile: K, V^T
 
   // K fragment (A of S^T) for k-step st = 8 a + c: key row l % 32, granule 2 st + l / 32
   auto k_bases = [&](int ln, uint32_t* kx) {
@@ -159,7 +162,7 @@ void fwd_wide_kernel(FwdArgs a) {
   bool fresh = true;        // no PV product accumulated yet in this attempt
   FFPA_LDS uint32_t* restart_flag = (FFPA_LDS uint32_t*)(smem + FB);
 
-  if (n_tiles > 0) issue_tile(Kr, KB, 0);
+  if (n_tiles > 0) issue_k_tile(0);
 
   for (int j = 0; j < n_tiles; ++j) {
     const int j0 = j * kWideBc;
@@ -177,9 +180,15 @@ void fwd_wide_kernel(FwdArgs a) {
     wait_vmcnt<0>();
     wait_lgkm0();
     barrier();
-    issue_vt_tile(j);
     f32x16 s_acc, s_odd;
     {
+      uint32_t vlo;
+      {
+        int lnc = lane;
+        asm volatile("" : "+v"(lnc));
+        vlo = vt_lane_offset(lnc);
+        asm volatile("" : "+v"(vlo));  // opaque: each copy then adds a scalar offset
+      }
       u32x4 kf[kKAhead];
       uint32_t kx[8];
       k_bases(lj, kx);
@@ -188,6 +197,9 @@ void fwd_wide_kernel(FwdArgs a) {
       for (int st = 0; st < kKAhead; ++st) kf[st] = kread(st);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
+#pragma unroll
+        for (int r = 0; r < NVC; ++r)
+          if ((r * (NS / 2)) / NVC == st) vt_copy(j, r, vlo);
         const u32x4 a0 = kf[st % kKAhead];
         if (st + kKAhead < NS) kf[st % kKAhead] = kread(st + kKAhead);
         f32x16& acc = (st & 1) ? s_odd : s_acc;
@@ -274,12 +286,11 @@ void fwd_wide_kernel(FwdArgs a) {
         m_ref = fmaxf(m_ref, mx);
         l_run = 0.f;
         fresh = true;
-        issue_tile(Kr, KB, 0);
+        issue_k_tile(0);
         j = -1;
         continue;
       }
     }
-    if (j + 1 < n_tiles) issue_tile(Kr, KB, j + 1);
     // The PV products, as a lambda instantiated for the first tile of an
     // attempt (FRESH: the t2 = 0 product of each block starts from C = 0) and
     // for the others, so that no MFMA of the hot loop sits behind a branch.
@@ -299,8 +310,15 @@ void fwd_wide_kernel(FwdArgs a) {
       u32x4 vf[kVAhead];
 #pragma unroll
       for (int st = 0; st < kVAhead; ++st) vf[st] = vread(st);
+      int lnc = lane;
+      asm volatile("" : "+v"(lnc));
 #pragma unroll
       for (int st = 0; st < NSV; ++st) {
+        // K(j+1); on the last tile rows past the key range (range-checked
+        // zeros) or, causal, rows nobody reads: harmless, and branch-free
+#pragma unroll
+        for (int r = 0; r < NKC; ++r)
+          if ((r * (NSV / 2)) / NKC == st) k_copy(j + 1, r, lnc);
         const int db = st % NDB, t2 = st / NDB;
         const u32x4 vbits = vf[st % kVAhead];
         if (st + kVAhead < NSV) vf[st % kVAhead] = vread(st + kVAhead);
