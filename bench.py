@@ -33,6 +33,8 @@ PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6}  # MI355X dense MFMA, published
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("head_dim_attention_flash_amd/csrc/fwd_prefill.hpp",
+                  "head_dim_attention_flash_amd/csrc/fwd_vt.hpp",
+                  "head_dim_attention_flash_amd/csrc/fwd_vt.hip",
                   "head_dim_attention_flash_amd/csrc/ffpa_common.hpp")
 COPY_BYTES = 1 << 30  # the calibration copy moves 1 GiB in and 1 GiB out
 
@@ -254,6 +256,7 @@ def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
                      "traffic": measured_traffic(f"{name}:{accum}")},
         "kernel_ms": {"mean": round(mean_ms, 4), "median": round(per[len(per) // 2], 4),
                       "min": round(per[0], 4)},
+        "timed_call": "fwd_vt_kernel (V transposed into the workspace) + the attention kernel",
     }
     if with_cpu:
         line["cpu_baseline"] = cpu_baseline(w, inp, cpu_heads)
@@ -266,7 +269,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="self")
     ap.add_argument("--accum", default="f32", choices=["f32", "f16"])
     ap.add_argument("--cpu-heads", type=int, default=2,
