@@ -39,11 +39,22 @@ KERNEL_SOURCES = ("head_dim_attention_flash_amd/csrc/fwd_prefill.hpp",
 COPY_BYTES = 1 << 30  # the calibration copy moves 1 GiB in and 1 GiB out
 
 
-def kernel_source_hash() -> str:
+CSRC = "head_dim_attention_flash_amd/csrc/"
+# sources each family of recorded counters was taken on
+COUNTER_SOURCES = {
+    "fwd": KERNEL_SOURCES,
+    "wide": KERNEL_SOURCES + (CSRC + "fwd_wide.hpp",),
+    "bwd": (CSRC + "bwd.hpp", CSRC + "ffpa_common.hpp"),
+    "decode": (CSRC + "decode.hpp", CSRC + "ffpa_common.hpp"),
+}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -60,6 +71,21 @@ def measured_traffic(key: str):
     if not rec or rec.get("source_sha") != kernel_source_hash():
         return None
     return int(rec["hbm_bytes"])
+
+
+def recorded_counters(key: str):
+    """rocprofv3 counter values recorded in profiles/counters.json for `key`
+    (MFMA utilisation, HBM bytes), or None if missing or taken on other sources."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    family = rec.get("family") if rec else None
+    if not rec or family not in COUNTER_SOURCES or \
+            rec.get("source_sha") != kernel_source_hash(COUNTER_SOURCES[family]):
+        return None
+    return {k: v for k, v in rec.items() if k not in ("family", "source_sha", "command")}
 
 
 def counted_flops(B, Hq, Nq, Nkv, D, causal=False, backward=False) -> float:
@@ -182,7 +208,8 @@ def run_backward(ffpa, W, name, steps, warmup):
             "value": round(tflops, 2), "unit": "TFLOPS (5 GEMMs counted)",
             "ms_per_call": round(mean_ms, 4), "kernels": "prep + dK/dV + dQ",
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4)}}
+                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4)},
+            "rocprof": recorded_counters(name)}
 
 
 def decode_bytes(w) -> int:
@@ -221,7 +248,8 @@ def run_decode(ffpa, W, steps, warmup):
             "kernels": "split-KV + combine",
             "tflops": round(counted_flops(w.B, w.Hq, 1, w.Nkv, w.D) / (mean_ms * 1e-3) / 1e12, 3),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)},
+            "rocprof": recorded_counters("decode")}
 
 
 def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
@@ -257,6 +285,7 @@ def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
         "kernel_ms": {"mean": round(mean_ms, 4), "median": round(per[len(per) // 2], 4),
                       "min": round(per[0], 4)},
         "timed_call": "fwd_vt_kernel (V transposed into the workspace) + the attention kernel",
+        "rocprof": recorded_counters(f"{name}:{accum}"),
     }
     if with_cpu:
         line["cpu_baseline"] = cpu_baseline(w, inp, cpu_heads)
