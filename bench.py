@@ -331,8 +331,10 @@ def main(argv=None) -> int:
             for acc in ("f32", "f16"):
                 line = run_one(ffpa, W, n, acc, args.steps, args.warmup, False, 0)
                 print(json.dumps(line), flush=True)
+        for n in ("bwd", "bwd_causal", "bwd_d1024", "bwd_d1024_causal"):
+            print(json.dumps(run_backward(ffpa, W, n, max(3, args.steps // 2), 2)), flush=True)
         return 0
-    if args.workload in ("bwd", "bwd_causal"):
+    if args.workload.startswith("bwd"):
         print(json.dumps(run_backward(ffpa, W, args.workload, args.steps, args.warmup)), flush=True)
         return 0
     if args.workload == "decode":

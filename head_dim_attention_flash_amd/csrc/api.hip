@@ -105,6 +105,14 @@ BwdLauncher bwd_launcher(int D, int bf16) {
     FFPA_CASE(384)
     FFPA_CASE(448)
     FFPA_CASE(512)
+    FFPA_CASE(576)
+    FFPA_CASE(640)
+    FFPA_CASE(704)
+    FFPA_CASE(768)
+    FFPA_CASE(832)
+    FFPA_CASE(896)
+    FFPA_CASE(960)
+    FFPA_CASE(1024)
 #undef FFPA_CASE
     default:
       return nullptr;
@@ -278,7 +286,7 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   if (!(scale == scale)) return fail(FFPA_ERR_INVALID_ARG, "scale is NaN");
   BwdLauncher launch = bwd_launcher(D, dtype == FFPA_BF16);
   if (launch == nullptr)
-    return fail(FFPA_ERR_UNSUPPORTED, "the backward is built for D = 64, 128, ..., 512");
+    return fail(FFPA_ERR_UNSUPPORTED, "the backward is built for D = 64, 128, ..., 1024");
 
   ffpa::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
@@ -292,8 +300,9 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = scale * ffpa::kLog2e;
-  const int64_t wg_dkdv = (int64_t)B * Hkv * ((Nkv + 63) / 64);
-  const int64_t wg_dq = (int64_t)B * Hq * ((Nq + 63) / 64);
+  const int rows = ffpa::bwd_rows_per_wg(D);  // keys per dK/dV workgroup, queries per dQ one
+  const int64_t wg_dkdv = (int64_t)B * Hkv * ((Nkv + rows - 1) / rows);
+  const int64_t wg_dq = (int64_t)B * Hq * ((Nq + rows - 1) / rows);
   if (wg_dkdv >= (int64_t(1) << 31) || wg_dq >= (int64_t(1) << 31) ||
       (int64_t)B * Hq * nq_pad / 4 >= (int64_t(1) << 31))
     return fail(FFPA_ERR_UNSUPPORTED, "grid too large");

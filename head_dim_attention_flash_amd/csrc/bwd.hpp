@@ -1,5 +1,5 @@
 // Backward attention kernels (head dimensions that are multiples of 64, up to
-// 512): dQ, dK and dV of O = softmax(scale * Q K^T + mask) V, given dO and
+// 1024): dQ, dK and dV of O = softmax(scale * Q K^T + mask) V, given dO and
 // the forward's per-row logsumexp.
 //
 // The gradients are those of the "naive_math" definition (section 3 of the
@@ -32,6 +32,14 @@
 // 512-byte halves hold the two halves of D, and granule g (8 elements) of a
 // half is stored at g ^ swz4(row), which keeps both the 16-byte row reads
 // and the transposed 8-byte reads conflict-free.
+//
+// Above D = 512 (BwdShape): the same waves split D in four parts instead of
+// two (D is padded with zero columns to a multiple of 128, so a part is a
+// whole number of 32-column blocks, at most 256), a workgroup covers one row
+// block of 32, the partial sums are reduced over four waves, and the staged
+// rows take 2 KiB (four 512-byte part slots). Two such tiles fill 128 KiB,
+// so they are single-buffered: the next tile is copied once every wave is
+// done with the current one.
 #pragma once
 
 #include "ffpa_common.hpp"
@@ -62,12 +70,37 @@ struct BwdArgs {
 };
 
 constexpr int kBwdRows = 32;                       // rows per staged tile
-constexpr int kBwdRowBytes = 1024;                 // LDS row pitch
-constexpr int kBwdHalfBytes = 512;                 // one half of D
-constexpr int kBwdTile = kBwdRows * kBwdRowBytes;  // 32 KiB
+constexpr int kBwdPartBytes = 512;                 // LDS slot of one part of a row
 constexpr int kBwdXchg = 8 * 1024;                 // per wave: partial S and dP tiles, fp32
-constexpr int kBwdLds = 4 * kBwdTile + 4 * kBwdXchg;  // 160 KiB
+constexpr int kBwdLds = 160 * 1024;                // tiles (128 KiB) + swap area (32 KiB)
 constexpr int kBwdPad = 64;                        // workspace row padding
+
+// Zero that the compiler cannot see through: an MFMA operand register that
+// holds zero padding then stays a register (a visible constant would be
+// rematerialised by VALU writes right before each MFMA, inside its hazard
+// window).
+__device__ inline u32x4 opaque_zero4() {
+  uint32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return u32x4{z, z, z, z};
+}
+
+// How a head dimension is split over the 4 waves of a workgroup.
+template <int D>
+struct BwdShape {
+  static constexpr int NP = D > 512 ? 4 : 2;                        // parts of D
+  static constexpr int DP = NP == 2 ? D : (D + 127) / 128 * 128;    // D padded with zero columns
+  static constexpr int DW = DP / NP;                                // columns per part
+  static constexpr int ROWB = NP * kBwdPartBytes;                   // LDS bytes per staged row
+  static constexpr int TILE = kBwdRows * ROWB;                      // bytes per staged tile
+  static constexpr int NB = NP == 2 ? 2 : 1;                        // buffers per staged tensor
+  static constexpr int RB = 4 / NP;                                 // row blocks of 32 per workgroup
+  static constexpr int ROWS = kBwdRows * RB;                        // keys (dK/dV) or queries (dQ) per workgroup
+  static_assert(DW % 32 == 0 && DW <= 256, "a part is whole 32-column blocks, at most 256");
+  static_assert(4 * NB * TILE / 2 + 4 * kBwdXchg <= kBwdLds, "LDS budget");
+};
+// rows per workgroup of the two main kernels (host side: grid sizes)
+inline int bwd_rows_per_wg(int D) { return D > 512 ? kBwdRows : 2 * kBwdRows; }
 
 // ---------------------------------------------------------------------------
 // Shared pieces of the two main kernels.
@@ -79,21 +112,28 @@ constexpr int kBwdPad = 64;                        // workspace row padding
 // (t % 32) ^ swz4(row) of that half. The whole offset sits in the range-
 // checked per-lane offset: rows past the end and granules past D/2 read as
 // zeros (the latter without memory traffic).
+// Copy instruction n fills 1 KiB: row n / S, part slots 2 (n % S) and
+// 2 (n % S) + 1 (S = ROWB / 1 KiB); lane t writes slot t % 32 of part
+// 2 (n % S) + t / 32. Columns at or past D (zero padding) are never loaded.
 template <int D>
 __device__ inline void bwd_copy_row(__amdgpu_buffer_rsrc_t rs, FFPA_LDS char* dst, int row0,
                                     int wave, int lane, int r) {
-  constexpr int SG = D / 16;  // granules per half
-  const int u = lane & 31, half = lane >> 5;
+  using S = BwdShape<D>;
+  constexpr int SUB = S::ROWB / 1024;
+  const int u = lane & 31;
   const int n = wave + 4 * r;
-  const int gl = u ^ swz4(n);
-  const uint32_t lanepart = gl < SG ? (uint32_t)(half * SG + gl) << 4 : 0x80000000u;
-  dma16(rs, lanepart + (uint32_t)(row0 + n) * (D * 2), dst + n * kBwdRowBytes);
+  const int row = n / SUB, part = 2 * (n % SUB) + (lane >> 5);
+  const int gl = u ^ swz4(row);
+  const int col = part * S::DW + 8 * gl;
+  const bool ok = gl < S::DW / 8 && (S::DP == D || col < D);
+  const uint32_t lanepart = ok ? (uint32_t)col << 1 : 0x80000000u;
+  dma16(rs, lanepart + (uint32_t)(row0 + row) * (D * 2), dst + n * 1024);
 }
 template <int D>
 __device__ inline void bwd_copy_tile(__amdgpu_buffer_rsrc_t rs, FFPA_LDS char* dst, int row0,
                                      int wave, int lane) {
 #pragma unroll
-  for (int r = 0; r < kBwdRows / 4; ++r) bwd_copy_row<D>(rs, dst, row0, wave, lane, r);
+  for (int r = 0; r < kBwdRows * BwdShape<D>::ROWB / 1024 / 4; ++r) bwd_copy_row<D>(rs, dst, row0, wave, lane, r);
 }
 
 // The 16 copies of a wave for the next pair of tiles (8 rows of each),
@@ -111,12 +151,13 @@ __device__ inline void bwd_copy_spread(__amdgpu_buffer_rsrc_t ra, FFPA_LDS char*
 }
 
 // 16-byte row reads (MFMA A operand, m = row): lane l reads row l % 32,
-// granule 2 st + l / 32 of half `hf`, st = 8 a + c. Per-lane bases for c.
+// granule 2 st + l / 32 of part `hf`, st = 8 a + c. Per-lane bases for c.
+template <int ROWB>
 __device__ inline void bwd_row_bases(int ln, int hf, uint32_t* ax) {
   const int r = ln & 31, h = ln >> 5, x = swz4(r);
 #pragma unroll
   for (int c = 0; c < 8; ++c)
-    ax[c] = (uint32_t)(r * kBwdRowBytes + hf * kBwdHalfBytes + (((2 * c + h) ^ x) << 4));
+    ax[c] = (uint32_t)(r * ROWB + hf * kBwdPartBytes + (((2 * c + h) ^ x) << 4));
 }
 __device__ inline uint32_t bwd_row_addr(const uint32_t* ax, int st) { return ax[st & 7] + 256 * (st >> 3); }
 
@@ -125,6 +166,7 @@ __device__ inline uint32_t bwd_row_addr(const uint32_t* ax, int st) { return ax[
 // 16 t2 + 8 (e / 4) + 4 (l / 32) + e % 4, e = 0..7 (two ds_read_b64_tr_b16).
 // That row order matches the C layout of a 32x32 MFMA result whose m index
 // is the row, so a P or dS tile feeds the B operand straight from registers.
+template <int ROWB>
 __device__ inline void bwd_tr_bases(int ln, int hf, uint32_t* tx) {
   const int G = ln >> 4, gi = ln & 15;
   const int vrow = 4 * (G >> 1) + (gi >> 2);
@@ -134,18 +176,22 @@ __device__ inline void bwd_tr_bases(int ln, int hf, uint32_t* tx) {
     const int row = vrow + 8 * r8, x = swz4(row);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      tx[4 * r8 + e] = (uint32_t)(row * kBwdRowBytes + hf * kBwdHalfBytes + (((4 * e + y) ^ x) << 4) +
+      tx[4 * r8 + e] = (uint32_t)(row * ROWB + hf * kBwdPartBytes + (((4 * e + y) ^ x) << 4) +
                                   (gi & 1) * 8);
   }
 }
+template <int ROWB>
 __device__ inline u32x4 bwd_tr_read(const FFPA_LDS char* tile, const uint32_t* tx, int db, int t2) {
-  const uint32_t off = 256 * (db >> 2) + 16 * t2 * kBwdRowBytes;
+  const uint32_t off = 256 * (db >> 2) + 16 * t2 * ROWB;
   return join8(lds_read_tr(tile + tx[db & 3] + off), lds_read_tr(tile + tx[4 + (db & 3)] + off));
 }
 
-// Swap partial products with the partner wave (same rows, other half of D)
-// and add its part: afterwards s and p hold the full contractions. Contains
-// a workgroup barrier (every wave calls it).
+// Swap partial products with the waves holding the other parts of D for the
+// same rows and add them up: afterwards s and p hold the full contractions.
+// Every wave of a row block forms the same sum in the same order (part 0
+// first), so all of them hold identical values. Contains a workgroup barrier
+// (every wave calls it).
+template <int NP>
 __device__ inline void bwd_exchange(FFPA_LDS char* xbase, int wave, int lane, f32x16& s, f32x16& p) {
   FFPA_LDS f32x4* mine = (FFPA_LDS f32x4*)(xbase + wave * kBwdXchg) + lane;
 #pragma unroll
@@ -155,14 +201,34 @@ __device__ inline void bwd_exchange(FFPA_LDS char* xbase, int wave, int lane, f3
   }
   wait_lgkm0();
   barrier();
-  const FFPA_LDS f32x4* other = (const FFPA_LDS f32x4*)(xbase + (wave ^ 1) * kBwdXchg) + lane;
+  if constexpr (NP == 2) {
+    // a + b is the same in either order
+    const FFPA_LDS f32x4* other = (const FFPA_LDS f32x4*)(xbase + (wave ^ 1) * kBwdXchg) + lane;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f32x4 x = other[64 * j], y = other[64 * (4 + j)];
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 x = other[64 * j], y = other[64 * (4 + j)];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s[4 * j + e] += x[e];
-      p[4 * j + e] += y[e];
+      for (int e = 0; e < 4; ++e) {
+        s[4 * j + e] += x[e];
+        p[4 * j + e] += y[e];
+      }
+    }
+  } else {
+    // every part read back from LDS, the own one included, and summed in
+    // place in part order
+    const int first = wave - wave % NP;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const FFPA_LDS f32x4* src = (const FFPA_LDS f32x4*)(xbase + (first + q) * kBwdXchg) + lane;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 x = src[64 * j], y = src[64 * (4 + j)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[4 * j + e] = q == 0 ? x[e] : s[4 * j + e] + x[e];
+          p[4 * j + e] = q == 0 ? y[e] : p[4 * j + e] + y[e];
+        }
+      }
     }
   }
 }
@@ -222,17 +288,20 @@ __device__ inline void bwd_stage_rows(FFPA_LDS char* st, const f32x16* acc, floa
     }
 }
 
-// Store `rows` (<= 32) staged rows to dst (row pitch D elements), 16 bytes
-// per lane and instruction.
+// Store `rows` (<= 32) staged rows of part `hf` to dst (row pitch D
+// elements, dst at the part's first column), 16 bytes per lane and
+// instruction; columns at or past D (zero padding) are not stored.
 template <int D, class T>
-__device__ inline void bwd_store_rows(T* dst, const FFPA_LDS char* st, int rows, int lane) {
-  constexpr int SG = D / 16;
+__device__ inline void bwd_store_rows(T* dst, const FFPA_LDS char* st, int rows, int hf, int lane) {
+  using S = BwdShape<D>;
+  constexpr int SG = S::DW / 8;  // granules per staged row
+  const int gmax = S::DP == D ? SG : min(SG, (D - hf * S::DW) / 8);
 #pragma unroll
   for (int it = 0; it < SG / 2; ++it) {
     const int c = it * 64 + lane;
     const int r = c / SG, g = c % SG;
     const u32x4 x = *(const FFPA_LDS u32x4*)(st + r * 512 + ((g ^ (r & 15)) << 4));
-    if (r < rows) *(u32x4*)(dst + (size_t)r * D + 8 * g) = x;
+    if (r < rows && g < gmax) *(u32x4*)(dst + (size_t)r * D + 8 * g) = x;
   }
 }
 
@@ -284,12 +353,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 template <int D, bool BF16, bool ROWMASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
-  static_assert(D % 64 == 0 && D <= 512, "D must be a multiple of 64, at most 512");
+  static_assert(D % 64 == 0 && D <= 1024, "D must be a multiple of 64, at most 1024");
   using E = Elem<BF16>;
   using T = typename E::scalar;
   using V8 = typename E::vec8;
-  constexpr int DW = D / 2, NS = DW / 16, NDB = DW / 32;
-  constexpr int QB = 0, OB = 2 * kBwdTile, XB = 4 * kBwdTile;
+  using Sh = BwdShape<D>;
+  constexpr int DW = Sh::DW, NS = DW / 16, NDB = DW / 32;
+  constexpr int QB = 0, OB = Sh::NB * Sh::TILE, XB = 2 * Sh::NB * Sh::TILE;
   constexpr int NT = 2 * NDB;                   // phase-2 steps per accumulator set
   constexpr int kTAhead = NT < 4 ? NT : 4;      // transposed-read lookahead
 
@@ -297,26 +367,35 @@ void bwd_dkdv_kernel(BwdArgs a) {
   FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kb = wave >> 1, hf = wave & 1;
+  const int kb = wave / Sh::NP, hf = wave % Sh::NP;
 
-  const int n_kt = (a.Nkv + 63) / 64;
+  const int n_kt = (a.Nkv + Sh::ROWS - 1) / Sh::ROWS;
   const int t = xcd_logical(blockIdx.x, a.wg_dkdv);
   const int kt = t % n_kt, bhk = t / n_kt;
   const int hk = bhk % a.Hkv, b = bhk / a.Hkv;
   const int g = a.Hq / a.Hkv;
-  const int kw = kt * 64 + 32 * kb;
+  const int kw = kt * Sh::ROWS + 32 * kb;
 
-  // K and V of the wave's keys, its half of D: B operands (k = d, n = key)
+  // K and V of the wave's keys, its part of D: B operands (k = d, n = key);
+  // padding columns (at or past D) are zeros
   u32x4 kf[NS], vf[NS];
   {
     const int key = min(kw + (lane & 31), a.Nkv - 1);  // keys past the end: never stored
-    const size_t off = ((size_t)(b * a.Hkv + hk) * a.Nkv + key) * D + hf * DW + 8 * (lane >> 5);
+    const int col0 = hf * DW + 8 * (lane >> 5);
+    const size_t off = ((size_t)(b * a.Hkv + hk) * a.Nkv + key) * D + col0;
     const u32x4* kp = (const u32x4*)((const T*)a.k + off);
     const u32x4* vp = (const u32x4*)((const T*)a.v + off);
+    const u32x4 z = opaque_zero4();
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      kf[st] = kp[2 * st];
-      vf[st] = vp[2 * st];
+      const bool in = Sh::DP == D || col0 + 16 * st < D;
+      kf[st] = in ? kp[2 * st] : z;
+      vf[st] = in ? vp[2 * st] : z;
+    }
+    if constexpr (Sh::DP != D) {
+      // settle the operands in AGPRs once (not copied in before every MFMA)
+#pragma unroll
+      for (int st = 0; st < NS; ++st) asm volatile("" : "+a"(kf[st]), "+a"(vf[st]));
     }
   }
   wait_vmcnt0_visible();
@@ -329,7 +408,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   const int n_qt = (a.Nq + kBwdRows - 1) / kBwdRows;
-  const int qt0 = a.causal ? min(kt * 2, n_qt) : 0;  // earlier query tiles see none of these keys
+  const int qt0 = a.causal ? min(kt * Sh::ROWS / kBwdRows, n_qt) : 0;  // earlier query tiles see none of these keys
   const int per_head = n_qt - qt0;
   const int n_it = g * per_head;
   const uint32_t q_bytes = (uint32_t)a.Nq * D * 2;
@@ -338,11 +417,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int hh = hk * g + it / per_head;
     const int qt = qt0 + it % per_head;
     const size_t hoff = (size_t)(b * a.Hq + hh) * a.Nq * D * 2;
-    const int s = it & 1;
+    const int s = it % Sh::NB;
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    bwd_copy_tile<D>(make_rsrc((const char*)a.q + hoff, q_bytes), smem + QB + s * kBwdTile, qt * kBwdRows, wave, ln);
-    bwd_copy_tile<D>(make_rsrc((const char*)a.dout + hoff, q_bytes), smem + OB + s * kBwdTile, qt * kBwdRows, wave, ln);
+    bwd_copy_tile<D>(make_rsrc((const char*)a.q + hoff, q_bytes), smem + QB + s * Sh::TILE, qt * kBwdRows, wave, ln);
+    bwd_copy_tile<D>(make_rsrc((const char*)a.dout + hoff, q_bytes), smem + OB + s * Sh::TILE, qt * kBwdRows, wave, ln);
   };
 
   f32x16 dv[NDB], dk[NDB];
@@ -376,9 +455,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
     const int hh = hk * g + it / per_head;
     const int qt = qt0 + it % per_head;
-    const int s = it & 1;
-    const FFPA_LDS char* qtile = smem + QB + s * kBwdTile;
-    const FFPA_LDS char* otile = smem + OB + s * kBwdTile;
+    const int s = it % Sh::NB;
+    const FFPA_LDS char* qtile = smem + QB + s * Sh::TILE;
+    const FFPA_LDS char* otile = smem + OB + s * Sh::TILE;
     int lj = lane;
     asm volatile("" : "+v"(lj));
     const int hij = lj >> 5;
@@ -412,17 +491,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
       const size_t hoff = (size_t)(b * a.Hq + hn) * a.Nq * D * 2;
       const __amdgpu_buffer_rsrc_t Qn = make_rsrc((const char*)a.q + hoff, q_bytes);
       const __amdgpu_buffer_rsrc_t On = make_rsrc((const char*)a.dout + hoff, q_bytes);
-      FFPA_LDS char* qd = smem + QB + (s ^ 1) * kBwdTile;
-      FFPA_LDS char* od = smem + OB + (s ^ 1) * kBwdTile;
+      FFPA_LDS char* qd = smem + QB + (s ^ 1) * Sh::TILE;
+      FFPA_LDS char* od = smem + OB + (s ^ 1) * Sh::TILE;
       int lc = lane;
       asm volatile("" : "+v"(lc));
       uint32_t ax[8];
-      bwd_row_bases(lj, hf, ax);
+      bwd_row_bases<Sh::ROWB>(lj, hf, ax);
       bwd_partials<BF16, NS>(qtile, otile, ax, kf, vf, sacc, pacc, [&](int st) {
-        if (has_next) bwd_copy_spread<D>(Qn, qd, On, od, qn * kBwdRows, wave, lc, st, NS > 1 ? NS / 2 : 1);
+        // double-buffered: the next tile's copies go out here
+        if (Sh::NB == 2 && has_next)
+          bwd_copy_spread<D>(Qn, qd, On, od, qn * kBwdRows, wave, lc, st, NS > 1 ? NS / 2 : 1);
       });
     }
-    bwd_exchange(smem + XB, wave, lj, sacc, pacc);
+    bwd_exchange<Sh::NP>(smem + XB, wave, lj, sacc, pacc);
 
     // P and dS; register i holds query 8 (i / 4) + 4 hi + i % 4 of the tile
     float pv[16], dsv[16];
@@ -477,21 +558,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
       {
         int lv = lane;
         asm volatile("" : "+v"(lv));
-        bwd_tr_bases(lv, hf, tx);
+        bwd_tr_bases<Sh::ROWB>(lv, hf, tx);
       }
       u32x4 fo[kTAhead], fq[kTAhead];
 #pragma unroll
       for (int st = 0; st < kTAhead; ++st) {
-        fo[st] = bwd_tr_read(otile, tx, st % NDB, st / NDB);
-        fq[st] = bwd_tr_read(qtile, tx, st % NDB, st / NDB);
+        fo[st] = bwd_tr_read<Sh::ROWB>(otile, tx, st % NDB, st / NDB);
+        fq[st] = bwd_tr_read<Sh::ROWB>(qtile, tx, st % NDB, st / NDB);
       }
 #pragma unroll
       for (int st = 0; st < NT; ++st) {
         const int db = st % NDB, t2 = st / NDB;
         const u32x4 x = fo[st % kTAhead], y = fq[st % kTAhead];
         if (st + kTAhead < NT) {
-          fo[st % kTAhead] = bwd_tr_read(otile, tx, (st + kTAhead) % NDB, (st + kTAhead) / NDB);
-          fq[st % kTAhead] = bwd_tr_read(qtile, tx, (st + kTAhead) % NDB, (st + kTAhead) / NDB);
+          fo[st % kTAhead] = bwd_tr_read<Sh::ROWB>(otile, tx, (st + kTAhead) % NDB, (st + kTAhead) / NDB);
+          fq[st % kTAhead] = bwd_tr_read<Sh::ROWB>(qtile, tx, (st + kTAhead) % NDB, (st + kTAhead) / NDB);
         }
         const u32x4 pb = __builtin_bit_cast(u32x4, pf[t2]), sb = __builtin_bit_cast(u32x4, sf[t2]);
         if (st == 0) mfma32_asm<BF16, false, true, false, true>(dv[db], x, pb);
@@ -500,6 +581,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
         // on the loop's exit or back edge right after it
         if (st == NT - 1) mfma32_asm<BF16, false, false, false, false, true>(dk[db], y, sb);
         else mfma32_asm<BF16, false, false>(dk[db], y, sb);
+      }
+    }
+    if constexpr (Sh::NB == 1) {
+      // single buffer: the next tile is copied once every wave is done with this one
+      if (it + 1 < n_it) {
+        wait_lgkm0();
+        barrier();
+        issue(it + 1);
       }
     }
   }
@@ -523,8 +612,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   {
     const size_t row0 = ((size_t)(b * a.Hkv + hk) * a.Nkv + kw) * D + hf * DW;
     const int rows = min(kBwdRows, a.Nkv - kw);
-    bwd_store_rows<D>((T*)a.dv + row0, stg, rows, lane);
-    bwd_store_rows<D>((T*)a.dk + row0, stg + 16384, rows, lane);
+    bwd_store_rows<D>((T*)a.dv + row0, stg, rows, hf, lane);
+    bwd_store_rows<D>((T*)a.dk + row0, stg + 16384, rows, hf, lane);
   }
 }
 
@@ -538,12 +627,13 @@ void bwd_dkdv_kernel(BwdArgs a) {
 template <int D, bool BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(BwdArgs a) {
-  static_assert(D % 64 == 0 && D <= 512, "D must be a multiple of 64, at most 512");
+  static_assert(D % 64 == 0 && D <= 1024, "D must be a multiple of 64, at most 1024");
   using E = Elem<BF16>;
   using T = typename E::scalar;
   using V8 = typename E::vec8;
-  constexpr int DW = D / 2, NS = DW / 16, NDB = DW / 32;
-  constexpr int KB = 0, VB = 2 * kBwdTile, XB = 4 * kBwdTile;
+  using Sh = BwdShape<D>;
+  constexpr int DW = Sh::DW, NS = DW / 16, NDB = DW / 32;
+  constexpr int KB = 0, VB = Sh::NB * Sh::TILE, XB = 2 * Sh::NB * Sh::TILE;
   constexpr int NT = 2 * NDB;
   constexpr int kTAhead = NT < 6 ? NT : 6;
 
@@ -551,28 +641,37 @@ void bwd_dq_kernel(BwdArgs a) {
   FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int qb = wave >> 1, hf = wave & 1;
+  const int qb = wave / Sh::NP, hf = wave % Sh::NP;
 
-  const int n_qb = (a.Nq + 63) / 64;
+  const int n_qb = (a.Nq + Sh::ROWS - 1) / Sh::ROWS;
   const int t = xcd_logical(blockIdx.x, a.wg_dq);
   int qblk = t % n_qb;
   const int bh = t / n_qb;
   if (a.causal) qblk = n_qb - 1 - qblk;  // longest rows first
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
-  const int qw = qblk * 64 + 32 * qb;
+  const int qw = qblk * Sh::ROWS + 32 * qb;
 
-  // Q and dO of the wave's rows, its half of D: B operands (k = d, n = query)
+  // Q and dO of the wave's rows, its part of D: B operands (k = d, n =
+  // query); padding columns (at or past D) are zeros
   u32x4 qf[NS], of[NS];
   {
     const int qr = min(qw + (lane & 31), a.Nq - 1);  // rows past the end: never stored
-    const size_t off = ((size_t)(b * a.Hq + h) * a.Nq + qr) * D + hf * DW + 8 * (lane >> 5);
+    const int col0 = hf * DW + 8 * (lane >> 5);
+    const size_t off = ((size_t)(b * a.Hq + h) * a.Nq + qr) * D + col0;
     const u32x4* qp = (const u32x4*)((const T*)a.q + off);
     const u32x4* op = (const u32x4*)((const T*)a.dout + off);
+    const u32x4 z = opaque_zero4();
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      qf[st] = qp[2 * st];
-      of[st] = op[2 * st];
+      const bool in = Sh::DP == D || col0 + 16 * st < D;
+      qf[st] = in ? qp[2 * st] : z;
+      of[st] = in ? op[2 * st] : z;
+    }
+    if constexpr (Sh::DP != D) {
+      // settle the operands in AGPRs once (not copied in before every MFMA)
+#pragma unroll
+      for (int st = 0; st < NS; ++st) asm volatile("" : "+a"(qf[st]), "+a"(of[st]));
     }
   }
   // this lane's row: lse2 (+inf past Nq) and delta, from the padded workspace
@@ -582,7 +681,7 @@ void bwd_dq_kernel(BwdArgs a) {
   wait_vmcnt0_visible();
 
   int kv_end = a.Nkv;
-  if (a.causal) kv_end = min(kv_end, min(qblk * 64 + 64, a.Nq));  // keys <= last row of the block
+  if (a.causal) kv_end = min(kv_end, min(qblk * Sh::ROWS + Sh::ROWS, a.Nq));  // keys <= last row of the block
   const int n_kt = (kv_end + kBwdRows - 1) / kBwdRows;
   const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Nkv * D * 2;
   const uint32_t kv_bytes = (uint32_t)a.Nkv * D * 2;
@@ -591,11 +690,11 @@ void bwd_dq_kernel(BwdArgs a) {
   const uint16_t* mk = (const uint16_t*)a.mask;
 
   auto issue = [&](int j) {
-    const int s = j & 1;
+    const int s = j % Sh::NB;
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    bwd_copy_tile<D>(Kr, smem + KB + s * kBwdTile, j * kBwdRows, wave, ln);
-    bwd_copy_tile<D>(Vr, smem + VB + s * kBwdTile, j * kBwdRows, wave, ln);
+    bwd_copy_tile<D>(Kr, smem + KB + s * Sh::TILE, j * kBwdRows, wave, ln);
+    bwd_copy_tile<D>(Vr, smem + VB + s * Sh::TILE, j * kBwdRows, wave, ln);
   };
 
   f32x16 dq[NDB];
@@ -621,9 +720,9 @@ void bwd_dq_kernel(BwdArgs a) {
   for (int j = 0; j < n_kt; ++j) {
 #pragma unroll
     for (int d = 0; d < NDB; ++d) asm volatile("" : "+a"(dq[d]));
-    const int s = j & 1;
-    const FFPA_LDS char* ktile = smem + KB + s * kBwdTile;
-    const FFPA_LDS char* vtile = smem + VB + s * kBwdTile;
+    const int s = j % Sh::NB;
+    const FFPA_LDS char* ktile = smem + KB + s * Sh::TILE;
+    const FFPA_LDS char* vtile = smem + VB + s * Sh::TILE;
     int lj = lane;
     asm volatile("" : "+v"(lj));
     const int hij = lj >> 5;
@@ -652,17 +751,19 @@ void bwd_dq_kernel(BwdArgs a) {
     f32x16 sacc, pacc;
     {
       const bool has_next = j + 1 < n_kt;
-      FFPA_LDS char* kd = smem + KB + (s ^ 1) * kBwdTile;
-      FFPA_LDS char* vd = smem + VB + (s ^ 1) * kBwdTile;
+      FFPA_LDS char* kd = smem + KB + (s ^ 1) * Sh::TILE;
+      FFPA_LDS char* vd = smem + VB + (s ^ 1) * Sh::TILE;
       int lc = lane;
       asm volatile("" : "+v"(lc));
       uint32_t ax[8];
-      bwd_row_bases(lj, hf, ax);
+      bwd_row_bases<Sh::ROWB>(lj, hf, ax);
       bwd_partials<BF16, NS>(ktile, vtile, ax, qf, of, sacc, pacc, [&](int st) {
-        if (has_next) bwd_copy_spread<D>(Kr, kd, Vr, vd, (j + 1) * kBwdRows, wave, lc, st, NS > 1 ? NS / 2 : 1);
+        // double-buffered: the next tile's copies go out here
+        if (Sh::NB == 2 && has_next)
+          bwd_copy_spread<D>(Kr, kd, Vr, vd, (j + 1) * kBwdRows, wave, lc, st, NS > 1 ? NS / 2 : 1);
       });
     }
-    bwd_exchange(smem + XB, wave, lj, sacc, pacc);
+    bwd_exchange<Sh::NP>(smem + XB, wave, lj, sacc, pacc);
 
     float dsv[16];
 #pragma unroll
@@ -689,16 +790,16 @@ void bwd_dq_kernel(BwdArgs a) {
       {
         int lv = lane;
         asm volatile("" : "+v"(lv));
-        bwd_tr_bases(lv, hf, tx);
+        bwd_tr_bases<Sh::ROWB>(lv, hf, tx);
       }
       u32x4 fk[kTAhead];
 #pragma unroll
-      for (int st = 0; st < kTAhead; ++st) fk[st] = bwd_tr_read(ktile, tx, st % NDB, st / NDB);
+      for (int st = 0; st < kTAhead; ++st) fk[st] = bwd_tr_read<Sh::ROWB>(ktile, tx, st % NDB, st / NDB);
 #pragma unroll
       for (int st = 0; st < NT; ++st) {
         const int db = st % NDB, t2 = st / NDB;
         const u32x4 x = fk[st % kTAhead];
-        if (st + kTAhead < NT) fk[st % kTAhead] = bwd_tr_read(ktile, tx, (st + kTAhead) % NDB, (st + kTAhead) / NDB);
+        if (st + kTAhead < NT) fk[st % kTAhead] = bwd_tr_read<Sh::ROWB>(ktile, tx, (st + kTAhead) % NDB, (st + kTAhead) / NDB);
         const u32x4 sb = __builtin_bit_cast(u32x4, sf[t2]);
         // first MFMA pads for the VALU writes of dS; the last for accumulator
         // copies the compiler may place on the loop's exit or back edge
@@ -706,6 +807,14 @@ void bwd_dq_kernel(BwdArgs a) {
         else if (st == 0) mfma32_asm<BF16, false, true, false, true>(dq[db], x, sb);
         else if (st == NT - 1) mfma32_asm<BF16, false, true, false, false, true>(dq[db], x, sb);
         else mfma32_asm<BF16, false, true>(dq[db], x, sb);
+      }
+    }
+    if constexpr (Sh::NB == 1) {
+      // single buffer: the next tile is copied once every wave is done with this one
+      if (j + 1 < n_kt) {
+        wait_lgkm0();
+        barrier();
+        issue(j + 1);
       }
     }
   }
@@ -720,7 +829,7 @@ void bwd_dq_kernel(BwdArgs a) {
   bwd_stage_rows<BF16, NDB>(stg, dq, a.scale, lane);
   {
     const size_t row0 = ((size_t)(b * a.Hq + h) * a.Nq + qw) * D + hf * DW;
-    bwd_store_rows<D>((T*)a.dq + row0, stg, min(kBwdRows, a.Nq - qw), lane);
+    bwd_store_rows<D>((T*)a.dq + row0, stg, min(kBwdRows, a.Nq - qw), hf, lane);
   }
 }
 

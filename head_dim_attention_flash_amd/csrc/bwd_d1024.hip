@@ -1,0 +1,7 @@
+// Instances of the backward kernels for head dimension 1024.
+#include "bwd.hpp"
+
+namespace ffpa {
+template hipError_t launch_bwd<1024, false>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd<1024, true>(const BwdArgs&, hipStream_t);
+}  // namespace ffpa

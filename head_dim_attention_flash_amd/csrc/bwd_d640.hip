@@ -1,0 +1,7 @@
+// Instances of the backward kernels for head dimension 640.
+#include "bwd.hpp"
+
+namespace ffpa {
+template hipError_t launch_bwd<640, false>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd<640, true>(const BwdArgs&, hipStream_t);
+}  // namespace ffpa

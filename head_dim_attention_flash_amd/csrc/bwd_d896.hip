@@ -1,0 +1,7 @@
+// Instances of the backward kernels for head dimension 896.
+#include "bwd.hpp"
+
+namespace ffpa {
+template hipError_t launch_bwd<896, false>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd<896, true>(const BwdArgs&, hipStream_t);
+}  // namespace ffpa

@@ -98,7 +98,7 @@ def test_forward_validation(kw, code):
     (dict(workspace=0, workspace_bytes=1 << 20), ffpa.ERR_WORKSPACE),
     (dict(workspace=P, workspace_bytes=16), ffpa.ERR_WORKSPACE),
     (dict(workspace=P, workspace_bytes=1 << 30, mask=P, mask_rows=5), ffpa.ERR_INVALID_ARG),
-    (dict(workspace=P, workspace_bytes=1 << 30, D=576), ffpa.ERR_UNSUPPORTED),
+    (dict(workspace=P, workspace_bytes=1 << 30, D=544), ffpa.ERR_UNSUPPORTED),
     (dict(workspace=P, workspace_bytes=1 << 30, D=96), ffpa.ERR_UNSUPPORTED),
 ])
 def test_backward_validation(kw, code):

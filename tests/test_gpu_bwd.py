@@ -125,6 +125,11 @@ CASES = [
     (1, 1, 1, 256, 256, 448),
     (1, 2, 2, 64, 300, 192),     # Nkv > Nq
     (1, 2, 2, 70, 33, 384),      # Nq > Nkv
+    # above 512: D in four parts per workgroup, zero-padded to a multiple of 128
+    (1, 2, 2, 100, 80, 576),     # padded to 640, ragged
+    (1, 2, 1, 70, 130, 1024),    # GQA g = 2
+    (1, 1, 1, 64, 64, 640),
+    (1, 2, 2, 40, 90, 960),      # padded to 1024
 ]
 
 

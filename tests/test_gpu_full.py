@@ -78,7 +78,7 @@ def test_decode(lib):
 UNIT = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
-@pytest.mark.parametrize("name", ["bwd", "bwd_causal"])
+@pytest.mark.parametrize("name", ["bwd", "bwd_causal", "bwd_d1024", "bwd_d1024_causal"])
 def test_full_size_backward(lib, name):
     """The backward at its benchmark size after this library's own forward (the
     path bench.py times); whole heads of dQ, dK, dV against the oracle.
@@ -97,7 +97,8 @@ def test_full_size_backward(lib, name):
     o, lse = lib.attention(q, k, v, causal=w.causal, scale=w.scale, return_lse=True)
     dq, dk, dv = lib.attention_backward(do, q, k, v, o, lse, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
-    for b, h in [(0, 0), (w.B - 1, w.Hq - 1)]:
+    heads = [(0, 0), (w.B - 1, w.Hq - 1)] if w.D <= 512 else [(w.B - 1, w.Hq - 1)]
+    for b, h in heads:
         sl = lambda t: t[b:b + 1, h:h + 1]
         rq, rk, rv = attn_bwd(sl(q), sl(k), sl(v), sl(do), w.scale, causal=w.causal)
         for nm, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):

@@ -81,6 +81,10 @@ WORKLOADS = {
     "bwd": _w("bwd", 4, 1, 32, 32, 8192, 8192, 512, dtype="bf16", backward=True),
     "bwd_causal": _w("bwd_causal", 4, 1, 32, 32, 8192, 8192, 512, dtype="bf16", causal=True,
                      backward=True),
+    # the backward at the top of the head-dimension range
+    "bwd_d1024": _w("bwd_d1024", 4, 1, 32, 32, 8192, 8192, 1024, dtype="bf16", backward=True),
+    "bwd_d1024_causal": _w("bwd_d1024_causal", 4, 1, 32, 32, 8192, 8192, 1024, dtype="bf16",
+                           causal=True, backward=True),
 }
 for _d in (320, 448, 512, 576, 768, 1024):
     for _acc in ("f32", "f16"):
