@@ -128,8 +128,9 @@ size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
  * FFPA_ACC_F32. workspace: at least ffpa_attn_bwd_workspace_size(...) bytes,
  * 16-byte aligned (holds delta_i = sum_d dO_id O_id and lse_i log2(e) per
  * query row, rows padded to a multiple of 64). Three kernels are enqueued:
- * the delta pass, then dK/dV, then dQ. Built for D a multiple of 64 up to 512,
- * with either mask shape; other valid shapes return FFPA_ERR_UNSUPPORTED.
+ * the delta pass, then dK/dV, then dQ. Built for D a multiple of 64 up to
+ * 1024, with either mask shape; other valid shapes (D not a multiple of 64)
+ * return FFPA_ERR_UNSUPPORTED.
  * The gradients are those of sum(dout * O) ("FFPA Attention Benchmark",
  * "More Benchmark": the backward counted as 5 GEMMs).
  */
