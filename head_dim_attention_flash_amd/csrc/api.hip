@@ -27,18 +27,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 using FwdLauncher = hipError_t (*)(const ffpa::FwdArgs&, size_t, hipStream_t);
 
-template <int D>
+template <int D, bool VT>
 FwdLauncher pick_fwd(int bf16, int acc16) {
-  if (bf16) return acc16 ? ffpa::launch_fwd_prefill<D, true, true> : ffpa::launch_fwd_prefill<D, true, false>;
-  return acc16 ? ffpa::launch_fwd_prefill<D, false, true> : ffpa::launch_fwd_prefill<D, false, false>;
+  if (bf16) return acc16 ? ffpa::launch_fwd_prefill<D, true, true, VT> : ffpa::launch_fwd_prefill<D, true, false, VT>;
+  return acc16 ? ffpa::launch_fwd_prefill<D, false, true, VT> : ffpa::launch_fwd_prefill<D, false, false, VT>;
 }
 
-FwdLauncher fwd_launcher(int D, int bf16, int acc16, size_t* ring_bytes) {
+FwdLauncher fwd_launcher(int D, int bf16, int acc16, bool vt, size_t* ring_bytes) {
   switch (D) {
-#define FFPA_CASE(DD)                             \
-  case DD:                                        \
-    *ring_bytes = ffpa::fwd_ring_bytes<DD>();     \
-    return pick_fwd<DD>(bf16, acc16);
+#define FFPA_CASE(DD)                                                  \
+  case DD:                                                             \
+    *ring_bytes = ffpa::fwd_ring_bytes<DD>();                          \
+    return vt ? pick_fwd<DD, true>(bf16, acc16) : pick_fwd<DD, false>(bf16, acc16);
     FFPA_CASE(64)
     FFPA_CASE(128)
     FFPA_CASE(192)
@@ -161,8 +161,9 @@ size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
     const size_t s = (size_t)ffpa::dec_splits(B, Hq, Nkv);
     return (size_t)B * Hq * s * ((size_t)D + 1) * sizeof(float);
   }
-  // the transposed copy of V the attention kernels read
-  if (D % 64 == 0) return ffpa::fwd_vt_bytes(B, Hkv, Nkv, D);
+  // the transposed copy of V the attention kernels read (always above
+  // D = 512; up to 512 when the problem repays the pass)
+  if (D % 64 == 0 && (D > 512 || ffpa::fwd_use_vt(Hq, Hkv, Nq))) return ffpa::fwd_vt_bytes(B, Hkv, Nkv, D);
   return 0;
 }
 
@@ -229,7 +230,8 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   }
 
   size_t ring = 0;
-  FwdLauncher launch = fwd_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, &ring);
+  const bool vt = ffpa::fwd_use_vt(Hq, Hkv, Nq);
+  FwdLauncher launch = fwd_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, vt, &ring);
   if (launch == nullptr) return fail(FFPA_ERR_UNSUPPORTED, "this head dimension is not built yet");
   size_t lds = ring + ffpa::kFwdFlagBytes;
   // a key bias is staged in LDS when it fits beside the tiles; otherwise the
@@ -252,7 +254,7 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   a.total_wg = (int)total;
   a.vt = workspace;
   a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
-  hipError_t e = ffpa::launch_fwd_vt(v, workspace, B * Hkv, Nkv, D, (hipStream_t)stream);
+  hipError_t e = vt ? ffpa::launch_fwd_vt(v, workspace, B * Hkv, Nkv, D, (hipStream_t)stream) : hipSuccess;
   if (e == hipSuccess) e = launch(a, lds, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return FFPA_OK;

@@ -2,8 +2,8 @@
 #include "fwd_prefill.hpp"
 
 namespace ffpa {
-template hipError_t launch_fwd_prefill<64, false, false>(const FwdArgs&, size_t, hipStream_t);
-template hipError_t launch_fwd_prefill<64, true, false>(const FwdArgs&, size_t, hipStream_t);
-template hipError_t launch_fwd_prefill<64, false, true>(const FwdArgs&, size_t, hipStream_t);
-template hipError_t launch_fwd_prefill<64, true, true>(const FwdArgs&, size_t, hipStream_t);
+#define FFPA_INST(BF, ACC, VT) template hipError_t launch_fwd_prefill<64, BF, ACC, VT>(const FwdArgs&, size_t, hipStream_t);
+FFPA_INST(false, false, true) FFPA_INST(true, false, true) FFPA_INST(false, true, true) FFPA_INST(true, true, true)
+FFPA_INST(false, false, false) FFPA_INST(true, false, false) FFPA_INST(false, true, false) FFPA_INST(true, true, false)
+#undef FFPA_INST
 }  // namespace ffpa

@@ -87,7 +87,7 @@ constexpr float fwd_tau() {
 }
 constexpr float kRescaleTau = 8.0f;  // fp16-accumulator path: move m_ref past this
 
-template <int D, bool BF16, bool ACC16>
+template <int D, bool BF16, bool ACC16, bool VT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fwd_prefill_kernel(FwdArgs a) {
   static_assert(D % 64 == 0 && D <= 512, "D must be a multiple of 64, at most 512");
@@ -128,9 +128,11 @@ void fwd_prefill_kernel(FwdArgs a) {
   const size_t kv_off = ((size_t)(b * a.Hkv + hk) * a.Nkv) * D * 2;
   const uint32_t kv_bytes = (uint32_t)a.Nkv * D * 2;  // rows >= Nkv read as zeros
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc((const char*)a.k + kv_off, kv_bytes);
+  // V: its transposed copy (VT), or V itself, staged like K
   const uint32_t vt_row = (uint32_t)a.nkv_pad * 2;  // bytes per row of V^T
   const __amdgpu_buffer_rsrc_t Vr =
-      make_rsrc((const char*)a.vt + (size_t)(b * a.Hkv + hk) * D * vt_row, (uint32_t)D * vt_row);
+      VT ? make_rsrc((const char*)a.vt + (size_t)(b * a.Hkv + hk) * D * vt_row, (uint32_t)D * vt_row)
+         : make_rsrc((const char*)a.v + kv_off, kv_bytes);
 
   // ---- key range
   int kv_end = a.Nkv;
@@ -213,6 +215,15 @@ void fwd_prefill_kernel(FwdArgs a) {
         dma16(Vr, voff, smem + VB + n * 1024);
       }
   };
+  // the V copies of either layout: per-lane setup, then the copies of step st
+  auto v_lane_offsets = [&](int ln, uint32_t* lo) {
+    if constexpr (VT) vt_lane_offsets(ln, lo);
+    else lo[0] = (uint32_t)ln;
+  };
+  auto v_copy_spread = [&](int tile, int st, int span, const uint32_t* lo) {
+    if constexpr (VT) issue_spread_v(tile, st, span, lo);
+    else issue_spread(Vr, VB, tile, st, span, (int)lo[0]);
+  };
 
   // ---- LDS read addresses: per-lane bases (recomputed at the start of each
   // phase, so they are live only there) plus compile-time offsets < 64 KiB.
@@ -231,13 +242,38 @@ void fwd_prefill_kernel(FwdArgs a) {
   // 8 positions hold the keys the lane's P operand pairs with (vt_key).
   // Sixteen consecutive lanes read sixteen consecutive rows: two rows share a
   // 256-byte bank window, and (row / 2) % 8 spreads the pairs over it.
+  //
+  // Without the transposed copy (!VT), V is staged like K and V^T fragments
+  // come from transposed reads: group G = lane/16, i = lane%16 reads row
+  // 32 kb + 16 t2 + 8 r8 + 4 (G/2) + i/4 at columns 32 db + 16 (G%2) + 4 (i%4),
+  // i.e. logical granule 4 db + y with y = 2 (G%2) + (i%4)/2, at half the LDS
+  // byte rate of 16-byte reads. The host takes this layout when the problem
+  // has too few queries per key to repay the transposition pass.
   auto v_bases = [&](int ln, uint32_t* vx) {
-    const int r = ln & 31, h = ln >> 5, x = (r >> 1) & 7;
+    if constexpr (VT) {
+      const int r = ln & 31, h = ln >> 5, x = (r >> 1) & 7;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) vx[p] = (uint32_t)(VB + r * 128 + (((2 * p + h) ^ x) << 4));
+      for (int p = 0; p < 4; ++p) vx[p] = (uint32_t)(VB + r * 128 + (((2 * p + h) ^ x) << 4));
+    } else {
+      const int G = ln >> 4, gi = ln & 15;
+      const int vrow = 4 * (G >> 1) + (gi >> 2);
+      const int y = 2 * (G & 1) + ((gi & 3) >> 1);
+#pragma unroll
+      for (int r8 = 0; r8 < 2; ++r8) {
+        const int row = vrow + 8 * r8, x = swz4(row);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vx[4 * r8 + e] = (uint32_t)(VB + row * ROWB + (((4 * e + y) ^ x) << 4) + (gi & 1) * 8);
+      }
+    }
   };
-  auto v_addr = [&](const uint32_t* vx, int db, int kb, int t2) -> uint32_t {
-    return vx[2 * kb + t2] + 4096 * db;
+  auto v_read = [&](const uint32_t* vx, int db, int kb, int t2) -> u32x4 {
+    if constexpr (VT) {
+      return lds_read16(smem + vx[2 * kb + t2] + 4096 * db);
+    } else {
+      const uint32_t off = 256 * (db >> 2) + (32 * kb + 16 * t2) * ROWB;
+      return join8(lds_read_tr(smem + vx[db & 3] + off), lds_read_tr(smem + vx[4 + (db & 3)] + off));
+    }
   };
 
   // ---- accumulators
@@ -395,11 +431,11 @@ void fwd_prefill_kernel(FwdArgs a) {
         {
           int lnc = lane;
           asm volatile("" : "+v"(lnc));
-          vt_lane_offsets(lnc, vlo);
+          v_lane_offsets(lnc, vlo);
         }
 #pragma unroll
         for (int c = 0; c < 2 * NS; ++c) {
-          issue_spread_v(j, c, NS, vlo);
+          v_copy_spread(j, c, NS, vlo);
           const u32x4 a0 = kf[c % kKA];
           if (c + kKA < 2 * NS) kf[c % kKA] = kread(c + kKA);
           const int st = c % NS;
@@ -426,7 +462,7 @@ void fwd_prefill_kernel(FwdArgs a) {
       auto v_phase = [&](auto fresh_tag) {
         constexpr bool FRESH = decltype(fresh_tag)::value;
         constexpr int NSV = 4 * NDB;
-        uint32_t vx[4];
+        uint32_t vx[8];
         {
           int lv = lane;
           asm volatile("" : "+v"(lv));
@@ -434,7 +470,7 @@ void fwd_prefill_kernel(FwdArgs a) {
         }
         auto vread = [&](int st) {
           const int p = st / NDB, db = st % NDB;
-          return lds_read16(smem + v_addr(vx, db, p >> 1, p & 1));
+          return v_read(vx, db, p >> 1, p & 1);
         };
         u32x4 vf[kVAhead];
 #pragma unroll
@@ -541,11 +577,11 @@ void fwd_prefill_kernel(FwdArgs a) {
       {
         int lnc = lane;
         asm volatile("" : "+v"(lnc));
-        vt_lane_offsets(lnc, vlo);
+        v_lane_offsets(lnc, vlo);
       }
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        issue_spread_v(j, st, NS > 1 ? NS / 2 : 1, vlo);
+        v_copy_spread(j, st, NS > 1 ? NS / 2 : 1, vlo);
         const u32x4 a0 = kf[st % kKAhead][0], a1 = kf[st % kKAhead][1];
         if (st + kKAhead < NS) {
           kf[st % kKAhead][0] = kread(st + kKAhead, 0);
@@ -725,7 +761,7 @@ void fwd_prefill_kernel(FwdArgs a) {
         kb = p >> 1;
         t2 = p & 1;
       };
-      uint32_t vx[4];
+      uint32_t vx[8];
       {
         int lv = lane;
         asm volatile("" : "+v"(lv));
@@ -734,7 +770,7 @@ void fwd_prefill_kernel(FwdArgs a) {
       auto vread = [&](int st) {
         int db, kb, t2;
         step(st, db, kb, t2);
-        return lds_read16(smem + v_addr(vx, db, kb, t2));
+        return v_read(vx, db, kb, t2);
       };
       u32x4 vf[kVAhead];
 #pragma unroll
@@ -914,9 +950,9 @@ void fwd_prefill_kernel(FwdArgs a) {
 
 // Host launcher. lds_bytes = tile buffers + key-bias bytes (the caller checks
 // <= 160 KiB).
-template <int D, bool BF16, bool ACC16>
+template <int D, bool BF16, bool ACC16, bool VT>
 hipError_t launch_fwd_prefill(const FwdArgs& a, size_t lds_bytes, hipStream_t stream) {
-  auto kern = fwd_prefill_kernel<D, BF16, ACC16>;
+  auto kern = fwd_prefill_kernel<D, BF16, ACC16, VT>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;

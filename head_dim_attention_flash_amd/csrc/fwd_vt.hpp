@@ -30,6 +30,17 @@ __host__ __device__ inline int fwd_nkv_pad(int nkv) { return (nkv + 63) / 64 * 6
 // key stored at position pos of a V^T row (an involution)
 __host__ __device__ inline int vt_key(int pos) { return (pos & ~12) | ((pos & 4) << 1) | ((pos & 8) >> 1); }
 
+// Whether the prefill kernel (D <= 512) stages V from its transposed copy.
+// The pass moves 2 |V| bytes (~0.09 ms per 256 MiB of V at HBM speed); the
+// attention kernel then runs ~5 % faster. Per kv head that pays off once a
+// head's queries are many compared with its keys: the pass costs about
+// 180 / Nq of the kernel time per query head sharing the kv head, so it is
+// taken when Nq * Hq >= 3072 * Hkv (self-attention at 8K: yes; cross-attention
+// with 1K queries over 8K keys: no). Above D = 512 the copy is always used.
+__host__ __device__ inline bool fwd_use_vt(int Hq, int Hkv, int Nq) {
+  return (long long)Nq * Hq >= 3072LL * Hkv;
+}
+
 // bytes of the transposed copy of V for these sizes
 inline size_t fwd_vt_bytes(int B, int Hkv, int Nkv, int D) {
   return (size_t)B * Hkv * D * (size_t)fwd_nkv_pad(Nkv) * 2;

@@ -100,10 +100,12 @@ typedef enum {
  *               bytes, 16-byte aligned (NULL allowed when that size is 0).
  *               Nq = 1 takes the split-KV decode path, which keeps
  *               per-key-range partial outputs (fp32 o and log-sum-exp) there.
- *               Nq > 1 first writes a transposed copy of V there ([B, Hkv,
- *               D, Nkv rounded up to 64], dtype, zero past Nkv: the size of
- *               V) and the attention kernel reads its V operand from it. The
- *               call owns the workspace until the work it enqueued has
+ *               For Nq > 1 with D > 512, or D <= 512 and Nq * Hq >=
+ *               3072 * Hkv (many queries per key), the call first writes a
+ *               transposed copy of V there ([B, Hkv, D, Nkv rounded up to
+ *               64], dtype, zero past Nkv: the size of V) and the attention
+ *               kernel reads its V operand from it; otherwise it needs none.
+ *               The call owns the workspace until the work it enqueued has
  *               finished.
  *   stream    : hipStream_t to enqueue on.
  * Built today: every D (multiple of 32, <= 1024) for Nq = 1; for Nq > 1, D a

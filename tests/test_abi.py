@@ -78,10 +78,10 @@ def bwd(**kw):
     (dict(k=P + 8), ffpa.ERR_INVALID_ARG),
     (dict(lse=P + 4), ffpa.ERR_INVALID_ARG),
     (dict(scale=float("nan")), ffpa.ERR_INVALID_ARG),
-    # Nq > 1, D <= 512: the transposed copy of V lives in the workspace
-    (dict(workspace=0, workspace_bytes=0), ffpa.ERR_WORKSPACE),
-    (dict(workspace=P, workspace_bytes=64 * 64 * 2 * 2 - 1), ffpa.ERR_WORKSPACE),
-    (dict(workspace=P + 8, workspace_bytes=1 << 20), ffpa.ERR_INVALID_ARG),
+    # many queries per key: the transposed copy of V lives in the workspace
+    (dict(Nq=4096, workspace=0, workspace_bytes=0), ffpa.ERR_WORKSPACE),
+    (dict(Nq=4096, workspace=P, workspace_bytes=64 * 64 * 2 * 2 - 1), ffpa.ERR_WORKSPACE),
+    (dict(Nq=4096, workspace=P + 8, workspace_bytes=1 << 20), ffpa.ERR_INVALID_ARG),
 ])
 def test_forward_validation(kw, code):
     assert fwd(**kw) == code
@@ -107,10 +107,13 @@ def test_backward_validation(kw, code):
 
 
 def test_forward_workspace_holds_transposed_v():
-    # [B, Hkv, D, Nkv rounded up to 64] in the 16-bit input type
-    assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 8, 8, 64, 0) == 2 * 64 * 64 * 2
+    # [B, Hkv, D, Nkv rounded up to 64] in the 16-bit input type, when the
+    # problem has Nq * Hq >= 3072 * Hkv (up to D = 512) or D > 512
+    assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 3072, 8, 64, 0) == 2 * 64 * 64 * 2
+    assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 3071, 8, 64, 0) == 0
     assert ffpa.ffpa_attn_fwd_workspace_size(2, 32, 8, 8192, 8191, 512, 1) == 2 * 8 * 512 * 8192 * 2
-    assert ffpa.ffpa_attn_fwd_workspace_size(1, 4, 1, 100, 65, 320, 0) == 320 * 128 * 2
+    assert ffpa.ffpa_attn_fwd_workspace_size(1, 4, 1, 800, 65, 320, 0) == 320 * 128 * 2
+    assert ffpa.ffpa_attn_fwd_workspace_size(1, 32, 32, 1024, 8192, 512, 0) == 0  # cross-attention
     assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 100, 300, 1024, 0) == 2 * 1024 * 320 * 2
 
 

@@ -108,7 +108,19 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("shape", CASES, ids=lambda s: "x".join(map(str, s)))
+# Up to D = 512 the library stages V from a transposed copy when a head's
+# queries are many compared with its keys (Nq * Hq >= 3072 * Hkv), and reads V
+# with transposed LDS reads otherwise: the shapes above take the second layout
+# (and D > 512 always the copy), these the first.
+CASES_VT = [
+    (1, 1, 1, 3100, 100, 512),   # ragged queries and keys
+    (1, 4, 1, 800, 200, 320),    # GQA g = 4
+    (1, 1, 1, 3072, 64, 64),     # exactly at the threshold
+    (1, 2, 2, 3200, 150, 448),
+]
+
+
+@pytest.mark.parametrize("shape", CASES + CASES_VT, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("accum", ["f32", "f16"])
 @pytest.mark.parametrize("variant", ["plain", "causal", "mask", "causal_mask", "qmask", "causal_qmask"])
