@@ -15,17 +15,19 @@
 // so that each lane's accumulators all belong to one query row (l % 32): the
 // online-softmax rescale is a per-lane scalar and P goes from the S
 // accumulators into the B operand of the second MFMA without leaving
-// registers. V is staged from its transposed copy (fwd_vt.hpp), so both
-// operands read from LDS are plain 16-byte reads.
+// registers. With VT, V is staged from its transposed copy (fwd_vt.hpp), so
+// both operands read from LDS are plain 16-byte reads; without it (problems
+// with few queries per key, where the copy would not pay) V is staged like K
+// and its fragments come from transposed 8-byte reads.
 //
 // Staging: one LDS buffer holds the K tile (64 keys x D, one 1 KiB row per
-// key), another the V^T tile (D rows x 64 keys, 128 bytes per row), both
-// swizzled. The copy of V(j) is spread over the K(j) phase and the copy of
-// K(j+1) over the V(j) phase, so each copy has one phase of MFMA work to
-// land, and a tile costs two workgroup barriers. Copies go straight from
-// global memory to LDS (buffer_load ... lds); the K buffer resource's range
-// ends at row Nkv, so rows past the end read as zeros, and V^T is zero past
-// Nkv by construction.
+// key), another the V^T tile (D rows x 64 keys, 128 bytes per row) or the V
+// tile (like K), all swizzled. The copy of V(j) is spread over the K(j) phase
+// and the copy of K(j+1) over the V(j) phase, so each copy has one phase of
+// MFMA work to land, and a tile costs two workgroup barriers. Copies go
+// straight from global memory to LDS (buffer_load ... lds); the K and V
+// buffer resources' ranges end at row Nkv, so rows past the end read as
+// zeros, and V^T is zero past Nkv by construction.
 #pragma once
 
 #include "ffpa_common.hpp"
