@@ -51,12 +51,18 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
+    """Hash of the code in `sources`, comments and blank lines left out (a
+    record taken on a kernel stays valid through edits of its comments)."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for rel in sources:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
