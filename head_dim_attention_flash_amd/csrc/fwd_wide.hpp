@@ -18,8 +18,12 @@
 //   3. runs the online softmax (restart-based reference max, as in the
 //      prefill kernel with fp32 accumulation);
 //   4. accumulates O^T_half += V_half^T P^T.
-// Tiles are 32 keys. A staged K tile holds both halves, each half row in its
-// own 1 KiB LDS row (granules XOR-swizzled by swz4(row)): 64 KiB. V is staged
+// Tiles are 32 keys. A staged K tile holds both halves, each as 32 dense rows
+// of W / 8 granules (wide_k_pos: granules swizzled inside groups of 16, 8 or
+// 4 by the row, so that sixteen lanes reading sixteen rows hit distinct
+// banks whatever the pitch), at most 64 KiB. Dense rows let every copy
+// instruction carry a full 1 KiB: the copy path costs per instruction, not
+// per byte, and bounds this kernel. V is staged
 // from its transposed copy (fwd_vt.hpp): D rows of 32 keys, 64 bytes each,
 // also 64 KiB, read with plain 16-byte reads. As in the prefill kernel the
 // copy of V(j) is issued when the K(j) phase starts and the copy of K(j+1)
@@ -35,8 +39,17 @@
 namespace ffpa {
 
 constexpr int kWideBc = 32;                      // keys per tile
-constexpr int kWideHalfTile = kWideBc * 1024;    // one half of a staged tile
-constexpr int kWideTile = 2 * kWideHalfTile;     // 64 KiB
+constexpr int kWideTile = 64 * 1024;             // LDS buffer of one staged K or V^T tile
+
+// Stored position of logical granule g of row r of a dense K half-tile with
+// P granules per row: XOR swizzle inside aligned groups of 16, 8 or 4 granules
+// by P % 16 (an involution, so it also maps positions back to granules).
+__device__ inline int wide_k_pos(int P, int r, int g) {
+  const int m = P % 16;
+  const int G = m == 0 ? 16 : (m == 8 ? 8 : 4);
+  const int x = m == 0 ? swz4(r) : (m == 8 ? (r >> 1) & 7 : (r >> 2) & 3);
+  return (g & ~(G - 1)) | ((g & (G - 1)) ^ x);
+}
 constexpr int kWideXchg = 4096;                  // per wave: a 32 x 32 fp32 tile
 constexpr int kWideLds = 2 * kWideTile + 4 * kWideXchg + 16;
 
@@ -48,6 +61,7 @@ void fwd_wide_kernel(FwdArgs a) {
   using V8 = typename E::vec8;
   constexpr int W = D / 2;              // elements per half
   constexpr int SG = W / 8;             // granules per half row (36 .. 64)
+  constexpr int HALF = kWideBc * SG * 16;  // bytes of one dense K half-tile
   constexpr int NS = W / 16;            // k-steps of the partial product
   constexpr int NDB = W / 32;           // output d-blocks of the half
   constexpr int KB = 0, VB = kWideTile, XB = 2 * kWideTile, FB = 2 * kWideTile + 4 * kWideXchg;
@@ -102,19 +116,22 @@ void fwd_wide_kernel(FwdArgs a) {
 
   // ---- copies: instruction n of a tile (n = wave + 4 r, r < 16) fills half
   // n / 32 of key row n % 32; lane i writes slot i = logical granule i ^ swz4(row)
+  // copy instruction n (n = wave + 4 r, r < SG / 4) fills 1 KiB of a dense
+  // half-tile: half n / (SG / 2), slots 64 (n % (SG / 2)) + lane, slot s
+  // holding granule wide_k_pos(row, s % SG) of row s / SG
   auto k_copy = [&](int tile, int r, int ln) {
     const int n = wave + 4 * r;
-    const int row = n & 31, half = n >> 5;
-    const int lg = ln ^ swz4(row);
-    const uint32_t lanepart = lg < SG ? (uint32_t)(half * SG + lg) << 4 : 0x80000000u;
-    const uint32_t voff = lanepart + (uint32_t)(tile * kWideBc + row) * (D * 2);
-    dma16(Kr, voff, smem + KB + half * kWideHalfTile + row * 1024);
+    const int half = n / (SG / 2), nn = n % (SG / 2);
+    const int sl = 64 * nn + ln;
+    const int row = sl / SG, g = wide_k_pos(SG, row, sl % SG);
+    const uint32_t voff = (uint32_t)((half * W + 8 * g) * 2) + (uint32_t)(tile * kWideBc + row) * (D * 2);
+    dma16(Kr, voff, smem + KB + half * HALF + nn * 1024);
   };
   auto issue_k_tile = [&](int tile) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) k_copy(tile, r, ln);
+    for (int r = 0; r < SG / 4; ++r) k_copy(tile, r, ln);
   };
 
   // ---- copy of one V^T tile (D rows of 32 keys = 64 bytes). Copy
@@ -133,14 +150,14 @@ void fwd_wide_kernel(FwdArgs a) {
   // phase before the one that reads them (copy r at step r span / count):
   // issued in one burst, they held the wave's MFMAs back while the copy
   // instructions queued.
-  constexpr int NKC = 16, NVC = D / 64;  // copies per wave per tile: K, V^T
+  constexpr int NKC = SG / 4, NVC = D / 64;  // copies per wave per tile: K, V^T
 
   // K fragment (A of S^T) for k-step st = 8 a + c: key row l % 32, granule 2 st + l / 32
   auto k_bases = [&](int ln, uint32_t* kx) {
-    const int r = ln & 31, hh = ln >> 5, x = swz4(r);
+    const int r = ln & 31, hh = ln >> 5;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      kx[c] = (uint32_t)(KB + hf * kWideHalfTile + r * 1024 + (((2 * c + hh) ^ x) << 4));
+      kx[c] = (uint32_t)(KB + hf * HALF + r * (SG * 16) + (wide_k_pos(SG, r, 2 * c + hh) << 4));
   };
   // V^T fragment (A of O^T_half) for d-block db and the 16-key step t2: row
   // W hf + 32 db + l % 32 of the V^T tile, logical granule 2 t2 + l / 32,
