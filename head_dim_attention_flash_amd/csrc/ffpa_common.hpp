@@ -196,6 +196,19 @@ __device__ inline typename Elem<BF16>::vec8 pack8(float a0, float a1, float a2, 
 // ---------------------------------------------------------------------------
 __device__ __host__ inline int swz4(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
 
+// Stored position of logical granule g of row r in a staged tile of dense
+// rows, P granules (16 bytes) each, P a multiple of 4: XOR swizzle inside
+// aligned groups of 16, 8 or 4 granules chosen by P % 16, so that sixteen
+// lanes reading the same logical granule of sixteen consecutive rows hit
+// distinct banks whatever the pitch. An involution: it also maps a stored
+// position back to its logical granule.
+__device__ __host__ inline int dense_pos(int P, int r, int g) {
+  const int m = P % 16;
+  const int G = m == 0 ? 16 : (m == 8 ? 8 : 4);
+  const int x = m == 0 ? swz4(r) : (m == 8 ? (r >> 1) & 7 : (r >> 2) & 3);
+  return (g & ~(G - 1)) | ((g & (G - 1)) ^ x);
+}
+
 // Stored granule of logical granule g of row `row` (and, the map being an
 // involution within each group, the logical granule of stored granule g).
 template <int GPR>

@@ -20,8 +20,8 @@
 // with few queries per key, where the copy would not pay) V is staged like K
 // and its fragments come from transposed 8-byte reads.
 //
-// Staging: one LDS buffer holds the K tile (64 keys x D, one 1 KiB row per
-// key), another the V^T tile (D rows x 64 keys, 128 bytes per row) or the V
+// Staging: one LDS buffer holds the K tile (64 keys x D, dense rows of D x 2
+// bytes), another the V^T tile (D rows x 64 keys, 128 bytes per row) or the V
 // tile (like K), all swizzled. The copy of V(j) is spread over the K(j) phase
 // and the copy of K(j+1) over the V(j) phase, so each copy has one phase of
 // MFMA work to land, and a tile costs two workgroup barriers. Copies go
@@ -98,7 +98,8 @@ void fwd_prefill_kernel(FwdArgs a) {
   constexpr int ROWB = kFwdRowBytes;      // bytes per LDS row (D * 2 used)
   constexpr int GPR = D / 8;              // 16-byte granules of data per row
   constexpr int TILEB = kFwdBc * ROWB;    // bytes per tile buffer
-  constexpr int NDMA = kFwdBc / kFwdWaves;  // K copies per wave per tile (one per row)
+  constexpr int NDMA = kFwdBc / kFwdWaves;  // V copies per wave per tile without VT (one per row)
+  constexpr int NDMAK = GPR / kFwdWaves;     // K copies per wave per tile (dense rows)
   constexpr int NDMAV = D / (8 * kFwdWaves);  // V^T copies per wave per tile (8 rows each)
   constexpr int NDB = D / 32;             // output d-blocks of 32
   constexpr int KB = 0, VB = TILEB;       // buffer offsets
@@ -195,6 +196,33 @@ void fwd_prefill_kernel(FwdArgs a) {
     for (int r = 0; r < NDMA; ++r)
       if ((r * span) / NDMA == st) issue_copy(rs, buf, tile, r, ln);
   };
+  // ---- copy of one K tile as 64 dense rows of GPR granules (dense_pos):
+  // copy instruction n (n = wave + 4 r, r < GPR / 4) fills slots 64 n + lane
+  // of the tile, slot s holding granule dense_pos(GPR, row, s % GPR) of row
+  // s / GPR. Every instruction carries a full 1 KiB, which matters below
+  // D = 512: the copy path costs per instruction, not per byte.
+  auto k_copy = [&](int tile, int r, int ln) {
+    if constexpr (GPR == 64) {
+      issue_copy(Kr, KB, tile, r, ln);  // one row per instruction: the same layout
+    } else {
+      const int n = wave + kFwdWaves * r;
+      const int sl = 64 * n + ln;
+      const int row = sl / GPR, g = dense_pos(GPR, row, sl % GPR);
+      const uint32_t voff = (uint32_t)(g << 4) + (uint32_t)(tile * kFwdBc + row) * (D * 2);
+      dma16(Kr, voff, smem + KB + n * 1024);
+    }
+  };
+  auto issue_k_tile = [&](int tile) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int r = 0; r < NDMAK; ++r) k_copy(tile, r, ln);
+  };
+  auto issue_spread_k = [&](int tile, int st, int span, int ln) {
+#pragma unroll
+    for (int r = 0; r < NDMAK; ++r)
+      if ((r * span) / NDMAK == st) k_copy(tile, r, ln);
+  };
   // ---- copy of one V^T tile (D rows of 64 keys = 128 bytes). Copy
   // instruction n (n = wave + 4 r) fills LDS rows 8 n .. 8 n + 7: lane i
   // writes slot i % 8 of row 8 n + i / 8, which holds the logical granule
@@ -230,14 +258,15 @@ void fwd_prefill_kernel(FwdArgs a) {
   // ---- LDS read addresses: per-lane bases (recomputed at the start of each
   // phase, so they are live only there) plus compile-time offsets < 64 KiB.
   // K fragment (A of S^T) for d-step s = 8 a + c: row 32 kb + l32, logical
-  // granule 16 a + 2 c + hi, stored at 16 a + ((2 c + hi) ^ swz4(row)).
+  // granule 16 a + 2 c + hi, stored at 16 a + dense_pos(row, 2 c + hi) (the
+  // swizzle groups divide 16, and rows 32 apart swizzle alike).
   auto k_bases = [&](int ln, uint32_t* kx) {
-    const int r = ln & 31, h = ln >> 5, x = swz4(r);
+    const int r = ln & 31, h = ln >> 5;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) kx[c] = (uint32_t)(KB + r * ROWB + (((2 * c + h) ^ x) << 4));
+    for (int c = 0; c < 8; ++c) kx[c] = (uint32_t)(KB + r * (GPR * 16) + (dense_pos(GPR, r, 2 * c + h) << 4));
   };
   auto k_addr = [&](const uint32_t* kx, int st, int kb) -> uint32_t {
-    return kx[st & 7] + 256 * (st >> 3) + 32 * kb * ROWB;
+    return kx[st & 7] + 256 * (st >> 3) + 32 * kb * (GPR * 16);
   };
   // V^T fragment (A of O^T) for d-block db and the 16-key step (kb, t2):
   // row 32 db + l32 of the V^T tile, logical granule 4 kb + 2 t2 + hi, whose
@@ -306,7 +335,7 @@ void fwd_prefill_kernel(FwdArgs a) {
     constexpr int NS = D / 16;        // d-steps of one chain
     constexpr int kKA = 6;            // K fragments read ahead
     float mx_prev = -INFINITY;        // the previous tile's row max (log2 domain)
-    issue_tile(Kr, KB, 0);
+    issue_k_tile(0);
     for (int j = 0; j <= n_tiles; ++j) {
       const int j0 = j * kFwdBc;
       int lj = lane;
@@ -329,7 +358,7 @@ void fwd_prefill_kernel(FwdArgs a) {
           m_ref = fmaxf(m_ref, mx_prev);
           l_run = 0.f;
           fresh = true;
-          issue_tile(Kr, KB, 0);
+          issue_k_tile(0);
           j = -1;
           continue;
         }
@@ -483,7 +512,7 @@ void fwd_prefill_kernel(FwdArgs a) {
         for (int st = 0; st < NSV; ++st) {
           // on the last tile this copies rows past the key range (range-checked
           // zeros) or, causal, rows nobody reads: harmless, and branch-free
-          issue_spread(Kr, KB, j + 1, st, NSV / 2, lnc);
+          issue_spread_k(j + 1, st, NSV / 2, lnc);
           const int p = st / NDB, db = st % NDB;
           const int kb = p >> 1, t2 = p & 1;
           const u32x4 vbits = vf[st % kVAhead];
@@ -534,7 +563,7 @@ void fwd_prefill_kernel(FwdArgs a) {
       fresh = false;
     }
   } else {
-  issue_tile(Kr, KB, 0);
+  issue_k_tile(0);
 
   for (int j = 0; j < n_tiles; ++j) {
     const int j0 = j * kFwdBc;
@@ -734,7 +763,7 @@ void fwd_prefill_kernel(FwdArgs a) {
         m_ref = fmaxf(m_ref, mx);
         l_run = 0.f;
         fresh = true;
-        issue_tile(Kr, KB, 0);
+        issue_k_tile(0);
         j = -1;
         continue;
       }
@@ -800,7 +829,7 @@ void fwd_prefill_kernel(FwdArgs a) {
       for (int st = 0; st < NSV; ++st) {
         // on the last tile this copies rows past the key range (range-checked
         // zeros) or, causal, rows nobody reads: harmless, and branch-free
-        issue_spread(Kr, KB, j + 1, st, NSV / 2, lnc);
+        issue_spread_k(j + 1, st, NSV / 2, lnc);
         int db, kb, t2;
         step(st, db, kb, t2);
         const u32x4 vbits = vf[st % kVAhead];

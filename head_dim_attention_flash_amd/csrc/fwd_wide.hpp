@@ -19,7 +19,7 @@
 //      prefill kernel with fp32 accumulation);
 //   4. accumulates O^T_half += V_half^T P^T.
 // Tiles are 32 keys. A staged K tile holds both halves, each as 32 dense rows
-// of W / 8 granules (wide_k_pos: granules swizzled inside groups of 16, 8 or
+// of W / 8 granules (dense_pos: granules swizzled inside groups of 16, 8 or
 // 4 by the row, so that sixteen lanes reading sixteen rows hit distinct
 // banks whatever the pitch), at most 64 KiB. Dense rows let every copy
 // instruction carry a full 1 KiB: the copy path costs per instruction, not
@@ -41,15 +41,6 @@ namespace ffpa {
 constexpr int kWideBc = 32;                      // keys per tile
 constexpr int kWideTile = 64 * 1024;             // LDS buffer of one staged K or V^T tile
 
-// Stored position of logical granule g of row r of a dense K half-tile with
-// P granules per row: XOR swizzle inside aligned groups of 16, 8 or 4 granules
-// by P % 16 (an involution, so it also maps positions back to granules).
-__device__ inline int wide_k_pos(int P, int r, int g) {
-  const int m = P % 16;
-  const int G = m == 0 ? 16 : (m == 8 ? 8 : 4);
-  const int x = m == 0 ? swz4(r) : (m == 8 ? (r >> 1) & 7 : (r >> 2) & 3);
-  return (g & ~(G - 1)) | ((g & (G - 1)) ^ x);
-}
 constexpr int kWideXchg = 4096;                  // per wave: a 32 x 32 fp32 tile
 constexpr int kWideLds = 2 * kWideTile + 4 * kWideXchg + 16;
 
@@ -118,12 +109,12 @@ void fwd_wide_kernel(FwdArgs a) {
   // n / 32 of key row n % 32; lane i writes slot i = logical granule i ^ swz4(row)
   // copy instruction n (n = wave + 4 r, r < SG / 4) fills 1 KiB of a dense
   // half-tile: half n / (SG / 2), slots 64 (n % (SG / 2)) + lane, slot s
-  // holding granule wide_k_pos(row, s % SG) of row s / SG
+  // holding granule dense_pos(row, s % SG) of row s / SG
   auto k_copy = [&](int tile, int r, int ln) {
     const int n = wave + 4 * r;
     const int half = n / (SG / 2), nn = n % (SG / 2);
     const int sl = 64 * nn + ln;
-    const int row = sl / SG, g = wide_k_pos(SG, row, sl % SG);
+    const int row = sl / SG, g = dense_pos(SG, row, sl % SG);
     const uint32_t voff = (uint32_t)((half * W + 8 * g) * 2) + (uint32_t)(tile * kWideBc + row) * (D * 2);
     dma16(Kr, voff, smem + KB + half * HALF + nn * 1024);
   };
@@ -157,7 +148,7 @@ void fwd_wide_kernel(FwdArgs a) {
     const int r = ln & 31, hh = ln >> 5;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      kx[c] = (uint32_t)(KB + hf * HALF + r * (SG * 16) + (wide_k_pos(SG, r, 2 * c + hh) << 4));
+      kx[c] = (uint32_t)(KB + hf * HALF + r * (SG * 16) + (dense_pos(SG, r, 2 * c + hh) << 4));
   };
   // V^T fragment (A of O^T_half) for d-block db and the 16-key step t2: row
   // W hf + 32 db + l % 32 of the V^T tile, logical granule 2 t2 + l / 32,
