@@ -223,7 +223,7 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     a.total_wg = (int)total;
     a.vt = workspace;
     a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
-    hipError_t e = ffpa::launch_fwd_vt(v, workspace, B * Hkv, Nkv, D, (hipStream_t)stream);
+    hipError_t e = ffpa::launch_fwd_vt(v, workspace, B * Hkv, Nkv, D, ffpa::kWideBc, (hipStream_t)stream);
     if (e == hipSuccess) e = launch(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return FFPA_OK;
@@ -254,7 +254,8 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   a.total_wg = (int)total;
   a.vt = workspace;
   a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
-  hipError_t e = vt ? ffpa::launch_fwd_vt(v, workspace, B * Hkv, Nkv, D, (hipStream_t)stream) : hipSuccess;
+  hipError_t e =
+      vt ? ffpa::launch_fwd_vt(v, workspace, B * Hkv, Nkv, D, a.nkv_pad, (hipStream_t)stream) : hipSuccess;
   if (e == hipSuccess) e = launch(a, lds, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return FFPA_OK;

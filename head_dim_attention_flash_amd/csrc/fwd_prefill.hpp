@@ -39,7 +39,8 @@ struct FwdArgs {
   const void* q;
   const void* k;
   const void* v;
-  const void* vt;     // V transposed, [B, Hkv, D, nkv_pad] (fwd_vt.hpp); prefill kernel only
+  const void* vt;     // V transposed (fwd_vt.hpp): [B, Hkv, D, nkv_pad] for the prefill
+                      // kernel, [B, Hkv, nkv_pad / 32, D, 32] for the wide one
   int nkv_pad;        // Nkv rounded up to a multiple of 64
   void* o;
   float* lse;         // may be null
@@ -134,7 +135,7 @@ void fwd_prefill_kernel(FwdArgs a) {
   // V: its transposed copy (VT), or V itself, staged like K
   const uint32_t vt_row = (uint32_t)a.nkv_pad * 2;  // bytes per row of V^T
   const __amdgpu_buffer_rsrc_t Vr =
-      VT ? make_rsrc((const char*)a.vt + (size_t)(b * a.Hkv + hk) * D * vt_row, (uint32_t)D * vt_row)
+      VT ? make_rsrc((const char*)a.vt + (size_t)(b * a.Hkv + hk) * D * a.nkv_pad * 2, (uint32_t)D * a.nkv_pad * 2)
          : make_rsrc((const char*)a.v + kv_off, kv_bytes);
 
   // ---- key range

@@ -6,11 +6,11 @@
 namespace ffpa {
 
 // One workgroup moves a 64-key x 64-column block of one (b, hk) slice through
-// LDS: 16-byte loads along rows of V, 16-byte stores along rows of V^T. Keys
-// at or past Nkv are written as zeros.
+// LDS: 16-byte loads along rows of V, 16-byte stores along the d rows of the
+// V^T blocks. Keys at or past Nkv are written as zeros.
 __global__ __launch_bounds__(256) void fwd_vt_kernel(const uint16_t* __restrict__ v,
                                                      uint16_t* __restrict__ vt, int Nkv,
-                                                     int nkv_pad, int D, int n_ktiles,
+                                                     int nkv_pad, int D, int kb, int n_ktiles,
                                                      int n_dtiles) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];  // 144-byte rows
   const int t = threadIdx.x;
@@ -39,17 +39,19 @@ __global__ __launch_bounds__(256) void fwd_vt_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       y[e] = (uint32_t)tile[vt_key(8 * kg + 2 * e)][d] | ((uint32_t)tile[vt_key(8 * kg + 2 * e + 1)][d] << 16);
-    *(u32x4*)(dst + (size_t)(d0 + d) * nkv_pad + k0 + 8 * kg) = y;
+    const int pos = k0 + 8 * kg;  // 8 positions, inside one block (kb % 8 == 0)
+    *(u32x4*)(dst + (size_t)(pos / kb) * D * kb + (size_t)(d0 + d) * kb + pos % kb) = y;
   }
 }
 
-hipError_t launch_fwd_vt(const void* v, void* vt, int BH, int Nkv, int D, hipStream_t stream) {
+hipError_t launch_fwd_vt(const void* v, void* vt, int BH, int Nkv, int D, int kb, hipStream_t stream) {
   const int nkv_pad = fwd_nkv_pad(Nkv);
+  if (kb <= 0 || kb % 32 != 0 || nkv_pad % kb != 0) return hipErrorInvalidValue;
   const int n_ktiles = nkv_pad / 64, n_dtiles = D / 64;
   const int64_t grid = (int64_t)BH * n_ktiles * n_dtiles;
   if (grid >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fwd_vt_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const uint16_t*)v, (uint16_t*)vt, Nkv, nkv_pad, D, n_ktiles, n_dtiles);
+                     (const uint16_t*)v, (uint16_t*)vt, Nkv, nkv_pad, D, kb, n_ktiles, n_dtiles);
   return hipGetLastError();
 }
 

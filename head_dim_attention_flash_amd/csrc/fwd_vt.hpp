@@ -5,11 +5,15 @@
 // V. Reading those from a row-major V tile in LDS takes transposed 8-byte
 // reads (ds_read_b64_tr_b16), which the LDS serves at half the rate of plain
 // 16-byte reads; the P V phase of every tile was bound by them. This pass
-// writes V once in the transposed layout
-//     vt[b, hk, d, pos]  = v[b, hk, vt_key(pos), d]   for vt_key(pos) < Nkv
-//     vt[b, hk, d, pos]  = 0                          otherwise, pos < nkv_pad
+// writes V once in a transposed layout, in blocks of kb positions:
+//     vt[b, hk, pos / kb, d, pos % kb] = v[b, hk, vt_key(pos), d]  for vt_key(pos) < Nkv
+//     vt[b, hk, pos / kb, d, pos % kb] = 0                         otherwise, pos < nkv_pad
 // (nkv_pad = Nkv rounded up to a multiple of 64), so the forward reads its
-// operand with plain 16-byte reads. vt_key swaps bits 2 and 3 of the
+// operand with plain 16-byte reads. With kb the keys of one kernel tile, a
+// staged tile is one contiguous block of D * kb * 2 bytes: every copy
+// instruction then covers whole 128-byte lines and a tile touches one or two
+// translation pages, where rows of nkv_pad positions would spread a tile over
+// D rows nkv_pad * 2 bytes apart (with 64-byte row pieces at 32-key tiles). vt_key swaps bits 2 and 3 of the
 // position: within each group of 16 keys the order is 0-3, 8-11, 4-7, 12-15.
 // That is the order in which the score accumulators hand P to the B operand
 // of the P V product (lane half h holds keys 4h .. 4h+3 and 8+4h .. 8+4h+3
@@ -47,7 +51,8 @@ inline size_t fwd_vt_bytes(int B, int Hkv, int Nkv, int D) {
 }
 
 // Enqueues the transpose of v [B*Hkv, Nkv, D] (16-bit elements, D a multiple
-// of 64) into vt [B*Hkv, D, nkv_pad].
-hipError_t launch_fwd_vt(const void* v, void* vt, int BH, int Nkv, int D, hipStream_t stream);
+// of 64) into vt [B*Hkv, nkv_pad / kb, D, kb]; kb is a multiple of 32 that
+// divides nkv_pad (kb = nkv_pad: one block, rows of all positions).
+hipError_t launch_fwd_vt(const void* v, void* vt, int BH, int Nkv, int D, int kb, hipStream_t stream);
 
 }  // namespace ffpa

@@ -23,11 +23,19 @@
 // 4 by the row, so that sixteen lanes reading sixteen rows hit distinct
 // banks whatever the pitch), at most 64 KiB. Dense rows let every copy
 // instruction carry a full 1 KiB: the copy path costs per instruction, not
-// per byte, and bounds this kernel. V is staged
-// from its transposed copy (fwd_vt.hpp): D rows of 32 keys, 64 bytes each,
-// also 64 KiB, read with plain 16-byte reads. As in the prefill kernel the
-// copy of V(j) is issued when the K(j) phase starts and the copy of K(j+1)
-// when the V(j) phase starts.
+// per byte. V is staged from its transposed copy (fwd_vt.hpp), written in
+// blocks of 32 keys so that a tile is one contiguous block of D rows of 64
+// bytes (64 KiB at D = 1024): every copy instruction then covers whole
+// 128-byte lines, where rows of all positions gave 64-byte pieces D rows
+// apart (8 % faster at D = 1024). The tile is read with plain 16-byte
+// reads. As in the prefill kernel the copy of V(j) is issued when the K(j)
+// phase starts and the copy of K(j+1) when the V(j) phase starts.
+//
+// What bounds it is the feed from L2: each staged byte serves 64 query rows
+// (the fp32 O of more rows does not fit the register file at D = 1024), so
+// a launch moves twice the prefill kernel's L2-to-LDS bytes per flop, at
+// about the same aggregate rate (8.5-10 TB/s). Overlapping the softmax and the score
+// swap with the MFMAs (a one-tile software pipeline) measured no faster.
 //
 // Accumulation is fp32 (the fp16-accumulator request maps to this kernel too:
 // it is at least as accurate).
@@ -82,9 +90,10 @@ void fwd_wide_kernel(FwdArgs a) {
   const size_t kv_off = ((size_t)(b * a.Hkv + hk) * a.Nkv) * D * 2;
   const uint32_t kv_bytes = (uint32_t)a.Nkv * D * 2;  // rows >= Nkv read as zeros
   const __amdgpu_buffer_rsrc_t Kr = make_rsrc((const char*)a.k + kv_off, kv_bytes);
-  const uint32_t vt_row = (uint32_t)a.nkv_pad * 2;  // bytes per row of V^T
+  // V^T in blocks of one tile: [tile][d][32 keys], D * 64 bytes per tile
+  constexpr uint32_t vt_row = kWideBc * 2;  // bytes per d row of a block
   const __amdgpu_buffer_rsrc_t Vr =
-      make_rsrc((const char*)a.vt + (size_t)(b * a.Hkv + hk) * D * vt_row, (uint32_t)D * vt_row);
+      make_rsrc((const char*)a.vt + (size_t)(b * a.Hkv + hk) * D * a.nkv_pad * 2, (uint32_t)D * a.nkv_pad * 2);
 
   int kv_end = a.Nkv;
   if (a.causal) kv_end = min(kv_end, min(q0 + 64, a.Nq));  // keys <= last row of the block
@@ -135,7 +144,7 @@ void fwd_wide_kernel(FwdArgs a) {
   };
   auto vt_copy = [&](int tile, int r, uint32_t lo) {
     const int n = wave + 4 * r;
-    dma16(Vr, lo + (uint32_t)(16 * n) * vt_row + (uint32_t)tile * (kWideBc * 2), smem + VB + n * 1024);
+    dma16(Vr, lo + (uint32_t)(16 * n) * vt_row + (uint32_t)tile * (D * vt_row), smem + VB + n * 1024);
   };
   // The copies of a tile are spread over the first `span` MFMA steps of the
   // phase before the one that reads them (copy r at step r span / count):

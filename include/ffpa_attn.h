@@ -102,9 +102,11 @@ typedef enum {
  *               per-key-range partial outputs (fp32 o and log-sum-exp) there.
  *               For Nq > 1 with D > 512, or D <= 512 and Nq * Hq >=
  *               3072 * Hkv (many queries per key), the call first writes a
- *               transposed copy of V there ([B, Hkv, D, Nkv rounded up to
- *               64], dtype, zero past Nkv: the size of V) and the attention
- *               kernel reads its V operand from it; otherwise it needs none.
+ *               transposed copy of V there, dtype, zero past Nkv, the size
+ *               of V with the keys padded to P = Nkv rounded up to 64:
+ *               [B, Hkv, D, P] for D <= 512, and in blocks of 32 keys
+ *               [B, Hkv, P / 32, D, 32] for D > 512. The attention kernel
+ *               reads its V operand from it; otherwise the call needs none.
  *               The call owns the workspace until the work it enqueued has
  *               finished.
  *   stream    : hipStream_t to enqueue on.

@@ -107,7 +107,7 @@ def test_backward_validation(kw, code):
 
 
 def test_forward_workspace_holds_transposed_v():
-    # [B, Hkv, D, Nkv rounded up to 64] in the 16-bit input type, when the
+    # V^T of the size of V with Nkv rounded up to 64, in the 16-bit input type, when the
     # problem has Nq * Hq >= 3072 * Hkv (up to D = 512) or D > 512
     assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 3072, 8, 64, 0) == 2 * 64 * 64 * 2
     assert ffpa.ffpa_attn_fwd_workspace_size(1, 2, 2, 3071, 8, 64, 0) == 0

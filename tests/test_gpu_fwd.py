@@ -105,6 +105,9 @@ CASES = [
     (2, 4, 2, 130, 77, 768),    # GQA, Nq > Nkv
     (1, 2, 2, 64, 300, 1024),
     (1, 3, 1, 100, 100, 640),   # GQA g = 3
+    (1, 2, 2, 70, 20, 832),     # D above 512, one partial key tile
+    (1, 2, 1, 90, 1, 896),      # D above 512, a single key
+    (1, 2, 2, 33, 64, 960),     # D above 512, two whole key tiles
 ]
 
 
