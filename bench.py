@@ -44,7 +44,7 @@ CSRC = "head_dim_attention_flash_amd/csrc/"
 COUNTER_SOURCES = {
     "fwd": KERNEL_SOURCES,
     "wide": KERNEL_SOURCES + (CSRC + "fwd_wide.hpp",),
-    "bwd": (CSRC + "bwd.hpp", CSRC + "ffpa_common.hpp"),
+    "bwd": (CSRC + "bwd.hpp", CSRC + "ffpa_common.hpp", CSRC + "fwd_vt.hpp", CSRC + "fwd_vt.hip"),
     "decode": (CSRC + "decode.hpp", CSRC + "ffpa_common.hpp"),
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
@@ -212,7 +212,8 @@ def run_backward(ffpa, W, name, steps, warmup):
     torch.cuda.empty_cache()
     return {"workload": f"{name}: B={w.B} H={w.Hq} N={w.Nq} D={w.D} {w.dtype} causal={w.causal}",
             "value": round(tflops, 2), "unit": "TFLOPS (5 GEMMs counted)",
-            "ms_per_call": round(mean_ms, 4), "kernels": "prep + dK/dV + dQ",
+            "ms_per_call": round(mean_ms, 4),
+            "kernels": "prep + K^T copy + dK/dV (stores dS) + dQ from dS",
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(tflops / peak, 4)},
             "rocprof": recorded_counters(name)}

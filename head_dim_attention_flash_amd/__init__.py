@@ -19,7 +19,8 @@ from typing import Optional
 
 __all__ = [
     "load", "FFPAError", "ffpa_attn_fwd", "ffpa_attn_bwd", "ffpa_attn_fwd_workspace_size",
-    "ffpa_attn_bwd_workspace_size", "ffpa_last_error", "ffpa_version", "attention",
+    "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min", "ffpa_last_error",
+    "ffpa_version", "attention",
     "attention_backward", "F16", "BF16", "ACC_F32", "ACC_F16", "LIB_PATH", "EXPORTED",
 ]
 
@@ -34,7 +35,8 @@ _STATUS = {1: "FFPA_ERR_INVALID_ARG", 2: "FFPA_ERR_UNSUPPORTED", 3: "FFPA_ERR_WO
 
 # Symbols declared in include/ffpa_attn.h.
 EXPORTED = ("ffpa_attn_fwd", "ffpa_attn_fwd_workspace_size", "ffpa_attn_bwd",
-            "ffpa_attn_bwd_workspace_size", "ffpa_last_error", "ffpa_version")
+            "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min", "ffpa_last_error",
+            "ffpa_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -64,6 +66,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffpa_attn_fwd_workspace_size.restype = sz
     lib.ffpa_attn_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.ffpa_attn_bwd_workspace_size.restype = sz
+    lib.ffpa_attn_bwd_workspace_size_min.argtypes = [i, i, i, i, i, i, i]
+    lib.ffpa_attn_bwd_workspace_size_min.restype = sz
     lib.ffpa_last_error.argtypes = []
     lib.ffpa_last_error.restype = ctypes.c_char_p
     lib.ffpa_version.argtypes = []
@@ -91,6 +95,10 @@ def ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype) -> int:
 
 def ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype) -> int:
     return load().ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype)
+
+
+def ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype) -> int:
+    return load().ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype)
 
 
 def ffpa_attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
@@ -187,8 +195,12 @@ def attention(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float
 
 
 def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None,
-                       scale: Optional[float] = None):
-    """(dq, dk, dv) of attention on the current HIP stream; o, lse from ``attention``."""
+                       scale: Optional[float] = None, store_ds: bool = True):
+    """(dq, dk, dv) of attention on the current HIP stream; o, lse from ``attention``.
+
+    store_ds: give the call the workspace that keeps dS between the dK/dV and
+    dQ passes (ffpa_attn_bwd_workspace_size); False gives it the minimum
+    (ffpa_attn_bwd_workspace_size_min), and dQ recomputes S and dP."""
     import torch
 
     B, Hq, Hkv, Nq, Nkv, D = _dims(q, k, v)
@@ -196,7 +208,8 @@ def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     mptr, mrows = _mask_args(mask, q, Nq, Nkv)
     dt = _dtype_code(q)
-    ws_bytes = ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt)
+    size = ffpa_attn_bwd_workspace_size if store_ds else ffpa_attn_bwd_workspace_size_min
+    ws_bytes = size(B, Hq, Hkv, Nq, Nkv, D, dt)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(ffpa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),

@@ -261,11 +261,25 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   return FFPA_OK;
 }
 
-size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {
+size_t ffpa_attn_bwd_workspace_size_min(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {
   (void)Hkv; (void)Nkv; (void)D; (void)dtype;
   if (B < 1 || Hq < 1 || Nq < 1) return 0;
   // delta and lse * log2(e) per query row, rows padded to a multiple of 64
   return 2 * (size_t)B * Hq * (size_t)bwd_nq_pad(Nq) * sizeof(float);
+}
+
+// bytes of the stored-dS path's K^T copy and dS blocks (after the row data)
+static size_t bwd_kt_bytes(int B, int Hkv, int Nkv, int D) {
+  return (size_t)B * Hkv * D * (size_t)ffpa::fwd_nkv_pad(Nkv) * 2;
+}
+static size_t bwd_ds_bytes(int B, int Hq, int Nq, int Nkv) {
+  return (size_t)B * Hq * (size_t)((Nq + 31) / 32) * (size_t)((Nkv + 31) / 32) * 2048;
+}
+
+size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {
+  const size_t base = ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  if (base == 0 || Hkv < 1 || Nkv < 1 || D < 1) return base;
+  return base + bwd_kt_bytes(B, Hkv, Nkv, D) + bwd_ds_bytes(B, Hq, Nq, Nkv);
 }
 
 int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -283,9 +297,11 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(mask) ||
       !aligned16(workspace))
     return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-  const size_t need = ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  const size_t need = ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype);
   if (workspace == nullptr || workspace_bytes < need)
-    return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_bwd_workspace_size()");
+    return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_bwd_workspace_size_min()");
+  // the whole size: dS is stored by the dK/dV pass and dQ reads it back
+  const bool store_ds = workspace_bytes >= ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
   if (!(scale == scale)) return fail(FFPA_ERR_INVALID_ARG, "scale is NaN");
   BwdLauncher launch = bwd_launcher(D, dtype == FFPA_BF16);
   if (launch == nullptr)
@@ -311,6 +327,17 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
     return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
   a.wg_dkdv = (int)wg_dkdv;
   a.wg_dq = (int)wg_dq;
+  if (store_ds) {
+    const int rq = ffpa::bwd_dq_ds_rows(D);
+    const int64_t wg_dq_ds = (int64_t)B * Hq * ((Nq + rq - 1) / rq);
+    if (wg_dq_ds >= (int64_t(1) << 31)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
+    a.wg_dq_ds = (int)wg_dq_ds;
+    a.nqt = (Nq + 31) / 32;
+    a.nkt = (Nkv + 31) / 32;
+    a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
+    a.kt = (char*)workspace + need;
+    a.ds = (char*)a.kt + bwd_kt_bytes(B, Hkv, Nkv, D);
+  }
   hipError_t e = launch(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return FFPA_OK;

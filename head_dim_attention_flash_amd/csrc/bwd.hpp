@@ -43,6 +43,7 @@
 #pragma once
 
 #include "ffpa_common.hpp"
+#include "fwd_vt.hpp"
 
 namespace ffpa {
 
@@ -67,13 +68,46 @@ struct BwdArgs {
   float scale_log2;  // scale * log2(e)
   int wg_dkdv;       // B * Hkv * ceil(Nkv / 64)
   int wg_dq;         // B * Hq * ceil(Nq / 64)
+  // stored-dS path (null ds: dQ recomputes S and dP instead)
+  void* ds;          // workspace: dS in blocks of 32 queries x 32 keys (bwd_ds_block)
+  void* kt;          // workspace: K^T in blocks of 32 keys (fwd_vt.hpp layout)
+  int nqt, nkt;      // ceil(Nq / 32), ceil(Nkv / 32)
+  int nkv_pad;       // Nkv rounded up to 64
+  int wg_dq_ds;      // B * Hq * ceil(Nq / bwd_dq_ds_rows(D))
 };
+
+// The stored dS. Block (bh, qt, kt) holds dS[q][key] for the 32 queries of
+// tile qt and the 32 keys of tile kt of head bh = b Hq + h: 2 KiB, 32 rows of
+// 64 bytes (one per query), whose positions hold the keys in the order
+// vt_key(pos) of fwd_vt.hpp, so that 16-byte granule 2 t2 + h of a row
+// pairs with granule 2 t2 + h of a K^T row of the same tile (the MFMA
+// operand pieces of key step t2 and lane half h).
+__host__ __device__ inline size_t bwd_ds_block(int bh, int qt, int kt, int nqt, int nkt) {
+  return (((size_t)bh * nqt + qt) * nkt + kt) * 2048;
+}
+// queries per workgroup of the stored-dS dQ kernel
+__host__ __device__ inline int bwd_dq_ds_rows(int D) { return D > 512 ? 64 : 128; }
 
 constexpr int kBwdRows = 32;                       // rows per staged tile
 constexpr int kBwdPartBytes = 512;                 // LDS slot of one part of a row
 constexpr int kBwdXchg = 8 * 1024;                 // per wave: partial S and dP tiles, fp32
 constexpr int kBwdLds = 160 * 1024;                // tiles (128 KiB) + swap area (32 KiB)
 constexpr int kBwdPad = 64;                        // workspace row padding
+
+// This lane's index in the wave (0..63), computed where it is used: the asm
+// is opaque, so the compiler keeps no lane-id register live across a loop
+// (which it would for threadIdx.x) when registers are short.
+__device__ inline int lane_id_here() {
+  int x;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n v_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+  return x;
+}
+
+// A compile-time integer as a type, to instantiate a generic lambda per value.
+template <int I>
+struct IntTag {
+  static constexpr int value = I;
+};
 
 // Zero that the compiler cannot see through: an MFMA operand register that
 // holds zero padding then stays a register (a visible constant would be
@@ -418,8 +452,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int qt = qt0 + it % per_head;
     const size_t hoff = (size_t)(b * a.Hq + hh) * a.Nq * D * 2;
     const int s = it % Sh::NB;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+    const int ln = lane_id_here();
     bwd_copy_tile<D>(make_rsrc((const char*)a.q + hoff, q_bytes), smem + QB + s * Sh::TILE, qt * kBwdRows, wave, ln);
     bwd_copy_tile<D>(make_rsrc((const char*)a.dout + hoff, q_bytes), smem + OB + s * Sh::TILE, qt * kBwdRows, wave, ln);
   };
@@ -435,7 +468,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   auto load_rows = [&](int it) {
     const int hh = hk * g + it / per_head;
     const int qt = qt0 + it % per_head;
-    const size_t rb = (size_t)(b * a.Hq + hh) * a.nq_pad + qt * kBwdRows + 4 * (lane >> 5);
+    const size_t rb = (size_t)(b * a.Hq + hh) * a.nq_pad + qt * kBwdRows + 4 * (lane_id_here() >> 5);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       l2n[j] = *(const f32x4*)(a.lse2 + rb + 8 * j);
@@ -458,8 +491,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int s = it % Sh::NB;
     const FFPA_LDS char* qtile = smem + QB + s * Sh::TILE;
     const FFPA_LDS char* otile = smem + OB + s * Sh::TILE;
-    int lj = lane;
-    asm volatile("" : "+v"(lj));
+    const int lj = lane_id_here();
     const int hij = lj >> 5;
     const int my_k = kw + (lj & 31);
 
@@ -493,8 +525,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
       const __amdgpu_buffer_rsrc_t On = make_rsrc((const char*)a.dout + hoff, q_bytes);
       FFPA_LDS char* qd = smem + QB + (s ^ 1) * Sh::TILE;
       FFPA_LDS char* od = smem + OB + (s ^ 1) * Sh::TILE;
-      int lc = lane;
-      asm volatile("" : "+v"(lc));
+      const int lc = lane_id_here();
       uint32_t ax[8];
       bwd_row_bases<Sh::ROWB>(lj, hf, ax);
       bwd_partials<BF16, NS>(qtile, otile, ax, kf, vf, sacc, pacc, [&](int st) {
@@ -546,6 +577,57 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[t2]), "+v"(sf[t2]));
 
+    // dS for the dQ pass: lane (key, h) holds dS of 16 queries of its key;
+    // the dQ product needs each query's keys in one lane. One MFMA per wave
+    // transposes a half: with A = the packed dS of query step t2 = hf (m =
+    // key, k = 16 queries) and B = the 0/1 matrix that maps k back to its
+    // query n, C[key][q] = dS[q][key] for the 16 queries of the step (exact:
+    // each sum has one nonzero term). Lane (q, h) of C then holds keys
+    // 8 (i / 4) + 4 h + i % 4, i.e. positions 8 h .. 8 h + 7 and 16 + 8 h ..
+    // of the block row in vt_key order: two 16-byte stores.
+    // (t2 a constant in each instance: an operand picked by a runtime index
+    // made the compiler rebuild the packed tiles inside the products below)
+    auto store_ds = [&](auto t2_tag, const V8& sfa) {
+      constexpr int t2 = decltype(t2_tag)::value;
+      const int qn = lj & 31, hn = lj >> 5;
+      const int r = qn - 16 * t2;  // the query's index within the step
+      const bool mine = (unsigned)r < 16u;
+      // the 1 sits at element e = 4 ((r / 8) % 2) + r % 4 of lane half (r / 4) % 2
+      const int e = 4 * ((r >> 3) & 1) + (r & 3);
+      const uint32_t one = (mine && ((r >> 2) & 1) == hn) ? (BF16 ? 0x3F80u : 0x3C00u) << (16 * (e & 1)) : 0u;
+      u32x4 ib;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) ib[w] = (e >> 1) == w ? one : 0u;
+      f32x16 tr;
+      mfma32_asm<BF16, false, false, true, true, true>(tr, __builtin_bit_cast(u32x4, sfa), ib);
+      // the values are 16-bit numbers held exactly in fp32: bf16 keeps the
+      // high halves (one byte permute per pair), fp16 converts exactly
+      auto pk = [&](float x, float y) -> uint32_t {
+        if constexpr (BF16)
+          return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, y), __builtin_bit_cast(uint32_t, x), 0x07060302u);
+        else
+          return E::pack2(x, y);
+      };
+      if (mine) {
+        char* blk = (char*)a.ds + bwd_ds_block(b * a.Hq + hh, qt, kw / 32, a.nqt, a.nkt) + qn * 64;
+        const u32x4 g0 = {pk(tr[0], tr[1]), pk(tr[2], tr[3]), pk(tr[4], tr[5]), pk(tr[6], tr[7])};
+        const u32x4 g1 = {pk(tr[8], tr[9]), pk(tr[10], tr[11]), pk(tr[12], tr[13]), pk(tr[14], tr[15])};
+        // non-temporal: dS is read once, by the dQ pass; kept out of the
+        // way of the Q and dO tiles in L2 (8 % faster than plain stores)
+        __builtin_nontemporal_store(g0, (u32x4*)(blk + 16 * hn));
+        __builtin_nontemporal_store(g1, (u32x4*)(blk + 16 * (2 + hn)));
+      }
+      // the stores go out here, not among the products below (their data
+      // would stay live there)
+      asm volatile("" ::: "memory");
+    };
+    if (a.ds != nullptr && kw < a.Nkv) {
+      if (hf == 0) store_ds(IntTag<0>{}, sf[0]);
+      else if (hf == 1) store_ds(IntTag<1>{}, sf[1]);
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[t2]), "+v"(sf[t2]));
+
     // the next tile's lse2 and delta, waited for at its barrier
     if constexpr (!ROWMASK) {
       if (it + 1 < n_it) load_rows(it + 1);
@@ -556,8 +638,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     {
       uint32_t tx[8];
       {
-        int lv = lane;
-        asm volatile("" : "+v"(lv));
+        const int lv = lane_id_here();
         bwd_tr_bases<Sh::ROWB>(lv, hf, tx);
       }
       u32x4 fo[kTAhead], fq[kTAhead];
@@ -607,13 +688,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
   wait_lgkm0();
   barrier();
   FFPA_LDS char* stg = smem + wave * 2 * 16384;
-  bwd_stage_rows<BF16, NDB>(stg, dv, 1.f, lane);
-  bwd_stage_rows<BF16, NDB>(stg + 16384, dk, a.scale, lane);
+  const int le = lane_id_here();
+  bwd_stage_rows<BF16, NDB>(stg, dv, 1.f, le);
+  bwd_stage_rows<BF16, NDB>(stg + 16384, dk, a.scale, le);
   {
     const size_t row0 = ((size_t)(b * a.Hkv + hk) * a.Nkv + kw) * D + hf * DW;
     const int rows = min(kBwdRows, a.Nkv - kw);
-    bwd_store_rows<D>((T*)a.dv + row0, stg, rows, hf, lane);
-    bwd_store_rows<D>((T*)a.dk + row0, stg + 16384, rows, hf, lane);
+    bwd_store_rows<D>((T*)a.dv + row0, stg, rows, hf, le);
+    bwd_store_rows<D>((T*)a.dk + row0, stg + 16384, rows, hf, le);
   }
 }
 
@@ -833,6 +915,196 @@ void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 3b. dQ from the stored dS: dQ^T += K^T dS^T per key tile, nothing
+// recomputed. Wave (qb, hf) owns queries qw = ROWS qblk + 32 qb .. +31 and
+// part hf of D (D <= 512: all of D, 4 query blocks per workgroup; above: two
+// halves, 2 query blocks). The K^T tile (D rows of 32 keys, 64 bytes each,
+// from the blocked transposed copy) is staged in LDS, double-buffered, and
+// read with plain 16-byte reads as the A operand; the dS block of the wave's
+// queries comes straight from global memory as the B operand, one tile
+// ahead. Under causal masking the blocks above the diagonal were never
+// written (their dS is zero): a wave skips the products of those tiles.
+// ---------------------------------------------------------------------------
+constexpr int kBwdDqDsLds = 128 * 1024;
+
+template <int D, bool BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_ds_kernel(BwdArgs a) {
+  static_assert(D % 64 == 0 && D <= 1024, "D must be a multiple of 64, at most 1024");
+  using E = Elem<BF16>;
+  using T = typename E::scalar;
+  constexpr int NQP = D > 512 ? 2 : 1;  // parts of D
+  constexpr int DQ = D / NQP;           // columns per wave
+  constexpr int NDB = DQ / 32;
+  constexpr int ROWS = 32 * (4 / NQP);  // queries per workgroup
+  constexpr int TILE = D * 64;          // bytes of a staged K^T tile
+  constexpr int NVC = D / 64;           // copy instructions per wave and tile
+  constexpr int NT = 2 * NDB;           // MFMA steps per tile: st = NDB t2 + db
+  constexpr int kAhead = NT < 8 ? NT : 8;
+  // accumulator blocks in AGPRs; the rest in VGPRs (all 256 AGPRs taken
+  // makes the allocator spill)
+  constexpr int kAcc = NDB < 12 ? NDB : 12;
+  static_assert(2 * TILE <= kBwdDqDsLds && 4 * 32 * 1024 <= kBwdDqDsLds, "LDS budget");
+
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qb = wave / NQP, hf = wave % NQP;
+
+  const int n_qb = (a.Nq + ROWS - 1) / ROWS;
+  const int t = xcd_logical(blockIdx.x, a.wg_dq_ds);
+  int qblk = t % n_qb;
+  const int bh = t / n_qb;
+  if (a.causal) qblk = n_qb - 1 - qblk;  // longest rows first
+  const int h = bh % a.Hq, b = bh / a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int qw = qblk * ROWS + 32 * qb;
+  const int qt = qw / 32;
+
+  int kv_end = a.Nkv;
+  if (a.causal) kv_end = min(kv_end, min(qblk * ROWS + ROWS, a.Nq));  // keys <= last row of the block
+  const int n_kt = (kv_end + 31) / 32;
+  // tiles with products for this wave: all, or (causal) those with keys <= its last row
+  int my_end = a.causal ? min(n_kt, qt + 1) : n_kt;
+  if (qw >= a.Nq) my_end = 0;  // a block past the last query: no dS rows
+
+  const uint32_t kt_bytes = (uint32_t)D * a.nkv_pad * 2;
+  const __amdgpu_buffer_rsrc_t Ktr =
+      make_rsrc((const char*)a.kt + (size_t)(b * a.Hkv + hk) * kt_bytes, kt_bytes);
+  // this lane's dS pieces: row l % 32 of the wave's block, granule 2 t2 + l / 32
+  const char* dsrow = (const char*)a.ds + (my_end > 0 ? bwd_ds_block(bh, qt, 0, a.nqt, a.nkt) : 0) +
+                      (lane & 31) * 64 + (lane >> 5) * 16;
+
+  // copy instruction n (n = wave + 4 r, r < NVC) fills LDS rows 16 n .. 16 n +
+  // 15 of a tile: lane i writes slot i % 4 of row 16 n + i / 4, which holds
+  // the logical granule (i % 4) ^ ((row / 4) % 4), and (row / 4) % 4 =
+  // (i / 16) % 4 whatever n is
+  uint32_t lo;
+  {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    lo = (uint32_t)(ln >> 2) * 64 + (uint32_t)(((ln & 3) ^ ((ln >> 4) & 3)) << 4);
+    asm volatile("" : "+v"(lo));
+  }
+  auto kt_copy = [&](int j, int r) {
+    const int n = wave + 4 * r;
+    dma16(Ktr, lo + (uint32_t)(16 * n) * 64 + (uint32_t)j * TILE, smem + (j & 1) * TILE + n * 1024);
+  };
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dq[i] = f32x16{};
+  u32x4 bn[2];  // dS pieces of the next tile
+  auto load_ds = [&](int j) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+      bn[t2] = __builtin_nontemporal_load((const u32x4*)(dsrow + (size_t)j * 2048 + 32 * t2));
+  };
+  if (n_kt > 0) {
+    if (my_end > 0) load_ds(0);
+    wait_vmcnt0_visible();
+#pragma unroll
+    for (int r = 0; r < NVC; ++r) kt_copy(0, r);
+  }
+
+  for (int j = 0; j < n_kt; ++j) {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      if (d < kAcc) asm volatile("" : "+a"(dq[d]));
+      else asm volatile("" : "+v"(dq[d]));
+    }
+    wait_vmcnt<0>();  // this wave's copies of tile j landed ...
+    wait_lgkm0();
+    barrier();        // ... everyone's; tile j - 1's buffer is free
+    const bool more = j + 1 < n_kt;
+    if (j < my_end) {
+      u32x4 bc[2] = {bn[0], bn[1]};
+      // the compiler's wait for the dS loads falls here, before any copy is in flight
+      asm volatile("" ::"v"(bc[0]), "v"(bc[1]));
+      if (j + 1 < my_end) load_ds(j + 1);
+      uint32_t vx[2];
+      {
+        int lv = lane;
+        asm volatile("" : "+v"(lv));
+        const int r = lv & 31, hh = lv >> 5;
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+          vx[t2] = (uint32_t)((j & 1) * TILE + (DQ * hf + r) * 64 + (((2 * t2 + hh) ^ ((r >> 2) & 3)) << 4));
+      }
+      auto aread = [&](int st) { return lds_read16(smem + vx[st / NDB] + 2048 * (st % NDB)); };
+      u32x4 af[kAhead];
+#pragma unroll
+      for (int st = 0; st < kAhead; ++st) af[st] = aread(st);
+#pragma unroll
+      for (int st = 0; st < NT; ++st) {
+        // the next tile's copies, spread over the first half of the steps
+#pragma unroll
+        for (int r = 0; r < NVC; ++r)
+          if (more && (r * (NT / 2)) / NVC == st) kt_copy(j + 1, r);
+        const int db = st % NDB, t2 = st / NDB;
+        const u32x4 x = af[st % kAhead];
+        if (st + kAhead < NT) af[st % kAhead] = aread(st + kAhead);
+        // the first MFMA pads for a VALU copy of the dS pieces, the last for
+        // accumulator copies on the loop's exit or back edge
+        if (db < kAcc) {
+          if (st == 0) mfma32_asm<BF16, false, true, false, true>(dq[db], x, bc[t2]);
+          else if (st == NT - 1) mfma32_asm<BF16, false, true, false, false, true>(dq[db], x, bc[t2]);
+          else mfma32_asm<BF16, false, true>(dq[db], x, bc[t2]);
+        } else {
+          if (st == 0) mfma32_asm<BF16, false, false, false, true>(dq[db], x, bc[t2]);
+          else if (st == NT - 1) mfma32_asm<BF16, false, false, false, false, true>(dq[db], x, bc[t2]);
+          else mfma32_asm<BF16, false, false>(dq[db], x, bc[t2]);
+        }
+      }
+    } else if (more) {
+#pragma unroll
+      for (int r = 0; r < NVC; ++r) kt_copy(j + 1, r);
+    }
+  }
+  wait_vmcnt<0>();
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 4" ::: "memory");
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) {
+    if (d < kAcc) asm volatile("" : "+a"(dq[d]));
+    else asm volatile("" : "+v"(dq[d]));
+  }
+
+  // ---- epilogue: 32 rows of the wave's part through LDS (1 KiB pitch,
+  // granule g of row r at g ^ (r % 16)), then 16-byte stores along rows
+  wait_lgkm0();
+  barrier();
+  FFPA_LDS char* stg = smem + wave * 32 * 1024;
+  {
+    const int r = lane & 31, hie = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const u32x2 w = {E::pack2(dq[db][4 * g4] * a.scale, dq[db][4 * g4 + 1] * a.scale),
+                         E::pack2(dq[db][4 * g4 + 2] * a.scale, dq[db][4 * g4 + 3] * a.scale)};
+        const int g = 4 * db + g4;
+        *(FFPA_LDS u32x2*)(stg + r * 1024 + ((g ^ (r & 15)) << 4) + 8 * hie) = w;
+      }
+  }
+  {
+    constexpr int SG = DQ / 8;
+    constexpr int NIT = (32 * SG + 63) / 64;
+    T* dst = (T*)a.dq + ((size_t)bh * a.Nq + qw) * D + DQ * hf;
+    const int rows = min(32, a.Nq - qw);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int c = it * 64 + lane;
+      const int r = c / SG, g = c % SG;
+      if (r < rows) {
+        const u32x4 x = *(const FFPA_LDS u32x4*)(stg + r * 1024 + ((g ^ (r & 15)) << 4));
+        *(u32x4*)(dst + (size_t)r * D + 8 * g) = x;
+      }
+    }
+  }
+}
+
 // Host launcher: the three kernels in order on `stream`.
 template <int D, bool BF16>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
@@ -850,6 +1122,18 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   if (attr2 != hipSuccess) return attr2;
   const int64_t rows = (int64_t)a.B * a.Hq * a.nq_pad;
   hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  if (a.ds != nullptr) {
+    // stored-dS path: K^T for the dQ pass, dK/dV (which writes dS), dQ = scale dS K
+    auto kdqs = bwd_dq_ds_kernel<D, BF16>;
+    static const hipError_t attr3 =
+        hipFuncSetAttribute((const void*)kdqs, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdDqDsLds);
+    if (attr3 != hipSuccess) return attr3;
+    const hipError_t e = launch_fwd_vt(a.k, a.kt, a.B * a.Hkv, a.Nkv, D, 32, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kdkdv, dim3(a.wg_dkdv), dim3(256), kBwdLds, stream, a);
+    hipLaunchKernelGGL(kdqs, dim3(a.wg_dq_ds), dim3(256), kBwdDqDsLds, stream, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(kdkdv, dim3(a.wg_dkdv), dim3(256), kBwdLds, stream, a);
   hipLaunchKernelGGL(kdq, dim3(a.wg_dq), dim3(256), kBwdLds, stream, a);
   return hipGetLastError();

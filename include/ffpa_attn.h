@@ -129,10 +129,16 @@ size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
  * layout as q, k, v). o and lse must be the forward's outputs for the same
  * q, k, v, scale, causal and mask. dk and dv of a K/V head sum the
  * contributions of all query heads that share it. accum_dtype must be
- * FFPA_ACC_F32. workspace: at least ffpa_attn_bwd_workspace_size(...) bytes,
- * 16-byte aligned (holds delta_i = sum_d dO_id O_id and lse_i log2(e) per
- * query row, rows padded to a multiple of 64). Three kernels are enqueued:
- * the delta pass, then dK/dV, then dQ. Built for D a multiple of 64 up to
+ * FFPA_ACC_F32. workspace: 16-byte aligned, at least
+ * ffpa_attn_bwd_workspace_size_min(...) bytes (delta_i = sum_d dO_id O_id
+ * and lse_i log2(e) per query row, rows padded to a multiple of 64). Given
+ * ffpa_attn_bwd_workspace_size(...) bytes or more, the call also keeps a
+ * transposed copy of K and the bf16/fp16 dS of every visible 32 x 32 block
+ * there (B * Hq * ceil(Nq/32) * ceil(Nkv/32) * 2 KiB: 4 GiB at B = 1,
+ * Hq = 32, N = 8192): the dK/dV pass writes dS and the dQ pass reads it
+ * back (one product instead of three). With less, dQ recomputes S and dP.
+ * Both give the same gradients up to rounding. Kernels enqueued: the delta
+ * pass, [the K transpose], dK/dV, dQ. Built for D a multiple of 64 up to
  * 1024, with either mask shape; other valid shapes (D not a multiple of 64)
  * return FFPA_ERR_UNSUPPORTED.
  * The gradients are those of sum(dout * O) ("FFPA Attention Benchmark",
@@ -144,8 +150,11 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
                   const void* mask, int mask_rows, int accum_dtype, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace ffpa_attn_bwd needs for these sizes. */
+/* Bytes of workspace ffpa_attn_bwd runs fastest with (dS stored) for these sizes. */
 size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
+
+/* The least workspace ffpa_attn_bwd accepts (dQ then recomputes S and dP). */
+size_t ffpa_attn_bwd_workspace_size_min(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
 
 /* Thread-local message describing the last non-OK status ("" if none). */
 const char* ffpa_last_error(void);

@@ -122,3 +122,13 @@ def test_workspace_queries_are_pure_functions():
     b = ffpa.ffpa_attn_fwd_workspace_size(16, 32, 32, 1, 8192, 512, 0)
     assert a == b and a >= 0
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 32, 8192, 8192, 512, 1) >= 32 * 8192 * 4
+
+
+def test_backward_workspace_sizes():
+    # the minimum: delta and lse * log2(e) per query row, rows padded to 64
+    assert ffpa.ffpa_attn_bwd_workspace_size_min(2, 4, 2, 100, 70, 320, 0) == 2 * 2 * 4 * 128 * 4
+    # stored dS: + K^T (keys padded to 64) + 2 KiB per 32 x 32 block of every head
+    full = ffpa.ffpa_attn_bwd_workspace_size(2, 4, 2, 100, 70, 320, 0)
+    assert full == 2 * 2 * 4 * 128 * 4 + 2 * 2 * 320 * 128 * 2 + 2 * 4 * 4 * 3 * 2048
+    assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 32, 8192, 8192, 512, 1) == (
+        2 * 32 * 8192 * 4 + 32 * 512 * 8192 * 2 + 32 * 256 * 256 * 2048)

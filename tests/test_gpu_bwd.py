@@ -91,7 +91,7 @@ def _compare(name, got, ref, dtype, label, bound=None):
         assert rel <= REL[dtype], f"{label}: {name} rel L2 {rel}"
 
 
-def _run_case(lib, shape, dtype, causal, with_mask, seed, mask_rows=1):
+def _run_case(lib, shape, dtype, causal, with_mask, seed, mask_rows=1, store_ds=True):
     B, Hq, Hkv, Nq, Nkv, D = shape
     q, k, v, do, mask = _inputs(seed, B, Hq, Hkv, Nq, Nkv, D, dtype, with_mask,
                                 mask_rows=Nq if mask_rows != 1 else 1)
@@ -102,10 +102,12 @@ def _run_case(lib, shape, dtype, causal, with_mask, seed, mask_rows=1):
     lse_in = torch.from_numpy(lse_ref).to(torch.float32).cuda()
     dq, dk, dv = lib.attention_backward(do.cuda(), q.cuda(), k.cuda(), v.cuda(), o_in, lse_in,
                                         causal=causal,
-                                        mask=None if mask is None else mask.cuda(), scale=scale)
+                                        mask=None if mask is None else mask.cuda(), scale=scale,
+                                        store_ds=store_ds)
     torch.cuda.synchronize()
     rq, rk, rv = attn_bwd(q, k, v, do, scale, causal=causal, mask=m2)
-    label = f"{shape}-{dtype}-{'causal' if causal else 'full'}-{'mask' if with_mask else 'nomask'}"
+    label = (f"{shape}-{dtype}-{'causal' if causal else 'full'}-{'mask' if with_mask else 'nomask'}"
+             f"-{'stored dS' if store_ds else 'recomputed dS'}")
     print(label, flush=True)
     bounds = (_rounding_bounds(q, k, v, do, scale, causal, m2, (rq, rk, rv), dtype)
               if dtype == "bf16" else {})
@@ -139,6 +141,16 @@ CASES = [
 def test_backward_matches_oracle(lib, shape, dtype, variant):
     _run_case(lib, shape, dtype, "causal" in variant, "mask" in variant, 300 + sum(shape),
               mask_rows="q" if "qmask" in variant else 1)
+
+
+# With only the minimal workspace, the dQ pass recomputes S and dP instead of
+# reading back the dS that the dK/dV pass stored.
+@pytest.mark.parametrize("shape", [CASES[1], CASES[2], CASES[4], CASES[9], CASES[10]],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("variant", ["plain", "causal_mask", "causal_qmask"])
+def test_backward_minimal_workspace_matches_oracle(lib, shape, variant):
+    _run_case(lib, shape, "bf16", "causal" in variant, "mask" in variant, 300 + sum(shape),
+              mask_rows="q" if "qmask" in variant else 1, store_ds=False)
 
 
 def test_backward_deterministic(lib):
