@@ -135,7 +135,6 @@ int check_common(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, con
     return fail(FFPA_ERR_UNSUPPORTED, "accum_dtype must be FFPA_ACC_F32 or FFPA_ACC_F16");
   if (D % 32 != 0 || D > FFPA_MAX_HEAD_DIM)
     return fail(FFPA_ERR_UNSUPPORTED, "D must be a multiple of 32 and at most 1024");
-  // element counts must index with 32-bit row offsets inside one (b, h) slice
   // byte offsets inside one (b, h) slice, one tile past its end included, fit 32 bits
   if ((int64_t)(Nq + 128) * D >= (int64_t(1) << 31) || (int64_t)(Nkv + 128) * D >= (int64_t(1) << 31))
     return fail(FFPA_ERR_UNSUPPORTED, "(N + 128) * D must be below 2^31");
