@@ -43,7 +43,7 @@ struct DecArgs {
 };
 
 constexpr int kDecStep = 8;        // keys per step
-constexpr int kDecTargetWaves = 4096;  // 256 CUs x 16 waves
+constexpr int kDecTargetWaves = 2048;  // 256 CUs x 8 waves (4096 streamed 3 % slower)
 constexpr int kDecMinKeys = 256;   // smallest key range worth a wave
 constexpr int kDecMaxSplits = 64;
 
