@@ -71,10 +71,12 @@ struct Elem<true> {
   __device__ static inline float to_f32(uint16_t bits) {
     return __builtin_bit_cast(float, (uint32_t)bits << 16);
   }
+  // Round-to-nearest-even pack of two floats: one v_cvt_pk_bf16_f32 (two
+  // scalar conversions compile to two of them plus a shift and an or).
   __device__ static inline uint32_t pack2(float a, float b) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
   }
 };
 
