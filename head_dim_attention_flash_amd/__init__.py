@@ -195,12 +195,14 @@ def attention(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float
 
 
 def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None,
-                       scale: Optional[float] = None, store_ds: bool = True):
+                       scale: Optional[float] = None, store_ds: Optional[bool] = None):
     """(dq, dk, dv) of attention on the current HIP stream; o, lse from ``attention``.
 
-    store_ds: give the call the workspace that keeps dS between the dK/dV and
-    dQ passes (ffpa_attn_bwd_workspace_size); False gives it the minimum
-    (ffpa_attn_bwd_workspace_size_min), and dQ recomputes S and dP."""
+    store_ds: True gives the call the workspace that keeps dS between the dK/dV
+    and dQ passes (ffpa_attn_bwd_workspace_size, 2 KiB per 32 x 32 block of
+    every head); False gives it the minimum (ffpa_attn_bwd_workspace_size_min),
+    and dQ recomputes S and dP. None (default): True when that workspace takes
+    at most half of the device memory free now."""
     import torch
 
     B, Hq, Hkv, Nq, Nkv, D = _dims(q, k, v)
@@ -208,6 +210,9 @@ def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     mptr, mrows = _mask_args(mask, q, Nq, Nkv)
     dt = _dtype_code(q)
+    if store_ds is None:
+        free, _ = torch.cuda.mem_get_info(q.device)
+        store_ds = ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt) <= free // 2
     size = ffpa_attn_bwd_workspace_size if store_ds else ffpa_attn_bwd_workspace_size_min
     ws_bytes = size(B, Hq, Hkv, Nq, Nkv, D, dt)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
