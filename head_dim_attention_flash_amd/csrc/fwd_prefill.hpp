@@ -807,22 +807,26 @@ void fwd_prefill_kernel(FwdArgs a) {
       u32x4 vf[kVAhead];
 #pragma unroll
       for (int st = 0; st < kVAhead; ++st) vf[st] = vread(st);
-      f32x16 acc_e, acc_o;  // fp16 path: per-tile products of the pair's even / odd block
-      auto fold = [&](const f32x16& acc, int d2) {
-        // o16 <- o16 * oscale + acc, in packed fp16
+      // fp16 path: per-tile products of a pair's even / odd block, two sets
+      // (pairs alternate): the fold of pair q into the fp16 accumulator runs
+      // beside the products of pair q + 1
+      f32x16 acc_e[2], acc_o[2];
+      // o16 <- o16 * oscale + acc, in packed fp16, for half hh of block d2
+      auto fold_half = [&](const f32x16& acc, int d2, int hh) {
         const f16x2 sc = {(_Float16)oscale, (_Float16)oscale};
+        u32x4 w = o16[2 * d2 + hh];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 w = o16[2 * d2 + hh];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            f16x2 cur = f16x2_from_bits(w[e]);
-            const f16x2 add = {(_Float16)acc[8 * hh + 2 * e], (_Float16)acc[8 * hh + 2 * e + 1]};
-            cur = cur * sc + add;
-            w[e] = __builtin_bit_cast(uint32_t, cur);
-          }
-          o16[2 * d2 + hh] = w;
+        for (int e = 0; e < 4; ++e) {
+          f16x2 cur = f16x2_from_bits(w[e]);
+          const f16x2 add = {(_Float16)acc[8 * hh + 2 * e], (_Float16)acc[8 * hh + 2 * e + 1]};
+          cur = cur * sc + add;
+          w[e] = __builtin_bit_cast(uint32_t, cur);
         }
+        o16[2 * d2 + hh] = w;
+      };
+      auto fold = [&](const f32x16& acc, int d2) {
+        fold_half(acc, d2, 0);
+        fold_half(acc, d2, 1);
       };
       int lnc = lane;
       asm volatile("" : "+v"(lnc));
@@ -838,24 +842,34 @@ void fwd_prefill_kernel(FwdArgs a) {
         const u32x4 pb = __builtin_bit_cast(u32x4, pf[kb][t2]);
         const bool first = kb == 0 && t2 == 0, last = kb == 1 && t2 == 1;
         if constexpr (ACC16) {
-          // per-tile products in VGPRs; the pair's last MFMA pads for the
-          // VALU that folds both into the fp16 accumulator
+          // per-tile products in VGPRs, set q % 2 for pair q = st / 8; the
+          // last pair's last MFMA pads for the fold after the loop
+          const int q = st >> 3, set = q & 1;
+          const bool final_mfma = st == NSV - 1;
           if ((st & 1) == 0) {
             if (first) {
-              if (st == 0) mfma32_asm<BF16, false, false, true, true>(acc_e, vbits, pb);
-              else mfma32_asm<BF16, false, false, true>(acc_e, vbits, pb);
+              if (st == 0) mfma32_asm<BF16, false, false, true, true>(acc_e[set], vbits, pb);
+              else mfma32_asm<BF16, false, false, true>(acc_e[set], vbits, pb);
             } else {
-              mfma32_asm<BF16, false, false>(acc_e, vbits, pb);
+              mfma32_asm<BF16, false, false>(acc_e[set], vbits, pb);
             }
           } else {
-            if (first) mfma32_asm<BF16, false, false, true>(acc_o, vbits, pb);
-            else if (last) mfma32_asm<BF16, false, false, false, false, true>(acc_o, vbits, pb);
-            else mfma32_asm<BF16, false, false>(acc_o, vbits, pb);
+            if (first) mfma32_asm<BF16, false, false, true>(acc_o[set], vbits, pb);
+            else if (final_mfma) mfma32_asm<BF16, false, false, false, false, true>(acc_o[set], vbits, pb);
+            else mfma32_asm<BF16, false, false>(acc_o[set], vbits, pb);
           }
-          if (last && (st & 1)) {
-            pin_after_pad(acc_e);
-            fold(acc_e, db - 1);
-            fold(acc_o, db);
+          // pair q - 1 folds at steps 6 (even block) and 7 (odd block) of
+          // pair q: seven MFMAs of pair q have issued since its last one
+          if (q > 0 && (st & 7) == 6) {
+            pin_after_pad(acc_e[set ^ 1]);
+            pin_after_pad(acc_o[set ^ 1]);
+            fold(acc_e[set ^ 1], 2 * (q - 1));
+          }
+          if (q > 0 && (st & 7) == 7) fold(acc_o[set ^ 1], 2 * (q - 1) + 1);
+          if (final_mfma) {
+            pin_after_pad(acc_e[set]);
+            fold(acc_e[set], 2 * q);
+            fold(acc_o[set], 2 * q + 1);
           }
         } else {
           // the first pair starts every block's chain (C = 0 on a fresh
