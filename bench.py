@@ -305,7 +305,8 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 25 forward calls (~0.1 s at the headline size): the clock ramps up over the first ~10
+    ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="self")
     ap.add_argument("--accum", default="f32", choices=["f32", "f16"])
     ap.add_argument("--cpu-heads", type=int, default=2,
@@ -351,9 +352,10 @@ def main(argv=None) -> int:
                    not args.no_cpu_baseline, args.cpu_heads)
     if not args.no_paths:
         line["paths"] = {
-            "backward": run_backward(ffpa, W, "bwd", max(3, args.steps // 2), 2),
-            "backward_causal": run_backward(ffpa, W, "bwd_causal", max(3, args.steps // 2), 2),
-            "decode": run_decode(ffpa, W, args.steps, args.warmup),
+            # warm-up of ~50-80 ms each, past the clock ramp
+            "backward": run_backward(ffpa, W, "bwd", max(3, args.steps // 2), 5),
+            "backward_causal": run_backward(ffpa, W, "bwd_causal", max(3, args.steps // 2), 8),
+            "decode": run_decode(ffpa, W, args.steps, max(args.warmup, 50)),
         }
     print(json.dumps(line), flush=True)
     if args.copy_calibration:
