@@ -110,21 +110,39 @@ def _blas_threads() -> int:
         return os.cpu_count() or 1
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, heads: int) -> dict:
-    """The float64 oracle timed on the host on `heads` query heads of the workload."""
-    from oracle import attn_fwd
+    """The float64 oracle timed on the host on `heads` query heads of the workload.
+
+    The inputs are copied to the host and widened to float64 before the clock
+    starts; the timed region is the oracle's arithmetic alone. The value is the
+    sample's own throughput (counted flops of the heads timed / time), not an
+    extrapolation: the heads are independent and identical in work."""
+    from oracle import attn_fwd, to_f64
 
     g = w.Hq // w.Hkv
     hk = max(1, (heads + g - 1) // g)
-    q = inp["q"][:, :heads].cpu()
-    k = inp["k"][:, :hk].cpu()
-    v = inp["v"][:, :hk].cpu()
-    mask = None if inp.get("mask") is None else inp["mask"].cpu()
+    q = to_f64(inp["q"][:, :heads])
+    k = to_f64(inp["k"][:, :hk])
+    v = to_f64(inp["v"][:, :hk])
+    mask = None if inp.get("mask") is None else to_f64(inp["mask"])
     t0 = time.perf_counter()
     attn_fwd(q, k, v, w.scale, causal=w.causal, mask=mask)
     dt = time.perf_counter() - t0
     fl = counted_flops(1, heads, w.Nq, w.Nkv, w.D, w.causal)
     return {"value": fl / dt / 1e12, "unit": "TFLOPS", "cores": _blas_threads(), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{heads} of {w.B * w.Hq} (b, h) heads of the same workload, float64 numpy, "
                       f"{dt:.2f} s"}
 
@@ -259,6 +277,17 @@ def run_decode(ffpa, W, steps, warmup):
             "rocprof": recorded_counters("decode")}
 
 
+def timed_call(w) -> str:
+    """The kernels one timed forward call enqueues (mirrors the library's choice)."""
+    if w.Nq == 1:
+        return "dec_split_kernel + dec_combine_kernel"
+    if w.D > 512:
+        return "fwd_vt_kernel (V transposed, blocks of 32 keys) + fwd_wide_kernel"
+    if w.Nq * w.Hq >= 3072 * w.Hkv:
+        return "fwd_vt_kernel (V transposed into the workspace) + fwd_prefill_kernel"
+    return "fwd_prefill_kernel (V staged as is)"
+
+
 def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
     import torch
 
@@ -291,7 +320,7 @@ def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
                      "traffic": measured_traffic(f"{name}:{accum}")},
         "kernel_ms": {"mean": round(mean_ms, 4), "median": round(per[len(per) // 2], 4),
                       "min": round(per[0], 4)},
-        "timed_call": "fwd_vt_kernel (V transposed into the workspace) + the attention kernel",
+        "timed_call": timed_call(w),
         "rocprof": recorded_counters(f"{name}:{accum}"),
     }
     if with_cpu:
@@ -348,15 +377,19 @@ def main(argv=None) -> int:
     if args.workload == "decode":
         print(json.dumps(run_decode(ffpa, W, args.steps, args.warmup)), flush=True)
         return 0
-    line = run_one(ffpa, W, args.workload, args.accum, args.steps, args.warmup,
-                   not args.no_cpu_baseline, args.cpu_heads)
+    paths = None
     if not args.no_paths:
-        line["paths"] = {
-            # warm-up of ~50-80 ms each, past the clock ramp
+        # measured first: their calls (hundreds of ms of GPU work) also bring
+        # the clock past its ramp before the headline's warm-up steps
+        paths = {
             "backward": run_backward(ffpa, W, "bwd", max(3, args.steps // 2), 5),
             "backward_causal": run_backward(ffpa, W, "bwd_causal", max(3, args.steps // 2), 8),
             "decode": run_decode(ffpa, W, args.steps, max(args.warmup, 50)),
         }
+    line = run_one(ffpa, W, args.workload, args.accum, args.steps, args.warmup,
+                   not args.no_cpu_baseline, args.cpu_heads)
+    if paths is not None:
+        line["paths"] = paths
     print(json.dumps(line), flush=True)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device="cuda").normal_()

@@ -150,14 +150,32 @@ def _dims(q, k, v):
             raise ValueError("tensors must be contiguous device tensors")
         if t.dtype != q.dtype:
             raise ValueError("q, k, v must share a dtype")
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
     return B, Hq, Hkv, Nq, Nkv, D
+
+
+def _check_tensor(t, name, shape, dtype, device):
+    """Host-side check of a tensor whose pointer goes to the kernels: they read
+    or write it as a dense row-major block of exactly `shape` in `dtype`."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (an expanded or strided view is not)")
 
 
 def _mask_args(mask, q, Nq, Nkv):
     if mask is None:
         return 0, 0
-    if mask.dtype != q.dtype or not mask.is_contiguous() or not mask.is_cuda:
-        raise ValueError("mask must be a contiguous device tensor in q's dtype")
+    if mask.dtype != q.dtype or not mask.is_contiguous() or not mask.is_cuda or \
+            mask.device != q.device:
+        raise ValueError("mask must be a contiguous tensor in q's dtype on q's device")
     rows = mask.numel() // Nkv if Nkv else 0
     if mask.numel() != rows * Nkv or rows not in (1, Nq):
         raise ValueError("mask must have Nkv columns and 1 or Nq rows ([1,1,1,Nkv] or [1,1,Nq,Nkv])")
@@ -172,17 +190,25 @@ def attention(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float
 
     B, Hq, Hkv, Nq, Nkv, D = _dims(q, k, v)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
+    if out is None:
+        o = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", q.shape, q.dtype, q.device)
+        o = out
     lse = None
-    if return_lse or lse_out is not None:
-        lse = (torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
-               if lse_out is None else lse_out)
+    if lse_out is not None:
+        _check_tensor(lse_out, "lse_out", (B, Hq, Nq), torch.float32, q.device)
+        lse = lse_out
+    elif return_lse:
+        lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
     mptr, mrows = _mask_args(mask, q, Nq, Nkv)
     dt = _dtype_code(q)
     ws_bytes = ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt)
     if workspace is not None and ws_bytes:
         if workspace.numel() * workspace.element_size() < ws_bytes:
             raise FFPAError(ERR_WORKSPACE, "workspace smaller than ffpa_attn_fwd_workspace_size()")
+        if not workspace.is_contiguous() or workspace.device != q.device:
+            raise ValueError("workspace must be a contiguous tensor on q's device")
         ws = workspace
     else:
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
@@ -195,30 +221,33 @@ def attention(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float
 
 
 def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None,
-                       scale: Optional[float] = None, store_ds: Optional[bool] = None):
+                       scale: Optional[float] = None, store_ds: bool = True,
+                       workspace_bytes: Optional[int] = None):
     """(dq, dk, dv) of attention on the current HIP stream; o, lse from ``attention``.
 
-    store_ds: True gives the call the workspace that keeps dS between the dK/dV
-    and dQ passes (ffpa_attn_bwd_workspace_size, 2 KiB per 32 x 32 block of
-    every head); False gives it the minimum (ffpa_attn_bwd_workspace_size_min),
-    and dQ recomputes S and dP. None (default): True when that workspace takes
-    at most half of the device memory free now."""
+    store_ds=True (default) gives the call ffpa_attn_bwd_workspace_size bytes:
+    the dK/dV pass keeps dS for the dQ pass, over chunks of kv heads whose dS
+    fits a bounded buffer. store_ds=False gives it the minimum
+    (ffpa_attn_bwd_workspace_size_min): dQ then recomputes S and dP.
+    workspace_bytes overrides either size (at least the minimum; the library
+    takes the stored-dS path when it holds K^T and one kv head's dS)."""
     import torch
 
     B, Hq, Hkv, Nq, Nkv, D = _dims(q, k, v)
+    _check_tensor(dout, "dout", q.shape, q.dtype, q.device)
+    _check_tensor(o, "o", q.shape, q.dtype, q.device)
+    _check_tensor(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     mptr, mrows = _mask_args(mask, q, Nq, Nkv)
     dt = _dtype_code(q)
-    if store_ds is None:
-        free, _ = torch.cuda.mem_get_info(q.device)
-        store_ds = ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt) <= free // 2
-    size = ffpa_attn_bwd_workspace_size if store_ds else ffpa_attn_bwd_workspace_size_min
-    ws_bytes = size(B, Hq, Hkv, Nq, Nkv, D, dt)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if workspace_bytes is None:
+        size = ffpa_attn_bwd_workspace_size if store_ds else ffpa_attn_bwd_workspace_size_min
+        workspace_bytes = size(B, Hq, Hkv, Nq, Nkv, D, dt)
+    ws = torch.empty(max(workspace_bytes, 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(ffpa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv,
                          Nq, Nkv, D, scale, int(causal), mptr, mrows, ACC_F32, dt, ws.data_ptr(),
-                         ws_bytes, stream))
+                         workspace_bytes, stream))
     return dq, dk, dv

@@ -2,6 +2,7 @@
 // The operation and its conventions are documented in include/ffpa_attn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <string>
 
@@ -90,7 +91,7 @@ DecLauncher dec_launcher(int D, int bf16) {
 // Keys a decode row sees: top-left causal leaves row 0 only key 0.
 int dec_kv_end(int Nkv, int causal) { return causal ? 1 : Nkv; }
 
-using BwdLauncher = hipError_t (*)(const ffpa::BwdArgs&, hipStream_t);
+using BwdLauncher = hipError_t (*)(const ffpa::BwdArgs&, int, hipStream_t);
 
 BwdLauncher bwd_launcher(int D, int bf16) {
   switch (D) {
@@ -222,8 +223,8 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     a.total_wg = (int)total;
     a.vt = workspace;
     a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
-    hipError_t e = ffpa::launch_fwd_vt(v, workspace, B * Hkv, Nkv, D, ffpa::kWideBc, (hipStream_t)stream);
-    if (e == hipSuccess) e = launch(a, (hipStream_t)stream);
+    if (!ffpa::fwd_vt_grid_ok(B * Hkv, Nkv, D)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
+    const hipError_t e = launch(a, (hipStream_t)stream);  // V^T pass, then the kernel
     if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return FFPA_OK;
   }
@@ -253,9 +254,8 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   a.total_wg = (int)total;
   a.vt = workspace;
   a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
-  hipError_t e =
-      vt ? ffpa::launch_fwd_vt(v, workspace, B * Hkv, Nkv, D, a.nkv_pad, (hipStream_t)stream) : hipSuccess;
-  if (e == hipSuccess) e = launch(a, lds, (hipStream_t)stream);
+  if (vt && !ffpa::fwd_vt_grid_ok(B * Hkv, Nkv, D)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
+  const hipError_t e = launch(a, lds, (hipStream_t)stream);  // [V^T pass,] the kernel
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return FFPA_OK;
 }
@@ -267,18 +267,34 @@ size_t ffpa_attn_bwd_workspace_size_min(int B, int Hq, int Hkv, int Nq, int Nkv,
   return 2 * (size_t)B * Hq * (size_t)bwd_nq_pad(Nq) * sizeof(float);
 }
 
-// bytes of the stored-dS path's K^T copy and dS blocks (after the row data)
+// bytes of the stored-dS path's K^T copy and of the dS blocks of one kv
+// head's query heads (after the row data)
 static size_t bwd_kt_bytes(int B, int Hkv, int Nkv, int D) {
   return (size_t)B * Hkv * D * (size_t)ffpa::fwd_nkv_pad(Nkv) * 2;
 }
-static size_t bwd_ds_bytes(int B, int Hq, int Nq, int Nkv) {
-  return (size_t)B * Hq * (size_t)((Nq + 31) / 32) * (size_t)((Nkv + 31) / 32) * 2048;
+static size_t bwd_ds_bytes_kvhead(int Hq, int Hkv, int Nq, int Nkv) {
+  return (size_t)(Hq / Hkv) * (size_t)((Nq + 31) / 32) * (size_t)((Nkv + 31) / 32) * 2048;
+}
+
+// dS budget of the size query: the dK/dV and dQ passes run over chunks of kv
+// heads whose dS fits it (at least one kv head's group per chunk).
+constexpr size_t kBwdDsBudget = size_t(1) << 30;
+
+static int bwd_default_chunk(int B, int Hq, int Hkv, int Nq, int Nkv) {
+  const size_t per = bwd_ds_bytes_kvhead(Hq, Hkv, Nq, Nkv);
+  const int64_t nkv = (int64_t)B * Hkv;
+  const int64_t fit = (int64_t)(kBwdDsBudget / per);
+  // equal chunks: the fewest that respect the budget, then the chunk size
+  // that spreads the heads evenly over them
+  const int64_t chunks = (nkv + std::max<int64_t>(fit, 1) - 1) / std::max<int64_t>(fit, 1);
+  return (int)((nkv + chunks - 1) / chunks);
 }
 
 size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {
   const size_t base = ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype);
-  if (base == 0 || Hkv < 1 || Nkv < 1 || D < 1) return base;
-  return base + bwd_kt_bytes(B, Hkv, Nkv, D) + bwd_ds_bytes(B, Hq, Nq, Nkv);
+  if (base == 0 || Hkv < 1 || Nkv < 1 || D < 1 || Hq % Hkv != 0) return base;
+  const int chunk = bwd_default_chunk(B, Hq, Hkv, Nq, Nkv);
+  return base + bwd_kt_bytes(B, Hkv, Nkv, D) + (size_t)chunk * bwd_ds_bytes_kvhead(Hq, Hkv, Nq, Nkv);
 }
 
 int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -299,8 +315,13 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   const size_t need = ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_bwd_workspace_size_min()");
-  // the whole size: dS is stored by the dK/dV pass and dQ reads it back
-  const bool store_ds = workspace_bytes >= ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  // room for K^T and the dS of at least one kv head's group: dS is stored by
+  // the dK/dV pass and dQ reads it back, over chunks of kv heads that fit
+  const size_t kt_b = bwd_kt_bytes(B, Hkv, Nkv, D);
+  const size_t ds_per = bwd_ds_bytes_kvhead(Hq, Hkv, Nq, Nkv);
+  const size_t room = workspace_bytes > need + kt_b ? workspace_bytes - need - kt_b : 0;
+  const bool store_ds = room >= ds_per;
+  const int chunk_kv = store_ds ? (int)std::min<size_t>((size_t)B * Hkv, room / ds_per) : 0;
   if (!(scale == scale)) return fail(FFPA_ERR_INVALID_ARG, "scale is NaN");
   BwdLauncher launch = bwd_launcher(D, dtype == FFPA_BF16);
   if (launch == nullptr)
@@ -329,15 +350,16 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   if (store_ds) {
     const int rq = ffpa::bwd_dq_ds_rows(D);
     const int64_t wg_dq_ds = (int64_t)B * Hq * ((Nq + rq - 1) / rq);
-    if (wg_dq_ds >= (int64_t(1) << 31)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
+    if (wg_dq_ds >= (int64_t(1) << 31) || !ffpa::fwd_vt_grid_ok(B * Hkv, Nkv, D))
+      return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
     a.wg_dq_ds = (int)wg_dq_ds;
     a.nqt = (Nq + 31) / 32;
     a.nkt = (Nkv + 31) / 32;
     a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
     a.kt = (char*)workspace + need;
-    a.ds = (char*)a.kt + bwd_kt_bytes(B, Hkv, Nkv, D);
+    a.ds = (char*)a.kt + kt_b;
   }
-  hipError_t e = launch(a, (hipStream_t)stream);
+  const hipError_t e = launch(a, chunk_kv, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return FFPA_OK;
 }

@@ -1105,37 +1105,87 @@ void bwd_dq_ds_kernel(BwdArgs a) {
   }
 }
 
-// Host launcher: the three kernels in order on `stream`.
+// Sets the dynamic-LDS limit of every kernel launch_bwd<D, BF16> may enqueue.
+// Called (through launch_bwd) before the first launch, so that a failure here
+// leaves nothing enqueued.
 template <int D, bool BF16>
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+hipError_t prepare_bwd() {
+  static const hipError_t e = [] {
+    hipError_t r = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, BF16, false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
+    if (r == hipSuccess)
+      r = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, BF16, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
+    if (r == hipSuccess)
+      r = hipFuncSetAttribute((const void*)bwd_dq_kernel<D, BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kBwdLds);
+    if (r == hipSuccess)
+      r = hipFuncSetAttribute((const void*)bwd_dq_ds_kernel<D, BF16>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kBwdDqDsLds);
+    return r;
+  }();
+  return e;
+}
+
+// The arguments of a chunk of n kv heads starting at flattened kv head f0
+// (f = b Hkv + hk): every tensor is [B, H, ...] contiguous, so heads f0 ..
+// f0 + n - 1 (and their query heads f g .. f g + g - 1) are one contiguous
+// run, and the chunk is the problem B = 1, Hkv = n, Hq = n g on offset
+// pointers. The dS buffer is not offset: each chunk reuses it from the start.
+template <int D>
+BwdArgs bwd_chunk_args(const BwdArgs& a, int f0, int n) {
+  const int g = a.Hq / a.Hkv;
+  const size_t fq = (size_t)f0 * g;
+  BwdArgs c = a;
+  c.q = (const char*)a.q + fq * a.Nq * D * 2;
+  c.o = (const char*)a.o + fq * a.Nq * D * 2;
+  c.dout = (const char*)a.dout + fq * a.Nq * D * 2;
+  c.dq = (char*)a.dq + fq * a.Nq * D * 2;
+  c.lse = a.lse + fq * a.Nq;
+  c.delta = a.delta + fq * a.nq_pad;
+  c.lse2 = a.lse2 + fq * a.nq_pad;
+  c.k = (const char*)a.k + (size_t)f0 * a.Nkv * D * 2;
+  c.v = (const char*)a.v + (size_t)f0 * a.Nkv * D * 2;
+  c.dk = (char*)a.dk + (size_t)f0 * a.Nkv * D * 2;
+  c.dv = (char*)a.dv + (size_t)f0 * a.Nkv * D * 2;
+  c.kt = (char*)a.kt + (size_t)f0 * D * a.nkv_pad * 2;
+  c.B = 1;
+  c.Hkv = n;
+  c.Hq = n * g;
+  const int rows = bwd_rows_per_wg(D), rq = bwd_dq_ds_rows(D);
+  c.wg_dkdv = n * ((a.Nkv + rows - 1) / rows);
+  c.wg_dq = n * g * ((a.Nq + rows - 1) / rows);
+  c.wg_dq_ds = n * g * ((a.Nq + rq - 1) / rq);
+  return c;
+}
+
+// Host launcher: the kernels in order on `stream`. With the stored-dS path
+// (a.ds set) the dK/dV and dQ passes run per chunk of `chunk_kv` kv heads
+// (the dS buffer holds one chunk); otherwise once over the whole problem.
+// The caller has checked the grid sizes.
+template <int D, bool BF16>
+hipError_t launch_bwd(const BwdArgs& a, int chunk_kv, hipStream_t stream) {
+  const hipError_t pe = prepare_bwd<D, BF16>();
+  if (pe != hipSuccess) return pe;
   const bool rowmask = a.mask != nullptr && a.mask_rows > 1;
   auto kdkdv = rowmask ? bwd_dkdv_kernel<D, BF16, true> : bwd_dkdv_kernel<D, BF16, false>;
-  auto kdq = bwd_dq_kernel<D, BF16>;
-  static const hipError_t attr1 = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, BF16, false>,
-                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
-  static const hipError_t attr1m = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, BF16, true>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
-  static const hipError_t attr2 =
-      hipFuncSetAttribute((const void*)kdq, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
-  if (attr1 != hipSuccess) return attr1;
-  if (attr1m != hipSuccess) return attr1m;
-  if (attr2 != hipSuccess) return attr2;
   const int64_t rows = (int64_t)a.B * a.Hq * a.nq_pad;
   hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
   if (a.ds != nullptr) {
-    // stored-dS path: K^T for the dQ pass, dK/dV (which writes dS), dQ = scale dS K
-    auto kdqs = bwd_dq_ds_kernel<D, BF16>;
-    static const hipError_t attr3 =
-        hipFuncSetAttribute((const void*)kdqs, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdDqDsLds);
-    if (attr3 != hipSuccess) return attr3;
+    // stored-dS path: K^T for the dQ pass, then per chunk dK/dV (which writes
+    // the chunk's dS) and dQ = scale dS K
     const hipError_t e = launch_fwd_vt(a.k, a.kt, a.B * a.Hkv, a.Nkv, D, 32, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kdkdv, dim3(a.wg_dkdv), dim3(256), kBwdLds, stream, a);
-    hipLaunchKernelGGL(kdqs, dim3(a.wg_dq_ds), dim3(256), kBwdDqDsLds, stream, a);
+    const int nkv = a.B * a.Hkv;
+    for (int f0 = 0; f0 < nkv; f0 += chunk_kv) {
+      const BwdArgs c = bwd_chunk_args<D>(a, f0, min(chunk_kv, nkv - f0));
+      hipLaunchKernelGGL(kdkdv, dim3(c.wg_dkdv), dim3(256), kBwdLds, stream, c);
+      hipLaunchKernelGGL((bwd_dq_ds_kernel<D, BF16>), dim3(c.wg_dq_ds), dim3(256), kBwdDqDsLds, stream, c);
+    }
     return hipGetLastError();
   }
   hipLaunchKernelGGL(kdkdv, dim3(a.wg_dkdv), dim3(256), kBwdLds, stream, a);
-  hipLaunchKernelGGL(kdq, dim3(a.wg_dq), dim3(256), kBwdLds, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3(a.wg_dq), dim3(256), kBwdLds, stream, a);
   return hipGetLastError();
 }
 

@@ -2,6 +2,6 @@
 #include "bwd.hpp"
 
 namespace ffpa {
-template hipError_t launch_bwd<128, false>(const BwdArgs&, hipStream_t);
-template hipError_t launch_bwd<128, true>(const BwdArgs&, hipStream_t);
+template hipError_t launch_bwd<128, false>(const BwdArgs&, int, hipStream_t);
+template hipError_t launch_bwd<128, true>(const BwdArgs&, int, hipStream_t);
 }  // namespace ffpa

@@ -995,13 +995,19 @@ void fwd_prefill_kernel(FwdArgs a) {
 }
 
 // Host launcher. lds_bytes = tile buffers + key-bias bytes (the caller checks
-// <= 160 KiB).
+// <= 160 KiB). With VT the transposed copy of V is written into a.vt first.
+// The kernel's LDS limit is set before anything is enqueued, so a failure
+// there leaves the stream untouched.
 template <int D, bool BF16, bool ACC16, bool VT>
 hipError_t launch_fwd_prefill(const FwdArgs& a, size_t lds_bytes, hipStream_t stream) {
   auto kern = fwd_prefill_kernel<D, BF16, ACC16, VT>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;
+  if constexpr (VT) {
+    const hipError_t e = launch_fwd_vt(a.v, const_cast<void*>(a.vt), a.B * a.Hkv, a.Nkv, D, a.nkv_pad, stream);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(kern, dim3(a.total_wg), dim3(256), lds_bytes, stream, a);
   return hipGetLastError();
 }

@@ -50,6 +50,11 @@ inline size_t fwd_vt_bytes(int B, int Hkv, int Nkv, int D) {
   return (size_t)B * Hkv * D * (size_t)fwd_nkv_pad(Nkv) * 2;
 }
 
+// Whether the grid of the transpose fits (checked by the callers before any launch).
+inline bool fwd_vt_grid_ok(int BH, int Nkv, int D) {
+  return (long long)BH * (fwd_nkv_pad(Nkv) / 64) * (D / 64) < (1LL << 31);
+}
+
 // Enqueues the transpose of v [B*Hkv, Nkv, D] (16-bit elements, D a multiple
 // of 64) into vt [B*Hkv, nkv_pad / kb, D, kb]; kb is a multiple of 32 that
 // divides nkv_pad (kb = nkv_pad: one block, rows of all positions).

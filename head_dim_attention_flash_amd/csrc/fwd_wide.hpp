@@ -420,12 +420,16 @@ void fwd_wide_kernel(FwdArgs a) {
   }
 }
 
+// Host launcher: the transposed copy of V (blocks of 32 keys) into a.vt, then
+// the kernel. The LDS limit is set before anything is enqueued.
 template <int D, bool BF16>
 hipError_t launch_fwd_wide(const FwdArgs& a, hipStream_t stream) {
   auto kern = fwd_wide_kernel<D, BF16>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);
   if (attr != hipSuccess) return attr;
+  const hipError_t e = launch_fwd_vt(a.v, const_cast<void*>(a.vt), a.B * a.Hkv, a.Nkv, D, kWideBc, stream);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(a.total_wg), dim3(256), kWideLds, stream, a);
   return hipGetLastError();
 }

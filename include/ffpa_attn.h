@@ -131,16 +131,24 @@ size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
  * contributions of all query heads that share it. accum_dtype must be
  * FFPA_ACC_F32. workspace: 16-byte aligned, at least
  * ffpa_attn_bwd_workspace_size_min(...) bytes (delta_i = sum_d dO_id O_id
- * and lse_i log2(e) per query row, rows padded to a multiple of 64). Given
- * ffpa_attn_bwd_workspace_size(...) bytes or more, the call also keeps a
- * transposed copy of K and the bf16/fp16 dS of every visible 32 x 32 block
- * there (B * Hq * ceil(Nq/32) * ceil(Nkv/32) * 2 KiB: 4 GiB at B = 1,
- * Hq = 32, N = 8192): the dK/dV pass writes dS and the dQ pass reads it
- * back (one product instead of three). With less, dQ recomputes S and dP.
- * Both give the same gradients up to rounding. Kernels enqueued: the delta
- * pass, [the K transpose], dK/dV, dQ. Built for D a multiple of 64 up to
- * 1024, with either mask shape; other valid shapes (D not a multiple of 64)
- * return FFPA_ERR_UNSUPPORTED.
+ * and lse_i log2(e) per query row, rows padded to a multiple of 64). The
+ * path is chosen by the workspace size alone:
+ *  - with room beyond the minimum for a transposed copy of K (the size of K,
+ *    keys padded to 64) and the dS blocks of at least one kv head's query
+ *    heads (g * ceil(Nq/32) * ceil(Nkv/32) * 2 KiB, g = Hq / Hkv), the dK/dV
+ *    pass stores dS (bf16/fp16, per 32 x 32 block) and the dQ pass reads it
+ *    back (one product instead of three). Both passes run over chunks of as
+ *    many kv heads as the dS room holds, reusing it chunk after chunk;
+ *  - with less, dQ recomputes S and dP.
+ * ffpa_attn_bwd_workspace_size(...) gives the stored-dS path a dS buffer of at
+ * most 1 GiB (or one kv head's group, if that is larger), in equal chunks:
+ * at B = 1, Hq = Hkv = 32, N = 8192, D = 512 that is 8 heads of 128 MiB.
+ * Every path and chunk size gives the same gradients up to rounding order;
+ * a given workspace size always gives the same bits. Kernels enqueued: the
+ * delta pass, then [the K transpose, then per chunk: dK/dV, dQ] or
+ * [dK/dV, dQ]. Built for D a multiple of 64 up to 1024, with either mask
+ * shape; other valid shapes (D not a multiple of 64) return
+ * FFPA_ERR_UNSUPPORTED.
  * The gradients are those of sum(dout * O) ("FFPA Attention Benchmark",
  * "More Benchmark": the backward counted as 5 GEMMs).
  */
@@ -150,7 +158,7 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
                   const void* mask, int mask_rows, int accum_dtype, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace ffpa_attn_bwd runs fastest with (dS stored) for these sizes. */
+/* Bytes of workspace for the stored-dS path with its default, bounded dS buffer. */
 size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
 
 /* The least workspace ffpa_attn_bwd accepts (dQ then recomputes S and dP). */

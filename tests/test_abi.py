@@ -127,8 +127,18 @@ def test_workspace_queries_are_pure_functions():
 def test_backward_workspace_sizes():
     # the minimum: delta and lse * log2(e) per query row, rows padded to 64
     assert ffpa.ffpa_attn_bwd_workspace_size_min(2, 4, 2, 100, 70, 320, 0) == 2 * 2 * 4 * 128 * 4
-    # stored dS: + K^T (keys padded to 64) + 2 KiB per 32 x 32 block of every head
+    # stored dS: + K^T (keys padded to 64) + 2 KiB per 32 x 32 block of the heads of
+    # one chunk; small problems are one chunk
     full = ffpa.ffpa_attn_bwd_workspace_size(2, 4, 2, 100, 70, 320, 0)
     assert full == 2 * 2 * 4 * 128 * 4 + 2 * 2 * 320 * 128 * 2 + 2 * 4 * 4 * 3 * 2048
+    # 8K: 128 MiB of dS per head, at most 1 GiB of it: 4 chunks of 8 heads
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 32, 8192, 8192, 512, 1) == (
-        2 * 32 * 8192 * 4 + 32 * 512 * 8192 * 2 + 32 * 256 * 256 * 2048)
+        2 * 32 * 8192 * 4 + 32 * 512 * 8192 * 2 + 8 * 256 * 256 * 2048)
+    # 16K: 512 MiB per head, 2 per chunk; GQA 32/8: a kv head's group is 4 query heads
+    assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 32, 16384, 16384, 512, 0) == (
+        2 * 32 * 16384 * 4 + 32 * 512 * 16384 * 2 + 2 * 512 * 512 * 2048)
+    assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 8, 16384, 16384, 512, 0) == (
+        2 * 32 * 16384 * 4 + 8 * 512 * 16384 * 2 + 1 * 4 * 512 * 512 * 2048)
+    # 33 heads of 128 MiB: 5 chunks of 7 (the fewest within 1 GiB, spread evenly)
+    assert ffpa.ffpa_attn_bwd_workspace_size(1, 33, 33, 8192, 8192, 64, 0) == (
+        2 * 33 * 8192 * 4 + 33 * 64 * 8192 * 2 + 7 * 256 * 256 * 2048)

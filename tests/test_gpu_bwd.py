@@ -186,3 +186,43 @@ def test_backward_causal_keys_past_queries_get_zero(lib):
     torch.cuda.synchronize()
     assert torch.count_nonzero(dk[:, :, Nq:]).item() == 0
     assert torch.count_nonzero(dv[:, :, Nq:]).item() == 0
+
+
+@pytest.mark.parametrize("shape,causal,mask_rows", [
+    ((2, 6, 3, 150, 170, 512), False, 0),   # 6 kv heads over two batches: chunks cross b
+    ((1, 8, 2, 100, 130, 320), True, 1),    # GQA g = 4, causal, key bias
+    ((1, 3, 3, 70, 90, 1024), False, 70),   # D above 512, per-query mask
+])
+def test_backward_chunks_give_the_same_bits(lib, shape, causal, mask_rows):
+    """The stored-dS path runs the dK/dV and dQ passes over chunks of kv heads
+    that fit the dS room of the workspace. Chunks of 1 and 2 kv heads (room for
+    exactly that much dS) must give the bits of the one-chunk default, and the
+    default must match the oracle."""
+    B, Hq, Hkv, Nq, Nkv, D = shape
+    dtype = "bf16"
+    q, k, v, do, mask = _inputs(90 + sum(shape), B, Hq, Hkv, Nq, Nkv, D, dtype, mask_rows > 0,
+                                mask_rows=max(mask_rows, 1))
+    q, k, v, do = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    mk = None if mask is None else mask.cuda()
+    scale = 1.0 / math.sqrt(D)
+    o, lse = lib.attention(q, k, v, causal=causal, mask=mk, scale=scale, return_lse=True)
+    ref = lib.attention_backward(do, q, k, v, o, lse, causal=causal, mask=mk, scale=scale)
+    dt = lib.BF16
+    base = lib.ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dt)
+    kt = B * Hkv * D * ((Nkv + 63) // 64 * 64) * 2
+    per = (Hq // Hkv) * ((Nq + 31) // 32) * ((Nkv + 31) // 32) * 2048
+    full = lib.ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt)
+    assert full == base + kt + B * Hkv * per  # small problems: one chunk
+    for chunk in (1, 2):
+        print(f"case {shape} causal={causal} mask_rows={mask_rows} chunk={chunk}", flush=True)
+        got = lib.attention_backward(do, q, k, v, o, lse, causal=causal, mask=mk, scale=scale,
+                                     workspace_bytes=base + kt + chunk * per + per - 1)
+        torch.cuda.synchronize()
+        for nm, a_, b_ in zip(("dQ", "dK", "dV"), got, ref):
+            assert torch.equal(a_, b_), f"chunk {chunk}: {nm} differs from the one-chunk result"
+    m2 = None if mask is None else mask.view(-1, Nkv)
+    qc, kc, vc, doc = q.cpu(), k.cpu(), v.cpu(), do.cpu()
+    refs = attn_bwd(qc, kc, vc, doc, scale, causal=causal, mask=m2)
+    bounds = _rounding_bounds(qc, kc, vc, doc, scale, causal, m2, refs, dtype)
+    for nm, g_, r_ in zip(("dQ", "dK", "dV"), ref, refs):
+        _compare(nm, g_, r_, dtype, f"chunks-{shape}", bounds[nm])
