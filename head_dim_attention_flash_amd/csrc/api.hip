@@ -12,6 +12,7 @@
 #include "fwd_prefill.hpp"
 #include "fwd_vt.hpp"
 #include "fwd_wide.hpp"
+#include "fwd_wide16.hpp"
 
 namespace {
 
@@ -56,10 +57,14 @@ FwdLauncher fwd_launcher(int D, int bf16, int acc16, bool vt, size_t* ring_bytes
 
 using WideLauncher = hipError_t (*)(const ffpa::FwdArgs&, hipStream_t);
 
-WideLauncher wide_launcher(int D, int bf16) {
+// fp32 output accumulator: fwd_wide_kernel (64 rows per workgroup); fp16:
+// fwd_wide16_kernel (wide16_rows<D>() rows per workgroup, 128 up to D = 768)
+WideLauncher wide_launcher(int D, int bf16, int acc16, int* rows) {
   switch (D) {
-#define FFPA_CASE(DD) \
-  case DD:            \
+#define FFPA_CASE(DD)                                                                       \
+  case DD:                                                                                  \
+    *rows = acc16 ? ffpa::wide16_rows<DD>() : 64;                                           \
+    if (acc16) return bf16 ? ffpa::launch_fwd_wide16<DD, true> : ffpa::launch_fwd_wide16<DD, false>; \
     return bf16 ? ffpa::launch_fwd_wide<DD, true> : ffpa::launch_fwd_wide<DD, false>;
     FFPA_CASE(576) FFPA_CASE(640) FFPA_CASE(704) FFPA_CASE(768)
     FFPA_CASE(832) FFPA_CASE(896) FFPA_CASE(960) FFPA_CASE(1024)
@@ -206,7 +211,8 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
 
   if (D > 512) {
     // head dimensions above 512: D split across wave pairs
-    WideLauncher launch = wide_launcher(D, dtype == FFPA_BF16);
+    int rows = 64;
+    WideLauncher launch = wide_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, &rows);
     if (launch == nullptr)
       return fail(FFPA_ERR_UNSUPPORTED, "for Nq > 1, D above 512 must be a multiple of 64");
     ffpa::FwdArgs a{};
@@ -217,7 +223,7 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
     a.bias_lds = 0;
     a.causal = causal;
     a.scale_log2 = scale * ffpa::kLog2e;
-    a.n_qtiles = (Nq + 63) / 64;
+    a.n_qtiles = (Nq + rows - 1) / rows;
     const int64_t total = (int64_t)B * Hq * a.n_qtiles;
     if (total >= (int64_t(1) << 31)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
     a.total_wg = (int)total;

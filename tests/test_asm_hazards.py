@@ -74,3 +74,12 @@ def test_checker_flags_valu_sgpr_write_before_vector_memory():
     ok = ["v_readlane_b32 s1, v82, 3", "s_nop 4",
           "buffer_load_dwordx4 v2, s[36:39], s1 offen lds", "s_endpgm"]
     assert H.check_kernel(ok) == []
+
+
+def test_scratch_is_rejected_but_agpr_parking_is_not():
+    meta = ("  - .agpr_count: 12\n    .name: kern_a\n    .private_segment_fixed_size: 16\n"
+            "    .vgpr_spill_count: 3\n"
+            "  - .agpr_count: 250\n    .name: kern_b\n    .private_segment_fixed_size: 0\n"
+            "    .vgpr_spill_count: 2\n")
+    out = H.scratch_users(meta)
+    assert len(out) == 1 and out[0].startswith("kern_a")

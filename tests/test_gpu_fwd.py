@@ -108,6 +108,8 @@ CASES = [
     (1, 2, 2, 70, 20, 832),     # D above 512, one partial key tile
     (1, 2, 1, 90, 1, 896),      # D above 512, a single key
     (1, 2, 2, 33, 64, 960),     # D above 512, two whole key tiles
+    (1, 2, 2, 300, 250, 704),   # fp16 accumulation: three 128-row blocks, the last ragged
+    (1, 4, 2, 129, 96, 576),    # fp16 accumulation: one row past a 128-row block
 ]
 
 
@@ -141,7 +143,7 @@ def test_forward_matches_oracle(lib, shape, dtype, accum, variant):
     _compare(o, lse, q, k, v, scale, causal, mask, dtype, accum, f"{shape}-{dtype}-{accum}-{variant}")
 
 
-@pytest.mark.parametrize("D", [64, 320, 512])
+@pytest.mark.parametrize("D", [64, 320, 512, 704, 1024])
 @pytest.mark.parametrize("accum", ["f32", "f16"])
 def test_zero_query_gives_mean_and_log_n(lib, D, accum):
     _, k, v, _ = _inputs(7, 1, 2, 2, 8, 300, D, "fp16")
@@ -152,16 +154,17 @@ def test_zero_query_gives_mean_and_log_n(lib, D, accum):
     assert np.abs(to_f64(lse) - math.log(300)).max() <= 1e-5
 
 
+@pytest.mark.parametrize("D", [320, 768, 960])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("accum", ["f32", "f16"])
-def test_single_key_returns_v0_exactly(lib, dtype, accum):
-    q, k, v, _ = _inputs(8, 1, 2, 2, 150, 1, 320, dtype)
+def test_single_key_returns_v0_exactly(lib, D, dtype, accum):
+    q, k, v, _ = _inputs(8, 1, 2, 2, 150, 1, D, dtype)
     o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), accum=accum)
     want_o = v
     if accum == "f16" and dtype == "bf16":  # the fp16 accumulator holds V rounded to fp16
         want_o = v.to(torch.float16).to(torch.bfloat16)
     assert torch.equal(o.cpu(), want_o.expand_as(o)), "Nkv = 1 must return V[0] bit-exactly"
-    scale = float(np.float32(1.0 / math.sqrt(320)))
+    scale = float(np.float32(1.0 / math.sqrt(D)))
     want = scale * np.einsum("bhnd,bhd->bhn", to_f64(q), to_f64(k)[:, :, 0])
     np.testing.assert_allclose(to_f64(lse), want, atol=2e-4, rtol=0)
 
@@ -200,7 +203,7 @@ def test_deterministic(lib):
 
 
 @pytest.mark.parametrize("slope", [0.05, 0.5])
-@pytest.mark.parametrize("D", [128, 512, 1024])
+@pytest.mark.parametrize("D", [128, 512, 640, 1024])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("accum", ["f32", "f16"])
 def test_growing_row_max(lib, slope, D, dtype, accum):
