@@ -11,23 +11,25 @@
 // pair of elements per tile), so |O| never exceeds max |V|.
 //
 // Why a kernel of its own: the fp16 O takes half the registers of the fp32
-// one, and what bounds the wide forward is the feed of staged K and V^T
-// bytes from L2 into each workgroup's LDS, which shrinks with the query rows
-// a workgroup serves. Up to D = 768 a wave here holds two row blocks of 32
-// queries (Q and O of 64 rows for its half of D: W / 2 + W / 2 registers,
-// W = D / 2), so a workgroup serves 128 rows per staged byte, twice the fp32
-// kernel's 64, and every K or V^T fragment read from LDS feeds two MFMAs.
-// Above D = 768 two row blocks do not fit beside the per-tile products, and
-// a wave holds one row block (64 rows per workgroup).
+// one. Up to D = 768 a wave then holds Q and O of its 32 rows for all of D
+// (D / 4 + D / 4 registers), like the prefill kernel does up to D = 512 with
+// an fp32 O, and a workgroup serves 128 rows: per staged K and V^T byte twice
+// the rows of the fp32 wide kernel (what bounds that one is the feed of
+// staged bytes from L2), no partial scores to swap between waves, and one
+// softmax per row. Above D = 768 Q and O of 32 rows exceed a wave's
+// registers, and D is split across wave pairs as in fwd_wide.hpp (64 rows
+// per workgroup; per tile the pair swaps its partial S^T through LDS and
+// adds, a + b being the same in either order, so both waves take identical
+// softmax decisions).
 //
-// Layout (as fwd_wide.hpp): 4 waves = 2 row groups x 2 halves of D; a K tile
-// is 32 keys in two dense half-tiles, a V^T tile D rows of 32 keys from the
-// transposed copy in blocks of 32 keys; per tile each wave computes the
-// partial S^T over its half, swaps it with the wave holding the other half of
-// the same rows through LDS and adds (a + b is the same in either order, so
-// both waves take identical softmax decisions), rescales, and accumulates
-// O^T_half += V_half^T P^T into per-tile fp32 products that are folded into
-// the fp16 O while the next products run.
+// Per 32-key tile each wave computes S^T over its part of D (two MFMA chains,
+// even and odd k-steps), [swaps and adds,] rescales, and accumulates
+// O^T += V^T P^T into per-tile fp32 products of two d-blocks at a time, folded
+// into the fp16 O while the next two d-blocks' products run. Staging as in
+// fwd_wide.hpp: a K tile of 32 keys as dense rows (one part-tile per part of
+// D), a V^T tile of D rows of 32 keys from the transposed copy in blocks of
+// 32 keys; the copies of V(j) are spread over the K(j) phase and those of
+// K(j + 1) over the V(j) phase.
 #pragma once
 
 #include "ffpa_common.hpp"
@@ -36,31 +38,38 @@
 
 namespace ffpa {
 
-// row blocks of 32 queries per wave
+// parts of D per row block: 1 (a wave holds all of D for its rows) or 2 (a
+// wave pair splits D)
 template <int D>
-constexpr int wide16_rb() {
-  return D <= 768 ? 2 : 1;
+constexpr int wide16_nh() {
+  return D <= 768 ? 1 : 2;
 }
-// query rows per workgroup
+// query rows per workgroup: 4 / NH row blocks of 32
 template <int D>
 constexpr int wide16_rows() {
-  return 64 * wide16_rb<D>();
+  return (4 / wide16_nh<D>()) * 32;
 }
 // LDS bytes of one staged K or V^T tile (32 keys x D)
 template <int D>
 constexpr int wide16_tile() {
   return kWideBc * D * 2;
 }
-// bytes per row of the epilogue's staging: whole groups of 16 granules
+// The epilogue stages each wave's 32 rows x W columns (W = D / NH) through
+// LDS in one pass, or two passes of W / 2 columns when W > 512; a staged row
+// takes whole groups of 16 granules.
+template <int D>
+constexpr int wide16_epi_passes() {
+  return D / wide16_nh<D>() > 512 ? 2 : 1;
+}
 template <int D>
 constexpr int wide16_pitch() {
-  return (D / 16 + 15) / 16 * 256;
+  return (D / wide16_nh<D>() / wide16_epi_passes<D>() / 8 + 15) / 16 * 256;
 }
-// LDS: two tiles and the score swap area, or the epilogue's staging of 32
-// rows per wave if that is larger
+// LDS: two tiles and, NH = 2, the score swap area; or the epilogue's staging
+// if that is larger
 template <int D>
 constexpr int wide16_lds() {
-  constexpr int loop = 2 * wide16_tile<D>() + 4 * wide16_rb<D>() * kWideXchg;
+  constexpr int loop = 2 * wide16_tile<D>() + (wide16_nh<D>() == 2 ? 4 * kWideXchg : 0);
   constexpr int epi = 4 * 32 * wide16_pitch<D>();
   return loop > epi ? loop : epi;
 }
@@ -71,33 +80,30 @@ void fwd_wide16_kernel(FwdArgs a) {
   static_assert(D % 64 == 0 && D > 512 && D <= 1024, "D must be a multiple of 64 in (512, 1024]");
   using E = Elem<BF16>;
   using V8 = typename E::vec8;
-  constexpr int RB = wide16_rb<D>();
+  constexpr int NH = wide16_nh<D>();
   constexpr int ROWS = wide16_rows<D>();
-  constexpr int W = D / 2;                 // elements per half
-  constexpr int SG = W / 8;                // granules per half row (36 .. 64)
-  constexpr int HALF = kWideBc * SG * 16;  // bytes of one dense K half-tile
-  constexpr int NS = W / 16;               // k-steps of the partial product
-  constexpr int NDB = W / 32;              // output d-blocks of the half
+  constexpr int W = D / NH;                // elements per part of D
+  constexpr int SG = W / 8;                // granules per part of a row (52 .. 96)
+  constexpr int PART = kWideBc * SG * 16;  // bytes of one dense K part-tile
+  constexpr int NS = W / 16;               // k-steps of the (partial) product
+  constexpr int NDB = W / 32;              // output d-blocks of the part
   constexpr int TILE = wide16_tile<D>();
   constexpr int KB = 0, VB = TILE, XB = 2 * TILE;
-  // fragments read ahead (registers are short with two row blocks)
-  constexpr int kKAhead = RB == 2 ? (D > 640 ? 4 : 6) : 8;
-  constexpr int kVAhead = RB == 2 && D > 704 ? 2 : 4;
-  constexpr int NKC = SG / 4, NVC = D / 64;  // copy instructions per wave per tile: K, V^T
-  // P V products: unit u = (d-block, row block); units go in groups of two
-  // (the same d-block for both row blocks when RB = 2, two d-blocks when
-  // RB = 1), each group's MFMAs in the order (u0, t2 0), (u1, t2 0), (u0, t2 1),
-  // (u1, t2 1), so that consecutive MFMAs write different accumulators.
-  constexpr int NU = NDB * RB;
-  constexpr int NG = (NU + 1) / 2;
-  constexpr int NSV = 2 * NU;  // MFMA steps of the V phase
+  constexpr int kKAhead = 8;               // K fragments read ahead
+  constexpr int kVAhead = 4;               // V^T fragments read ahead
+  constexpr int NKC = D / 64, NVC = D / 64;  // copy instructions per wave per tile: K, V^T
+  // P V products go in groups of two d-blocks (the last group alone when NDB
+  // is odd); a group's MFMAs run (d0, t2 0), (d1, t2 0), (d0, t2 1), (d1, t2 1),
+  // so that consecutive MFMAs write different accumulators
+  constexpr int NSV = 2 * NDB;  // MFMA steps of the V phase
+  static_assert(NS % 2 == 0, "two score chains of equal length");
 
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = wave >> 1, hf = wave & 1;
+  const int rg = wave / NH, hf = wave % NH;  // row block, part of D
 
   // ---- workgroup -> (b, h, block of ROWS rows)
   const int n_qb = (a.Nq + ROWS - 1) / ROWS;
@@ -108,7 +114,7 @@ void fwd_wide16_kernel(FwdArgs a) {
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
   const int q0 = qb * ROWS;
-  const int qg = q0 + 32 * RB * rg;  // first row of this wave; block r starts at qg + 32 r
+  const int qw = q0 + 32 * rg;  // first row of this wave
 
   const size_t kv_off = ((size_t)(b * a.Hkv + hk) * a.Nkv) * D * 2;
   const uint32_t kv_bytes = (uint32_t)a.Nkv * D * 2;  // rows >= Nkv read as zeros
@@ -123,37 +129,43 @@ void fwd_wide16_kernel(FwdArgs a) {
   const bool has_mask = a.mask_rows > 0;
   const uint16_t* mk = (const uint16_t*)a.mask;
 
-  // ---- Q^T halves in registers: lane holds Q[qg + 32 r + l % 32][W hf + 16 s + 8 (l / 32) .. +7]
-  u32x4 qf[RB][NS];
+  // ---- Q^T part in registers: lane holds Q[qw + l % 32][W hf + 16 s + 8 (l / 32) .. +7]
+  u32x4 qf[NS];
   {
     const typename E::scalar* Q = (const typename E::scalar*)a.q + ((size_t)(b * a.Hq + h) * a.Nq) * D;
+    const int qrow = min(qw + (lane & 31), a.Nq - 1);
+    const u32x4* qp = (const u32x4*)(Q + (size_t)qrow * D + W * hf + 8 * (lane >> 5));
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int qrow = min(qg + 32 * r + (lane & 31), a.Nq - 1);
-      const u32x4* qp = (const u32x4*)(Q + (size_t)qrow * D + W * hf + 8 * (lane >> 5));
-#pragma unroll
-      for (int s = 0; s < NS; ++s) qf[r][s] = qp[2 * s];
-    }
+    for (int s = 0; s < NS; ++s) qf[s] = qp[2 * s];
   }
   // compiler-visible: later waits then never hold for the copies in flight
   wait_vmcnt0_visible();
 
-  // ---- copies (the layouts of fwd_wide.hpp): K instruction n (n = wave + 4 r,
-  // r < SG / 4) fills 1 KiB of a dense half-tile, V^T instruction n (r < D / 64)
-  // fills V^T rows 16 n .. 16 n + 15
-  auto k_copy = [&](int tile, int r, int ln) {
+  // ---- copies (the layouts of fwd_wide.hpp). K instruction n (n = wave + 4 r,
+  // r < D / 64) fills 1 KiB of a dense part-tile: part n / (SG / 2), slots
+  // 64 (n % (SG / 2)) + lane, slot s holding granule dense_pos(row, s % SG) of
+  // row s / SG. V^T instruction n (r < D / 64) fills V^T rows 16 n .. 16 n + 15.
+  // The lane's offset within a tile for each of its K copies is computed once
+  // (a division by the row pitch and the swizzle: ~15 VALU instructions per
+  // copy and tile otherwise) and kept in spare AGPRs; a copy then costs a
+  // register read and the tile's offset.
+  uint32_t koff[NKC];
+#pragma unroll
+  for (int r = 0; r < NKC; ++r) {
     const int n = wave + 4 * r;
-    const int half = n / (SG / 2), nn = n % (SG / 2);
-    const int sl = 64 * nn + ln;
+    const int part = n / (SG / 2), nn = n % (SG / 2);
+    const int sl = 64 * nn + lane;
     const int row = sl / SG, g = dense_pos(SG, row, sl % SG);
-    const uint32_t voff = (uint32_t)((half * W + 8 * g) * 2) + (uint32_t)(tile * kWideBc + row) * (D * 2);
-    dma16(Kr, voff, smem + KB + half * HALF + nn * 1024);
+    koff[r] = (uint32_t)((part * W + 8 * g) * 2) + (uint32_t)row * (D * 2);
+  }
+  auto k_copy = [&](int tile, int r) {
+    const int n = wave + 4 * r;
+    const int part = n / (SG / 2), nn = n % (SG / 2);
+    dma16(Kr, koff[r] + (uint32_t)(tile * kWideBc) * (D * 2), smem + KB + part * PART + nn * 1024);
   };
   auto issue_k_tile = [&](int tile) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int r = 0; r < NKC; ++r) k_copy(tile, r, ln);
+    for (int r = 0; r < NKC; ++r) k_copy(tile, r);
   };
   auto vt_lane_offset = [&](int ln) {
     return (uint32_t)(ln >> 2) * vt_row + (uint32_t)(((ln & 3) ^ ((ln >> 4) & 3)) << 4);
@@ -167,9 +179,9 @@ void fwd_wide16_kernel(FwdArgs a) {
     const int r = ln & 31, hh = ln >> 5;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      kx[c] = (uint32_t)(KB + hf * HALF + r * (SG * 16) + (dense_pos(SG, r, 2 * c + hh) << 4));
+      kx[c] = (uint32_t)(KB + hf * PART + r * (SG * 16) + (dense_pos(SG, r, 2 * c + hh) << 4));
   };
-  // V^T fragment (A of O^T_half) for d-block db and 16-key step t2: row
+  // V^T fragment (A of O^T) for d-block db and 16-key step t2: row
   // W hf + 32 db + l % 32 of the tile, logical granule 2 t2 + l / 32 (vt_key order)
   auto v_bases = [&](int ln, uint32_t* vx) {
     const int r = ln & 31, hh = ln >> 5;
@@ -178,34 +190,31 @@ void fwd_wide16_kernel(FwdArgs a) {
       vx[t2] = (uint32_t)(VB + (W * hf + r) * 64 + (((2 * t2 + hh) ^ ((r >> 2) & 3)) << 4));
   };
 
-  // ---- fp16 output accumulator: block (r, db) holds O^T[32 db .. +31][row]
-  // of the lane's row as 16 packed fp16 (two u32x4: elements 0-7, 8-15 of the
-  // MFMA C layout)
-  u32x4 o16[RB][NDB][2];
+  // ---- fp16 output accumulator: block db holds O^T[32 db .. +31][row] of the
+  // lane's row as 16 packed fp16 (two u32x4: elements 0-7, 8-15 of the MFMA C
+  // layout)
+  u32x4 o16[NDB][2];
 #pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) o16[r][d][0] = o16[r][d][1] = u32x4{0, 0, 0, 0};
-  float m_ref[RB], l_run[RB];  // reference max (log2 domain) and the full row sum
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    m_ref[r] = -INFINITY;
-    l_run[r] = 0.f;
-  }
+  for (int d = 0; d < NDB; ++d) o16[d][0] = o16[d][1] = u32x4{0, 0, 0, 0};
+  float m_ref = -INFINITY;  // reference max (log2 domain)
+  float l_run = 0.f;        // the full row sum, relative to m_ref
 
   if (n_tiles > 0) issue_k_tile(0);
 
   for (int j = 0; j < n_tiles; ++j) {
     const int j0 = j * kWideBc;
+#pragma unroll
+    for (int r = 0; r < NKC; ++r) asm volatile("" : "+a"(koff[r]));
     int lj = lane;
     asm volatile("" : "+v"(lj));
     const int hij = lj >> 5;
+    const int my_q = qw + (lj & 31);
 
-    // ===== K phase: partial S^T over this half for each row block
+    // ===== K phase: S^T (NH = 2: partial, over this part of D)
     wait_vmcnt<0>();
     wait_lgkm0();
     barrier();
-    f32x16 s_acc[RB], s_odd;  // RB = 1: two chains (even / odd k-steps)
+    f32x16 s_acc, s_odd;  // two chains: even / odd k-steps
     {
       uint32_t vlo;
       {
@@ -227,69 +236,45 @@ void fwd_wide16_kernel(FwdArgs a) {
           if ((r * (NS / 2)) / NVC == st) vt_copy(j, r, vlo);
         const u32x4 a0 = kf[st % kKAhead];
         if (st + kKAhead < NS) kf[st % kKAhead] = kread(st + kKAhead);
-        if constexpr (RB == 2) {
-          if (st == 0) {
-            mfma32_asm<BF16, true, false, true>(s_acc[0], a0, qf[0][st]);
-            mfma32_asm<BF16, true, false, true>(s_acc[1], a0, qf[1][st]);
-          } else if (st == NS - 1) {
-            mfma32_asm<BF16, true, false>(s_acc[0], a0, qf[0][st]);
-            mfma32_asm<BF16, true, false, false, false, true>(s_acc[1], a0, qf[1][st]);
-          } else {
-            mfma32_asm<BF16, true, false>(s_acc[0], a0, qf[0][st]);
-            mfma32_asm<BF16, true, false>(s_acc[1], a0, qf[1][st]);
-          }
-        } else {
-          f32x16& acc = (st & 1) ? s_odd : s_acc[0];
-          if (st < 2) mfma32_asm<BF16, true, false, true>(acc, a0, qf[0][st]);
-          else if (st == NS - 1) mfma32_asm<BF16, true, false, false, false, true>(acc, a0, qf[0][st]);
-          else mfma32_asm<BF16, true, false>(acc, a0, qf[0][st]);
-        }
+        f32x16& acc = (st & 1) ? s_odd : s_acc;
+        if (st < 2) mfma32_asm<BF16, true, false, true>(acc, a0, qf[st]);
+        else if (st == NS - 1) mfma32_asm<BF16, true, false, false, false, true>(acc, a0, qf[st]);
+        else mfma32_asm<BF16, true, false>(acc, a0, qf[st]);
       }
     }
-    // every chain ends at least 19 wait states before this VALU (the last MFMA pads)
+    // both chains end at least 19 wait states before this VALU (the last MFMA pads)
+    pin_after_pad(s_acc);
+    pin_after_pad(s_odd);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) pin_after_pad(s_acc[r]);
-    if constexpr (RB == 1) {
-      pin_after_pad(s_odd);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s_acc[0][i] += s_odd[i];
-    }
+    for (int i = 0; i < 16; ++i) s_acc[i] += s_odd[i];
 
-    // ===== swap partial scores with the other half's wave; add
-    {
-      FFPA_LDS f32x4* mine = (FFPA_LDS f32x4*)(smem + XB + wave * RB * kWideXchg) + lj;
+    // ===== NH = 2: swap partial scores with the other part's wave; add
+    if constexpr (NH == 2) {
+      FFPA_LDS f32x4* mine = (FFPA_LDS f32x4*)(smem + XB + wave * kWideXchg) + lj;
 #pragma unroll
-      for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          mine[256 * r + 64 * jj] =
-              f32x4{s_acc[r][4 * jj], s_acc[r][4 * jj + 1], s_acc[r][4 * jj + 2], s_acc[r][4 * jj + 3]};
+      for (int jj = 0; jj < 4; ++jj)
+        mine[64 * jj] = f32x4{s_acc[4 * jj], s_acc[4 * jj + 1], s_acc[4 * jj + 2], s_acc[4 * jj + 3]};
       wait_lgkm0();
       barrier();
-      const FFPA_LDS f32x4* other = (const FFPA_LDS f32x4*)(smem + XB + (wave ^ 1) * RB * kWideXchg) + lj;
+      const FFPA_LDS f32x4* other = (const FFPA_LDS f32x4*)(smem + XB + (wave ^ 1) * kWideXchg) + lj;
 #pragma unroll
-      for (int r = 0; r < RB; ++r)
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 x = other[64 * jj];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const f32x4 x = other[256 * r + 64 * jj];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s_acc[r][4 * jj + e] += x[e];
-        }
+        for (int e = 0; e < 4; ++e) s_acc[4 * jj + e] += x[e];
+      }
     }
 
-    // ===== online softmax per row block (log2 domain), renormalised every
-    // tile; register i of the scores holds key j0 + 8 (i / 4) + 4 hi + i % 4
-    const int kb0 = j0 + 4 * hij;
-    V8 pf[RB][2];
-    float oscale[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int qw = qg + 32 * r;
-      const int my_q = qw + (lj & 31);
+    // ===== online softmax (log2 domain), renormalised every tile; register i
+    // of the scores holds key j0 + 8 (i / 4) + 4 hi + i % 4
+    V8 pf[2];
+    float oscale;
+    {
+      const int kb0 = j0 + 4 * hij;
       const bool need_mask = has_mask || (j0 + kWideBc > a.Nkv) || (a.causal && j0 + kWideBc - 1 > qw);
       float tv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tv[i] = s_acc[r][i] * a.scale_log2;
+      for (int i = 0; i < 16; ++i) tv[i] = s_acc[i] * a.scale_log2;
       if (need_mask) {
         const uint16_t* mrow = mk + (size_t)min(my_q, a.Nq - 1) * a.mask_stride;
         int klim = a.Nkv - kb0;
@@ -306,38 +291,36 @@ void fwd_wide16_kernel(FwdArgs a) {
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, tv[i]);
       mx = fmaxf(mx, swap_halves(mx));
       float alpha = 1.f;
-      if (__builtin_amdgcn_ballot_w64(mx > m_ref[r] + kRescaleTau) != 0) {  // wave-uniform
-        const float m_new = fmaxf(m_ref[r], mx);
-        alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_ref[r] - m_new);
-        m_ref[r] = m_new;
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleTau) != 0) {  // wave-uniform
+        const float m_new = fmaxf(m_ref, mx);
+        alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_ref - m_new);
+        m_ref = m_new;
       }
-      const float m_use = (m_ref[r] == -INFINITY) ? 0.f : m_ref[r];
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         tv[i] = exp2_fast(tv[i] - m_use);
         psum += tv[i];
       }
-      const float l_old = l_run[r];
+      const float l_old = l_run;
       const float l_new = alpha * l_old + psum + swap_halves(psum);
-      l_run[r] = l_new;
+      l_run = l_new;
       const float pscale = l_new > 0.f ? 1.f / l_new : 0.f;
-      oscale[r] = alpha * l_old * pscale;
+      oscale = alpha * l_old * pscale;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const float* x = &tv[8 * t2];
-        pf[r][t2] = pack8<BF16>(x[0] * pscale, x[1] * pscale, x[2] * pscale, x[3] * pscale, x[4] * pscale,
-                                x[5] * pscale, x[6] * pscale, x[7] * pscale);
+        pf[t2] = pack8<BF16>(x[0] * pscale, x[1] * pscale, x[2] * pscale, x[3] * pscale, x[4] * pscale,
+                             x[5] * pscale, x[6] * pscale, x[7] * pscale);
       }
     }
     // P is the B operand of inline-asm MFMAs: every VALU write of it happens
     // here, before the barrier (the first MFMA of the phase pads as well)
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[r][t2]));
+    for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[t2]));
 
-    // ===== V phase: per-tile products V_half^T P^T, folded into the fp16 O
+    // ===== V phase: per-tile products V^T P^T, folded into the fp16 O
     wait_vmcnt<0>();
     wait_lgkm0();
     barrier();
@@ -348,40 +331,30 @@ void fwd_wide16_kernel(FwdArgs a) {
         asm volatile("" : "+v"(lv));
         v_bases(lv, vx);
       }
-      // unit u -> (d-block, row block); step s -> (group, unit of the group, t2)
-      auto unit_db = [](int u) { return RB == 2 ? u >> 1 : u; };
-      auto unit_r = [](int u) { return RB == 2 ? (u & 1) : 0; };
+      // step s -> group g = s / 4, d-block of the group uu, key step t2
       auto step_of = [](int s, int& g, int& uu, int& t2) {
         g = s >> 2;
         const int k = s & 3;
-        const bool pair = 2 * g + 1 < NU;
+        const bool pair = 2 * g + 1 < NDB;
         uu = pair ? (k & 1) : 0;
         t2 = pair ? (k >> 1) : k;
       };
-      // V^T fragment reads: RB = 2 shares one read between the two units of a
-      // group (same d-block); RB = 1 reads one per step
-      auto ev_of = [&](int s) {
+      auto vread = [&](int s) {
         int g, uu, t2;
         step_of(s, g, uu, t2);
-        return RB == 2 ? 2 * g + t2 : s;
-      };
-      constexpr int NEV = RB == 2 ? 2 * NG : NSV;
-      auto vread_ev = [&](int e) {
-        const int db = RB == 2 ? (e >> 1) : unit_db(2 * (e >> 2) + ((2 * (e >> 2) + 1 < NU) ? (e & 1) : 0));
-        const int t2 = RB == 2 ? (e & 1) : ((2 * (e >> 2) + 1 < NU) ? ((e & 3) >> 1) : (e & 3));
-        return lds_read16(smem + vx[t2] + 2048 * db);
+        return lds_read16(smem + vx[t2] + 2048 * (2 * g + uu));
       };
       u32x4 vf[kVAhead];
 #pragma unroll
-      for (int e = 0; e < kVAhead && e < NEV; ++e) vf[e] = vread_ev(e);
+      for (int s = 0; s < kVAhead && s < NSV; ++s) vf[s] = vread(s);
 
-      f32x16 pv[2][2];  // [set = group % 2][unit of the group]
-      auto fold_unit = [&](const f32x16& acc, int u) {
-        const int db = unit_db(u), r = unit_r(u);
-        const f16x2 sc = {(_Float16)oscale[r], (_Float16)oscale[r]};
+      f32x16 pv[2][2];  // [set = group % 2][d-block of the group]
+      const f16x2 sc = {(_Float16)oscale, (_Float16)oscale};
+      // o16 <- o16 * oscale + acc, in packed fp16
+      auto fold_block = [&](const f32x16& acc, int db) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          u32x4 w = o16[r][db][hh];
+          u32x4 w = o16[db][hh];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             f16x2 cur = f16x2_from_bits(w[e]);
@@ -389,39 +362,32 @@ void fwd_wide16_kernel(FwdArgs a) {
             cur = cur * sc + add;
             w[e] = __builtin_bit_cast(uint32_t, cur);
           }
-          o16[r][db][hh] = w;
+          o16[db][hh] = w;
         }
       };
+      // A group's fold runs as one block of VALU work between the MFMAs of
+      // the next two groups: spread in quarters between the next group's
+      // MFMAs it measured 8-9 % slower.
       auto fold_group = [&](int g) {
-        fold_unit(pv[g & 1][0], 2 * g);
-        if (2 * g + 1 < NU) fold_unit(pv[g & 1][1], 2 * g + 1);
+        fold_block(pv[g & 1][0], 2 * g);
+        if (2 * g + 1 < NDB) fold_block(pv[g & 1][1], 2 * g + 1);
         // the folded values exist here, before the next MFMAs (which reuse
         // this set's registers two groups later)
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-          if (2 * g + uu >= NU) continue;
-          const int db = unit_db(2 * g + uu), r = unit_r(2 * g + uu);
-          asm volatile("" : "+v"(o16[r][db][0]), "+v"(o16[r][db][1]));
-        }
+        asm volatile("" : "+v"(o16[2 * g][0]), "+v"(o16[2 * g][1]));
+        if (2 * g + 1 < NDB) asm volatile("" : "+v"(o16[2 * g + 1][0]), "+v"(o16[2 * g + 1][1]));
       };
-      int lnc = lane;
-      asm volatile("" : "+v"(lnc));
 #pragma unroll
       for (int s = 0; s < NSV; ++s) {
         // K(j+1); on the last tile rows past the key range (range-checked
         // zeros) or, causal, rows nobody reads: harmless, and branch-free
 #pragma unroll
         for (int r = 0; r < NKC; ++r)
-          if ((r * (NSV / 2)) / NKC == s) k_copy(j + 1, r, lnc);
+          if ((r * (NSV / 2)) / NKC == s) k_copy(j + 1, r);
         int g, uu, t2;
         step_of(s, g, uu, t2);
-        const int u = 2 * g + uu;
-        const int e = ev_of(s);
-        const u32x4 vbits = vf[e % kVAhead];
-        // the last use of event e: read e + kVAhead into its slot
-        const bool last_use = RB == 2 ? (uu == 1 || 2 * g + 1 >= NU) : true;
-        if (last_use && e + kVAhead < NEV) vf[e % kVAhead] = vread_ev(e + kVAhead);
-        const u32x4 pb = __builtin_bit_cast(u32x4, pf[unit_r(u)][t2]);
+        const u32x4 vbits = vf[s % kVAhead];
+        if (s + kVAhead < NSV) vf[s % kVAhead] = vread(s + kVAhead);
+        const u32x4 pb = __builtin_bit_cast(u32x4, pf[t2]);
         f32x16& acc = pv[g & 1][uu];
         // padded after: the last step (the last group folds right after it)
         // and the last step of group 1, before group 0's fold, which no
@@ -454,49 +420,53 @@ void fwd_wide16_kernel(FwdArgs a) {
   }
   wait_vmcnt<0>();  // no copy may still target this workgroup's LDS when it ends
 
-  // ===== epilogue: each row block's rows of the half go through LDS (32 rows
-  // per wave, pitch of whole 16-granule groups), then out as contiguous pieces
-  // of W elements per row
-  constexpr int PITCH = wide16_pitch<D>();  // bytes per staged row
+  // ===== epilogue: the wave's 32 rows of its part go through LDS (in EP
+  // passes of W / EP columns, a staged row taking whole groups of 16
+  // granules), then out as contiguous pieces of W / EP elements per row
+  constexpr int EP = wide16_epi_passes<D>();
+  constexpr int NDBP = NDB / EP;   // d-blocks per pass
+  constexpr int SGP = 4 * NDBP;    // granules per row and pass
+  constexpr int PITCH = wide16_pitch<D>();
+  static_assert(NDB % EP == 0 && PITCH >= SGP * 16, "epilogue passes");
   static_assert(4 * 32 * PITCH <= wide16_lds<D>(), "epilogue staging fits the LDS");
   wait_lgkm0();
   barrier();  // every wave is done with the tile buffers
   FFPA_LDS char* ostage = smem + wave * 32 * PITCH;
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const int qw = qg + 32 * r;
+  for (int pe = 0; pe < EP; ++pe) {
     {
       const int rr = lane & 31, hie = lane >> 5;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int dq = 0; dq < NDBP; ++dq)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const u32x4 w = o16[r][db][g4 >> 1];
+          const u32x4 w = o16[NDBP * pe + dq][g4 >> 1];
           const f16x2 p0 = f16x2_from_bits(w[2 * (g4 & 1)]);
           const f16x2 p1 = f16x2_from_bits(w[2 * (g4 & 1) + 1]);
           const u32x2 st = {E::pack2((float)p0[0], (float)p0[1]), E::pack2((float)p1[0], (float)p1[1])};
-          const int gg = 4 * db + g4;  // elements 32 db + 8 g4 + 4 hi .. +3
+          const int gg = 4 * dq + g4;  // elements 32 dq + 8 g4 + 4 hi .. +3 of the pass
           *(FFPA_LDS u32x2*)(ostage + rr * PITCH + ((gg ^ (rr & 15)) << 4) + 8 * hie) = st;
         }
     }
     {
-      typename E::scalar* O = (typename E::scalar*)a.o + ((size_t)(b * a.Hq + h) * a.Nq + qw) * D + W * hf;
+      typename E::scalar* O =
+          (typename E::scalar*)a.o + ((size_t)(b * a.Hq + h) * a.Nq + qw) * D + W * hf + 32 * NDBP * pe;
       const int rows = min(32, a.Nq - qw);
-      constexpr int NIT = (32 * SG + 63) / 64;
+      constexpr int NIT = (32 * SGP + 63) / 64;
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int c = it * 64 + lane;
-        const int rr = c / SG, gg = c % SG;
+        const int rr = c / SGP, gg = c % SGP;
         if (rr < rows) {
           const u32x4 x = *(const FFPA_LDS u32x4*)(ostage + rr * PITCH + ((gg ^ (rr & 15)) << 4));
           *(u32x4*)(O + (size_t)rr * D + 8 * gg) = x;
         }
       }
     }
-    if (hf == 0 && a.lse != nullptr && (lane >> 5) == 0 && qw + lane < a.Nq) {
-      float* L = a.lse + (size_t)(b * a.Hq + h) * a.Nq + qw + lane;
-      *L = l_run[r] > 0.f ? (m_ref[r] + __builtin_amdgcn_logf(l_run[r])) * kLn2 : -INFINITY;
-    }
+  }
+  if (hf == 0 && a.lse != nullptr && (lane >> 5) == 0 && qw + lane < a.Nq) {
+    float* L = a.lse + (size_t)(b * a.Hq + h) * a.Nq + qw + lane;
+    *L = l_run > 0.f ? (m_ref + __builtin_amdgcn_logf(l_run)) * kLn2 : -INFINITY;
   }
 }
 
