@@ -29,8 +29,13 @@
  *  - a query row whose every score is -inf gets O = 0 and lse = -inf;
  *  - lse is natural-log and includes scale and mask;
  *  - "fp16 accumulation" (FFPA_ACC_F16): gfx950 has no MFMA with an fp16
- *    result, so scores and every MFMA partial stay fp32; the running output
- *    accumulator is held in fp16, kept normalised so it cannot overflow.
+ *    result, so scores and every MFMA partial (one key tile's P V product)
+ *    stay fp32; the running output accumulator is held in fp16, kept
+ *    normalised (|O| <= max |V|), and each tile's product is rounded to fp16
+ *    when folded into it. For bf16 inputs the accumulator is fp16 as well:
+ *    V entries must then lie inside fp16's range (|v| < 65520); an element
+ *    whose product reaches fp16 infinity makes that output element
+ *    non-finite (use FFPA_ACC_F32 for such data).
  *
  * Layout. All tensors are dense, row-major and contiguous:
  *   q, o, dout, dq : [B, Hq,  Nq,  D]  (element type = dtype)
@@ -111,10 +116,16 @@ typedef enum {
  *               finished.
  *   stream    : hipStream_t to enqueue on.
  * Built today: every D (multiple of 32, <= 1024) for Nq = 1; for Nq > 1, D a
- * multiple of 64 up to 1024 (D > 512 runs a kernel that splits D across wave
- * pairs). Both mask shapes are built on every path. Other valid shapes (Nq > 1
- * with D not a multiple of 64) return FFPA_ERR_UNSUPPORTED before any launch.
- * With Nq = 1 the accumulation is fp32 whatever accum_dtype asks for.
+ * multiple of 64 up to 1024. Both mask shapes are built on every path. Other
+ * valid shapes (Nq > 1 with D not a multiple of 64) return
+ * FFPA_ERR_UNSUPPORTED before any launch. The accumulator, by path:
+ *  - Nq > 1, D <= 512: fp32 or fp16 as accum_dtype asks (one kernel each);
+ *  - Nq > 1, D > 512: FFPA_ACC_F32 runs a kernel that splits D across wave
+ *    pairs with an fp32 accumulator (64 query rows per workgroup);
+ *    FFPA_ACC_F16 runs one with the fp16 accumulator (128 rows per
+ *    workgroup up to D = 768, where a wave holds all of D; 64 above);
+ *  - Nq = 1 (decode, bound by memory bandwidth): fp32 whatever accum_dtype
+ *    asks for (at least as accurate as asked).
  */
 int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,

@@ -286,3 +286,34 @@ def test_query_mask_equals_deleting_keys_per_row(lib, shape):
         oo, lo = attn_fwd(q[:, :, r:r + 1], k[:, :, ks], v[:, :, ks], scale)
         assert np.abs(to_f64(o[:, :, r:r + 1]) - oo).max() <= 1e-2
         assert np.abs(to_f64(lse[:, :, r:r + 1]) - lo).max() <= 2e-3
+
+
+@pytest.mark.parametrize("D", [320, 768])
+def test_bf16_inputs_with_the_fp16_accumulator(lib, D):
+    """bf16 inputs with FFPA_ACC_F16 accumulate O in fp16 (the reading of
+    "fp16 accumulation" the header documents). Inside fp16's range the result
+    is right to the rounding of an fp16 accumulator, also at |V| ~ 6e4; a
+    column of V whose products reach fp16 infinity (|v| = 1e5) makes that
+    output column non-finite and leaves the others untouched; fp32
+    accumulation gets it right."""
+    q, k, v, _ = _inputs(31, 1, 2, 2, 150, 200, D, "bf16")
+    scale = 1.0 / math.sqrt(D)
+    big = v.clone()
+    big[:, :, :, 5] = 6.0e4
+    o, lse = _run(lib, q.cuda(), k.cuda(), big.cuda(), accum="f16", scale=scale)
+    oo, lo = attn_fwd(q, k, big, scale)
+    og = to_f64(o)
+    others = [c for c in range(D) if c != 5]
+    assert np.abs(og[..., others] - oo[..., others]).max() <= TOL["f16"]
+    # fp16 spacing is 32 there; one rounding per fold of a key tile, 4-7 folds here
+    assert np.abs(og[..., 5] - oo[..., 5]).max() <= 2.0 ** -7 * 6.0e4
+    huge = v.clone()
+    huge[:, :, :, 5] = 1.0e5
+    o, lse = _run(lib, q.cuda(), k.cuda(), huge.cuda(), accum="f16", scale=scale)
+    oo, lo = attn_fwd(q, k, huge, scale)
+    og = to_f64(o)
+    assert not np.isfinite(og[..., 5]).any()
+    assert np.abs(og[..., others] - oo[..., others]).max() <= TOL["f16"]
+    assert np.abs(to_f64(lse) - lo).max() <= 2e-3
+    o32, _ = _run(lib, q.cuda(), k.cuda(), huge.cuda(), accum="f32", scale=scale)
+    assert np.abs(to_f64(o32)[..., 5] - oo[..., 5]).max() <= 2.0 ** -8 * 1.0e5 * 2

@@ -86,6 +86,9 @@ WORKLOADS = {
     "bwd_d1024_causal": _w("bwd_d1024_causal", 4, 1, 32, 32, 8192, 8192, 1024, dtype="bf16",
                            causal=True, backward=True),
 }
+# bf16 variants of the variant family (same float32 draws as the fp16 ones)
+for _n in ("cross", "gqa", "causal", "nonaligned", "mask"):
+    WORKLOADS[f"{_n}_bf16"] = WORKLOADS[_n].replace(name=f"{_n}_bf16", dtype="bf16")
 for _d in (320, 448, 512, 576, 768, 1024):
     for _acc in ("f32", "f16"):
         WORKLOADS[f"dsweep{_d}_{_acc}"] = _w(f"dsweep{_d}_{_acc}", 3, 1, 32, 32, 8192, 8192, _d,
