@@ -18,7 +18,8 @@ import os
 from typing import Optional
 
 __all__ = [
-    "load", "FFPAError", "ffpa_attn_fwd", "ffpa_attn_bwd", "ffpa_attn_fwd_workspace_size",
+    "load", "FFPAError", "ffpa_attn_fwd", "ffpa_attn_fwd_noalloc", "ffpa_attn_bwd",
+    "ffpa_attn_fwd_workspace_size",
     "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min", "ffpa_last_error",
     "ffpa_version", "attention",
     "attention_backward", "F16", "BF16", "ACC_F32", "ACC_F16", "LIB_PATH", "EXPORTED",
@@ -34,7 +35,7 @@ _STATUS = {1: "FFPA_ERR_INVALID_ARG", 2: "FFPA_ERR_UNSUPPORTED", 3: "FFPA_ERR_WO
            4: "FFPA_ERR_HIP"}
 
 # Symbols declared in include/ffpa_attn.h.
-EXPORTED = ("ffpa_attn_fwd", "ffpa_attn_fwd_workspace_size", "ffpa_attn_bwd",
+EXPORTED = ("ffpa_attn_fwd", "ffpa_attn_fwd_workspace_size", "ffpa_attn_fwd_noalloc", "ffpa_attn_bwd",
             "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min", "ffpa_last_error",
             "ffpa_version")
 
@@ -59,6 +60,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.ffpa_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, i, i, vp, sz, vp]
     lib.ffpa_attn_fwd.restype = i
+    lib.ffpa_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, i, i, vp]
+    lib.ffpa_attn_fwd_noalloc.restype = i
     lib.ffpa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i,
                                   i, i, vp, sz, vp]
     lib.ffpa_attn_bwd.restype = i
@@ -107,6 +110,14 @@ def ffpa_attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, 
     return load().ffpa_attn_fwd(q, k, v, o, lse or None, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
                                 mask or None, mask_rows, accum_dtype, dtype, workspace or None,
                                 workspace_bytes, stream or None)
+
+
+def ffpa_attn_fwd_noalloc(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                          accum_dtype, dtype, stream) -> int:
+    """Raw C call of the forward that allocates nothing (no workspace arguments)."""
+    return load().ffpa_attn_fwd_noalloc(q, k, v, o, lse or None, B, Hq, Hkv, Nq, Nkv, D, scale,
+                                        causal, mask or None, mask_rows, accum_dtype, dtype,
+                                        stream or None)
 
 
 def ffpa_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask,

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "ffpa_attn.h"
@@ -172,19 +173,34 @@ size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
   return 0;
 }
 
-int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                  int Hkv, int Nq, int Nkv, int D, float scale, int causal, const void* mask,
-                  int mask_rows, int accum_dtype, int dtype, void* workspace, size_t workspace_bytes,
-                  void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Checks of ffpa_attn_fwd's arguments that come before the workspace.
+int fwd_check_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                   int Hkv, int Nq, int Nkv, int D, float scale, int causal, const void* mask,
+                   int mask_rows, int accum_dtype, int dtype) {
   if (!q || !k || !v || !o) return fail(FFPA_ERR_INVALID_ARG, "q, k, v and o must be non-null");
-  int st = check_common(B, Hq, Hkv, Nq, Nkv, D, causal, mask, mask_rows, accum_dtype, dtype);
+  const int st = check_common(B, Hq, Hkv, Nq, Nkv, D, causal, mask, mask_rows, accum_dtype, dtype);
   if (st != FFPA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(mask) || !aligned16(workspace))
+      !aligned16(mask))
     return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   if (!(scale == scale)) return fail(FFPA_ERR_INVALID_ARG, "scale is NaN");
-  const size_t need = ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  return FFPA_OK;
+}
+
+// The forward after its argument checks. allow_vt = false keeps the prefill
+// path (D <= 512) off the transposed copy of V, so that it needs no
+// workspace; otherwise the path is the one ffpa_attn_fwd_workspace_size sizes.
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Nq, int Nkv, int D, float scale, int causal, const void* mask,
+             int mask_rows, int accum_dtype, int dtype, void* workspace, size_t workspace_bytes,
+             bool allow_vt, void* stream) {
+  if (!aligned16(workspace)) return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const bool no_vt = !allow_vt && Nq > 1 && D <= 512;
+  const size_t need = no_vt ? 0 : ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
     return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_fwd_workspace_size()");
 
@@ -236,7 +252,7 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   }
 
   size_t ring = 0;
-  const bool vt = ffpa::fwd_use_vt(Hq, Hkv, Nq);
+  const bool vt = !no_vt && ffpa::fwd_use_vt(Hq, Hkv, Nq);
   FwdLauncher launch = fwd_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, vt, &ring);
   if (launch == nullptr) return fail(FFPA_ERR_UNSUPPORTED, "this head dimension is not built yet");
   size_t lds = ring + ffpa::kFwdFlagBytes;
@@ -264,6 +280,92 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   const hipError_t e = launch(a, lds, (hipStream_t)stream);  // [V^T pass,] the kernel
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return FFPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                  int Hkv, int Nq, int Nkv, int D, float scale, int causal, const void* mask,
+                  int mask_rows, int accum_dtype, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  g_err.clear();
+  const int st = fwd_check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                                accum_dtype, dtype);
+  if (st != FFPA_OK) return st;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
+                  dtype, workspace, workspace_bytes, true, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch of ffpa_attn_fwd_noalloc: one array in each GPU's memory, from the
+// library's load until the process ends. In host code `scratch` is only a
+// stand-in symbol: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and host code uses that address
+// (never the array's name) wherever it needs the memory.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the device that runs `stream` (the
+// current device for the null stream), looked up on the first call there.
+int scratch_address(void* stream, void** out) {
+  int dev = -1, cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess) e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("no device for the stream: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FFPA_ERR_UNSUPPORTED, "device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(FFPA_ERR_HIP, std::string("hipSetDevice failed: ") + hipGetErrorString(e));
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t back = dev != cur ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(FFPA_ERR_HIP, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+    if (back != hipSuccess)
+      return fail(FFPA_ERR_HIP, std::string("hipSetDevice failed: ") + hipGetErrorString(back));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FFPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ffpa_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                          int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
+                          const void* mask, int mask_rows, int accum_dtype, int dtype, void* stream) {
+  g_err.clear();
+  const int st = fwd_check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                                accum_dtype, dtype);
+  if (st != FFPA_OK) return st;
+  const size_t need = ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  if (need <= kNoAllocScratchBytes) {
+    void* ws = nullptr;
+    const int sa = scratch_address(stream, &ws);
+    if (sa != FFPA_OK) return sa;
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
+                    dtype, ws, kNoAllocScratchBytes, true, stream);
+  }
+  if (Nq > 1 && D <= 512)  // V staged as is: no scratch at all
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
+                    dtype, nullptr, 0, false, stream);
+  return fail(FFPA_ERR_WORKSPACE, "these sizes need " + std::to_string(need) +
+                                      " bytes of scratch; ffpa_attn_fwd_noalloc holds " +
+                                      std::to_string(kNoAllocScratchBytes));
 }
 
 size_t ffpa_attn_bwd_workspace_size_min(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {

@@ -67,7 +67,8 @@
  * (FFPA_ERR_HIP).
  *
  * Threading. The library holds no mutable global state besides the
- * thread-local error message; all entry points are reentrant.
+ * thread-local error message and, for ffpa_attn_fwd_noalloc, its per-GPU
+ * scratch array (see there); all other entry points are reentrant.
  */
 #ifndef FFPA_ATTN_H_
 #define FFPA_ATTN_H_
@@ -134,6 +135,30 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
 
 /* Bytes of workspace ffpa_attn_fwd needs for these sizes (0 if none). */
 size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
+
+/*
+ * Forward attention that allocates nothing and takes no workspace: for
+ * callers that cannot allocate device memory (work captured into a HIP graph,
+ * tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * results and error order as ffpa_attn_fwd without (workspace,
+ * workspace_bytes); it calls no allocating routine.
+ *  - Scratch: a 32 MiB array in each GPU's memory that the library holds from
+ *    its load until the process ends (one per GPU it runs on). When
+ *    ffpa_attn_fwd_workspace_size(...) <= 32 MiB the call runs exactly the
+ *    path of ffpa_attn_fwd with that array as its workspace (same bits).
+ *  - Larger needs: for Nq > 1 and D <= 512 the call stages V as is instead of
+ *    writing its transposed copy (no scratch; same results up to rounding
+ *    order); otherwise it returns FFPA_ERR_WORKSPACE before any launch.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *    GPU (several streams, or host threads) race on it; order them. The array
+ *    keeps whatever the last call left; every call writes what it reads.
+ *  - The stream's device is the one whose array is used; its address is looked
+ *    up (hipGetSymbolAddress) on the first call there, and a failure of that
+ *    lookup returns FFPA_ERR_HIP.
+ */
+int ffpa_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
+                          const void* mask, int mask_rows, int accum_dtype, int dtype, void* stream);
 
 /*
  * Backward attention: given dout = dL/dO, writes dq, dk, dv (same dtype and

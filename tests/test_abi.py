@@ -142,3 +142,26 @@ def test_backward_workspace_sizes():
     # 33 heads of 128 MiB: 5 chunks of 7 (the fewest within 1 GiB, spread evenly)
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 33, 33, 8192, 8192, 64, 0) == (
         2 * 33 * 8192 * 4 + 33 * 64 * 8192 * 2 + 7 * 256 * 256 * 2048)
+
+
+def fwd_noalloc(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nkv=8, D=64, scale=0.125,
+                causal=0, mask=0, mask_rows=0, accum_dtype=0, dtype=0, stream=0)
+    args.update(kw)
+    return ffpa.ffpa_attn_fwd_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), ffpa.ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), ffpa.ERR_INVALID_ARG),
+    (dict(D=1056), ffpa.ERR_UNSUPPORTED),
+    (dict(lse=P + 4), ffpa.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), ffpa.ERR_INVALID_ARG),
+    # above D = 512 the transposed copy of V is required: 64 MiB > the 32 MiB scratch
+    (dict(B=1, Hq=4, Hkv=4, Nq=4096, Nkv=8192, D=1024), ffpa.ERR_WORKSPACE),
+    # decode partials of 8192 heads x 1 key range x 1025 floats > 32 MiB
+    (dict(B=1024, Hq=8, Hkv=8, Nq=1, Nkv=4096, D=1024), ffpa.ERR_WORKSPACE),
+])
+def test_forward_noalloc_validation(kw, code):
+    assert fwd_noalloc(**kw) == code
+    assert ffpa.ffpa_last_error() != ""
