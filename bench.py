@@ -231,7 +231,8 @@ def run_backward(ffpa, W, name, steps, warmup):
     return {"workload": f"{name}: B={w.B} H={w.Hq} N={w.Nq} D={w.D} {w.dtype} causal={w.causal}",
             "value": round(tflops, 2), "unit": "TFLOPS (5 GEMMs counted)",
             "ms_per_call": round(mean_ms, 4),
-            "kernels": "prep + K^T copy + dK/dV (stores dS) + dQ from dS",
+            "kernels": "prep + K^T copy + per chunk of kv heads: dK/dV (stores dS) + dQ from dS",
+            "workspace_bytes": ws_bytes,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(tflops / peak, 4)},
             "rocprof": recorded_counters(name)}
@@ -277,12 +278,13 @@ def run_decode(ffpa, W, steps, warmup):
             "rocprof": recorded_counters("decode")}
 
 
-def timed_call(w) -> str:
+def timed_call(w, accum="f32") -> str:
     """The kernels one timed forward call enqueues (mirrors the library's choice)."""
     if w.Nq == 1:
         return "dec_split_kernel + dec_combine_kernel"
     if w.D > 512:
-        return "fwd_vt_kernel (V transposed, blocks of 32 keys) + fwd_wide_kernel"
+        return ("fwd_vt_kernel (V transposed, blocks of 32 keys) + " +
+                ("fwd_wide16_kernel" if accum == "f16" else "fwd_wide_kernel"))
     if w.Nq * w.Hq >= 3072 * w.Hkv:
         return "fwd_vt_kernel (V transposed into the workspace) + fwd_prefill_kernel"
     return "fwd_prefill_kernel (V staged as is)"
@@ -320,7 +322,7 @@ def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
                      "traffic": measured_traffic(f"{name}:{accum}")},
         "kernel_ms": {"mean": round(mean_ms, 4), "median": round(per[len(per) // 2], 4),
                       "min": round(per[0], 4)},
-        "timed_call": timed_call(w),
+        "timed_call": timed_call(w, accum),
         "rocprof": recorded_counters(f"{name}:{accum}"),
     }
     if with_cpu:
@@ -328,6 +330,37 @@ def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
     del inp
     torch.cuda.empty_cache()
     return line
+
+
+def run_forward_path(ffpa, W, name, accum, steps, warmup):
+    """One forward workload timed like the headline (whole call, HIP events)."""
+    import torch
+
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, device="cuda")
+    per, _ = time_forward(ffpa, w, inp, accum, steps, warmup)
+    mean_ms = sum(per) / len(per)
+    tflops = counted_flops(w.B, w.Hq, w.Nq, w.Nkv, w.D, w.causal) / (mean_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    del inp
+    torch.cuda.empty_cache()
+    return {"workload": f"{name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nkv={w.Nkv} D={w.D} "
+                        f"{w.dtype} causal={w.causal} mask={w.mask} accum={accum}",
+            "value": round(tflops, 2), "unit": "TFLOPS" + (" (causal: half counted)" if w.causal else ""),
+            "ms_per_call": round(mean_ms, 4), "timed_call": timed_call(w, accum),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4)}}
+
+
+# Forward workloads the default line measures beside the headline: every
+# variant in both dtypes, the fp16 accumulator, the head-dimension sweep with
+# both accumulators, and 16K sequences.
+FWD_PATHS = ([("self_bf16", "f32"), ("self", "f16"), ("self_bf16", "f16")] +
+             [(n, "f32") for n in ("cross", "gqa", "causal", "nonaligned", "mask")] +
+             [(n + "_bf16", "f32") for n in ("cross", "gqa", "causal", "nonaligned", "mask")] +
+             [(f"dsweep{d}_{a}", a) for d in (320, 448, 512, 576, 768, 1024) for a in ("f32", "f16")] +
+             [("self16k", "f32"), ("self16k_bf16", "f32"), ("causal16k", "f32"), ("nonaligned16k", "f32")])
+BWD_PATHS = ("bwd_causal", "bwd_d1024", "bwd16k", "bwd16k_causal")
 
 
 def main(argv=None) -> int:
@@ -379,16 +412,17 @@ def main(argv=None) -> int:
         return 0
     paths = None
     if not args.no_paths:
-        # measured first: their calls (hundreds of ms of GPU work) also bring
-        # the clock past its ramp before the headline's warm-up steps
-        paths = {
-            "backward": run_backward(ffpa, W, "bwd", max(3, args.steps // 2), 5),
-            "backward_causal": run_backward(ffpa, W, "bwd_causal", max(3, args.steps // 2), 8),
-            "decode": run_decode(ffpa, W, args.steps, max(args.warmup, 50)),
-        }
+        # the backward first: its calls (~0.2 s of GPU work) also bring the
+        # clock past its ramp before the headline's warm-up steps
+        paths = {"backward": run_backward(ffpa, W, "bwd", max(3, args.steps // 2), 5)}
     line = run_one(ffpa, W, args.workload, args.accum, args.steps, args.warmup,
                    not args.no_cpu_baseline, args.cpu_heads)
     if paths is not None:
+        for name in BWD_PATHS:
+            paths["backward" + name[3:]] = run_backward(ffpa, W, name, max(3, args.steps // 2), 3)
+        paths["decode"] = run_decode(ffpa, W, args.steps, max(args.warmup, 50))
+        paths["forward"] = {f"{n}:{a}": run_forward_path(ffpa, W, n, a, args.steps, args.warmup)
+                            for n, a in FWD_PATHS}
         line["paths"] = paths
     print(json.dumps(line), flush=True)
     if args.copy_calibration:

@@ -574,18 +574,6 @@ void fwd_prefill_kernel(FwdArgs a) {
     asm volatile("" : "+v"(lj));
     const int hij = lj >> 5;
     const int my_qj = qw + (lj & 31);
-    // Register placement for the whole loop. The Q fragments (read-only MFMA
-    // operands) live in AGPRs; the fp32 output accumulators fill the rest of
-    // the AGPRs and spill over into VGPRs. VGPRs then keep room for the score
-    // accumulators and for K/V fragments read ahead from LDS.
-    if constexpr (!ACC16) {
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        if (d < kOAgpr) asm volatile("" : "+a"(o_acc[d]));
-        else asm volatile("" : "+v"(o_acc[d]));
-      }
-    }
-
     // ===== K phase: S^T = K Q^T
     wait_vmcnt<0>();  // K(j) landed (this wave's copies) ...
     wait_lgkm0();
@@ -694,14 +682,7 @@ void fwd_prefill_kernel(FwdArgs a) {
     mx = fmaxf(mx, swap_halves(mx));
 
     float alpha = 1.f;
-    if constexpr (!ACC16) {
-      // first unmasked keys of this row: adopt their max (O and l are still 0)
-      if (m_ref == -INFINITY) m_ref = mx;
-      const bool broke = mx > m_ref + fwd_tau<BF16>();
-      // the ballot runs with the whole wave active; only the store is lane 0's
-      const uint32_t any_broke = __builtin_amdgcn_ballot_w64(broke) != 0 ? 1u : 0u;
-      if (lane == 0) restart_flag[wave] = any_broke;
-    } else {
+    {
       const bool need = mx > m_ref + kRescaleTau;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {  // wave-uniform branch
         const float m_new = fmaxf(m_ref, mx);
@@ -718,29 +699,20 @@ void fwd_prefill_kernel(FwdArgs a) {
         tv[kb][i] = exp2_fast(tv[kb][i] - m_use);
         psum += tv[kb][i];
       }
-    float pscale = 1.f, oscale = 1.f;
-    if constexpr (!ACC16) {
-      l_run += psum;
-    } else {
-      // normalised fp16 accumulator: O <- O * (alpha l_old / l_new) + (P / l_new) V
-      const float l_old = l_run;
-      const float l_new = alpha * l_old + psum + swap_halves(psum);
-      l_run = l_new;
-      pscale = l_new > 0.f ? 1.f / l_new : 0.f;
-      oscale = alpha * l_old * pscale;
-    }
+    // normalised fp16 accumulator: O <- O * (alpha l_old / l_new) + (P / l_new) V
+    const float l_old = l_run;
+    const float l_new = alpha * l_old + psum + swap_halves(psum);
+    l_run = l_new;
+    const float pscale = l_new > 0.f ? 1.f / l_new : 0.f;
+    const float oscale = alpha * l_old * pscale;
     V8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const float* x = &tv[kb][8 * t2];
-        if constexpr (ACC16) {
-          pf[kb][t2] = pack8<BF16>(x[0] * pscale, x[1] * pscale, x[2] * pscale, x[3] * pscale,
-                                   x[4] * pscale, x[5] * pscale, x[6] * pscale, x[7] * pscale);
-        } else {
-          pf[kb][t2] = pack8<BF16>(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
-        }
+        pf[kb][t2] = pack8<BF16>(x[0] * pscale, x[1] * pscale, x[2] * pscale, x[3] * pscale,
+                                 x[4] * pscale, x[5] * pscale, x[6] * pscale, x[7] * pscale);
       }
 
     // P is the B operand of MFMAs issued as inline asm, which the compiler
@@ -755,41 +727,16 @@ void fwd_prefill_kernel(FwdArgs a) {
     wait_vmcnt<0>();  // V(j) landed ...
     wait_lgkm0();
     barrier();        // ... everywhere; everyone is done with K(j)
-    if constexpr (!ACC16) {
-      const u32x4 f = *(const FFPA_LDS u32x4*)restart_flag;
-      if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // workgroup-uniform
-        // restart with the raised reference; O restarts from zero through
-        // `fresh` (the next PV product ignores the old accumulators), which
-        // avoids writing 256 accumulator registers here
-        m_ref = fmaxf(m_ref, mx);
-        l_run = 0.f;
-        fresh = true;
-        issue_k_tile(0);
-        j = -1;
-        continue;
-      }
-    }
-    // The PV products, as a lambda instantiated for the first tile of an
-    // attempt (FRESH: the first product of each block starts from C = 0) and
-    // for the others, so that no MFMA of the hot loop sits behind a branch.
-    auto v_phase = [&](auto fresh_tag) {
-      constexpr bool FRESH = decltype(fresh_tag)::value;
+    {
       // Step order: consecutive MFMAs write different accumulators (a
-      // dependent MFMA waits for its predecessor's result). fp32
-      // accumulators: step st = NDB p + db, p = 2 kb + t2 the (key block,
-      // k-step) pair. fp16 accumulator: d-blocks go in pairs, each with a
-      // per-tile product in VGPRs: st = 8 q + 2 p + side, db = 2 q + side.
-      // V^T fragments are read kVAhead MFMAs ahead of their use.
+      // dependent MFMA waits for its predecessor's result): d-blocks go in
+      // pairs, each with a per-tile product in VGPRs: st = 8 q + 2 p + side,
+      // db = 2 q + side, p = 2 kb + t2 the (key block, k-step) pair. V^T
+      // fragments are read kVAhead MFMAs ahead of their use.
       constexpr int NSV = 4 * NDB;
       auto step = [](int st, int& db, int& kb, int& t2) {
-        int p;
-        if constexpr (ACC16) {
-          p = (st & 7) >> 1;
-          db = 2 * (st >> 3) + (st & 1);
-        } else {
-          p = st / NDB;
-          db = st % NDB;
-        }
+        const int p = (st & 7) >> 1;
+        db = 2 * (st >> 3) + (st & 1);
         kb = p >> 1;
         t2 = p & 1;
       };
@@ -840,77 +787,38 @@ void fwd_prefill_kernel(FwdArgs a) {
         const u32x4 vbits = vf[st % kVAhead];
         if (st + kVAhead < NSV) vf[st % kVAhead] = vread(st + kVAhead);
         const u32x4 pb = __builtin_bit_cast(u32x4, pf[kb][t2]);
-        const bool first = kb == 0 && t2 == 0, last = kb == 1 && t2 == 1;
-        if constexpr (ACC16) {
-          // per-tile products in VGPRs, set q % 2 for pair q = st / 8; the
-          // last pair's last MFMA pads for the fold after the loop
-          const int q = st >> 3, set = q & 1;
-          const bool final_mfma = st == NSV - 1;
-          if ((st & 1) == 0) {
-            if (first) {
-              if (st == 0) mfma32_asm<BF16, false, false, true, true>(acc_e[set], vbits, pb);
-              else mfma32_asm<BF16, false, false, true>(acc_e[set], vbits, pb);
-            } else {
-              mfma32_asm<BF16, false, false>(acc_e[set], vbits, pb);
-            }
+        const bool first = kb == 0 && t2 == 0;
+        // per-tile products in VGPRs, set q % 2 for pair q = st / 8; the
+        // last pair's last MFMA pads for the fold after the loop
+        const int q = st >> 3, set = q & 1;
+        const bool final_mfma = st == NSV - 1;
+        if ((st & 1) == 0) {
+          if (first) {
+            if (st == 0) mfma32_asm<BF16, false, false, true, true>(acc_e[set], vbits, pb);
+            else mfma32_asm<BF16, false, false, true>(acc_e[set], vbits, pb);
           } else {
-            if (first) mfma32_asm<BF16, false, false, true>(acc_o[set], vbits, pb);
-            else if (final_mfma) mfma32_asm<BF16, false, false, false, false, true>(acc_o[set], vbits, pb);
-            else mfma32_asm<BF16, false, false>(acc_o[set], vbits, pb);
-          }
-          // pair q - 1 folds at steps 6 (even block) and 7 (odd block) of
-          // pair q: seven MFMAs of pair q have issued since its last one
-          if (q > 0 && (st & 7) == 6) {
-            pin_after_pad(acc_e[set ^ 1]);
-            pin_after_pad(acc_o[set ^ 1]);
-            fold(acc_e[set ^ 1], 2 * (q - 1));
-          }
-          if (q > 0 && (st & 7) == 7) fold(acc_o[set ^ 1], 2 * (q - 1) + 1);
-          if (final_mfma) {
-            pin_after_pad(acc_e[set]);
-            fold(acc_e[set], 2 * q);
-            fold(acc_o[set], 2 * q + 1);
+            mfma32_asm<BF16, false, false>(acc_e[set], vbits, pb);
           }
         } else {
-          // the first pair starts every block's chain (C = 0 on a fresh
-          // attempt); the first MFMA of the phase pads for the VALU that wrote
-          // P, the last one for accumulator copies on the loop's edges
-          const bool pad_after = st == NSV - 1;
-          if (db < kOAgpr) {
-            if (first) {
-              if (st == 0) {
-                if constexpr (FRESH) mfma32_asm<BF16, false, true, true, true>(o_acc[db], vbits, pb);
-                else mfma32_asm<BF16, false, true, false, true>(o_acc[db], vbits, pb);
-              } else {
-                if constexpr (FRESH) mfma32_asm<BF16, false, true, true>(o_acc[db], vbits, pb);
-                else mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
-              }
-            } else if (pad_after) {
-              mfma32_asm<BF16, false, true, false, false, true>(o_acc[db], vbits, pb);
-            } else {
-              mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
-            }
-          } else {
-            if (first) {
-              if (st == 0) {
-                if constexpr (FRESH) mfma32_asm<BF16, false, false, true, true>(o_acc[db], vbits, pb);
-                else mfma32_asm<BF16, false, false, false, true>(o_acc[db], vbits, pb);
-              } else {
-                if constexpr (FRESH) mfma32_asm<BF16, false, false, true>(o_acc[db], vbits, pb);
-                else mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
-              }
-            } else if (pad_after) {
-              mfma32_asm<BF16, false, false, false, false, true>(o_acc[db], vbits, pb);
-            } else {
-              mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
-            }
-          }
+          if (first) mfma32_asm<BF16, false, false, true>(acc_o[set], vbits, pb);
+          else if (final_mfma) mfma32_asm<BF16, false, false, false, false, true>(acc_o[set], vbits, pb);
+          else mfma32_asm<BF16, false, false>(acc_o[set], vbits, pb);
+        }
+        // pair q - 1 folds at steps 6 (even block) and 7 (odd block) of
+        // pair q: seven MFMAs of pair q have issued since its last one
+        if (q > 0 && (st & 7) == 6) {
+          pin_after_pad(acc_e[set ^ 1]);
+          pin_after_pad(acc_o[set ^ 1]);
+          fold(acc_e[set ^ 1], 2 * (q - 1));
+        }
+        if (q > 0 && (st & 7) == 7) fold(acc_o[set ^ 1], 2 * (q - 1) + 1);
+        if (final_mfma) {
+          pin_after_pad(acc_e[set]);
+          fold(acc_e[set], 2 * q);
+          fold(acc_o[set], 2 * q + 1);
         }
       }
-    };
-    if (!ACC16 && fresh) v_phase(BoolTag<true>{});
-    else v_phase(BoolTag<false>{});
-    fresh = false;
+    }
   }
   }
   wait_vmcnt<0>();  // no copy may still target this workgroup's LDS when it ends

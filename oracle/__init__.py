@@ -12,6 +12,8 @@ differences, closed forms (Q = 0, Nkv = 1, causal row 0, constant V) and
 structural invariants (masking = deleting keys, GQA = repeat_interleave,
 row independence, key permutation, backward sum rules).
 """
-from .attention import attn_bwd, attn_fwd, attn_probs, to_f64
+from .attention import (attn_bwd, attn_fwd, attn_probs, dropout_keep, dropout_threshold,
+                        philox4x32_10, to_f64)
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_probs", "to_f64"]
+__all__ = ["attn_fwd", "attn_bwd", "attn_probs", "to_f64", "philox4x32_10", "dropout_threshold",
+           "dropout_keep"]

@@ -97,6 +97,13 @@ def test_head_dim_sweep(lib, D, accum):
     _check_forward(lib, f"dsweep{D}_{accum}")
 
 
+@pytest.mark.parametrize("name", ["self16k", "self16k_bf16", "causal16k", "nonaligned16k"])
+@pytest.mark.parametrize("accum", ["f32", "f16"])
+def test_16k_forward(lib, name, accum):
+    """16K sequences (B1 H32 N16384 D512): whole heads against the oracle."""
+    _check_forward(lib, name, accum)
+
+
 def test_decode(lib):
     """Decode (one query row per head): 64 of the 512 heads, every one whole."""
     w = W.WORKLOADS["decode"]
@@ -139,7 +146,8 @@ def bf16_neighbours(x):
     return lo, hi
 
 
-@pytest.mark.parametrize("name", ["bwd", "bwd_causal", "bwd_d1024", "bwd_d1024_causal"])
+@pytest.mark.parametrize("name", ["bwd", "bwd_causal", "bwd_d1024", "bwd_d1024_causal", "bwd16k",
+                                  "bwd16k_causal"])
 def test_full_size_backward(lib, name):
     """The backward at its benchmark size after this library's own forward (the
     path bench.py times, with its default bounded workspace); whole heads of
@@ -166,7 +174,8 @@ def test_full_size_backward(lib, name):
     dq, dk, dv = lib.attention_backward(do, q, k, v, o, lse, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     assert w.dtype == "bf16"
-    for b, h in _heads(w):
+    # one whole head at 16K (the bound materialises P: 2 GiB per head), two below
+    for b, h in (_heads(w) if w.Nq <= 8192 else [(w.B - 1, w.Hq - 1)]):
         sl = lambda t: t[b:b + 1, h:h + 1].cpu()
         refs = attn_bwd(sl(q), sl(k), sl(v), sl(do), w.scale, causal=w.causal)
         bounds = _rounding_bounds(sl(q), sl(k), sl(v), sl(do), w.scale, w.causal, None, refs, "bf16")

@@ -27,7 +27,7 @@ MUTANTS = {
     "lse_dropped_log": ("m_safe + np.log(np.where(dead, 1.0, l))", "m_safe + 0.0 * l"),
     "softmax_unnormalised": ("e / np.where(dead, 1.0, l)[:, None]", "e"),
     "bwd_dropped_delta": ("ds = p * (dp - delta[:, None])", "ds = p * dp"),
-    "bwd_dv_no_group_sum": ("dv[b, hk] += p.T @ do", "dv[b, hk] = p.T @ do"),
+    "bwd_dv_no_group_sum": ("dv[b, hk] += (p * zc).T @ do", "dv[b, hk] = (p * zc).T @ do"),
     "bwd_dk_dropped_scale": ("dk[b, hk] += scale * (ds.T", "dk[b, hk] += (ds.T"),
     "bwd_dq_transposed": ("dq[b, h, r0:r1] = scale * (ds @ k[b, hk])",
                           "dq[b, h, r0:r1] = scale * (ds @ v[b, hk])"),

@@ -86,6 +86,16 @@ WORKLOADS = {
     "bwd_d1024_causal": _w("bwd_d1024_causal", 4, 1, 32, 32, 8192, 8192, 1024, dtype="bf16",
                            causal=True, backward=True),
 }
+# 16K sequences (the CuTeDSL tables of "FFPA Attention Benchmark" at 16K, D = 512)
+WORKLOADS.update({
+    "self16k": _w("self16k", 5, 1, 32, 32, 16384, 16384, 512),
+    "self16k_bf16": _w("self16k_bf16", 5, 1, 32, 32, 16384, 16384, 512, dtype="bf16"),
+    "causal16k": _w("causal16k", 5, 1, 32, 32, 16384, 16384, 512, causal=True),
+    "nonaligned16k": _w("nonaligned16k", 5, 1, 32, 32, 16383, 16383, 512),
+    "bwd16k": _w("bwd16k", 6, 1, 32, 32, 16384, 16384, 512, dtype="bf16", backward=True),
+    "bwd16k_causal": _w("bwd16k_causal", 6, 1, 32, 32, 16384, 16384, 512, dtype="bf16",
+                        causal=True, backward=True),
+})
 # bf16 variants of the variant family (same float32 draws as the fp16 ones)
 for _n in ("cross", "gqa", "causal", "nonaligned", "mask"):
     WORKLOADS[f"{_n}_bf16"] = WORKLOADS[_n].replace(name=f"{_n}_bf16", dtype="bf16")
