@@ -320,7 +320,8 @@ void fwd_prefill_kernel(FwdArgs a) {
   }
   float m_ref = -INFINITY;  // reference max (log2 domain)
   float l_run = 0.f;        // ACC32: this lane's partial row sum; ACC16: full row sum
-  bool fresh = true;        // ACC32: no PV product accumulated yet in this attempt
+  bool fresh = true;        // ACC32: no PV product accumulated yet
+  bool safe = false;        // ACC32: a tile broke m_ref + tau; the key loop reruns per tile
   // one word per wave: did a row of that wave break m_ref + tau in this tile
   FFPA_LDS uint32_t* restart_flag = (FFPA_LDS uint32_t*)(smem + fwd_ring_bytes<D>() +
                                                          (key_bias ? fwd_bias_bytes(a.Nkv) : 0));
@@ -354,14 +355,11 @@ void fwd_prefill_kernel(FwdArgs a) {
       if (j > 0) {
         const u32x4 f = *(const FFPA_LDS u32x4*)restart_flag;
         if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // workgroup-uniform
-          // restart with the raised reference; O restarts from zero through
-          // `fresh` (the next P V products ignore the old accumulators)
+          // the rest runs in the per-tile loop below, from the first tile,
+          // with the raised reference: no tile can force a second pass
           m_ref = fmaxf(m_ref, mx_prev);
-          l_run = 0.f;
-          fresh = true;
-          issue_k_tile(0);
-          j = -1;
-          continue;
+          safe = true;
+          break;
         }
       }
       if (j == n_tiles) break;
@@ -563,7 +561,23 @@ void fwd_prefill_kernel(FwdArgs a) {
       else v_phase(BoolTag<false>{});
       fresh = false;
     }
-  } else {
+  }
+  // ---- the per-tile loop: the fp16 accumulator (renormalised every tile),
+  // and with fp32 accumulation the safe mode after a tile broke the bound
+  // (P of a tile computed from the raised reference before its products;
+  // O rescaled when the reference rises by more than tau). Its score and
+  // product phases run one after the other.
+  if (ACC16 || safe) {
+  if constexpr (!ACC16) {
+    // the fast loop's copies in flight land before the buffers are reused;
+    // O and l start over
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    barrier();
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) o_acc[d] = f32x16{};
+    l_run = 0.f;
+  }
   issue_k_tile(0);
 
   for (int j = 0; j < n_tiles; ++j) {
@@ -574,6 +588,13 @@ void fwd_prefill_kernel(FwdArgs a) {
     asm volatile("" : "+v"(lj));
     const int hij = lj >> 5;
     const int my_qj = qw + (lj & 31);
+    if constexpr (!ACC16) {
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        if (d < kOAgpr) asm volatile("" : "+a"(o_acc[d]));
+        else asm volatile("" : "+v"(o_acc[d]));
+      }
+    }
     // ===== K phase: S^T = K Q^T
     wait_vmcnt<0>();  // K(j) landed (this wave's copies) ...
     wait_lgkm0();
@@ -683,11 +704,25 @@ void fwd_prefill_kernel(FwdArgs a) {
 
     float alpha = 1.f;
     {
-      const bool need = mx > m_ref + kRescaleTau;
+      const bool need = mx > m_ref + (ACC16 ? kRescaleTau : fwd_tau<BF16>());
       if (__builtin_amdgcn_ballot_w64(need) != 0) {  // wave-uniform branch
         const float m_new = fmaxf(m_ref, mx);
         alpha = (m_new == -INFINITY) ? 1.f : exp2_fast(m_ref - m_new);
         m_ref = m_new;
+        if constexpr (!ACC16) {
+          // fp32 O follows the raised reference; the pins keep the products
+          // of this tile behind the rescale
+#pragma unroll
+          for (int d = 0; d < NDB; ++d) {
+            if (d < kOAgpr) {
+              scale_agpr16(o_acc[d], alpha);
+              asm volatile("" : "+a"(o_acc[d]));
+            } else {
+              o_acc[d] *= alpha;
+              asm volatile("" : "+v"(o_acc[d]));
+            }
+          }
+        }
       }
     }
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
@@ -699,20 +734,29 @@ void fwd_prefill_kernel(FwdArgs a) {
         tv[kb][i] = exp2_fast(tv[kb][i] - m_use);
         psum += tv[kb][i];
       }
-    // normalised fp16 accumulator: O <- O * (alpha l_old / l_new) + (P / l_new) V
-    const float l_old = l_run;
-    const float l_new = alpha * l_old + psum + swap_halves(psum);
-    l_run = l_new;
-    const float pscale = l_new > 0.f ? 1.f / l_new : 0.f;
-    const float oscale = alpha * l_old * pscale;
+    // fp16: normalised accumulator, O <- O * (alpha l_old / l_new) + (P / l_new) V;
+    // fp32: O <- alpha O + P V, this lane's partial sum as in the fast loop
+    float pscale = 1.f, oscale = 1.f;
+    if constexpr (ACC16) {
+      const float l_old = l_run;
+      const float l_new = alpha * l_old + psum + swap_halves(psum);
+      l_run = l_new;
+      pscale = l_new > 0.f ? 1.f / l_new : 0.f;
+      oscale = alpha * l_old * pscale;
+    } else {
+      l_run = alpha * l_run + psum;
+    }
     V8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const float* x = &tv[kb][8 * t2];
-        pf[kb][t2] = pack8<BF16>(x[0] * pscale, x[1] * pscale, x[2] * pscale, x[3] * pscale,
-                                 x[4] * pscale, x[5] * pscale, x[6] * pscale, x[7] * pscale);
+        if constexpr (ACC16)
+          pf[kb][t2] = pack8<BF16>(x[0] * pscale, x[1] * pscale, x[2] * pscale, x[3] * pscale,
+                                   x[4] * pscale, x[5] * pscale, x[6] * pscale, x[7] * pscale);
+        else
+          pf[kb][t2] = pack8<BF16>(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
       }
 
     // P is the B operand of MFMAs issued as inline asm, which the compiler
@@ -729,14 +773,21 @@ void fwd_prefill_kernel(FwdArgs a) {
     barrier();        // ... everywhere; everyone is done with K(j)
     {
       // Step order: consecutive MFMAs write different accumulators (a
-      // dependent MFMA waits for its predecessor's result): d-blocks go in
-      // pairs, each with a per-tile product in VGPRs: st = 8 q + 2 p + side,
-      // db = 2 q + side, p = 2 kb + t2 the (key block, k-step) pair. V^T
-      // fragments are read kVAhead MFMAs ahead of their use.
+      // dependent MFMA waits for its predecessor's result). fp16: d-blocks go
+      // in pairs, each with a per-tile product in VGPRs: st = 8 q + 2 p +
+      // side, db = 2 q + side, p = 2 kb + t2 the (key block, k-step) pair.
+      // fp32: st = NDB p + db. V^T fragments are read kVAhead MFMAs ahead of
+      // their use.
       constexpr int NSV = 4 * NDB;
       auto step = [](int st, int& db, int& kb, int& t2) {
-        const int p = (st & 7) >> 1;
-        db = 2 * (st >> 3) + (st & 1);
+        int p;
+        if constexpr (ACC16) {
+          p = (st & 7) >> 1;
+          db = 2 * (st >> 3) + (st & 1);
+        } else {
+          p = st / NDB;
+          db = st % NDB;
+        }
         kb = p >> 1;
         t2 = p & 1;
       };
@@ -788,34 +839,49 @@ void fwd_prefill_kernel(FwdArgs a) {
         if (st + kVAhead < NSV) vf[st % kVAhead] = vread(st + kVAhead);
         const u32x4 pb = __builtin_bit_cast(u32x4, pf[kb][t2]);
         const bool first = kb == 0 && t2 == 0;
-        // per-tile products in VGPRs, set q % 2 for pair q = st / 8; the
-        // last pair's last MFMA pads for the fold after the loop
-        const int q = st >> 3, set = q & 1;
         const bool final_mfma = st == NSV - 1;
-        if ((st & 1) == 0) {
-          if (first) {
-            if (st == 0) mfma32_asm<BF16, false, false, true, true>(acc_e[set], vbits, pb);
-            else mfma32_asm<BF16, false, false, true>(acc_e[set], vbits, pb);
+        if constexpr (ACC16) {
+          // per-tile products in VGPRs, set q % 2 for pair q = st / 8; the
+          // last pair's last MFMA pads for the fold after the loop
+          const int q = st >> 3, set = q & 1;
+          if ((st & 1) == 0) {
+            if (first) {
+              if (st == 0) mfma32_asm<BF16, false, false, true, true>(acc_e[set], vbits, pb);
+              else mfma32_asm<BF16, false, false, true>(acc_e[set], vbits, pb);
+            } else {
+              mfma32_asm<BF16, false, false>(acc_e[set], vbits, pb);
+            }
           } else {
-            mfma32_asm<BF16, false, false>(acc_e[set], vbits, pb);
+            if (first) mfma32_asm<BF16, false, false, true>(acc_o[set], vbits, pb);
+            else if (final_mfma) mfma32_asm<BF16, false, false, false, false, true>(acc_o[set], vbits, pb);
+            else mfma32_asm<BF16, false, false>(acc_o[set], vbits, pb);
+          }
+          // pair q - 1 folds at steps 6 (even block) and 7 (odd block) of
+          // pair q: seven MFMAs of pair q have issued since its last one
+          if (q > 0 && (st & 7) == 6) {
+            pin_after_pad(acc_e[set ^ 1]);
+            pin_after_pad(acc_o[set ^ 1]);
+            fold(acc_e[set ^ 1], 2 * (q - 1));
+          }
+          if (q > 0 && (st & 7) == 7) fold(acc_o[set ^ 1], 2 * (q - 1) + 1);
+          if (final_mfma) {
+            pin_after_pad(acc_e[set]);
+            fold(acc_e[set], 2 * q);
+            fold(acc_o[set], 2 * q + 1);
           }
         } else {
-          if (first) mfma32_asm<BF16, false, false, true>(acc_o[set], vbits, pb);
-          else if (final_mfma) mfma32_asm<BF16, false, false, false, false, true>(acc_o[set], vbits, pb);
-          else mfma32_asm<BF16, false, false>(acc_o[set], vbits, pb);
-        }
-        // pair q - 1 folds at steps 6 (even block) and 7 (odd block) of
-        // pair q: seven MFMAs of pair q have issued since its last one
-        if (q > 0 && (st & 7) == 6) {
-          pin_after_pad(acc_e[set ^ 1]);
-          pin_after_pad(acc_o[set ^ 1]);
-          fold(acc_e[set ^ 1], 2 * (q - 1));
-        }
-        if (q > 0 && (st & 7) == 7) fold(acc_o[set ^ 1], 2 * (q - 1) + 1);
-        if (final_mfma) {
-          pin_after_pad(acc_e[set]);
-          fold(acc_e[set], 2 * q);
-          fold(acc_o[set], 2 * q + 1);
+          // fp32 O accumulates in place (zeroed before the loop); the first
+          // MFMA pads for the VALU that wrote P (and a rescale), the last for
+          // whatever reads the accumulators after the phase
+          if (db < kOAgpr) {
+            if (st == 0) mfma32_asm<BF16, false, true, false, true>(o_acc[db], vbits, pb);
+            else if (final_mfma) mfma32_asm<BF16, false, true, false, false, true>(o_acc[db], vbits, pb);
+            else mfma32_asm<BF16, false, true>(o_acc[db], vbits, pb);
+          } else {
+            if (st == 0) mfma32_asm<BF16, false, false, false, true>(o_acc[db], vbits, pb);
+            else if (final_mfma) mfma32_asm<BF16, false, false, false, false, true>(o_acc[db], vbits, pb);
+            else mfma32_asm<BF16, false, false>(o_acc[db], vbits, pb);
+          }
         }
       }
     }

@@ -15,8 +15,8 @@
 //   2. swaps it with the wave holding the other half of the same rows through
 //      LDS and adds (a + b is the same in either order, so both waves hold
 //      identical scores and take identical softmax decisions);
-//   3. runs the online softmax (restart-based reference max, as in the
-//      prefill kernel with fp32 accumulation);
+//   3. runs the online softmax: a reference max per row, raised (with O
+//      and l rescaled) only when a tile's max breaks it by more than tau;
 //   4. accumulates O^T_half += V_half^T P^T.
 // Tiles are 32 keys. A staged K tile holds both halves, each as 32 dense rows
 // of W / 8 granules (dense_pos: granules swizzled inside groups of 16, 8 or
@@ -50,7 +50,7 @@ constexpr int kWideBc = 32;                      // keys per tile
 constexpr int kWideTile = 64 * 1024;             // LDS buffer of one staged K or V^T tile
 
 constexpr int kWideXchg = 4096;                  // per wave: a 32 x 32 fp32 tile
-constexpr int kWideLds = 2 * kWideTile + 4 * kWideXchg + 16;
+constexpr int kWideLds = 2 * kWideTile + 4 * kWideXchg;
 
 template <int D, bool BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -63,7 +63,7 @@ void fwd_wide_kernel(FwdArgs a) {
   constexpr int HALF = kWideBc * SG * 16;  // bytes of one dense K half-tile
   constexpr int NS = W / 16;            // k-steps of the partial product
   constexpr int NDB = W / 32;           // output d-blocks of the half
-  constexpr int KB = 0, VB = kWideTile, XB = 2 * kWideTile, FB = 2 * kWideTile + 4 * kWideXchg;
+  constexpr int KB = 0, VB = kWideTile, XB = 2 * kWideTile;
   constexpr int kKAhead = 8;
   constexpr int kVAhead = 12;
   // fp32 accumulator d-blocks in AGPRs (beside the W/4 Q registers); the rest in VGPRs
@@ -176,8 +176,7 @@ void fwd_wide_kernel(FwdArgs a) {
   for (int i = 0; i < NDB; ++i) o_acc[i] = f32x16{};
   float m_ref = -INFINITY;  // reference max (log2 domain)
   float l_run = 0.f;        // this lane's partial row sum
-  bool fresh = true;        // no PV product accumulated yet in this attempt
-  FFPA_LDS uint32_t* restart_flag = (FFPA_LDS uint32_t*)(smem + FB);
+  bool fresh = true;        // no PV product accumulated yet
 
   if (n_tiles > 0) issue_k_tile(0);
 
@@ -270,11 +269,24 @@ void fwd_wide_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, tv[i]);
     mx = fmaxf(mx, swap_halves(mx));
-    if (m_ref == -INFINITY) m_ref = mx;
-    {
-      const bool broke = mx > m_ref + fwd_tau<BF16>();
-      const uint32_t any_broke = __builtin_amdgcn_ballot_w64(broke) != 0 ? 1u : 0u;
-      if (lane == 0) restart_flag[wave] = any_broke;
+    // The reference max rises (and O and l follow it) when a row's max breaks
+    // m_ref + tau; P = 2^(t - m_ref) then stays within 2^tau. The two waves
+    // of a pair hold identical scores, so they take identical decisions.
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + fwd_tau<BF16>()) != 0) {  // wave-uniform
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        if (d < kOAgpr) {
+          scale_agpr16(o_acc[d], alpha);
+          asm volatile("" : "+a"(o_acc[d]));
+        } else {
+          o_acc[d] *= alpha;
+          asm volatile("" : "+v"(o_acc[d]));
+        }
+      }
     }
     const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
     float psum = 0.f;
@@ -297,17 +309,6 @@ void fwd_wide_kernel(FwdArgs a) {
     wait_vmcnt<0>();
     wait_lgkm0();
     barrier();
-    {
-      const u32x4 f = *(const FFPA_LDS u32x4*)restart_flag;
-      if ((f[0] | f[1] | f[2] | f[3]) != 0) {  // workgroup-uniform: restart the key loop
-        m_ref = fmaxf(m_ref, mx);
-        l_run = 0.f;
-        fresh = true;
-        issue_k_tile(0);
-        j = -1;
-        continue;
-      }
-    }
     // The PV products, as a lambda instantiated for the first tile of an
     // attempt (FRESH: the t2 = 0 product of each block starts from C = 0) and
     // for the others, so that no MFMA of the hot loop sits behind a branch.
