@@ -19,6 +19,7 @@ from typing import Optional
 
 __all__ = [
     "load", "FFPAError", "ffpa_attn_fwd", "ffpa_attn_fwd_noalloc", "ffpa_attn_bwd",
+    "ffpa_attn_fwd_dropout", "ffpa_attn_bwd_dropout",
     "ffpa_attn_fwd_workspace_size",
     "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min", "ffpa_last_error",
     "ffpa_version", "attention",
@@ -36,8 +37,8 @@ _STATUS = {1: "FFPA_ERR_INVALID_ARG", 2: "FFPA_ERR_UNSUPPORTED", 3: "FFPA_ERR_WO
 
 # Symbols declared in include/ffpa_attn.h.
 EXPORTED = ("ffpa_attn_fwd", "ffpa_attn_fwd_workspace_size", "ffpa_attn_fwd_noalloc", "ffpa_attn_bwd",
-            "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min", "ffpa_last_error",
-            "ffpa_version")
+            "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min",
+            "ffpa_attn_fwd_dropout", "ffpa_attn_bwd_dropout", "ffpa_last_error", "ffpa_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -65,6 +66,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffpa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i,
                                   i, i, vp, sz, vp]
     lib.ffpa_attn_bwd.restype = i
+    u64 = ctypes.c_uint64
+    lib.ffpa_attn_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, i, i, f, u64,
+                                          vp, sz, vp]
+    lib.ffpa_attn_fwd_dropout.restype = i
+    lib.ffpa_attn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp,
+                                          i, i, i, f, u64, vp, sz, vp]
+    lib.ffpa_attn_bwd_dropout.restype = i
     lib.ffpa_attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.ffpa_attn_fwd_workspace_size.restype = sz
     lib.ffpa_attn_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
@@ -126,6 +134,33 @@ def ffpa_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, sca
     return load().ffpa_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale,
                                 causal, mask or None, mask_rows, accum_dtype, dtype,
                                 workspace or None, workspace_bytes, stream or None)
+
+
+def ffpa_attn_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                          accum_dtype, dtype, dropout_p, seed, workspace, workspace_bytes,
+                          stream) -> int:
+    """Raw C call of the forward with dropout on the probabilities."""
+    return load().ffpa_attn_fwd_dropout(q, k, v, o, lse or None, B, Hq, Hkv, Nq, Nkv, D, scale,
+                                        causal, mask or None, mask_rows, accum_dtype, dtype,
+                                        dropout_p, seed, workspace or None, workspace_bytes,
+                                        stream or None)
+
+
+def ffpa_attn_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
+                          mask, mask_rows, accum_dtype, dtype, dropout_p, seed, workspace,
+                          workspace_bytes, stream) -> int:
+    """Raw C call of the backward of the forward with dropout."""
+    return load().ffpa_attn_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D,
+                                        scale, causal, mask or None, mask_rows, accum_dtype, dtype,
+                                        dropout_p, seed, workspace or None, workspace_bytes,
+                                        stream or None)
+
+
+def _seed(seed) -> int:
+    seed = int(seed)
+    if not 0 <= seed < 1 << 64:
+        raise ValueError("seed must be an unsigned 64-bit integer")
+    return seed
 
 
 # ---------------------------------------------------------------------------
@@ -195,8 +230,12 @@ def _mask_args(mask, q, Nq, Nkv):
 
 def attention(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float] = None,
               accum: str = "f32", return_lse: bool = False, out=None, lse_out=None,
-              workspace=None):
-    """O = softmax(scale q k^T + mask) v on the current HIP stream (see include/ffpa_attn.h)."""
+              workspace=None, dropout_p: float = 0.0, seed: int = 0):
+    """O = softmax(scale q k^T + mask) v on the current HIP stream (see include/ffpa_attn.h).
+
+    dropout_p > 0 drops attention probabilities with the counter-based keep
+    mask of ffpa_attn_fwd_dropout (seed: unsigned 64-bit); the backward needs
+    the same dropout_p and seed."""
     import torch
 
     B, Hq, Hkv, Nq, Nkv, D = _dims(q, k, v)
@@ -224,16 +263,20 @@ def attention(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float
     else:
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(ffpa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                         lse.data_ptr() if lse is not None else 0, B, Hq, Hkv, Nq, Nkv, D, scale,
-                         int(causal), mptr, mrows, _accum_code(accum), dt,
-                         ws.data_ptr() if ws is not None else 0, ws_bytes, stream))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr() if lse is not None else 0,
+            B, Hq, Hkv, Nq, Nkv, D, scale, int(causal), mptr, mrows, _accum_code(accum), dt)
+    tail = (ws.data_ptr() if ws is not None else 0, ws_bytes, stream)
+    if dropout_p:
+        _check(ffpa_attn_fwd_dropout(*args, float(dropout_p), _seed(seed), *tail))
+    else:
+        _check(ffpa_attn_fwd(*args, *tail))
     return (o, lse) if return_lse else o
 
 
 def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None,
                        scale: Optional[float] = None, store_ds: bool = True,
-                       workspace_bytes: Optional[int] = None):
+                       workspace_bytes: Optional[int] = None, dropout_p: float = 0.0,
+                       seed: int = 0):
     """(dq, dk, dv) of attention on the current HIP stream; o, lse from ``attention``.
 
     store_ds=True (default) gives the call ffpa_attn_bwd_workspace_size bytes:
@@ -241,7 +284,8 @@ def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None
     fits a bounded buffer. store_ds=False gives it the minimum
     (ffpa_attn_bwd_workspace_size_min): dQ then recomputes S and dP.
     workspace_bytes overrides either size (at least the minimum; the library
-    takes the stored-dS path when it holds K^T and one kv head's dS)."""
+    takes the stored-dS path when it holds K^T and one kv head's dS).
+    dropout_p and seed: those of the forward (ffpa_attn_bwd_dropout)."""
     import torch
 
     B, Hq, Hkv, Nq, Nkv, D = _dims(q, k, v)
@@ -257,8 +301,12 @@ def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None
         workspace_bytes = size(B, Hq, Hkv, Nq, Nkv, D, dt)
     ws = torch.empty(max(workspace_bytes, 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(ffpa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv,
-                         Nq, Nkv, D, scale, int(causal), mptr, mrows, ACC_F32, dt, ws.data_ptr(),
-                         workspace_bytes, stream))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, scale, int(causal),
+            mptr, mrows, ACC_F32, dt)
+    tail = (ws.data_ptr(), workspace_bytes, stream)
+    if dropout_p:
+        _check(ffpa_attn_bwd_dropout(*args, float(dropout_p), _seed(seed), *tail))
+    else:
+        _check(ffpa_attn_bwd(*args, *tail))
     return dq, dk, dv

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <mutex>
 #include <string>
@@ -31,17 +32,19 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 using FwdLauncher = hipError_t (*)(const ffpa::FwdArgs&, size_t, hipStream_t);
 
 template <int D, bool VT>
-FwdLauncher pick_fwd(int bf16, int acc16) {
+FwdLauncher pick_fwd(int bf16, int acc16, bool drop) {
+  // dropout is built with the fp32 accumulator (the caller has checked)
+  if (drop) return bf16 ? ffpa::launch_fwd_prefill<D, true, false, VT, true> : ffpa::launch_fwd_prefill<D, false, false, VT, true>;
   if (bf16) return acc16 ? ffpa::launch_fwd_prefill<D, true, true, VT> : ffpa::launch_fwd_prefill<D, true, false, VT>;
   return acc16 ? ffpa::launch_fwd_prefill<D, false, true, VT> : ffpa::launch_fwd_prefill<D, false, false, VT>;
 }
 
-FwdLauncher fwd_launcher(int D, int bf16, int acc16, bool vt, size_t* ring_bytes) {
+FwdLauncher fwd_launcher(int D, int bf16, int acc16, bool vt, bool drop, size_t* ring_bytes) {
   switch (D) {
 #define FFPA_CASE(DD)                                                  \
   case DD:                                                             \
     *ring_bytes = ffpa::fwd_ring_bytes<DD>();                          \
-    return vt ? pick_fwd<DD, true>(bf16, acc16) : pick_fwd<DD, false>(bf16, acc16);
+    return vt ? pick_fwd<DD, true>(bf16, acc16, drop) : pick_fwd<DD, false>(bf16, acc16, drop);
     FFPA_CASE(64)
     FFPA_CASE(128)
     FFPA_CASE(192)
@@ -60,11 +63,12 @@ using WideLauncher = hipError_t (*)(const ffpa::FwdArgs&, hipStream_t);
 
 // fp32 output accumulator: fwd_wide_kernel (64 rows per workgroup); fp16:
 // fwd_wide16_kernel (wide16_rows<D>() rows per workgroup, 128 up to D = 768)
-WideLauncher wide_launcher(int D, int bf16, int acc16, int* rows) {
+WideLauncher wide_launcher(int D, int bf16, int acc16, bool drop, int* rows) {
   switch (D) {
 #define FFPA_CASE(DD)                                                                       \
   case DD:                                                                                  \
     *rows = acc16 ? ffpa::wide16_rows<DD>() : 64;                                           \
+    if (drop) return bf16 ? ffpa::launch_fwd_wide<DD, true, true> : ffpa::launch_fwd_wide<DD, false, true>; \
     if (acc16) return bf16 ? ffpa::launch_fwd_wide16<DD, true> : ffpa::launch_fwd_wide16<DD, false>; \
     return bf16 ? ffpa::launch_fwd_wide<DD, true> : ffpa::launch_fwd_wide<DD, false>;
     FFPA_CASE(576) FFPA_CASE(640) FFPA_CASE(704) FFPA_CASE(768)
@@ -177,6 +181,19 @@ size_t ffpa_attn_fwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
 
 namespace {
 
+// Dropout parameters from a probability: threshold t = round(256 p) in
+// float32 (an element is kept when its generator byte is >= t), the scale of
+// a kept element 256 / (256 - t). p must lie in [0, 1); t = 0 means none.
+int drop_params(float p, uint64_t seed, ffpa::DropParams* d) {
+  if (!(p >= 0.f && p < 1.f)) return fail(FFPA_ERR_INVALID_ARG, "dropout_p must lie in [0, 1)");
+  const float t = std::min(std::floor(256.f * p + 0.5f), 255.f);
+  d->t = (uint32_t)t;
+  d->seed_lo = (uint32_t)seed;
+  d->seed_hi = (uint32_t)(seed >> 32);
+  d->scale = d->t ? 256.f / (256.f - t) : 1.f;
+  return FFPA_OK;
+}
+
 // Checks of ffpa_attn_fwd's arguments that come before the workspace.
 int fwd_check_args(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                    int Hkv, int Nq, int Nkv, int D, float scale, int causal, const void* mask,
@@ -197,7 +214,10 @@ int fwd_check_args(const void* q, const void* k, const void* v, void* o, float* 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int Nq, int Nkv, int D, float scale, int causal, const void* mask,
              int mask_rows, int accum_dtype, int dtype, void* workspace, size_t workspace_bytes,
-             bool allow_vt, void* stream) {
+             bool allow_vt, void* stream, const ffpa::DropParams& drop = ffpa::DropParams{}) {
+  const bool dropout = drop.t != 0;
+  if (dropout && accum_dtype != FFPA_ACC_F32)
+    return fail(FFPA_ERR_UNSUPPORTED, "dropout is built with the fp32 accumulator (FFPA_ACC_F32)");
   if (!aligned16(workspace)) return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   const bool no_vt = !allow_vt && Nq > 1 && D <= 512;
   const size_t need = no_vt ? 0 : ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
@@ -220,6 +240,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.n_waves = (int)waves;
     a.part_o = (float*)workspace;
     a.part_lse = (float*)workspace + (size_t)waves * D;
+    a.drop = drop;
     hipError_t e = launch(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
     return FFPA_OK;
@@ -228,7 +249,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (D > 512) {
     // head dimensions above 512: D split across wave pairs
     int rows = 64;
-    WideLauncher launch = wide_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, &rows);
+    WideLauncher launch = wide_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, dropout, &rows);
     if (launch == nullptr)
       return fail(FFPA_ERR_UNSUPPORTED, "for Nq > 1, D above 512 must be a multiple of 64");
     ffpa::FwdArgs a{};
@@ -245,6 +266,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.total_wg = (int)total;
     a.vt = workspace;
     a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
+    a.drop = drop;
     if (!ffpa::fwd_vt_grid_ok(B * Hkv, Nkv, D)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
     const hipError_t e = launch(a, (hipStream_t)stream);  // V^T pass, then the kernel
     if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -253,7 +275,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
 
   size_t ring = 0;
   const bool vt = !no_vt && ffpa::fwd_use_vt(Hq, Hkv, Nq);
-  FwdLauncher launch = fwd_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, vt, &ring);
+  FwdLauncher launch = fwd_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, vt, dropout, &ring);
   if (launch == nullptr) return fail(FFPA_ERR_UNSUPPORTED, "this head dimension is not built yet");
   size_t lds = ring + ffpa::kFwdFlagBytes;
   // a key bias is staged in LDS when it fits beside the tiles; otherwise the
@@ -276,6 +298,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.total_wg = (int)total;
   a.vt = workspace;
   a.nkv_pad = ffpa::fwd_nkv_pad(Nkv);
+  a.drop = drop;
   if (vt && !ffpa::fwd_vt_grid_ok(B * Hkv, Nkv, D)) return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
   const hipError_t e = launch(a, lds, (hipStream_t)stream);  // [V^T pass,] the kernel
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -296,6 +319,21 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   if (st != FFPA_OK) return st;
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
                   dtype, workspace, workspace_bytes, true, stream);
+}
+
+int ffpa_attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                          int Hkv, int Nq, int Nkv, int D, float scale, int causal, const void* mask,
+                          int mask_rows, int accum_dtype, int dtype, float dropout_p, uint64_t seed,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  const int st = fwd_check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                                accum_dtype, dtype);
+  if (st != FFPA_OK) return st;
+  ffpa::DropParams drop{};
+  const int dst = drop_params(dropout_p, seed, &drop);
+  if (dst != FFPA_OK) return dst;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
+                  dtype, workspace, workspace_bytes, true, stream, drop);
 }
 
 }  // extern "C"
@@ -405,11 +443,15 @@ size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
   return base + bwd_kt_bytes(B, Hkv, Nkv, D) + (size_t)chunk * bwd_ds_bytes_kvhead(Hq, Hkv, Nq, Nkv);
 }
 
-int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
-                  int Nkv, int D, float scale, int causal, const void* mask, int mask_rows,
-                  int accum_dtype, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+             int Nkv, int D, float scale, int causal, const void* mask, int mask_rows,
+             int accum_dtype, int dtype, void* workspace, size_t workspace_bytes, void* stream,
+             bool with_drop, float dropout_p, uint64_t seed) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
     return fail(FFPA_ERR_INVALID_ARG, "q, k, v, o, dout, lse, dq, dk and dv must be non-null");
   int st = check_common(B, Hq, Hkv, Nq, Nkv, D, causal, mask, mask_rows, accum_dtype, dtype);
@@ -420,6 +462,11 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(mask) ||
       !aligned16(workspace))
     return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  ffpa::DropParams drop{};
+  if (with_drop) {
+    const int dst = drop_params(dropout_p, seed, &drop);
+    if (dst != FFPA_OK) return dst;
+  }
   const size_t need = ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_bwd_workspace_size_min()");
@@ -447,6 +494,8 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   a.causal = causal;
   a.scale = scale;
   a.scale_log2 = scale * ffpa::kLog2e;
+  a.drop = drop;
+  a.bh0 = 0;
   const int rows = ffpa::bwd_rows_per_wg(D);  // keys per dK/dV workgroup, queries per dQ one
   const int64_t wg_dkdv = (int64_t)B * Hkv * ((Nkv + rows - 1) / rows);
   const int64_t wg_dq = (int64_t)B * Hq * ((Nq + rows - 1) / rows);
@@ -470,6 +519,29 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
   const hipError_t e = launch(a, chunk_kv, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
   return FFPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+                  int Nkv, int D, float scale, int causal, const void* mask, int mask_rows,
+                  int accum_dtype, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                  accum_dtype, dtype, workspace, workspace_bytes, stream, false, 0.f, 0);
+}
+
+int ffpa_attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+                          int Nkv, int D, float scale, int causal, const void* mask, int mask_rows,
+                          int accum_dtype, int dtype, float dropout_p, uint64_t seed, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                  accum_dtype, dtype, workspace, workspace_bytes, stream, true, dropout_p, seed);
 }
 
 }  // extern "C"

@@ -74,6 +74,8 @@ struct BwdArgs {
   int nqt, nkt;      // ceil(Nq / 32), ceil(Nkv / 32)
   int nkv_pad;       // Nkv rounded up to 64
   int wg_dq_ds;      // B * Hq * ceil(Nq / bwd_dq_ds_rows(D))
+  DropParams drop;   // dropout of the forward (drop.t = 0: none)
+  int bh0;           // flattened query head of head 0 of this launch (the dropout counter)
 };
 
 // The stored dS. Block (bh, qt, kt) holds dS[q][key] for the 32 queries of
@@ -271,11 +273,11 @@ __device__ inline void bwd_exchange(FFPA_LDS char* xbase, int wave, int lane, f3
 // fragments are rows of the staged tiles `ta` and `tb`, B fragments the
 // register operands `fa` and `fb` (AGPRs). The chains end padded for the
 // VALU/LDS reads of their results.
-template <bool BF16, int NS, class StepFn>
+template <bool BF16, int NS, int AHEAD = 3, class StepFn>
 __device__ inline void bwd_partials(const FFPA_LDS char* ta, const FFPA_LDS char* tb, const uint32_t* ax,
                                     const u32x4* fa, const u32x4* fb, f32x16& s, f32x16& p,
                                     StepFn&& at_step) {
-  constexpr int kAhead = NS < 3 ? NS : 3;
+  constexpr int kAhead = NS < AHEAD ? NS : AHEAD;  // LDS reads in flight
   u32x4 xa[kAhead], xb[kAhead];
 #pragma unroll
   for (int st = 0; st < kAhead; ++st) {
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 //    dV^T[half] += dO^T P,  dK^T[half] += Q^T dS.
 // Accumulators: dV^T in AGPRs, dK^T in VGPRs (m = d, n = key).
 // ---------------------------------------------------------------------------
-template <int D, bool BF16, bool ROWMASK>
+template <int D, bool BF16, bool ROWMASK, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
   static_assert(D % 64 == 0 && D <= 1024, "D must be a multiple of 64, at most 1024");
@@ -436,6 +438,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
   float bias2 = 0.f;  // this lane's key bias, log2 domain
   // per-query mask: a separate instance, so the common one keeps its registers
   constexpr bool row_mask = ROWMASK;
+  // lse2 and delta of the next tile are loaded during this one, except in the
+  // per-query-mask instance, which needs those registers
+  constexpr bool kPrefetch = !ROWMASK;
   if (a.mask != nullptr && !row_mask) {
     const int key = kw + (lane & 31);
     bias2 = key < a.Nkv ? E::to_f32(((const uint16_t*)a.mask)[key]) * kLog2e : -INFINITY;
@@ -476,7 +481,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   if (n_it > 0) {
-    if constexpr (!ROWMASK) load_rows(0);
+    if constexpr (kPrefetch) load_rows(0);
     issue(0);
   }
 
@@ -505,14 +510,18 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // this tile's copies are issued (a wait after them would hold for them).
     // (The per-query-mask instance has no registers to spare for the
     // prefetch: it loads them here.)
-    if constexpr (ROWMASK) load_rows(it);
+    if constexpr (!kPrefetch) load_rows(it);
     f32x4 l2[4], dl[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       l2[j] = l2n[j];
       dl[j] = dln[j];
-      if constexpr (!ROWMASK) asm volatile("" ::"v"(l2[j]), "v"(dl[j]));
+      if constexpr (kPrefetch) asm volatile("" ::"v"(l2[j]), "v"(dl[j]));
     }
+    // dropout keep bit i: the lane's key against query 8 (i / 4) + i % 4 + 4 hi
+    // of the tile (made before the products, while fewer registers are live)
+    const uint32_t keep =
+        DROP ? drop_bits_col(a.drop, a.bh0 + b * a.Hq + hh, my_k, qt * kBwdRows + 4 * hij) : 0u;
     // S = Q K^T and dP = dO V^T (32 q x 32 keys), partial over this half of
     // D; the copies of the next tile go out during its first half
     f32x16 sacc, pacc;
@@ -541,6 +550,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const int qg0 = qt * kBwdRows + 4 * hij;
     // the causal test is a separate instance of the loop (uniform branch),
     // so that non-causal tiles run no compares
+    // dropout (Z, scale c): P o Z c feeds dV (c applied at the end) and
+    // dS = P o (dP o Z c - delta)
     auto p_ds = [&](auto causal_tag) {
       constexpr bool CAUSAL = decltype(causal_tag)::value;
 #pragma unroll
@@ -558,8 +569,14 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
         if constexpr (CAUSAL) x = my_k > qg0 + 8 * j + e ? -INFINITY : x;
         const float p = exp2_fast(x);
-        pv[i] = p;
-        dsv[i] = p * (pacc[i] - dl[j][e]);
+        if constexpr (DROP) {
+          // the scale of the kept P is applied to dV at the end
+          pv[i] = keep_if_bit(p, keep, i);
+          dsv[i] = p * (keep_if_bit(pacc[i] * a.drop.scale, keep, i) - dl[j][e]);
+        } else {
+          pv[i] = p;
+          dsv[i] = p * (pacc[i] - dl[j][e]);
+        }
       }
     };
     if (a.causal && kw + 31 > qt * kBwdRows) p_ds(BoolTag<true>{});
@@ -629,7 +646,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[t2]), "+v"(sf[t2]));
 
     // the next tile's lse2 and delta, waited for at its barrier
-    if constexpr (!ROWMASK) {
+    if constexpr (kPrefetch) {
       if (it + 1 < n_it) load_rows(it + 1);
     }
 
@@ -689,7 +706,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   barrier();
   FFPA_LDS char* stg = smem + wave * 2 * 16384;
   const int le = lane_id_here();
-  bwd_stage_rows<BF16, NDB>(stg, dv, 1.f, le);
+  bwd_stage_rows<BF16, NDB>(stg, dv, DROP ? a.drop.scale : 1.f, le);
   bwd_stage_rows<BF16, NDB>(stg + 16384, dk, a.scale, le);
   {
     const size_t row0 = ((size_t)(b * a.Hkv + hk) * a.Nkv + kw) * D + hf * DW;
@@ -706,7 +723,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 //    P = 2^(scale_log2 S + bias_log2 - lse2), dS = P (dP - delta);
 //    dQ^T[half] += K^T dS^T   (accumulators in AGPRs, m = d, n = query).
 // ---------------------------------------------------------------------------
-template <int D, bool BF16>
+template <int D, bool BF16, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(BwdArgs a) {
   static_assert(D % 64 == 0 && D <= 1024, "D must be a multiple of 64, at most 1024");
@@ -828,6 +845,9 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) bias2[i] = kg0 + 8 * (i >> 2) + (i & 3) < a.Nkv ? 0.f : -INFINITY;
     }
+    // dropout keep bit i for the lane's row against key kg0 + 8 (i / 4) +
+    // i % 4 (made before the products, while fewer registers are live)
+    const uint32_t keep = DROP ? drop_bits_row(a.drop, a.bh0 + bh, my_q, kg0) : 0u;
     // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 q), partial over the
     // half; the copies of the next tile go out during its first half
     f32x16 sacc, pacc;
@@ -853,7 +873,11 @@ void bwd_dq_kernel(BwdArgs a) {
       float x = fmaf(sacc[i], a.scale_log2, bias2[i]) - lse2_me;
       if (a.causal && kg0 + 8 * (i >> 2) + (i & 3) > my_q) x = -INFINITY;
       const float p = exp2_fast(x);
-      dsv[i] = p * (pacc[i] - dl_me);
+      if constexpr (DROP) {
+        dsv[i] = p * (keep_if_bit(pacc[i] * a.drop.scale, keep, i) - dl_me);
+      } else {
+        dsv[i] = p * (pacc[i] - dl_me);
+      }
     }
     V8 sf[2];
 #pragma unroll
@@ -1111,18 +1135,16 @@ void bwd_dq_ds_kernel(BwdArgs a) {
 template <int D, bool BF16>
 hipError_t prepare_bwd() {
   static const hipError_t e = [] {
-    hipError_t r = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, BF16, false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
-    if (r == hipSuccess)
-      r = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, BF16, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
-    if (r == hipSuccess)
-      r = hipFuncSetAttribute((const void*)bwd_dq_kernel<D, BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              kBwdLds);
-    if (r == hipSuccess)
-      r = hipFuncSetAttribute((const void*)bwd_dq_ds_kernel<D, BF16>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kBwdDqDsLds);
-    return r;
+    const void* big[] = {(const void*)bwd_dkdv_kernel<D, BF16, false>, (const void*)bwd_dkdv_kernel<D, BF16, true>,
+                         (const void*)bwd_dkdv_kernel<D, BF16, false, true>,
+                         (const void*)bwd_dkdv_kernel<D, BF16, true, true>, (const void*)bwd_dq_kernel<D, BF16>,
+                         (const void*)bwd_dq_kernel<D, BF16, true>};
+    for (const void* k : big) {
+      const hipError_t r = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kBwdLds);
+      if (r != hipSuccess) return r;
+    }
+    return hipFuncSetAttribute((const void*)bwd_dq_ds_kernel<D, BF16>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kBwdDqDsLds);
   }();
   return e;
 }
@@ -1152,6 +1174,7 @@ BwdArgs bwd_chunk_args(const BwdArgs& a, int f0, int n) {
   c.B = 1;
   c.Hkv = n;
   c.Hq = n * g;
+  c.bh0 = a.bh0 + (int)fq;
   const int rows = bwd_rows_per_wg(D), rq = bwd_dq_ds_rows(D);
   c.wg_dkdv = n * ((a.Nkv + rows - 1) / rows);
   c.wg_dq = n * g * ((a.Nq + rows - 1) / rows);
@@ -1168,7 +1191,10 @@ hipError_t launch_bwd(const BwdArgs& a, int chunk_kv, hipStream_t stream) {
   const hipError_t pe = prepare_bwd<D, BF16>();
   if (pe != hipSuccess) return pe;
   const bool rowmask = a.mask != nullptr && a.mask_rows > 1;
-  auto kdkdv = rowmask ? bwd_dkdv_kernel<D, BF16, true> : bwd_dkdv_kernel<D, BF16, false>;
+  const bool drop = a.drop.t != 0;
+  auto kdkdv = drop ? (rowmask ? bwd_dkdv_kernel<D, BF16, true, true> : bwd_dkdv_kernel<D, BF16, false, true>)
+                    : (rowmask ? bwd_dkdv_kernel<D, BF16, true> : bwd_dkdv_kernel<D, BF16, false>);
+  auto kdq = drop ? bwd_dq_kernel<D, BF16, true> : bwd_dq_kernel<D, BF16>;
   const int64_t rows = (int64_t)a.B * a.Hq * a.nq_pad;
   hipLaunchKernelGGL((bwd_prep_kernel<D, BF16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
   if (a.ds != nullptr) {
@@ -1185,7 +1211,7 @@ hipError_t launch_bwd(const BwdArgs& a, int chunk_kv, hipStream_t stream) {
     return hipGetLastError();
   }
   hipLaunchKernelGGL(kdkdv, dim3(a.wg_dkdv), dim3(256), kBwdLds, stream, a);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16>), dim3(a.wg_dq), dim3(256), kBwdLds, stream, a);
+  hipLaunchKernelGGL(kdq, dim3(a.wg_dq), dim3(256), kBwdLds, stream, a);
   return hipGetLastError();
 }
 

@@ -40,6 +40,7 @@ struct DecArgs {
   int keys_per_split; // multiple of kDecStep
   float scale_log2;
   int n_waves;        // B * Hq * S
+  DropParams drop;    // dropout (drop.t = 0: none)
 };
 
 constexpr int kDecStep = 8;        // keys per step
@@ -147,6 +148,13 @@ __global__ __launch_bounds__(256) void dec_split_kernel(DecArgs a) {
     }
     const float m_new = fmaxf(m, mt);
     if (m_new == -INFINITY) continue;  // every key so far is masked
+    // dropout: the row is query 0; one generator call per 4 keys (the words
+    // are the same in every lane)
+    uint32_t dw[kDecStep / 4];
+    if (a.drop.t != 0) {
+#pragma unroll
+      for (int c = 0; c < kDecStep / 4; ++c) dw[c] = drop_row_word(a.drop, (int)bh, 0, k0 + 4 * c);
+    }
     const float alpha = exp2_fast(m - m_new);  // 0 when m = -inf
     l *= alpha;
 #pragma unroll
@@ -155,8 +163,9 @@ __global__ __launch_bounds__(256) void dec_split_kernel(DecArgs a) {
       for (int e = 0; e < 8; ++e) o[j][e] *= alpha;
 #pragma unroll
     for (int t = 0; t < kDecStep; ++t) {
-      const float p = exp2_fast(sc[t] - m_new);
-      l += p;
+      const float p0 = exp2_fast(sc[t] - m_new);
+      l += p0;
+      const float p = (a.drop.t != 0 && !drop_keeps(dw[t / 4], t % 4, a.drop.t)) ? 0.f : p0;
 #pragma unroll
       for (int j = 0; j < NG; ++j)
 #pragma unroll
@@ -168,7 +177,7 @@ __global__ __launch_bounds__(256) void dec_split_kernel(DecArgs a) {
     m = m_new;
   }
 
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = (l > 0.f ? 1.f / l : 0.f) * (a.drop.t != 0 ? a.drop.scale : 1.f);
   float* po = a.part_o + (size_t)wid * D;
 #pragma unroll
   for (int j = 0; j < NG; ++j) {

@@ -343,6 +343,133 @@ __device__ inline void scale_agpr16(f32x16& acc, float s) {
 }
 #undef FFPA_RESCALE1
 
+// ---------------------------------------------------------------------------
+// Dropout's random numbers: the counter-based generator Philox-4x32-10
+// (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2,
+// 3", SC 2011). Each of its 10 rounds multiplies two counter words by fixed
+// odd constants, recombines the halves of the 64-bit products with the other
+// two words and the key, and bumps the key by two further constants. One call
+// serves a block of 4 query rows x 4 keys of a head: counter (key / 4,
+// query / 4, b * Hq + h, 0) under the 64-bit seed; element (query, key) is the
+// byte key % 4 of output word query % 4, kept when it is >= t.
+// ---------------------------------------------------------------------------
+struct DropParams {
+  uint32_t t;        // threshold: 0 = no dropout; else round(256 p), 1 .. 255
+  uint32_t seed_lo;  // key words
+  uint32_t seed_hi;
+  float scale;       // 256 / (256 - t): the scale of a kept element
+};
+
+__device__ inline u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                      uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// The four dropout bytes of query row q for keys k4 .. k4 + 3 (k4 a multiple
+// of 4) of head bh, one per byte (key k4 + e in byte e).
+__device__ inline uint32_t drop_row_word(const DropParams& d, int bh, int q, int k4) {
+  const u32x4 w = philox4x32_10((uint32_t)k4 >> 2, (uint32_t)q >> 2, (uint32_t)bh, 0u, d.seed_lo, d.seed_hi);
+  const int r = q & 3;
+  return r == 0 ? w[0] : r == 1 ? w[1] : r == 2 ? w[2] : w[3];
+}
+
+// Whether byte e of a dropout word keeps its element.
+__device__ inline bool drop_keeps(uint32_t word, int e, uint32_t t) { return ((word >> (8 * e)) & 0xffu) >= t; }
+
+// Keep bits of one generator call: bit 4 r + e = byte e of word r kept
+// (query 4 c1 + r, key 4 c0 + e).
+__device__ inline uint32_t drop_block_bits(const u32x4 w, uint32_t t) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m |= (uint32_t)drop_keeps(w[r], e, t) << (4 * r + e);
+  return m;
+}
+
+// Value of x in lane j of this lane's quad (lanes 4 a .. 4 a + 3).
+template <int J>
+__device__ inline uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, J * 0x55, 0xf, 0xf, false);
+}
+
+// The four lanes of a quad hold four consecutive 4-aligned positions of one
+// orientation and need the same four generator calls; lane j of the quad
+// makes call j and the others read its 16 bits. Every lane of the wave must
+// be active.
+//
+// Row per lane (lane & 3 == q & 3): keep bits of query q against keys
+// k0 + 8 j + e (k0 a multiple of 4), bit 4 j + e.
+__device__ inline uint32_t drop_bits_row(const DropParams& d, int bh, int q, int k0) {
+  // opaque inputs: nothing of the call (the per-round keys included) is
+  // hoisted out of the caller's loop, where it would hold registers
+  uint32_t s0 = d.seed_lo, s1 = d.seed_hi;
+  asm volatile("" : "+v"(q), "+s"(s0), "+s"(s1));
+  const int r = q & 3;  // this lane's index in its quad
+  const uint32_t m = drop_block_bits(
+      philox4x32_10((uint32_t)(k0 + 8 * r) >> 2, (uint32_t)q >> 2, (uint32_t)bh, 0u, s0, s1), d.t);
+  const int sh = 4 * r;
+  uint32_t keep = ((quad_bcast<0>(m) >> sh) & 0xfu) | (((quad_bcast<1>(m) >> sh) & 0xfu) << 4) |
+                  (((quad_bcast<2>(m) >> sh) & 0xfu) << 8) | (((quad_bcast<3>(m) >> sh) & 0xfu) << 12);
+  asm volatile("" : "+v"(keep));  // finished here: one register stays live, not four
+  return keep;
+}
+
+// Key per lane (lane & 3 == k & 3): keep bits of key k against queries
+// q0 + 8 j + e (q0 a multiple of 4), bit 4 j + e.
+__device__ inline uint32_t drop_bits_col(const DropParams& d, int bh, int k, int q0) {
+  uint32_t s0 = d.seed_lo, s1 = d.seed_hi;
+  asm volatile("" : "+v"(k), "+s"(s0), "+s"(s1));  // opaque inputs, as in drop_bits_row
+  const int r = k & 3;  // this lane's index in its quad
+  const uint32_t m = drop_block_bits(
+      philox4x32_10((uint32_t)k >> 2, (uint32_t)(q0 + 8 * r) >> 2, (uint32_t)bh, 0u, s0, s1), d.t);
+  auto gather = [r](uint32_t mj) {  // bits r, 4 + r, 8 + r, 12 + r -> 0..3
+    uint32_t x = (mj >> r) & 0x1111u;
+    x |= x >> 3;
+    return (x | (x >> 6)) & 0xfu;
+  };
+  uint32_t keep = gather(quad_bcast<0>(m)) | (gather(quad_bcast<1>(m)) << 4) | (gather(quad_bcast<2>(m)) << 8) |
+                  (gather(quad_bcast<3>(m)) << 12);
+  asm volatile("" : "+v"(keep));  // finished here: one register stays live, not four
+  return keep;
+}
+
+// x where bit b (0..15) of `bits` is set, else +0. The bit-field extract and
+// the AND sit in one asm block, so the all-ones/zero mask lives only inside
+// it (the compiler's scheduler would otherwise make the 16 masks of a tile at
+// once, 16 registers where the kernels have none to spare). b is a constant
+// in unrolled callers, where the switch folds away.
+__device__ inline float keep_if_bit(float x, uint32_t bits, int b) {
+  float r = 0.f;
+  uint32_t m;
+#define FFPA_KEEP_BIT(B)                                                                                    \
+  case B:                                                                                                   \
+    asm("v_bfe_i32 %1, %2, " #B ", 1\n\tv_and_b32 %0, %3, %1" : "=v"(r), "=&v"(m) : "v"(bits), "v"(x)); \
+    break;
+  switch (b) {
+    FFPA_KEEP_BIT(0) FFPA_KEEP_BIT(1) FFPA_KEEP_BIT(2) FFPA_KEEP_BIT(3)
+    FFPA_KEEP_BIT(4) FFPA_KEEP_BIT(5) FFPA_KEEP_BIT(6) FFPA_KEEP_BIT(7)
+    FFPA_KEEP_BIT(8) FFPA_KEEP_BIT(9) FFPA_KEEP_BIT(10) FFPA_KEEP_BIT(11)
+    FFPA_KEEP_BIT(12) FFPA_KEEP_BIT(13) FFPA_KEEP_BIT(14) FFPA_KEEP_BIT(15)
+    default: break;
+  }
+#undef FFPA_KEEP_BIT
+  return r;
+}
+
 // Value of lane (l ^ 32) of x.
 __device__ inline float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 

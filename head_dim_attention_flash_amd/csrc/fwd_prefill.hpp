@@ -53,6 +53,7 @@ struct FwdArgs {
   float scale_log2;   // scale * log2(e)
   int n_qtiles;
   int total_wg;
+  DropParams drop;    // dropout (drop.t = 0: none)
 };
 
 constexpr int kFwdWaves = 4;
@@ -90,10 +91,11 @@ constexpr float fwd_tau() {
 }
 constexpr float kRescaleTau = 8.0f;  // fp16-accumulator path: move m_ref past this
 
-template <int D, bool BF16, bool ACC16, bool VT>
+template <int D, bool BF16, bool ACC16, bool VT, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fwd_prefill_kernel(FwdArgs a) {
   static_assert(D % 64 == 0 && D <= 512, "D must be a multiple of 64, at most 512");
+  static_assert(!(ACC16 && DROP), "dropout is built with fp32 accumulation");
   using E = Elem<BF16>;
   using V8 = typename E::vec8;
   constexpr int ROWB = kFwdRowBytes;      // bytes per LDS row (D * 2 used)
@@ -322,6 +324,13 @@ void fwd_prefill_kernel(FwdArgs a) {
   float l_run = 0.f;        // ACC32: this lane's partial row sum; ACC16: full row sum
   bool fresh = true;        // ACC32: no PV product accumulated yet
   bool safe = false;        // ACC32: a tile broke m_ref + tau; the key loop reruns per tile
+  // dropout of 16 scores of row q held by a lane, keys k0 + 8 g + e (g, e in
+  // 0..3; k0 a multiple of 4): the quad's four generator calls, one a lane
+  auto drop_half = [&](float* tv, int k0, int q) {
+    const uint32_t keep = drop_bits_row(a.drop, b * a.Hq + h, q, k0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tv[i] = keep_if_bit(tv[i], keep, i);
+  };
   // one word per wave: did a row of that wave break m_ref + tau in this tile
   FFPA_LDS uint32_t* restart_flag = (FFPA_LDS uint32_t*)(smem + fwd_ring_bytes<D>() +
                                                          (key_bias ? fwd_bias_bytes(a.Nkv) : 0));
@@ -415,7 +424,11 @@ void fwd_prefill_kernel(FwdArgs a) {
           l_run += tv[i];
         }
       };
-      auto half_pack = [&](const float* tv, V8* pf) {
+      // the MFMA operand P of half kb: dropout zeroes the dropped elements
+      // here (the row sum has the undropped ones); the scale of the kept ones
+      // is applied to O at the end
+      auto half_pack = [&](float* tv, V8* pf, int kb) {
+        if constexpr (DROP) drop_half(tv, j0 + 4 * hij + 32 * kb, my_qj);
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) {
           const float* x = &tv[8 * t2];
@@ -437,7 +450,7 @@ void fwd_prefill_kernel(FwdArgs a) {
           }
         }
         if (q == NS - 1) {
-          half_pack(tv, pf);
+          half_pack(tv, pf, kb);
 #pragma unroll
           for (int t2 = 0; t2 < 2; ++t2) asm volatile("" : "+v"(pf[t2]));
         }
@@ -751,6 +764,8 @@ void fwd_prefill_kernel(FwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
+        if constexpr (DROP)
+          if (t2 == 0) drop_half(tv[kb], j0 + 4 * hij + 32 * kb, my_qj);
         const float* x = &tv[kb][8 * t2];
         if constexpr (ACC16)
           pf[kb][t2] = pack8<BF16>(x[0] * pscale, x[1] * pscale, x[2] * pscale, x[3] * pscale,
@@ -913,6 +928,7 @@ void fwd_prefill_kernel(FwdArgs a) {
   if constexpr (!ACC16) {
     l_tot = l_run + swap_halves(l_run);
     inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if constexpr (DROP) inv *= a.drop.scale;
   } else {
     l_tot = l_run;
     inv = 1.f;
@@ -972,9 +988,9 @@ void fwd_prefill_kernel(FwdArgs a) {
 // <= 160 KiB). With VT the transposed copy of V is written into a.vt first.
 // The kernel's LDS limit is set before anything is enqueued, so a failure
 // there leaves the stream untouched.
-template <int D, bool BF16, bool ACC16, bool VT>
+template <int D, bool BF16, bool ACC16, bool VT, bool DROP = false>
 hipError_t launch_fwd_prefill(const FwdArgs& a, size_t lds_bytes, hipStream_t stream) {
-  auto kern = fwd_prefill_kernel<D, BF16, ACC16, VT>;
+  auto kern = fwd_prefill_kernel<D, BF16, ACC16, VT, DROP>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr != hipSuccess) return attr;

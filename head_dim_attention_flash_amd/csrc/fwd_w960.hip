@@ -4,4 +4,6 @@
 namespace ffpa {
 template hipError_t launch_fwd_wide<960, false>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd_wide<960, true>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd_wide<960, false, true>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd_wide<960, true, true>(const FwdArgs&, hipStream_t);
 }  // namespace ffpa

@@ -52,7 +52,7 @@ constexpr int kWideTile = 64 * 1024;             // LDS buffer of one staged K o
 constexpr int kWideXchg = 4096;                  // per wave: a 32 x 32 fp32 tile
 constexpr int kWideLds = 2 * kWideTile + 4 * kWideXchg;
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fwd_wide_kernel(FwdArgs a) {
   static_assert(D % 64 == 0 && D > 512 && D <= 1024, "D must be a multiple of 64 in (512, 1024]");
@@ -191,6 +191,10 @@ void fwd_wide_kernel(FwdArgs a) {
       if (d < kOAgpr) asm volatile("" : "+a"(o_acc[d]));
       else asm volatile("" : "+v"(o_acc[d]));
     }
+    // dropout keep bit i of the lane's row against key j0 + 4 hi + 8 (i / 4)
+    // + i % 4 (the quad's four generator calls, one a lane), made before the
+    // products while fewer registers are live
+    const uint32_t keep = DROP ? drop_bits_row(a.drop, b * a.Hq + h, my_qj, j0 + 4 * hij) : 0u;
 
     // ===== K phase: partial S^T over this half, two chains (even / odd k-steps)
     wait_vmcnt<0>();
@@ -296,6 +300,12 @@ void fwd_wide_kernel(FwdArgs a) {
       psum += tv[i];
     }
     l_run += psum;
+    if constexpr (DROP) {
+      // dropout: the row sum keeps the undropped P, O gets the scale of the
+      // kept elements at the end
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tv[i] = keep_if_bit(tv[i], keep, i);
+    }
     V8 pf[2];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
@@ -385,7 +395,7 @@ void fwd_wide_kernel(FwdArgs a) {
   // ===== epilogue: rows of the half through LDS (32 rows x 1 KiB per wave),
   // then stored as contiguous pieces of W elements per row
   const float l_tot = l_run + swap_halves(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * (DROP ? a.drop.scale : 1.f);
   wait_lgkm0();
   barrier();
   FFPA_LDS char* ostage = smem + wave * 32 * 1024;
@@ -423,9 +433,9 @@ void fwd_wide_kernel(FwdArgs a) {
 
 // Host launcher: the transposed copy of V (blocks of 32 keys) into a.vt, then
 // the kernel. The LDS limit is set before anything is enqueued.
-template <int D, bool BF16>
+template <int D, bool BF16, bool DROP = false>
 hipError_t launch_fwd_wide(const FwdArgs& a, hipStream_t stream) {
-  auto kern = fwd_wide_kernel<D, BF16>;
+  auto kern = fwd_wide_kernel<D, BF16, DROP>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds);
   if (attr != hipSuccess) return attr;

@@ -74,6 +74,7 @@
 #define FFPA_ATTN_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -199,6 +200,47 @@ size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
 
 /* The least workspace ffpa_attn_bwd accepts (dQ then recomputes S and dP). */
 size_t ffpa_attn_bwd_workspace_size_min(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
+
+/*
+ * Attention with dropout on the attention probabilities: the "dropout" case
+ * of the forward and backward tables of "FFPA Attention Benchmark", section
+ * "More Benchmark", which run it beside PyTorch SDPA. The pages fix neither
+ * the random numbers nor p; the reading taken here is SDPA's dropout_p:
+ *     O = (softmax(scale Q K^T + mask) o Z / (1 - p')) V,
+ * Z a 0/1 keep mask, dropped after the softmax; lse is that of the undropped
+ * scores. The keep mask is counter-based, so that the backward (and any
+ * checker) regenerates it from (seed, head, query, key) alone:
+ *  - generator: Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+ *    numbers: as easy as 1, 2, 3", SC 2011), key = (seed low 32 bits, seed
+ *    high 32 bits);
+ *  - one call per block of 4 queries x 4 keys of a head: counter
+ *    (key / 4, query / 4, b * Hq + h, 0); of its four 32-bit output words,
+ *    word query % 4 belongs to the query and byte key % 4 of that word (bits
+ *    8 (key % 4) .. +7) to the element;
+ *  - the element is kept when that byte is >= t, t = round(256 dropout_p)
+ *    computed in float32 (at most 255); kept elements are scaled by
+ *    256 / (256 - t). So p' = t / 256 exactly; dropout_p = 0 (t = 0) is the
+ *    plain attention, bit for bit the same as ffpa_attn_fwd / _bwd.
+ * dropout_p must lie in [0, 1): else FFPA_ERR_INVALID_ARG, checked after the
+ * pointer alignment (and, in the forward, scale) checks and before the
+ * workspace check. The dropout kernels accumulate in fp32: in the forward,
+ * t > 0 with accum_dtype = FFPA_ACC_F16 returns FFPA_ERR_UNSUPPORTED (before
+ * the workspace check). Workspace, layout, paths and errors otherwise as
+ * ffpa_attn_fwd and ffpa_attn_bwd (same workspace sizes). The backward must
+ * get the forward's seed and dropout_p.
+ */
+int ffpa_attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
+                          const void* mask, int mask_rows, int accum_dtype, int dtype,
+                          float dropout_p, uint64_t seed,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+int ffpa_attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv,
+                          int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
+                          const void* mask, int mask_rows, int accum_dtype, int dtype,
+                          float dropout_p, uint64_t seed,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Thread-local message describing the last non-OK status ("" if none). */
 const char* ffpa_last_error(void);

@@ -165,3 +165,59 @@ def fwd_noalloc(**kw):
 def test_forward_noalloc_validation(kw, code):
     assert fwd_noalloc(**kw) == code
     assert ffpa.ffpa_last_error() != ""
+
+
+def fwd_drop(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nkv=8, D=64, scale=0.125,
+                causal=0, mask=0, mask_rows=0, accum_dtype=0, dtype=0, dropout_p=0.1, seed=7,
+                workspace=0, workspace_bytes=0, stream=0)
+    args.update(kw)
+    return ffpa.ffpa_attn_fwd_dropout(*args.values())
+
+
+def bwd_drop(**kw):
+    args = dict(q=P, k=P, v=P, o=P, dout=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=2, Nq=8,
+                Nkv=8, D=64, scale=0.125, causal=0, mask=0, mask_rows=0, accum_dtype=0, dtype=0,
+                dropout_p=0.1, seed=7, workspace=0, workspace_bytes=0, stream=0)
+    args.update(kw)
+    return ffpa.ffpa_attn_bwd_dropout(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), ffpa.ERR_INVALID_ARG),
+    (dict(D=1056), ffpa.ERR_UNSUPPORTED),
+    (dict(lse=P + 4), ffpa.ERR_INVALID_ARG),
+    (dict(dropout_p=1.0), ffpa.ERR_INVALID_ARG),
+    (dict(dropout_p=-0.01), ffpa.ERR_INVALID_ARG),
+    (dict(dropout_p=float("nan")), ffpa.ERR_INVALID_ARG),
+    # p is checked before the workspace; the fp16 accumulator has no dropout
+    (dict(dropout_p=2.0, Nq=4096), ffpa.ERR_INVALID_ARG),
+    (dict(accum_dtype=1), ffpa.ERR_UNSUPPORTED),
+    (dict(accum_dtype=1, D=1024), ffpa.ERR_UNSUPPORTED),
+    (dict(Nq=4096), ffpa.ERR_WORKSPACE),
+])
+def test_forward_dropout_validation(kw, code):
+    assert fwd_drop(**kw) == code
+    assert ffpa.ffpa_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dq=0), ffpa.ERR_INVALID_ARG),
+    (dict(accum_dtype=1), ffpa.ERR_UNSUPPORTED),
+    (dict(dv=P + 8), ffpa.ERR_INVALID_ARG),
+    (dict(dropout_p=1.5), ffpa.ERR_INVALID_ARG),
+    (dict(dropout_p=float("inf")), ffpa.ERR_INVALID_ARG),
+    (dict(dropout_p=0.5), ffpa.ERR_WORKSPACE),
+    (dict(dropout_p=0.5, workspace=P, workspace_bytes=16), ffpa.ERR_WORKSPACE),
+])
+def test_backward_dropout_validation(kw, code):
+    assert bwd_drop(**kw) == code
+    assert ffpa.ffpa_last_error() != ""
+
+
+def test_binding_rejects_bad_seed():
+    with pytest.raises(ValueError):
+        ffpa._seed(-1)
+    with pytest.raises(ValueError):
+        ffpa._seed(1 << 64)
+    assert ffpa._seed((1 << 64) - 1) == (1 << 64) - 1

@@ -35,7 +35,8 @@ def _run(lib, q, k, v, *, causal=False, mask=None, accum="f32", scale=None):
 UNIT = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
-def _compare(o, lse, q, k, v, scale, causal, mask, dtype, accum, label, flat_gate=False):
+def _compare(o, lse, q, k, v, scale, causal, mask, dtype, accum, label, flat_gate=False,
+             dropout_p=0.0, seed=0):
     """Element-wise parity of O and lse against the oracle.
 
     flat_gate: the judged workloads' bound, max |dO| <= TOL[accum]. Otherwise
@@ -47,7 +48,8 @@ def _compare(o, lse, q, k, v, scale, causal, mask, dtype, accum, label, flat_gat
     applies.
     """
     m2 = None if mask is None else mask.view(-1, k.shape[2])
-    oo, lo = attn_fwd(q, k, v, scale, causal=causal, mask=m2)
+    drop = dict(dropout_p=dropout_p, seed=seed)
+    oo, lo = attn_fwd(q, k, v, scale, causal=causal, mask=m2, **drop)
     og = to_f64(o)
     lg = to_f64(lse)
     assert np.isfinite(og).all(), f"{label}: non-finite output"
@@ -61,7 +63,7 @@ def _compare(o, lse, q, k, v, scale, causal, mask, dtype, accum, label, flat_gat
     if flat_gate:
         assert err <= TOL[accum], f"{label}: max abs error {err} > {TOL[accum]}"
     else:
-        pv_abs, _ = attn_fwd(q, k, to_f64(v).__abs__(), scale, causal=causal, mask=m2)
+        pv_abs, _ = attn_fwd(q, k, to_f64(v).__abs__(), scale, causal=causal, mask=m2, **drop)
         bound = TOL[accum] + UNIT[dtype] * (np.abs(oo) + pv_abs)
         worst = (diff / bound).max()
         assert worst <= 1.0, f"{label}: error exceeds the bound by {worst:.3f}x (max abs {err})"
