@@ -160,7 +160,7 @@ def time_forward(ffpa, w, inp, accum, steps, warmup):
 
     def step():
         ffpa.attention(q, k, v, causal=w.causal, mask=mask, scale=w.scale, accum=accum, out=o,
-                       lse_out=lse, workspace=ws)
+                       lse_out=lse, workspace=ws, dropout_p=w.dropout_p, seed=w.cfg_id)
 
     for _ in range(warmup):
         step()
@@ -206,19 +206,24 @@ def run_backward(ffpa, W, name, steps, warmup):
     w = W.WORKLOADS[name]
     inp = W.make_inputs(w, device="cuda")
     q, k, v, do = inp["q"], inp["k"], inp["v"], inp["dout"]
-    o, lse = ffpa.attention(q, k, v, causal=w.causal, scale=w.scale, return_lse=True)
+    o, lse = ffpa.attention(q, k, v, causal=w.causal, scale=w.scale, return_lse=True,
+                            dropout_p=w.dropout_p, seed=w.cfg_id)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dt = ffpa.BF16 if w.dtype == "bf16" else ffpa.F16
     ws_bytes = ffpa.ffpa_attn_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, dt)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
 
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.scale,
+            int(w.causal), 0, 0, ffpa.ACC_F32, dt)
+    tail = (ws.data_ptr(), ws_bytes, stream)
+
     def call():
-        st = ffpa.ffpa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                                dv.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.scale,
-                                int(w.causal), 0, 0, ffpa.ACC_F32, dt, ws.data_ptr(), ws_bytes,
-                                stream)
+        if w.dropout_p:
+            st = ffpa.ffpa_attn_bwd_dropout(*args, w.dropout_p, w.cfg_id, *tail)
+        else:
+            st = ffpa.ffpa_attn_bwd(*args, *tail)
         if st != 0:
             raise ffpa.FFPAError(st, ffpa.ffpa_last_error())
 
@@ -228,7 +233,8 @@ def run_backward(ffpa, W, name, steps, warmup):
     peak = PEAK_TFLOPS[w.dtype]
     del inp, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
-    return {"workload": f"{name}: B={w.B} H={w.Hq} N={w.Nq} D={w.D} {w.dtype} causal={w.causal}",
+    return {"workload": f"{name}: B={w.B} H={w.Hq} N={w.Nq} D={w.D} {w.dtype} causal={w.causal}"
+                        + (f" dropout_p={w.dropout_p}" if w.dropout_p else ""),
             "value": round(tflops, 2), "unit": "TFLOPS (5 GEMMs counted)",
             "ms_per_call": round(mean_ms, 4),
             "kernels": "prep + K^T copy + per chunk of kv heads: dK/dV (stores dS) + dQ from dS",
@@ -345,7 +351,8 @@ def run_forward_path(ffpa, W, name, accum, steps, warmup):
     del inp
     torch.cuda.empty_cache()
     return {"workload": f"{name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nkv={w.Nkv} D={w.D} "
-                        f"{w.dtype} causal={w.causal} mask={w.mask} accum={accum}",
+                        f"{w.dtype} causal={w.causal} mask={w.mask} accum={accum}"
+                        + (f" dropout_p={w.dropout_p}" if w.dropout_p else ""),
             "value": round(tflops, 2), "unit": "TFLOPS" + (" (causal: half counted)" if w.causal else ""),
             "ms_per_call": round(mean_ms, 4), "timed_call": timed_call(w, accum),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
@@ -356,11 +363,11 @@ def run_forward_path(ffpa, W, name, accum, steps, warmup):
 # variant in both dtypes, the fp16 accumulator, the head-dimension sweep with
 # both accumulators, and 16K sequences.
 FWD_PATHS = ([("self_bf16", "f32"), ("self", "f16"), ("self_bf16", "f16")] +
-             [(n, "f32") for n in ("cross", "gqa", "causal", "nonaligned", "mask")] +
-             [(n + "_bf16", "f32") for n in ("cross", "gqa", "causal", "nonaligned", "mask")] +
+             [(n, "f32") for n in ("cross", "gqa", "causal", "nonaligned", "mask", "dropout")] +
+             [(n + "_bf16", "f32") for n in ("cross", "gqa", "causal", "nonaligned", "mask", "dropout")] +
              [(f"dsweep{d}_{a}", a) for d in (320, 448, 512, 576, 768, 1024) for a in ("f32", "f16")] +
              [("self16k", "f32"), ("self16k_bf16", "f32"), ("causal16k", "f32"), ("nonaligned16k", "f32")])
-BWD_PATHS = ("bwd_causal", "bwd_d1024", "bwd16k", "bwd16k_causal")
+BWD_PATHS = ("bwd_causal", "bwd_d1024", "bwd16k", "bwd16k_causal", "bwd_dropout")
 
 
 def main(argv=None) -> int:

@@ -156,7 +156,7 @@ def dropout_keep(seed, bh, rows, cols, t):
 
 
 def attn_fwd(q, k, v, scale, causal=False, mask=None, q_pos=None, row_block=1024, dropout_p=0.0,
-             seed=0):
+             seed=0, bh0=0):
     """O = softmax(scale * Q K^T + mask) V and the per-row log-sum-exp.
 
     q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nkv, D]; mask: None, [1, Nkv] or [Nq_total, Nkv].
@@ -164,8 +164,10 @@ def attn_fwd(q, k, v, scale, causal=False, mask=None, q_pos=None, row_block=1024
     they select the causal diagonal, the per-query mask rows and the dropout
     counters, so a subset of rows can be checked on its own (rows are
     independent).
-    dropout_p, seed: the dropout of the module docstring (0: none); the heads
-    given are heads 0.. of the problem (bh = b Hq + h).
+    dropout_p, seed: the dropout of the module docstring (0: none). The
+    counter of head (b, h) given is bh0 + b Hq + h: bh0 = 0 for a whole
+    problem; a single head (b', h') of a larger one, passed alone, takes
+    bh0 = b' Hq' + h' (its place in that problem).
     Returns (o [B, Hq, Nq, D], lse [B, Hq, Nq]) as float64.
     """
     q, k, v, mask = to_f64(q), to_f64(k), to_f64(v), to_f64(mask)
@@ -184,20 +186,22 @@ def attn_fwd(q, k, v, scale, causal=False, mask=None, q_pos=None, row_block=1024
                 s = _scores(q[b, h, r0:r1], k[b, hk], scale, mask, causal, pos[r0:r1])
                 p, lse[b, h, r0:r1] = _softmax_rows(s)
                 if t > 0:
-                    keep = dropout_keep(seed, b * Hq + h, pos[r0:r1], np.arange(Nkv), t)
+                    keep = dropout_keep(seed, bh0 + b * Hq + h, pos[r0:r1], np.arange(Nkv), t)
                     p = np.where(keep, p * (256.0 / (256 - t)), 0.0)
                 o[b, h, r0:r1] = p @ v[b, hk]
     return o, lse
 
 
-def attn_bwd(q, k, v, dout, scale, causal=False, mask=None, row_block=1024, dropout_p=0.0, seed=0):
+def attn_bwd(q, k, v, dout, scale, causal=False, mask=None, row_block=1024, dropout_p=0.0, seed=0,
+             bh0=0):
     """Gradients (dq, dk, dv) of sum(dout * attn_fwd(q, k, v)[0]) in float64.
 
     P is recomputed from q, k, v here; nothing from a GPU forward is used.
     dk, dv of K/V head hk accumulate over the query heads h with h // g == hk.
     With dropout (keep mask Z, scale c = 256 / (256 - t)) the output is
     (P o Z c) V, so dV = (P o Z c)^T dO, dP = (dO V^T) o Z c, and the rest as
-    without: delta_i = sum_j P_ij dP_ij, dS = P o (dP - delta).
+    without: delta_i = sum_j P_ij dP_ij, dS = P o (dP - delta). bh0: as in
+    attn_fwd.
     """
     q, k, v, dout, mask = to_f64(q), to_f64(k), to_f64(v), to_f64(dout), to_f64(mask)
     B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v, mask)
@@ -220,7 +224,7 @@ def attn_bwd(q, k, v, dout, scale, causal=False, mask=None, row_block=1024, drop
                 do = dout[b, h, r0:r1]
                 zc = 1.0
                 if t > 0:
-                    keep = dropout_keep(seed, b * Hq + h, pos[r0:r1], np.arange(Nkv), t)
+                    keep = dropout_keep(seed, bh0 + b * Hq + h, pos[r0:r1], np.arange(Nkv), t)
                     zc = np.where(keep, 256.0 / (256 - t), 0.0)
                 dv[b, hk] += (p * zc).T @ do
                 dp = (do @ v[b, hk].T) * zc

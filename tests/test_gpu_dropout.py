@@ -151,9 +151,10 @@ BWD_CASES = [
 ]
 
 
-def _drop_bounds(q, k, v, do, scale, causal, mask, refs, dtype, p, seed):
+def _drop_bounds(q, k, v, do, scale, causal, mask, refs, dtype, p, seed, bh0=0):
     """The bf16 rounding bounds of the plain backward test with P o Z c in
-    place of P where the dropped probabilities enter."""
+    place of P where the dropped probabilities enter (bh0: as in the oracle,
+    for one head of a larger problem)."""
     u = BUNIT[dtype]
     qd, kd, vd, dod = (to_f64(t) for t in (q, k, v, do))
     B, Hq, Nq, D = qd.shape
@@ -166,7 +167,7 @@ def _drop_bounds(q, k, v, do, scale, causal, mask, refs, dtype, p, seed):
     for b in range(B):
         for h in range(Hq):
             hk = h // g
-            zc = dropout_keep(seed, b * Hq + h, range(Nq), range(Nkv), t) * c
+            zc = dropout_keep(seed, bh0 + b * Hq + h, range(Nq), range(Nkv), t) * c
             pd = P[b, h] * zc
             dp = (dod[b, h] @ vd[b, hk].T) * zc
             delta = np.sum(P[b, h] * dp, axis=1)

@@ -41,10 +41,11 @@ def _check_forward(lib, name, accum=None, all_heads=False):
     w = W.WORKLOADS[name]
     accum = accum or w.accum
     print(f"case {name} accum={accum} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nkv={w.Nkv} "
-          f"D={w.D} {w.dtype} causal={w.causal} mask={w.mask}", flush=True)
+          f"D={w.D} {w.dtype} causal={w.causal} mask={w.mask} dropout_p={w.dropout_p}", flush=True)
     inp = W.make_inputs(w, device="cuda")
     o, lse = lib.attention(inp["q"], inp["k"], inp["v"], causal=w.causal, mask=inp["mask"],
-                           scale=w.scale, accum=accum, return_lse=True)
+                           scale=w.scale, accum=accum, return_lse=True, dropout_p=w.dropout_p,
+                           seed=w.cfg_id)
     torch.cuda.synchronize()
     g = w.Hq // w.Hkv
     mask = None if inp["mask"] is None else to_f64(inp["mask"])
@@ -53,7 +54,8 @@ def _check_forward(lib, name, accum=None, all_heads=False):
     for b, h in _heads(w, all_heads):
         hk = h // g
         oo, lo = attn_fwd(to_f64(inp["q"][b:b + 1, h:h + 1]), to_f64(inp["k"][b:b + 1, hk:hk + 1]),
-                          to_f64(inp["v"][b:b + 1, hk:hk + 1]), w.scale, causal=w.causal, mask=mask)
+                          to_f64(inp["v"][b:b + 1, hk:hk + 1]), w.scale, causal=w.causal, mask=mask,
+                          dropout_p=w.dropout_p, seed=w.cfg_id, bh0=b * w.Hq + h)
         og = to_f64(o[b, h])
         lg = to_f64(lse[b, h])
         assert np.isfinite(og).all(), f"{name}: non-finite output in head ({b}, {h})"
@@ -89,6 +91,13 @@ def test_headline_whole_tensor(lib):
 @pytest.mark.parametrize("accum", ["f32", "f16"])
 def test_full_size_forward(lib, name, accum):
     _check_forward(lib, name, accum)
+
+
+@pytest.mark.parametrize("name", ["dropout", "dropout_bf16"])
+def test_full_size_dropout_forward(lib, name):
+    """The dropout rows (8K, D = 512, p = 0.1, fp32 accumulation): whole heads
+    against the oracle with the same keep mask."""
+    _check_forward(lib, name, "f32")
 
 
 @pytest.mark.parametrize("D", [320, 448, 512, 576, 768, 1024])
@@ -147,7 +156,7 @@ def bf16_neighbours(x):
 
 
 @pytest.mark.parametrize("name", ["bwd", "bwd_causal", "bwd_d1024", "bwd_d1024_causal", "bwd16k",
-                                  "bwd16k_causal"])
+                                  "bwd16k_causal", "bwd_dropout"])
 def test_full_size_backward(lib, name):
     """The backward at its benchmark size after this library's own forward (the
     path bench.py times, with its default bounded workspace); whole heads of
@@ -164,21 +173,28 @@ def test_full_size_backward(lib, name):
     distance from the exact gradient rounded to bf16, max |d - rne(d*)|, is
     printed beside it."""
     from test_gpu_bwd import _rounding_bounds
+    from test_gpu_dropout import _drop_bounds
 
     w = W.WORKLOADS[name]
     print(f"case {name} B={w.B} Hq={w.Hq} Nq={w.Nq} Nkv={w.Nkv} D={w.D} causal={w.causal}",
           flush=True)
     inp = W.make_inputs(w, device="cuda")
     q, k, v, do = inp["q"], inp["k"], inp["v"], inp["dout"]
-    o, lse = lib.attention(q, k, v, causal=w.causal, scale=w.scale, return_lse=True)
-    dq, dk, dv = lib.attention_backward(do, q, k, v, o, lse, causal=w.causal, scale=w.scale)
+    drop = dict(dropout_p=w.dropout_p, seed=w.cfg_id)
+    o, lse = lib.attention(q, k, v, causal=w.causal, scale=w.scale, return_lse=True, **drop)
+    dq, dk, dv = lib.attention_backward(do, q, k, v, o, lse, causal=w.causal, scale=w.scale, **drop)
     torch.cuda.synchronize()
     assert w.dtype == "bf16"
     # one whole head at 16K (the bound materialises P: 2 GiB per head), two below
     for b, h in (_heads(w) if w.Nq <= 8192 else [(w.B - 1, w.Hq - 1)]):
         sl = lambda t: t[b:b + 1, h:h + 1].cpu()
-        refs = attn_bwd(sl(q), sl(k), sl(v), sl(do), w.scale, causal=w.causal)
-        bounds = _rounding_bounds(sl(q), sl(k), sl(v), sl(do), w.scale, w.causal, None, refs, "bf16")
+        if w.dropout_p:
+            refs = attn_bwd(sl(q), sl(k), sl(v), sl(do), w.scale, causal=w.causal, bh0=b * w.Hq + h, **drop)
+            bounds = _drop_bounds(sl(q), sl(k), sl(v), sl(do), w.scale, w.causal, None, refs, "bf16",
+                                  w.dropout_p, w.cfg_id, bh0=b * w.Hq + h)
+        else:
+            refs = attn_bwd(sl(q), sl(k), sl(v), sl(do), w.scale, causal=w.causal)
+            bounds = _rounding_bounds(sl(q), sl(k), sl(v), sl(do), w.scale, w.causal, None, refs, "bf16")
         for nm, got, ref in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
             g = to_f64(sl(got))
             assert np.isfinite(g).all()

@@ -172,9 +172,9 @@ def test_backward_matches_central_differences():
 SRC = inspect.getsource(oracle_mod)
 MUTANTS = {
     "output_unscaled": ("p = np.where(keep, p * (256.0 / (256 - t)), 0.0)", "p = np.where(keep, p, 0.0)"),
-    "mask_transposed": ("keep = dropout_keep(seed, b * Hq + h, pos[r0:r1], np.arange(Nkv), t)\n"
+    "mask_transposed": ("keep = dropout_keep(seed, bh0 + b * Hq + h, pos[r0:r1], np.arange(Nkv), t)\n"
                         "                    p = np.where",
-                        "keep = dropout_keep(seed, b * Hq + h, np.arange(Nkv), pos[r0:r1], t).T\n"
+                        "keep = dropout_keep(seed, bh0 + b * Hq + h, np.arange(Nkv), pos[r0:r1], t).T\n"
                         "                    p = np.where"),
     "counter_ignores_head": ("np.full(i.shape, bh, np.uint64)", "np.full(i.shape, 0, np.uint64)"),
     "bwd_dp_not_masked": ("dp = (do @ v[b, hk].T) * zc", "dp = (do @ v[b, hk].T)"),
@@ -229,3 +229,24 @@ def test_unmutated_oracle_passes_the_dropout_pins():
 def test_dropout_pins_reject_planted_mistake(name):
     old, new = MUTANTS[name]
     assert not _pins_pass(_mutant(old, new)), f"dropout pins did not catch mutant {name}"
+
+
+def test_one_head_alone_with_its_offset_is_that_head():
+    # a head (b, h) checked alone takes bh0 = b Hq + h: the same output and
+    # gradients as in the whole problem (B = 2, Hq = 3, GQA g = 3)
+    rng = np.random.default_rng(11)
+    q, k, v, do = (_rand(rng, 2, 3, 9, 8), _rand(rng, 2, 1, 12, 8), _rand(rng, 2, 1, 12, 8),
+                   _rand(rng, 2, 3, 9, 8))
+    kw = dict(dropout_p=0.4, seed=31)
+    o, lse = attn_fwd(q, k, v, 0.3, **kw)
+    grads = attn_bwd(q, k, v, do, 0.3, **kw)
+    for b, h in [(0, 0), (1, 2), (1, 0)]:
+        one = lambda t, hh: t[b:b + 1, hh:hh + 1]
+        o1, _ = attn_fwd(one(q, h), one(k, 0), one(v, 0), 0.3, bh0=b * 3 + h, **kw)
+        np.testing.assert_array_equal(o1[0, 0], o[b, h])
+        dq1, _, _ = attn_bwd(one(q, h), one(k, 0), one(v, 0), one(do, h), 0.3, bh0=b * 3 + h, **kw)
+        np.testing.assert_array_equal(dq1[0, 0], grads[0][b, h])
+        # without the offset the head would draw head 0's mask
+        if b * 3 + h:
+            o0, _ = attn_fwd(one(q, h), one(k, 0), one(v, 0), 0.3, **kw)
+            assert not np.array_equal(o0[0, 0], o[b, h])

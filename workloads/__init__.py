@@ -6,7 +6,8 @@ arithmetic (no products, no softmax, no reductions).
 
 Shapes follow the benchmark tables of "FFPA Attention Benchmark"
 (ffpa-attn.readthedocs.io, section "More Benchmark": self-attn, cross-attn,
-decode-attn, gqa, causal, attn-mask, non-aligned rows at D=512 and D=320).
+decode-attn, gqa, causal, attn-mask, dropout, non-aligned rows at D=512 and
+D=320).
 The pages state no value distribution, so every tensor is i.i.d. N(0, 1).
 The additive mask is the compact key-position bias of shape [1, 1, 1, Nkv]
 named in the "Quick Start" section of the same page; 10% of its entries are
@@ -51,6 +52,9 @@ class Workload:
     mask: Optional[str] = None  # None | "key" ([1,1,1,Nkv]) | "query" ([1,1,Nq,Nkv])
     mask_neg_inf_frac: float = 0.1
     backward: bool = False
+    # dropout on the probabilities: the pages' tables run a "dropout" case but
+    # state no probability; 0.1 is taken here (the seed is the cfg_id)
+    dropout_p: float = 0.0
 
     @property
     def scale(self) -> float:
@@ -96,8 +100,14 @@ WORKLOADS.update({
     "bwd16k_causal": _w("bwd16k_causal", 6, 1, 32, 32, 16384, 16384, 512, dtype="bf16",
                         causal=True, backward=True),
 })
+# the "dropout" rows of the same tables (forward and backward), 8K, D = 512
+WORKLOADS.update({
+    "dropout": _w("dropout", 2, 1, 32, 32, 8192, 8192, 512, dropout_p=0.1),
+    "bwd_dropout": _w("bwd_dropout", 4, 1, 32, 32, 8192, 8192, 512, dtype="bf16", backward=True,
+                      dropout_p=0.1),
+})
 # bf16 variants of the variant family (same float32 draws as the fp16 ones)
-for _n in ("cross", "gqa", "causal", "nonaligned", "mask"):
+for _n in ("cross", "gqa", "causal", "nonaligned", "mask", "dropout"):
     WORKLOADS[f"{_n}_bf16"] = WORKLOADS[_n].replace(name=f"{_n}_bf16", dtype="bf16")
 for _d in (320, 448, 512, 576, 768, 1024):
     for _acc in ("f32", "f16"):
