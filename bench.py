@@ -205,8 +205,8 @@ def run_backward(ffpa, W, name, steps, warmup):
 
     w = W.WORKLOADS[name]
     inp = W.make_inputs(w, device="cuda")
-    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["dout"]
-    o, lse = ffpa.attention(q, k, v, causal=w.causal, scale=w.scale, return_lse=True,
+    q, k, v, do, mask = inp["q"], inp["k"], inp["v"], inp["dout"], inp["mask"]
+    o, lse = ffpa.attention(q, k, v, causal=w.causal, mask=mask, scale=w.scale, return_lse=True,
                             dropout_p=w.dropout_p, seed=w.cfg_id)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dt = ffpa.BF16 if w.dtype == "bf16" else ffpa.F16
@@ -216,7 +216,8 @@ def run_backward(ffpa, W, name, steps, warmup):
 
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.scale,
-            int(w.causal), 0, 0, ffpa.ACC_F32, dt)
+            int(w.causal), mask.data_ptr() if mask is not None else 0,
+            (1 if w.mask == "key" else w.Nq) if mask is not None else 0, ffpa.ACC_F32, dt)
     tail = (ws.data_ptr(), ws_bytes, stream)
 
     def call():
@@ -233,8 +234,8 @@ def run_backward(ffpa, W, name, steps, warmup):
     peak = PEAK_TFLOPS[w.dtype]
     del inp, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
-    return {"workload": f"{name}: B={w.B} H={w.Hq} N={w.Nq} D={w.D} {w.dtype} causal={w.causal}"
-                        + (f" dropout_p={w.dropout_p}" if w.dropout_p else ""),
+    return {"workload": f"{name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nkv={w.Nkv} D={w.D} {w.dtype} "
+                        f"causal={w.causal} mask={w.mask}" + (f" dropout_p={w.dropout_p}" if w.dropout_p else ""),
             "value": round(tflops, 2), "unit": "TFLOPS (5 GEMMs counted)",
             "ms_per_call": round(mean_ms, 4),
             "kernels": "prep + K^T copy + per chunk of kv heads: dK/dV (stores dS) + dQ from dS",
@@ -367,7 +368,8 @@ FWD_PATHS = ([("self_bf16", "f32"), ("self", "f16"), ("self_bf16", "f16")] +
              [(n + "_bf16", "f32") for n in ("cross", "gqa", "causal", "nonaligned", "mask", "dropout")] +
              [(f"dsweep{d}_{a}", a) for d in (320, 448, 512, 576, 768, 1024) for a in ("f32", "f16")] +
              [("self16k", "f32"), ("self16k_bf16", "f32"), ("causal16k", "f32"), ("nonaligned16k", "f32")])
-BWD_PATHS = ("bwd_causal", "bwd_d1024", "bwd16k", "bwd16k_causal", "bwd_dropout")
+BWD_PATHS = ("bwd_causal", "bwd_cross", "bwd_decode", "bwd_gqa", "bwd_mask", "bwd_nonaligned", "bwd_dropout",
+             "bwd_d1024", "bwd16k", "bwd16k_causal")
 
 
 def main(argv=None) -> int:

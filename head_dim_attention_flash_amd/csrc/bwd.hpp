@@ -406,8 +406,20 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int kb = wave / Sh::NP, hf = wave % Sh::NP;
 
   const int n_kt = (a.Nkv + Sh::ROWS - 1) / Sh::ROWS;
-  const int t = xcd_logical(blockIdx.x, a.wg_dkdv);
-  const int kt = t % n_kt, bhk = t / n_kt;
+  int kt, bhk;
+  if (a.causal) {
+    // the work of a key block falls with its index: blocks go out in that
+    // order over all heads at once, longest first, so that list scheduling
+    // evens out the triangle whatever the number of heads (XCD ranges of
+    // one head's blocks would give some XCDs only long blocks)
+    const int nh = a.wg_dkdv / n_kt;
+    kt = blockIdx.x / nh;
+    bhk = blockIdx.x % nh;
+  } else {
+    const int t = xcd_logical(blockIdx.x, a.wg_dkdv);
+    kt = t % n_kt;
+    bhk = t / n_kt;
+  }
   const int hk = bhk % a.Hkv, b = bhk / a.Hkv;
   const int g = a.Hq / a.Hkv;
   const int kw = kt * Sh::ROWS + 32 * kb;
@@ -638,7 +650,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
       // would stay live there)
       asm volatile("" ::: "memory");
     };
-    if (a.ds != nullptr && kw < a.Nkv) {
+    // (causal: a block above the diagonal, all zero and never read, is not stored)
+    if (a.ds != nullptr && kw < a.Nkv && !(a.causal && kw / 32 > qt)) {
       if (hf == 0) store_ds(IntTag<0>{}, sf[0]);
       else if (hf == 1) store_ds(IntTag<1>{}, sf[1]);
     }
@@ -743,10 +756,18 @@ void bwd_dq_kernel(BwdArgs a) {
   const int qb = wave / Sh::NP, hf = wave % Sh::NP;
 
   const int n_qb = (a.Nq + Sh::ROWS - 1) / Sh::ROWS;
-  const int t = xcd_logical(blockIdx.x, a.wg_dq);
-  int qblk = t % n_qb;
-  const int bh = t / n_qb;
-  if (a.causal) qblk = n_qb - 1 - qblk;  // longest rows first
+  int qblk, bh;
+  if (a.causal) {
+    // longest rows (last query blocks) first over all heads at once, as in
+    // the dK/dV pass
+    const int nh = a.wg_dq / n_qb;
+    qblk = n_qb - 1 - (int)blockIdx.x / nh;
+    bh = blockIdx.x % nh;
+  } else {
+    const int t = xcd_logical(blockIdx.x, a.wg_dq);
+    qblk = t % n_qb;
+    bh = t / n_qb;
+  }
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
   const int qw = qblk * Sh::ROWS + 32 * qb;
@@ -978,10 +999,18 @@ void bwd_dq_ds_kernel(BwdArgs a) {
   const int qb = wave / NQP, hf = wave % NQP;
 
   const int n_qb = (a.Nq + ROWS - 1) / ROWS;
-  const int t = xcd_logical(blockIdx.x, a.wg_dq_ds);
-  int qblk = t % n_qb;
-  const int bh = t / n_qb;
-  if (a.causal) qblk = n_qb - 1 - qblk;  // longest rows first
+  int qblk, bh;
+  if (a.causal) {
+    // longest rows (last query blocks) first over all heads at once, as in
+    // the dK/dV pass
+    const int nh = a.wg_dq_ds / n_qb;
+    qblk = n_qb - 1 - (int)blockIdx.x / nh;
+    bh = blockIdx.x % nh;
+  } else {
+    const int t = xcd_logical(blockIdx.x, a.wg_dq_ds);
+    qblk = t % n_qb;
+    bh = t / n_qb;
+  }
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
   const int qw = qblk * ROWS + 32 * qb;

@@ -486,4 +486,19 @@ __device__ inline int xcd_logical(int bid, int total) {
   return x * per + (x < rem ? x : rem) + j;
 }
 
+// Causal passes: logical tile t (xcd_logical order) -> position p of its
+// block in longest-first order within head t / nblk. A head whose blocks fill
+// several XCD ranges exactly (the range of total / 8 tiles divides nblk)
+// would give the first XCD its longest blocks and the last its shortest; XCD
+// r of the s that share the head takes positions r, r + s, r + 2 s, ...
+// instead, so every XCD gets an even share of the triangle, longest first.
+__device__ inline int causal_position(int t, int nblk, int total) {
+  int p = t % nblk;
+  if (total % 8 == 0) {
+    const int per = total / 8;
+    if (per < nblk && nblk % per == 0) p = (p % per) * (nblk / per) + p / per;
+  }
+  return p;
+}
+
 }  // namespace ffpa

@@ -108,9 +108,9 @@ void fwd_wide16_kernel(FwdArgs a) {
   // ---- workgroup -> (b, h, block of ROWS rows)
   const int n_qb = (a.Nq + ROWS - 1) / ROWS;
   const int t = xcd_logical(blockIdx.x, a.total_wg);
-  int qb = t % n_qb;
+  // causal: longest rows (last query blocks) first
+  const int qb = a.causal ? n_qb - 1 - causal_position(t, n_qb, a.total_wg) : t % n_qb;
   const int bh = t / n_qb;
-  if (a.causal) qb = n_qb - 1 - qb;  // longest rows first
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
   const int q0 = qb * ROWS;

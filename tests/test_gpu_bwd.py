@@ -210,7 +210,8 @@ def test_backward_chunks_give_the_same_bits(lib, shape, causal, mask_rows):
     dt = lib.BF16
     base = lib.ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dt)
     kt = B * Hkv * D * ((Nkv + 63) // 64 * 64) * 2
-    per = (Hq // Hkv) * ((Nq + 31) // 32) * ((Nkv + 31) // 32) * 2048
+    nqt, nkt = (Nq + 31) // 32, (Nkv + 31) // 32
+    per = (Hq // Hkv) * nqt * nkt * 2048
     full = lib.ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt)
     assert full == base + kt + B * Hkv * per  # small problems: one chunk
     for chunk in (1, 2):
@@ -226,3 +227,12 @@ def test_backward_chunks_give_the_same_bits(lib, shape, causal, mask_rows):
     bounds = _rounding_bounds(qc, kc, vc, doc, scale, causal, m2, refs, dtype)
     for nm, g_, r_ in zip(("dQ", "dK", "dV"), ref, refs):
         _compare(nm, g_, r_, dtype, f"chunks-{shape}", bounds[nm])
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 2, 2048, 2048, 512), (1, 2, 1, 1024, 1024, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("store_ds", [True, False])
+def test_backward_causal_few_heads_long_rows(lib, shape, store_ds):
+    """Causal with few heads and long rows: the blocks of one head fill several
+    XCD ranges, whose causal work order interleaves them."""
+    _run_case(lib, shape, "fp16", True, False, 31, store_ds=store_ds)

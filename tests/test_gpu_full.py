@@ -156,11 +156,12 @@ def bf16_neighbours(x):
 
 
 @pytest.mark.parametrize("name", ["bwd", "bwd_causal", "bwd_d1024", "bwd_d1024_causal", "bwd16k",
-                                  "bwd16k_causal", "bwd_dropout"])
+                                  "bwd16k_causal", "bwd_dropout", "bwd_cross", "bwd_decode", "bwd_gqa",
+                                  "bwd_mask", "bwd_nonaligned"])
 def test_full_size_backward(lib, name):
     """The backward at its benchmark size after this library's own forward (the
-    path bench.py times, with its default bounded workspace); whole heads of
-    dQ, dK, dV against the oracle.
+    path bench.py times, with its default bounded workspace); whole kv-head
+    groups of dQ, dK, dV against the oracle.
 
     Gate, elementwise: the bound of the small-shape bf16 backward tests
     (test_gpu_bwd._rounding_bounds, from the oracle's P): 1e-2 plus twice the
@@ -176,39 +177,49 @@ def test_full_size_backward(lib, name):
     from test_gpu_dropout import _drop_bounds
 
     w = W.WORKLOADS[name]
-    print(f"case {name} B={w.B} Hq={w.Hq} Nq={w.Nq} Nkv={w.Nkv} D={w.D} causal={w.causal}",
-          flush=True)
+    print(f"case {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nkv={w.Nkv} D={w.D} causal={w.causal} "
+          f"mask={w.mask} dropout_p={w.dropout_p}", flush=True)
     inp = W.make_inputs(w, device="cuda")
-    q, k, v, do = inp["q"], inp["k"], inp["v"], inp["dout"]
+    q, k, v, do, mask = inp["q"], inp["k"], inp["v"], inp["dout"], inp["mask"]
     drop = dict(dropout_p=w.dropout_p, seed=w.cfg_id)
-    o, lse = lib.attention(q, k, v, causal=w.causal, scale=w.scale, return_lse=True, **drop)
-    dq, dk, dv = lib.attention_backward(do, q, k, v, o, lse, causal=w.causal, scale=w.scale, **drop)
+    o, lse = lib.attention(q, k, v, causal=w.causal, mask=mask, scale=w.scale, return_lse=True, **drop)
+    dq, dk, dv = lib.attention_backward(do, q, k, v, o, lse, causal=w.causal, mask=mask, scale=w.scale,
+                                        **drop)
     torch.cuda.synchronize()
     assert w.dtype == "bf16"
-    # one whole head at 16K (the bound materialises P: 2 GiB per head), two below
+    m2 = None if mask is None else to_f64(mask).reshape(-1, w.Nkv)
+    g = w.Hq // w.Hkv
+    # whole kv-head groups (the g query heads that share a K/V head, whose
+    # dK and dV sum over the group): one at 16K (the bound materialises P,
+    # 2 GiB per query head), two below
     for b, h in (_heads(w) if w.Nq <= 8192 else [(w.B - 1, w.Hq - 1)]):
-        sl = lambda t: t[b:b + 1, h:h + 1].cpu()
+        hk = h // g
+        hs = slice(hk * g, (hk + 1) * g)
+        qs, dos = q[b:b + 1, hs].cpu(), do[b:b + 1, hs].cpu()
+        ks, vs = k[b:b + 1, hk:hk + 1].cpu(), v[b:b + 1, hk:hk + 1].cpu()
+        bh0 = b * w.Hq + hk * g
         if w.dropout_p:
-            refs = attn_bwd(sl(q), sl(k), sl(v), sl(do), w.scale, causal=w.causal, bh0=b * w.Hq + h, **drop)
-            bounds = _drop_bounds(sl(q), sl(k), sl(v), sl(do), w.scale, w.causal, None, refs, "bf16",
-                                  w.dropout_p, w.cfg_id, bh0=b * w.Hq + h)
+            refs = attn_bwd(qs, ks, vs, dos, w.scale, causal=w.causal, mask=m2, bh0=bh0, **drop)
+            bounds = _drop_bounds(qs, ks, vs, dos, w.scale, w.causal, m2, refs, "bf16", w.dropout_p,
+                                  w.cfg_id, bh0=bh0)
         else:
-            refs = attn_bwd(sl(q), sl(k), sl(v), sl(do), w.scale, causal=w.causal)
-            bounds = _rounding_bounds(sl(q), sl(k), sl(v), sl(do), w.scale, w.causal, None, refs, "bf16")
-        for nm, got, ref in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs):
-            g = to_f64(sl(got))
-            assert np.isfinite(g).all()
-            diff = np.abs(g - ref)
+            refs = attn_bwd(qs, ks, vs, dos, w.scale, causal=w.causal, mask=m2)
+            bounds = _rounding_bounds(qs, ks, vs, dos, w.scale, w.causal, m2, refs, "bf16")
+        gots = (dq[b:b + 1, hs].cpu(), dk[b:b + 1, hk:hk + 1].cpu(), dv[b:b + 1, hk:hk + 1].cpu())
+        for nm, got, ref in zip(("dQ", "dK", "dV"), gots, refs):
+            gd = to_f64(got)
+            assert np.isfinite(gd).all()
+            diff = np.abs(gd - ref)
             ratio = (diff / bounds[nm]).max()
             lo, hi = bf16_neighbours(ref)
             tie = np.abs(ref - lo) == np.abs(hi - ref)
             even = (lo.astype(np.float32).view(np.uint32) >> 16) % 2 == 0
             rounded = np.where(tie, np.where(even, lo, hi), np.where(np.abs(ref - lo) < np.abs(hi - ref), lo, hi))
-            off_rne = np.where((g == lo) | (g == hi), 0.0, np.abs(g - rounded)).max()
-            rel = np.linalg.norm(g - ref) / np.linalg.norm(ref)
-            print(f"  parity {name} (b={b}, h={h}) {nm}: max|d - ref|={diff.max():.3e} "
-                  f"err/bound={ratio:.3f} max|d - rne(ref)|={off_rne:.3e} relL2={rel:.3e} "
-                  f"max|ref|={np.abs(ref).max():.3e}", flush=True)
+            off_rne = np.where((gd == lo) | (gd == hi), 0.0, np.abs(gd - rounded)).max()
+            rel = np.linalg.norm(gd - ref) / np.linalg.norm(ref)
+            print(f"  parity {name} (b={b}, kv head {hk}, query heads {hk * g}..{hk * g + g - 1}) {nm}: "
+                  f"max|d - ref|={diff.max():.3e} err/bound={ratio:.3f} max|d - rne(ref)|={off_rne:.3e} "
+                  f"relL2={rel:.3e} max|ref|={np.abs(ref).max():.3e}", flush=True)
             assert ratio <= 1.0, f"{name} {nm}: error exceeds the rounding bound by {ratio:.3f}x"
             assert rel <= 2.5e-2, f"{name} {nm}: rel L2 {rel}"
     del inp, o, lse, dq, dk, dv

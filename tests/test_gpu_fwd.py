@@ -319,3 +319,13 @@ def test_bf16_inputs_with_the_fp16_accumulator(lib, D):
     assert np.abs(to_f64(lse) - lo).max() <= 2e-3
     o32, _ = _run(lib, q.cuda(), k.cuda(), huge.cuda(), accum="f32", scale=scale)
     assert np.abs(to_f64(o32)[..., 5] - oo[..., 5]).max() <= 2.0 ** -8 * 1.0e5 * 2
+
+
+@pytest.mark.parametrize("D", [512, 1024])
+@pytest.mark.parametrize("accum", ["f32", "f16"])
+def test_causal_few_heads_long_rows(lib, D, accum):
+    """Causal with two heads of 4096 rows: each head's query blocks fill
+    several XCD ranges, whose causal work order interleaves the blocks."""
+    q, k, v, _ = _inputs(23, 1, 2, 2, 4096, 4096, D, "fp16")
+    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), causal=True, accum=accum)
+    _compare(o, lse, q, k, v, 1.0 / math.sqrt(D), True, None, "fp16", accum, f"causal-2x4096-D{D}-{accum}")

@@ -100,6 +100,14 @@ WORKLOADS.update({
     "bwd16k_causal": _w("bwd16k_causal", 6, 1, 32, 32, 16384, 16384, 512, dtype="bf16",
                         causal=True, backward=True),
 })
+# the backward of the other rows of the backward tables (bf16, 8K, D = 512)
+WORKLOADS.update({
+    "bwd_cross": _w("bwd_cross", 4, 1, 32, 32, 1024, 8192, 512, dtype="bf16", backward=True),
+    "bwd_decode": _w("bwd_decode", 4, 16, 32, 32, 1, 8192, 512, dtype="bf16", backward=True),
+    "bwd_gqa": _w("bwd_gqa", 4, 1, 32, 8, 8192, 8192, 512, dtype="bf16", backward=True),
+    "bwd_mask": _w("bwd_mask", 4, 1, 32, 32, 8192, 8192, 512, dtype="bf16", mask="key", backward=True),
+    "bwd_nonaligned": _w("bwd_nonaligned", 4, 1, 32, 32, 8191, 8191, 512, dtype="bf16", backward=True),
+})
 # the "dropout" rows of the same tables (forward and backward), 8K, D = 512
 WORKLOADS.update({
     "dropout": _w("dropout", 2, 1, 32, 32, 8192, 8192, 512, dropout_p=0.1),
