@@ -147,15 +147,19 @@ def cpu_baseline(w, inp, heads: int) -> dict:
                       f"{dt:.2f} s"}
 
 
-def time_forward(ffpa, w, inp, accum, steps, warmup):
+def time_forward(ffpa, w, inp, accum, steps, warmup, any_variant=False):
     import torch
 
     q, k, v, mask = inp["q"], inp["k"], inp["v"], inp.get("mask")
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=q.device)
-    # caller-owned workspace, allocated once (the transposed V of the prefill path)
-    ws_bytes = ffpa.ffpa_attn_fwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
-                                                 ffpa.BF16 if w.dtype == "bf16" else ffpa.F16)
+    # caller-owned workspace, allocated once (the transposed V of the prefill
+    # path); any_variant: room for whichever variant a tuning run picked
+    dt = ffpa.BF16 if w.dtype == "bf16" else ffpa.F16
+    ws_bytes = ffpa.ffpa_attn_fwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, dt)
+    if any_variant:
+        ws_bytes = max(ffpa.ffpa_attn_fwd_variant_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, dt,
+                                                                 int(w.causal), var) for var in range(4))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
 
     def step():
@@ -285,14 +289,19 @@ def run_decode(ffpa, W, steps, warmup):
             "rocprof": recorded_counters("decode")}
 
 
-def timed_call(w, accum="f32") -> str:
-    """The kernels one timed forward call enqueues (mirrors the library's choice)."""
+def timed_call(w, accum="f32", variant=0) -> str:
+    """The kernels one timed forward call enqueues (mirrors the library's
+    choice for `variant`, 0 = the default)."""
     if w.Nq == 1:
-        return "dec_split_kernel + dec_combine_kernel"
+        return "dec_split_kernel + dec_combine_kernel" + (f" (key ranges / {2 ** (variant - 1)})" if variant else "")
     if w.D > 512:
+        if variant == 0:
+            variant = 1 if (accum != "f16" or w.dropout_p) else (2 if w.D <= 768 else 3)
         return ("fwd_vt_kernel (V transposed, blocks of 32 keys) + " +
-                ("fwd_wide16_kernel" if accum == "f16" else "fwd_wide_kernel"))
-    if w.Nq * w.Hq >= 3072 * w.Hkv:
+                {1: "fwd_wide_kernel (fp32 accumulator, 64 rows)",
+                 2: "fwd_wide16_kernel (a wave holds all of D, 128 rows)",
+                 3: "fwd_wide16_kernel (a wave pair splits D, 64 rows)"}[variant])
+    if variant == 2 or (variant == 0 and w.Nq * w.Hq >= 3072 * w.Hkv):
         return "fwd_vt_kernel (V transposed into the workspace) + fwd_prefill_kernel"
     return "fwd_prefill_kernel (V staged as is)"
 
@@ -339,13 +348,22 @@ def run_one(ffpa, W, name, accum, steps, warmup, with_cpu, cpu_heads):
     return line
 
 
-def run_forward_path(ffpa, W, name, accum, steps, warmup):
-    """One forward workload timed like the headline (whole call, HIP events)."""
+def run_forward_path(ffpa, W, name, accum, steps, warmup, tune=False):
+    """One forward workload timed like the headline (whole call, HIP events).
+    tune: ffpa_attn_fwd_tune (level 2, "max") on the workload first, so that
+    the timed calls run the variant it picked."""
     import torch
 
     w = W.WORKLOADS[name]
     inp = W.make_inputs(w, device="cuda")
-    per, _ = time_forward(ffpa, w, inp, accum, steps, warmup)
+    tuned = None
+    if tune:
+        chosen, ms = ffpa.tune_forward(inp["q"], inp["k"], inp["v"], causal=w.causal, mask=inp["mask"],
+                                       scale=w.scale, accum=accum, level=2)
+        tuned = {"chosen_variant": chosen, "ms_per_variant": {str(k): round(t, 4) for k, t in ms.items()}}
+    per, _ = time_forward(ffpa, w, inp, accum, steps, warmup, any_variant=tune)
+    if tune:
+        ffpa.ffpa_attn_tune_reset()
     mean_ms = sum(per) / len(per)
     tflops = counted_flops(w.B, w.Hq, w.Nq, w.Nkv, w.D, w.causal) / (mean_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -355,9 +373,11 @@ def run_forward_path(ffpa, W, name, accum, steps, warmup):
                         f"{w.dtype} causal={w.causal} mask={w.mask} accum={accum}"
                         + (f" dropout_p={w.dropout_p}" if w.dropout_p else ""),
             "value": round(tflops, 2), "unit": "TFLOPS" + (" (causal: half counted)" if w.causal else ""),
-            "ms_per_call": round(mean_ms, 4), "timed_call": timed_call(w, accum),
+            "ms_per_call": round(mean_ms, 4),
+            "timed_call": timed_call(w, accum, tuned["chosen_variant"] if tuned else 0),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4)}}
+                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4)},
+            **({"tuned": tuned} if tuned else {})}
 
 
 # Forward workloads the default line measures beside the headline: every
@@ -368,6 +388,9 @@ FWD_PATHS = ([("self_bf16", "f32"), ("self", "f16"), ("self_bf16", "f16")] +
              [(n + "_bf16", "f32") for n in ("cross", "gqa", "causal", "nonaligned", "mask", "dropout")] +
              [(f"dsweep{d}_{a}", a) for d in (320, 448, 512, 576, 768, 1024) for a in ("f32", "f16")] +
              [("self16k", "f32"), ("self16k_bf16", "f32"), ("causal16k", "f32"), ("nonaligned16k", "f32")])
+# Forward workloads measured again after tuning (the variants differ most there)
+TUNED_PATHS = [("cross", "f32"), ("gqa", "f32"), ("dsweep576_f16", "f16"), ("dsweep768_f16", "f16"),
+               ("dsweep1024_f16", "f16")]
 BWD_PATHS = ("bwd_causal", "bwd_cross", "bwd_decode", "bwd_gqa", "bwd_mask", "bwd_nonaligned", "bwd_dropout",
              "bwd_d1024", "bwd16k", "bwd16k_causal")
 
@@ -432,6 +455,8 @@ def main(argv=None) -> int:
         paths["decode"] = run_decode(ffpa, W, args.steps, max(args.warmup, 50))
         paths["forward"] = {f"{n}:{a}": run_forward_path(ffpa, W, n, a, args.steps, args.warmup)
                             for n, a in FWD_PATHS}
+        paths["forward_tuned"] = {f"{n}:{a}": run_forward_path(ffpa, W, n, a, args.steps, args.warmup, tune=True)
+                                  for n, a in TUNED_PATHS}
         line["paths"] = paths
     print(json.dumps(line), flush=True)
     if args.copy_calibration:

@@ -19,7 +19,8 @@ from typing import Optional
 
 __all__ = [
     "load", "FFPAError", "ffpa_attn_fwd", "ffpa_attn_fwd_noalloc", "ffpa_attn_bwd",
-    "ffpa_attn_fwd_dropout", "ffpa_attn_bwd_dropout",
+    "ffpa_attn_fwd_dropout", "ffpa_attn_bwd_dropout", "ffpa_attn_fwd_variant",
+    "ffpa_attn_fwd_variant_workspace_size", "ffpa_attn_fwd_tune", "ffpa_attn_tune_reset", "tune_forward",
     "ffpa_attn_fwd_workspace_size",
     "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min", "ffpa_last_error",
     "ffpa_version", "attention",
@@ -38,7 +39,9 @@ _STATUS = {1: "FFPA_ERR_INVALID_ARG", 2: "FFPA_ERR_UNSUPPORTED", 3: "FFPA_ERR_WO
 # Symbols declared in include/ffpa_attn.h.
 EXPORTED = ("ffpa_attn_fwd", "ffpa_attn_fwd_workspace_size", "ffpa_attn_fwd_noalloc", "ffpa_attn_bwd",
             "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min",
-            "ffpa_attn_fwd_dropout", "ffpa_attn_bwd_dropout", "ffpa_last_error", "ffpa_version")
+            "ffpa_attn_fwd_dropout", "ffpa_attn_bwd_dropout", "ffpa_attn_fwd_variant",
+            "ffpa_attn_fwd_variant_workspace_size", "ffpa_attn_fwd_tune", "ffpa_attn_tune_reset",
+            "ffpa_last_error", "ffpa_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -73,6 +76,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffpa_attn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp,
                                           i, i, i, f, u64, vp, sz, vp]
     lib.ffpa_attn_bwd_dropout.restype = i
+    lib.ffpa_attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, i, i, i, vp, sz, vp]
+    lib.ffpa_attn_fwd_variant.restype = i
+    lib.ffpa_attn_fwd_variant_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i]
+    lib.ffpa_attn_fwd_variant_workspace_size.restype = sz
+    lib.ffpa_attn_fwd_tune.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, i, i, vp, sz, i,
+                                       ctypes.POINTER(i), ctypes.POINTER(f), vp]
+    lib.ffpa_attn_fwd_tune.restype = i
+    lib.ffpa_attn_tune_reset.argtypes = []
+    lib.ffpa_attn_tune_reset.restype = None
     lib.ffpa_attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.ffpa_attn_fwd_workspace_size.restype = sz
     lib.ffpa_attn_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
@@ -154,6 +166,33 @@ def ffpa_attn_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nkv
                                         scale, causal, mask or None, mask_rows, accum_dtype, dtype,
                                         dropout_p, seed, workspace or None, workspace_bytes,
                                         stream or None)
+
+
+def ffpa_attn_fwd_variant(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                          accum_dtype, dtype, variant, workspace, workspace_bytes, stream) -> int:
+    """Raw C call of the forward as a given variant (0 = default)."""
+    return load().ffpa_attn_fwd_variant(q, k, v, o, lse or None, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
+                                        mask or None, mask_rows, accum_dtype, dtype, variant,
+                                        workspace or None, workspace_bytes, stream or None)
+
+
+def ffpa_attn_fwd_variant_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype, causal, variant) -> int:
+    return load().ffpa_attn_fwd_variant_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype, causal, variant)
+
+
+def ffpa_attn_fwd_tune(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                       accum_dtype, dtype, workspace, workspace_bytes, level, stream):
+    """Raw C call of the tuner; returns (status, chosen variant, [ms of variants 1..3])."""
+    chosen = ctypes.c_int(0)
+    ms = (ctypes.c_float * 3)(-1.0, -1.0, -1.0)
+    st = load().ffpa_attn_fwd_tune(q, k, v, o, lse or None, B, Hq, Hkv, Nq, Nkv, D, scale, causal,
+                                   mask or None, mask_rows, accum_dtype, dtype, workspace or None,
+                                   workspace_bytes, level, ctypes.byref(chosen), ms, stream or None)
+    return st, chosen.value, list(ms)
+
+
+def ffpa_attn_tune_reset() -> None:
+    load().ffpa_attn_tune_reset()
 
 
 def _seed(seed) -> int:
@@ -271,6 +310,31 @@ def attention(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float
     else:
         _check(ffpa_attn_fwd(*args, *tail))
     return (o, lse) if return_lse else o
+
+
+def tune_forward(q, k, v, *, causal: bool = False, mask=None, scale: Optional[float] = None,
+                 accum: str = "f32", level: int = 2):
+    """Tune the forward of this problem (ffpa_attn_fwd_tune) on scratch outputs;
+    later ``attention`` calls of the same problem run the chosen variant.
+    Returns (chosen variant, {variant: ms per call})."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nkv, D = _dims(q, k, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
+    mptr, mrows = _mask_args(mask, q, Nq, Nkv)
+    dt = _dtype_code(q)
+    # room for every variant (the largest need is the transposed copy of V)
+    ws_bytes = max(ffpa_attn_fwd_variant_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt, int(causal), var)
+                   for var in range(4))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st, chosen, ms = ffpa_attn_fwd_tune(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                        B, Hq, Hkv, Nq, Nkv, D, scale, int(causal), mptr, mrows,
+                                        _accum_code(accum), dt, ws.data_ptr(), ws_bytes, int(level), stream)
+    _check(st)
+    return chosen, {i + 1: t for i, t in enumerate(ms) if t >= 0}
 
 
 def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None,

@@ -3,8 +3,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdint>
+#include <map>
 #include <mutex>
 #include <string>
 
@@ -61,17 +63,42 @@ FwdLauncher fwd_launcher(int D, int bf16, int acc16, bool vt, bool drop, size_t*
 
 using WideLauncher = hipError_t (*)(const ffpa::FwdArgs&, hipStream_t);
 
-// fp32 output accumulator: fwd_wide_kernel (64 rows per workgroup); fp16:
-// fwd_wide16_kernel (wide16_rows<D>() rows per workgroup, 128 up to D = 768)
-WideLauncher wide_launcher(int D, int bf16, int acc16, bool drop, int* rows) {
+// The wide kernels (D > 512), by tile shape:
+//   kWideF32:   fwd_wide_kernel, fp32 output accumulator, 64 rows per workgroup;
+//   kWide16One: fwd_wide16_kernel, fp16 accumulator, a wave holds all of D,
+//               128 rows per workgroup (D <= 768 only);
+//   kWide16Two: fwd_wide16_kernel, fp16 accumulator, a wave pair splits D,
+//               64 rows per workgroup.
+enum WideShape { kWideF32 = 1, kWide16One = 2, kWide16Two = 3 };
+
+WideLauncher wide_launcher(int D, int bf16, int shape, bool drop, int* rows) {
   switch (D) {
-#define FFPA_CASE(DD)                                                                       \
-  case DD:                                                                                  \
-    *rows = acc16 ? ffpa::wide16_rows<DD>() : 64;                                           \
-    if (drop) return bf16 ? ffpa::launch_fwd_wide<DD, true, true> : ffpa::launch_fwd_wide<DD, false, true>; \
-    if (acc16) return bf16 ? ffpa::launch_fwd_wide16<DD, true> : ffpa::launch_fwd_wide16<DD, false>; \
-    return bf16 ? ffpa::launch_fwd_wide<DD, true> : ffpa::launch_fwd_wide<DD, false>;
+#define FFPA_CASE(DD)                                                                                  \
+  case DD:                                                                                             \
+    if (drop || shape == kWideF32) {                                                                   \
+      *rows = 64;                                                                                      \
+      if (drop) return bf16 ? ffpa::launch_fwd_wide<DD, true, true> : ffpa::launch_fwd_wide<DD, false, true>; \
+      return bf16 ? ffpa::launch_fwd_wide<DD, true> : ffpa::launch_fwd_wide<DD, false>;               \
+    }                                                                                                  \
+    if (shape == kWide16Two) {                                                                         \
+      *rows = ffpa::wide16_rows<DD, 2>();                                                              \
+      return bf16 ? ffpa::launch_fwd_wide16<DD, true, 2> : ffpa::launch_fwd_wide16<DD, false, 2>;     \
+    }                                                                                                  \
+    if (DD > 768) return nullptr;                                                                      \
+    *rows = ffpa::wide16_rows<DD, 1>();                                                                \
+    return bf16 ? ffpa::launch_fwd_wide16<DD, true, 1> : ffpa::launch_fwd_wide16<DD, false, 1>;
     FFPA_CASE(576) FFPA_CASE(640) FFPA_CASE(704) FFPA_CASE(768)
+#undef FFPA_CASE
+#define FFPA_CASE(DD)                                                                                  \
+  case DD:                                                                                             \
+    if (drop || shape == kWideF32) {                                                                   \
+      *rows = 64;                                                                                      \
+      if (drop) return bf16 ? ffpa::launch_fwd_wide<DD, true, true> : ffpa::launch_fwd_wide<DD, false, true>; \
+      return bf16 ? ffpa::launch_fwd_wide<DD, true> : ffpa::launch_fwd_wide<DD, false>;               \
+    }                                                                                                  \
+    if (shape != kWide16Two) return nullptr;                                                           \
+    *rows = ffpa::wide16_rows<DD, 2>();                                                                \
+    return bf16 ? ffpa::launch_fwd_wide16<DD, true, 2> : ffpa::launch_fwd_wide16<DD, false, 2>;
     FFPA_CASE(832) FFPA_CASE(896) FFPA_CASE(960) FFPA_CASE(1024)
 #undef FFPA_CASE
     default:
@@ -208,21 +235,67 @@ int fwd_check_args(const void* q, const void* k, const void* v, void* o, float* 
   return FFPA_OK;
 }
 
-// The forward after its argument checks. allow_vt = false keeps the prefill
-// path (D <= 512) off the transposed copy of V, so that it needs no
-// workspace; otherwise the path is the one ffpa_attn_fwd_workspace_size sizes.
+// Forward variants: the tile shapes and staging layouts a problem can run
+// with (ffpa_attn_fwd_variant, ffpa_attn_fwd_tune). 0 = the default choice.
+//   Nq > 1, D <= 512: 1 = V staged as is, 2 = V from its transposed copy;
+//   Nq > 1, D > 512:  WideShape (1 = fp32 accumulator, 64 rows; 2 = fp16
+//                     accumulator, a wave holds all of D, 128 rows, D <= 768;
+//                     3 = fp16 accumulator, a wave pair splits D, 64 rows);
+//   Nq = 1:           1, 2, 3 = the default number of key ranges per head
+//                     divided by 1, 2, 4.
+constexpr int kMaxVariant = 3;
+
+// The variant 0 stands for, for this problem.
+int fwd_default_variant(int Hq, int Hkv, int Nq, int D, int accum_dtype, bool dropout) {
+  if (Nq == 1) return 1;
+  if (D > 512) return (dropout || accum_dtype != FFPA_ACC_F16) ? kWideF32 : (D <= 768 ? kWide16One : kWide16Two);
+  return ffpa::fwd_use_vt(Hq, Hkv, Nq) ? 2 : 1;
+}
+
+// Whether `variant` (after 0 is resolved) exists for this problem: the fp16-
+// accumulator shapes only where fp16 accumulation was asked for (fp32 is the
+// more accurate one), and not with dropout.
+bool fwd_variant_ok(int Nq, int D, int accum_dtype, bool dropout, int variant) {
+  if (variant < 1 || variant > kMaxVariant) return false;
+  if (Nq == 1) return true;
+  if (D > 512) {
+    if (variant == kWideF32) return true;
+    if (dropout || accum_dtype != FFPA_ACC_F16) return false;
+    return variant == kWide16Two || D <= 768;
+  }
+  return variant <= 2;
+}
+
+// Decode key ranges per head under `variant`.
+int dec_splits_for(int B, int Hq, int kv_end, int variant) {
+  const int s = ffpa::dec_splits(B, Hq, kv_end);
+  const int div = variant == 3 ? 4 : variant == 2 ? 2 : 1;
+  return std::max(1, s / div);
+}
+
+// Workspace bytes of a resolved variant.
+size_t fwd_variant_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, int variant) {
+  if (Nq == 1)
+    return (size_t)B * Hq * dec_splits_for(B, Hq, dec_kv_end(Nkv, causal), variant) * ((size_t)D + 1) * sizeof(float);
+  if (D > 512 || variant == 2) return ffpa::fwd_vt_bytes(B, Hkv, Nkv, D);
+  return 0;
+}
+
+// The forward after its argument checks, as `variant` (0 = default).
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
              int Hkv, int Nq, int Nkv, int D, float scale, int causal, const void* mask,
              int mask_rows, int accum_dtype, int dtype, void* workspace, size_t workspace_bytes,
-             bool allow_vt, void* stream, const ffpa::DropParams& drop = ffpa::DropParams{}) {
+             int variant, void* stream, const ffpa::DropParams& drop = ffpa::DropParams{}) {
   const bool dropout = drop.t != 0;
   if (dropout && accum_dtype != FFPA_ACC_F32)
     return fail(FFPA_ERR_UNSUPPORTED, "dropout is built with the fp32 accumulator (FFPA_ACC_F32)");
+  if (variant == 0) variant = fwd_default_variant(Hq, Hkv, Nq, D, accum_dtype, dropout);
+  if (!fwd_variant_ok(Nq, D, accum_dtype, dropout, variant))
+    return fail(FFPA_ERR_INVALID_ARG, "variant " + std::to_string(variant) + " does not exist for this problem");
   if (!aligned16(workspace)) return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-  const bool no_vt = !allow_vt && Nq > 1 && D <= 512;
-  const size_t need = no_vt ? 0 : ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  const size_t need = fwd_variant_bytes(B, Hq, Hkv, Nq, Nkv, D, causal, variant);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr))
-    return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_fwd_workspace_size()");
+    return fail(FFPA_ERR_WORKSPACE, "workspace smaller than this path needs (ffpa_attn_fwd_workspace_size())");
 
   if (Nq == 1) {
     // one query row per head: split-KV decode kernels
@@ -232,7 +305,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.mask = mask;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nkv = Nkv;
     a.kv_end = dec_kv_end(Nkv, causal);
-    a.splits = ffpa::dec_splits(B, Hq, a.kv_end);
+    a.splits = dec_splits_for(B, Hq, a.kv_end, variant);
     a.keys_per_split = ffpa::dec_keys_per_split(a.kv_end, a.splits);
     a.scale_log2 = scale * ffpa::kLog2e;
     const int64_t waves = (int64_t)B * Hq * a.splits;
@@ -247,9 +320,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   }
 
   if (D > 512) {
-    // head dimensions above 512: D split across wave pairs
+    // head dimensions above 512
     int rows = 64;
-    WideLauncher launch = wide_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, dropout, &rows);
+    WideLauncher launch = wide_launcher(D, dtype == FFPA_BF16, variant, dropout, &rows);
     if (launch == nullptr)
       return fail(FFPA_ERR_UNSUPPORTED, "for Nq > 1, D above 512 must be a multiple of 64");
     ffpa::FwdArgs a{};
@@ -274,7 +347,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   }
 
   size_t ring = 0;
-  const bool vt = !no_vt && ffpa::fwd_use_vt(Hq, Hkv, Nq);
+  const bool vt = variant == 2;
   FwdLauncher launch = fwd_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, vt, dropout, &ring);
   if (launch == nullptr) return fail(FFPA_ERR_UNSUPPORTED, "this head dimension is not built yet");
   size_t lds = ring + ffpa::kFwdFlagBytes;
@@ -305,6 +378,33 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   return FFPA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Tuned choices: problem key -> variant, filled by ffpa_attn_fwd_tune and read
+// by ffpa_attn_fwd (and ffpa_attn_fwd_noalloc) for the rest of the process.
+// ---------------------------------------------------------------------------
+using TuneKey = std::array<int64_t, 11>;
+std::mutex g_tune_mu;
+std::map<TuneKey, int> g_tuned;
+
+TuneKey tune_key(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, const void* mask, int mask_rows,
+                 int accum_dtype, int dtype) {
+  return {B, Hq, Hkv, Nq, Nkv, D, causal, mask ? mask_rows : 0, accum_dtype, dtype, 0};
+}
+
+// The tuned variant of this problem if it is recorded and fits the
+// workspace given; else 0 (the default).
+int tuned_variant(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int causal, const void* mask, int mask_rows,
+                  int accum_dtype, int dtype, size_t workspace_bytes) {
+  int var = 0;
+  {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    const auto it = g_tuned.find(tune_key(B, Hq, Hkv, Nq, Nkv, D, causal, mask, mask_rows, accum_dtype, dtype));
+    if (it != g_tuned.end()) var = it->second;
+  }
+  if (var != 0 && fwd_variant_bytes(B, Hq, Hkv, Nq, Nkv, D, causal, var) > workspace_bytes) var = 0;
+  return var;
+}
+
 }  // namespace
 
 extern "C" {
@@ -317,8 +417,102 @@ int ffpa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
   const int st = fwd_check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
                                 accum_dtype, dtype);
   if (st != FFPA_OK) return st;
+  const int var = tuned_variant(B, Hq, Hkv, Nq, Nkv, D, causal, mask, mask_rows, accum_dtype, dtype,
+                                workspace ? workspace_bytes : 0);
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
-                  dtype, workspace, workspace_bytes, true, stream);
+                  dtype, workspace, workspace_bytes, var, stream);
+}
+
+size_t ffpa_attn_fwd_variant_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype,
+                                            int causal, int variant) {
+  (void)dtype;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1 || variant < 0 || variant > kMaxVariant) return 0;
+  if (variant == 0) return ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  return fwd_variant_bytes(B, Hq, Hkv, Nq, Nkv, D, causal, variant);
+}
+
+int ffpa_attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                          int Hkv, int Nq, int Nkv, int D, float scale, int causal, const void* mask,
+                          int mask_rows, int accum_dtype, int dtype, int variant, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  const int st = fwd_check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                                accum_dtype, dtype);
+  if (st != FFPA_OK) return st;
+  if (variant < 0 || variant > kMaxVariant)
+    return fail(FFPA_ERR_INVALID_ARG, "variant must be 0 .. " + std::to_string(kMaxVariant));
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
+                  dtype, workspace, workspace_bytes, variant, stream);
+}
+
+int ffpa_attn_fwd_tune(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                       int Hkv, int Nq, int Nkv, int D, float scale, int causal, const void* mask,
+                       int mask_rows, int accum_dtype, int dtype, void* workspace, size_t workspace_bytes,
+                       int level, int* chosen, float* ms, void* stream) {
+  g_err.clear();
+  const int st = fwd_check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows,
+                                accum_dtype, dtype);
+  if (st != FFPA_OK) return st;
+  if (level != 1 && level != 2) return fail(FFPA_ERR_INVALID_ARG, "level must be 1 (fast) or 2 (max)");
+  if (!aligned16(workspace)) return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const int warm = level == 1 ? 1 : 3, reps = level == 1 ? 3 : 10;
+  const size_t ws_bytes = workspace ? workspace_bytes : 0;
+  bool runs[kMaxVariant + 1] = {};
+  int n_run = 0;
+  for (int var = 1; var <= kMaxVariant; ++var) {
+    runs[var] = fwd_variant_ok(Nq, D, accum_dtype, false, var) &&
+                fwd_variant_bytes(B, Hq, Hkv, Nq, Nkv, D, causal, var) <= ws_bytes;
+    n_run += runs[var];
+    if (ms) ms[var - 1] = -1.f;
+  }
+  if (n_run == 0) return fail(FFPA_ERR_WORKSPACE, "no variant fits the workspace given");
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  hipError_t e = hipEventCreate(&ev[0]);
+  if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+  if (e != hipSuccess) {
+    for (hipEvent_t x : ev)
+      if (x) (void)hipEventDestroy(x);
+    return fail(FFPA_ERR_HIP, std::string("hipEventCreate failed: ") + hipGetErrorString(e));
+  }
+  int best = 0, status = FFPA_OK;
+  float best_ms = 0.f;
+  for (int var = 1; var <= kMaxVariant && status == FFPA_OK; ++var) {
+    float t = -1.f;
+    if (runs[var]) {
+      for (int i = 0; i < warm + reps && status == FFPA_OK; ++i) {
+        if (i == warm && (e = hipEventRecord(ev[0], (hipStream_t)stream)) != hipSuccess) break;
+        status = fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
+                          dtype, workspace, workspace_bytes, var, stream);
+      }
+      if (status != FFPA_OK) break;
+      if (e == hipSuccess) e = hipEventRecord(ev[1], (hipStream_t)stream);
+      if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[0], ev[1]);
+      if (e != hipSuccess) break;
+      t /= reps;
+      if (best == 0 || t < best_ms) {
+        best = var;
+        best_ms = t;
+      }
+    }
+    if (ms) ms[var - 1] = t;
+  }
+  for (hipEvent_t x : ev) (void)hipEventDestroy(x);
+  if (status != FFPA_OK) return status;
+  if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("timing failed: ") + hipGetErrorString(e));
+  {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    g_tuned[tune_key(B, Hq, Hkv, Nq, Nkv, D, causal, mask, mask_rows, accum_dtype, dtype)] = best;
+  }
+  if (chosen) *chosen = best;
+  // o and lse end with the chosen variant's results
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype, dtype,
+                  workspace, workspace_bytes, best, stream);
+}
+
+void ffpa_attn_tune_reset(void) {
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  g_tuned.clear();
 }
 
 int ffpa_attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
@@ -333,7 +527,7 @@ int ffpa_attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, 
   const int dst = drop_params(dropout_p, seed, &drop);
   if (dst != FFPA_OK) return dst;
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
-                  dtype, workspace, workspace_bytes, true, stream, drop);
+                  dtype, workspace, workspace_bytes, 0, stream, drop);
 }
 
 }  // extern "C"
@@ -395,12 +589,15 @@ int ffpa_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, 
     void* ws = nullptr;
     const int sa = scratch_address(stream, &ws);
     if (sa != FFPA_OK) return sa;
+    // the variant ffpa_attn_fwd would take with this much workspace
+    const int var = tuned_variant(B, Hq, Hkv, Nq, Nkv, D, causal, mask, mask_rows, accum_dtype, dtype,
+                                  kNoAllocScratchBytes);
     return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
-                    dtype, ws, kNoAllocScratchBytes, true, stream);
+                    dtype, ws, kNoAllocScratchBytes, var, stream);
   }
   if (Nq > 1 && D <= 512)  // V staged as is: no scratch at all
     return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype,
-                    dtype, nullptr, 0, false, stream);
+                    dtype, nullptr, 0, 1, stream);
   return fail(FFPA_ERR_WORKSPACE, "these sizes need " + std::to_string(need) +
                                       " bytes of scratch; ffpa_attn_fwd_noalloc holds " +
                                       std::to_string(kNoAllocScratchBytes));

@@ -120,10 +120,10 @@ void fwd_prefill_kernel(FwdArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
 
   // ---- workgroup -> (b, h, q-tile)
-  const int t = xcd_logical(blockIdx.x, a.total_wg);
-  // causal: longest rows (last query tiles) first
-  const int qt = a.causal ? a.n_qtiles - 1 - causal_position(t, a.n_qtiles, a.total_wg) : t % a.n_qtiles;
+  int t = xcd_logical(blockIdx.x, a.total_wg);
+  int qt = t % a.n_qtiles;
   const int bh = t / a.n_qtiles;
+  if (a.causal) qt = a.n_qtiles - 1 - qt;  // longest rows first
   const int h = bh % a.Hq, b = bh / a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
   const int q0 = qt * kFwdRows;              // first row of the workgroup

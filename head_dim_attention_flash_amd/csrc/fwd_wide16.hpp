@@ -39,15 +39,16 @@
 namespace ffpa {
 
 // parts of D per row block: 1 (a wave holds all of D for its rows) or 2 (a
-// wave pair splits D)
+// wave pair splits D). The default: 1 up to D = 768 (above, all of D does not
+// fit a wave's registers); 2 is built for every D as the other tile shape.
 template <int D>
 constexpr int wide16_nh() {
   return D <= 768 ? 1 : 2;
 }
 // query rows per workgroup: 4 / NH row blocks of 32
-template <int D>
+template <int D, int NH = wide16_nh<D>()>
 constexpr int wide16_rows() {
-  return (4 / wide16_nh<D>()) * 32;
+  return (4 / NH) * 32;
 }
 // LDS bytes of one staged K or V^T tile (32 keys x D)
 template <int D>
@@ -57,33 +58,33 @@ constexpr int wide16_tile() {
 // The epilogue stages each wave's 32 rows x W columns (W = D / NH) through
 // LDS in one pass, or two passes of W / 2 columns when W > 512; a staged row
 // takes whole groups of 16 granules.
-template <int D>
+template <int D, int NH = wide16_nh<D>()>
 constexpr int wide16_epi_passes() {
-  return D / wide16_nh<D>() > 512 ? 2 : 1;
+  return D / NH > 512 ? 2 : 1;
 }
-template <int D>
+template <int D, int NH = wide16_nh<D>()>
 constexpr int wide16_pitch() {
-  return (D / wide16_nh<D>() / wide16_epi_passes<D>() / 8 + 15) / 16 * 256;
+  return (D / NH / wide16_epi_passes<D, NH>() / 8 + 15) / 16 * 256;
 }
 // LDS: two tiles and, NH = 2, the score swap area; or the epilogue's staging
 // if that is larger
-template <int D>
+template <int D, int NH = wide16_nh<D>()>
 constexpr int wide16_lds() {
-  constexpr int loop = 2 * wide16_tile<D>() + (wide16_nh<D>() == 2 ? 4 * kWideXchg : 0);
-  constexpr int epi = 4 * 32 * wide16_pitch<D>();
+  constexpr int loop = 2 * wide16_tile<D>() + (NH == 2 ? 4 * kWideXchg : 0);
+  constexpr int epi = 4 * 32 * wide16_pitch<D, NH>();
   return loop > epi ? loop : epi;
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, int NH = wide16_nh<D>()>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fwd_wide16_kernel(FwdArgs a) {
   static_assert(D % 64 == 0 && D > 512 && D <= 1024, "D must be a multiple of 64 in (512, 1024]");
+  static_assert(NH == 2 || D <= 768, "a wave holds all of D only up to D = 768");
   using E = Elem<BF16>;
   using V8 = typename E::vec8;
-  constexpr int NH = wide16_nh<D>();
-  constexpr int ROWS = wide16_rows<D>();
+  constexpr int ROWS = wide16_rows<D, NH>();
   constexpr int W = D / NH;                // elements per part of D
-  constexpr int SG = W / 8;                // granules per part of a row (52 .. 96)
+  constexpr int SG = W / 8;                // granules per part of a row (36 .. 96)
   constexpr int PART = kWideBc * SG * 16;  // bytes of one dense K part-tile
   constexpr int NS = W / 16;               // k-steps of the (partial) product
   constexpr int NDB = W / 32;              // output d-blocks of the part
@@ -423,12 +424,12 @@ void fwd_wide16_kernel(FwdArgs a) {
   // ===== epilogue: the wave's 32 rows of its part go through LDS (in EP
   // passes of W / EP columns, a staged row taking whole groups of 16
   // granules), then out as contiguous pieces of W / EP elements per row
-  constexpr int EP = wide16_epi_passes<D>();
+  constexpr int EP = wide16_epi_passes<D, NH>();
   constexpr int NDBP = NDB / EP;   // d-blocks per pass
   constexpr int SGP = 4 * NDBP;    // granules per row and pass
-  constexpr int PITCH = wide16_pitch<D>();
+  constexpr int PITCH = wide16_pitch<D, NH>();
   static_assert(NDB % EP == 0 && PITCH >= SGP * 16, "epilogue passes");
-  static_assert(4 * 32 * PITCH <= wide16_lds<D>(), "epilogue staging fits the LDS");
+  static_assert(4 * 32 * PITCH <= wide16_lds<D, NH>(), "epilogue staging fits the LDS");
   wait_lgkm0();
   barrier();  // every wave is done with the tile buffers
   FFPA_LDS char* ostage = smem + wave * 32 * PITCH;
@@ -471,17 +472,19 @@ void fwd_wide16_kernel(FwdArgs a) {
 }
 
 // Host launcher: the transposed copy of V (blocks of 32 keys) into a.vt, then
-// the kernel over ceil(Nq / wide16_rows<D>()) row blocks per head. The LDS
-// limit is set before anything is enqueued.
-template <int D, bool BF16>
+// the kernel over ceil(Nq / wide16_rows<D, NH>()) row blocks per head (the
+// caller sets a.total_wg for that shape). The LDS limit is set before
+// anything is enqueued.
+template <int D, bool BF16, int NH = wide16_nh<D>()>
 hipError_t launch_fwd_wide16(const FwdArgs& a, hipStream_t stream) {
-  auto kern = fwd_wide16_kernel<D, BF16>;
+  auto kern = fwd_wide16_kernel<D, BF16, NH>;
+  constexpr int lds = wide16_lds<D, NH>();
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, wide16_lds<D>());
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const hipError_t e = launch_fwd_vt(a.v, const_cast<void*>(a.vt), a.B * a.Hkv, a.Nkv, D, kWideBc, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(a.total_wg), dim3(256), wide16_lds<D>(), stream, a);
+  hipLaunchKernelGGL(kern, dim3(a.total_wg), dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 

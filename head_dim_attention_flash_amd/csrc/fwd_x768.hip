@@ -4,4 +4,7 @@
 namespace ffpa {
 template hipError_t launch_fwd_wide16<768, false>(const FwdArgs&, hipStream_t);
 template hipError_t launch_fwd_wide16<768, true>(const FwdArgs&, hipStream_t);
+// the other tile shape (a wave pair splits D, 64 rows per workgroup)
+template hipError_t launch_fwd_wide16<768, false, 2>(const FwdArgs&, hipStream_t);
+template hipError_t launch_fwd_wide16<768, true, 2>(const FwdArgs&, hipStream_t);
 }  // namespace ffpa

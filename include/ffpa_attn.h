@@ -67,7 +67,8 @@
  * (FFPA_ERR_HIP).
  *
  * Threading. The library holds no mutable global state besides the
- * thread-local error message and, for ffpa_attn_fwd_noalloc, its per-GPU
+ * thread-local error message, the table of tuned variants (mutex-guarded;
+ * see ffpa_attn_fwd_tune) and, for ffpa_attn_fwd_noalloc, its per-GPU
  * scratch array (see there); all other entry points are reentrant.
  */
 #ifndef FFPA_ATTN_H_
@@ -200,6 +201,61 @@ size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int
 
 /* The least workspace ffpa_attn_bwd accepts (dQ then recomputes S and dP). */
 size_t ffpa_attn_bwd_workspace_size_min(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
+
+/*
+ * Forward variants and tuning: the pages' benchmark tunes its kernels per
+ * problem ("FFPA Attention Benchmark", "Quick Start": --tune fast / --tune
+ * max; the H20 tables of "More Benchmark" are taken with autotuning). Here
+ * every problem has a few built variants (tile shape or staging layout), all
+ * computing the same attention:
+ *   Nq > 1, D <= 512: 1 = V staged in LDS as is (transposed by the LDS
+ *                     reads), 2 = V read from a transposed copy that the call
+ *                     first writes to the workspace;
+ *   Nq > 1, D > 512:  1 = fp32 output accumulator, 64 query rows per
+ *                     workgroup, D split across wave pairs; with
+ *                     accum_dtype = FFPA_ACC_F16 also 2 = fp16 accumulator,
+ *                     a wave holds all of D, 128 rows per workgroup (D <= 768)
+ *                     and 3 = fp16 accumulator, D split across wave pairs, 64
+ *                     rows per workgroup;
+ *   Nq = 1:           1, 2, 3 = the default number of key ranges per head
+ *                     (split-KV) divided by 1, 2, 4.
+ * Variant 0 is the library's default choice (the one ffpa_attn_fwd runs
+ * untuned). Results of different variants agree within the accuracy of the
+ * accumulator; a given variant always gives the same bits.
+ *
+ * ffpa_attn_fwd_variant: ffpa_attn_fwd as `variant` (0 .. 3); a variant that
+ * does not exist for the problem returns FFPA_ERR_INVALID_ARG (checked after
+ * the argument checks of ffpa_attn_fwd, before the workspace check). Its
+ * workspace is ffpa_attn_fwd_variant_workspace_size(...) bytes.
+ *
+ * ffpa_attn_fwd_tune: times every variant that exists for the problem and
+ * fits the workspace given (level 1 = "fast": 1 warm-up and 3 timed calls
+ * each; level 2 = "max": 3 and 10), on the caller's buffers and stream with
+ * HIP events, and records the fastest for this problem (sizes, causal, mask
+ * shape, accum_dtype, dtype) in a table of the process. Later ffpa_attn_fwd
+ * and ffpa_attn_fwd_noalloc calls of that problem run the recorded variant
+ * when their workspace holds what it needs (else the default). It writes o
+ * and lse (last with the chosen variant), and blocks the calling thread until
+ * the timing runs finish. chosen (nullable) receives the variant; ms
+ * (nullable, 3 floats) the mean milliseconds per call of variants 1 .. 3, -1
+ * for those not run. Returns FFPA_ERR_WORKSPACE if no variant fits the
+ * workspace; the table is guarded by a mutex. ffpa_attn_tune_reset empties it.
+ */
+int ffpa_attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
+                          const void* mask, int mask_rows, int accum_dtype, int dtype, int variant,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+size_t ffpa_attn_fwd_variant_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype,
+                                            int causal, int variant);
+
+int ffpa_attn_fwd_tune(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal,
+                       const void* mask, int mask_rows, int accum_dtype, int dtype,
+                       void* workspace, size_t workspace_bytes, int level, int* chosen, float* ms,
+                       void* stream);
+
+void ffpa_attn_tune_reset(void);
 
 /*
  * Attention with dropout on the attention probabilities: the "dropout" case

@@ -221,3 +221,51 @@ def test_binding_rejects_bad_seed():
     with pytest.raises(ValueError):
         ffpa._seed(1 << 64)
     assert ffpa._seed((1 << 64) - 1) == (1 << 64) - 1
+
+
+def fwd_var(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nkv=8, D=64, scale=0.125,
+                causal=0, mask=0, mask_rows=0, accum_dtype=0, dtype=0, variant=1, workspace=0,
+                workspace_bytes=0, stream=0)
+    args.update(kw)
+    return ffpa.ffpa_attn_fwd_variant(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), ffpa.ERR_INVALID_ARG),
+    (dict(variant=4), ffpa.ERR_INVALID_ARG),
+    (dict(variant=-1), ffpa.ERR_INVALID_ARG),
+    (dict(variant=3), ffpa.ERR_INVALID_ARG),                      # prefill has variants 1 and 2
+    (dict(variant=2), ffpa.ERR_WORKSPACE),                        # V^T needs workspace
+    (dict(variant=2, D=640), ffpa.ERR_INVALID_ARG),               # fp16-accumulator shape, fp32 asked
+    (dict(variant=2, D=832, accum_dtype=1), ffpa.ERR_INVALID_ARG),  # all of D in a wave: D <= 768
+    (dict(variant=3, D=832, accum_dtype=1), ffpa.ERR_WORKSPACE),
+    (dict(variant=3, Nq=1), ffpa.ERR_WORKSPACE),                  # decode, fewer key ranges
+])
+def test_forward_variant_validation(kw, code):
+    assert fwd_var(**kw) == code
+    assert ffpa.ffpa_last_error() != ""
+
+
+def test_variant_workspace_sizes():
+    vt = 2 * 8 * 640 * 512 * 2  # V^T of B=2, Hkv=8, Nkv=600 (padded to 640), D=512, fp16
+    assert ffpa.ffpa_attn_fwd_variant_workspace_size(2, 8, 8, 100, 600, 512, 0, 0, 1) == 0
+    assert ffpa.ffpa_attn_fwd_variant_workspace_size(2, 8, 8, 100, 600, 512, 0, 0, 2) == vt
+    assert ffpa.ffpa_attn_fwd_variant_workspace_size(2, 8, 8, 100, 600, 512, 0, 0, 0) == \
+        ffpa.ffpa_attn_fwd_workspace_size(2, 8, 8, 100, 600, 512, 0)
+    # decode: the default key ranges / 1, 2, 4 (never more than the default size)
+    sizes = [ffpa.ffpa_attn_fwd_variant_workspace_size(1, 4, 4, 1, 65536, 512, 0, 0, v) for v in (1, 2, 3)]
+    assert sizes[0] == ffpa.ffpa_attn_fwd_workspace_size(1, 4, 4, 1, 65536, 512, 0)
+    assert sizes[0] >= sizes[1] >= sizes[2] > 0
+    assert ffpa.ffpa_attn_fwd_variant_workspace_size(1, 4, 4, 1, 64, 512, 0, 0, 9) == 0
+
+
+def test_tune_validation():
+    st, _, _ = ffpa.ffpa_attn_fwd_tune(P, P, P, P, P, 1, 2, 2, 8, 8, 64, 0.125, 0, 0, 0, 0, 0, 0, 0, 3, 0)
+    assert st == ffpa.ERR_INVALID_ARG  # level must be 1 or 2
+    st, _, _ = ffpa.ffpa_attn_fwd_tune(0, P, P, P, P, 1, 2, 2, 8, 8, 64, 0.125, 0, 0, 0, 0, 0, 0, 0, 1, 0)
+    assert st == ffpa.ERR_INVALID_ARG
+    # D above 512: every variant needs the transposed copy of V; none fits no workspace
+    st, _, ms = ffpa.ffpa_attn_fwd_tune(P, P, P, P, P, 1, 2, 2, 8, 8, 640, 0.125, 0, 0, 0, 0, 0, 0, 0, 1, 0)
+    assert st == ffpa.ERR_WORKSPACE and ms == [-1.0, -1.0, -1.0]
+    ffpa.ffpa_attn_tune_reset()

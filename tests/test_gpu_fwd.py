@@ -325,7 +325,8 @@ def test_bf16_inputs_with_the_fp16_accumulator(lib, D):
 @pytest.mark.parametrize("accum", ["f32", "f16"])
 def test_causal_few_heads_long_rows(lib, D, accum):
     """Causal with two heads of 4096 rows: each head's query blocks fill
-    several XCD ranges, whose causal work order interleaves the blocks."""
+    several XCD ranges (for D above 512 the kernel then interleaves a head's
+    blocks over those ranges)."""
     q, k, v, _ = _inputs(23, 1, 2, 2, 4096, 4096, D, "fp16")
     o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), causal=True, accum=accum)
     _compare(o, lse, q, k, v, 1.0 / math.sqrt(D), True, None, "fp16", accum, f"causal-2x4096-D{D}-{accum}")
