@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6}  # MI355X dense MFMA, published
+PEAK_FP8_TFLOPS = 5033.2  # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ("head_dim_attention_flash_amd/csrc/fwd_prefill.hpp",
@@ -289,6 +290,39 @@ def run_decode(ffpa, W, steps, warmup):
             "rocprof": recorded_counters("decode")}
 
 
+def run_fp8(ffpa, W, name, steps, warmup):
+    """The fp8 forward (ffpa_attn_fwd_fp8) on a 16-bit workload: per-head amax,
+    e4m3 quantisation of Q, K and V^T into the workspace, then the fp8 attention
+    kernel; every kernel is inside the timed call. TFLOPS counted like the
+    16-bit forward, against the dense fp8 MFMA peak."""
+    import torch
+
+    w = W.WORKLOADS[name]
+    inp = W.make_inputs(w, device="cuda")
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o = torch.empty_like(q)
+    ws = torch.empty(ffpa.ffpa_attn_fwd_fp8_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        ffpa.attention_fp8(q, k, v, causal=w.causal, scale=w.scale, out=o, workspace=ws)
+
+    per = _time_calls(call, steps, warmup)
+    mean_ms = sum(per) / len(per)
+    tflops = counted_flops(w.B, w.Hq, w.Nq, w.Nkv, w.D, w.causal) / (mean_ms * 1e-3) / 1e12
+    ws_bytes = ws.numel()
+    del inp, o, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{name} fp8: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nkv={w.Nkv} D={w.D} "
+                        f"{w.dtype} in/out, e4m3 QK^T and PV, causal={w.causal}",
+            "value": round(tflops, 2), "unit": "TFLOPS" + (" (causal: half counted)" if w.causal else ""),
+            "ms_per_call": round(mean_ms, 4),
+            "kernels": "f8_zero + f8_amax + f8_quant_qk + f8_quant_vt + fwd_fp8_kernel",
+            "workspace_bytes": ws_bytes,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4)}}
+
+
 def timed_call(w, accum="f32", variant=0) -> str:
     """The kernels one timed forward call enqueues (mirrors the library's
     choice for `variant`, 0 = the default)."""
@@ -391,6 +425,8 @@ FWD_PATHS = ([("self_bf16", "f32"), ("self", "f16"), ("self_bf16", "f16")] +
 # Forward workloads measured again after tuning (the variants differ most there)
 TUNED_PATHS = [("cross", "f32"), ("gqa", "f32"), ("dsweep576_f16", "f16"), ("dsweep768_f16", "f16"),
                ("dsweep1024_f16", "f16")]
+# 16-bit workloads timed again through the fp8 forward
+FP8_PATHS = ("self", "self_bf16", "causal", "dsweep320_f32")
 BWD_PATHS = ("bwd_causal", "bwd_cross", "bwd_decode", "bwd_gqa", "bwd_mask", "bwd_nonaligned", "bwd_dropout",
              "bwd_d1024", "bwd16k", "bwd16k_causal")
 
@@ -439,6 +475,9 @@ def main(argv=None) -> int:
     if args.workload.startswith("bwd"):
         print(json.dumps(run_backward(ffpa, W, args.workload, args.steps, args.warmup)), flush=True)
         return 0
+    if args.workload.startswith("fp8:"):
+        print(json.dumps(run_fp8(ffpa, W, args.workload[4:], args.steps, args.warmup)), flush=True)
+        return 0
     if args.workload == "decode":
         print(json.dumps(run_decode(ffpa, W, args.steps, args.warmup)), flush=True)
         return 0
@@ -457,6 +496,7 @@ def main(argv=None) -> int:
                             for n, a in FWD_PATHS}
         paths["forward_tuned"] = {f"{n}:{a}": run_forward_path(ffpa, W, n, a, args.steps, args.warmup, tune=True)
                                   for n, a in TUNED_PATHS}
+        paths["forward_fp8"] = {n: run_fp8(ffpa, W, n, args.steps, args.warmup) for n in FP8_PATHS}
         line["paths"] = paths
     print(json.dumps(line), flush=True)
     if args.copy_calibration:

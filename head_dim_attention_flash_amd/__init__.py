@@ -21,6 +21,7 @@ __all__ = [
     "load", "FFPAError", "ffpa_attn_fwd", "ffpa_attn_fwd_noalloc", "ffpa_attn_bwd",
     "ffpa_attn_fwd_dropout", "ffpa_attn_bwd_dropout", "ffpa_attn_fwd_variant",
     "ffpa_attn_fwd_variant_workspace_size", "ffpa_attn_fwd_tune", "ffpa_attn_tune_reset", "tune_forward",
+    "ffpa_attn_fwd_fp8", "ffpa_attn_fwd_fp8_workspace_size", "attention_fp8",
     "ffpa_attn_fwd_workspace_size",
     "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min", "ffpa_last_error",
     "ffpa_version", "attention",
@@ -41,7 +42,7 @@ EXPORTED = ("ffpa_attn_fwd", "ffpa_attn_fwd_workspace_size", "ffpa_attn_fwd_noal
             "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min",
             "ffpa_attn_fwd_dropout", "ffpa_attn_bwd_dropout", "ffpa_attn_fwd_variant",
             "ffpa_attn_fwd_variant_workspace_size", "ffpa_attn_fwd_tune", "ffpa_attn_tune_reset",
-            "ffpa_last_error", "ffpa_version")
+            "ffpa_attn_fwd_fp8", "ffpa_attn_fwd_fp8_workspace_size", "ffpa_last_error", "ffpa_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -85,6 +86,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffpa_attn_fwd_tune.restype = i
     lib.ffpa_attn_tune_reset.argtypes = []
     lib.ffpa_attn_tune_reset.restype = None
+    lib.ffpa_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.ffpa_attn_fwd_fp8.restype = i
+    lib.ffpa_attn_fwd_fp8_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.ffpa_attn_fwd_fp8_workspace_size.restype = sz
     lib.ffpa_attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.ffpa_attn_fwd_workspace_size.restype = sz
     lib.ffpa_attn_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
@@ -193,6 +198,17 @@ def ffpa_attn_fwd_tune(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, m
 
 def ffpa_attn_tune_reset() -> None:
     load().ffpa_attn_tune_reset()
+
+
+def ffpa_attn_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype, workspace,
+                      workspace_bytes, stream) -> int:
+    """Raw C call of the fp8 forward."""
+    return load().ffpa_attn_fwd_fp8(q, k, v, o, lse or None, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype,
+                                    workspace or None, workspace_bytes, stream or None)
+
+
+def ffpa_attn_fwd_fp8_workspace_size(B, Hq, Hkv, Nq, Nkv, D) -> int:
+    return load().ffpa_attn_fwd_fp8_workspace_size(B, Hq, Hkv, Nq, Nkv, D)
 
 
 def _seed(seed) -> int:
@@ -335,6 +351,36 @@ def tune_forward(q, k, v, *, causal: bool = False, mask=None, scale: Optional[fl
                                         _accum_code(accum), dt, ws.data_ptr(), ws_bytes, int(level), stream)
     _check(st)
     return chosen, {i + 1: t for i, t in enumerate(ms) if t >= 0}
+
+
+def attention_fp8(q, k, v, *, causal: bool = False, scale: Optional[float] = None,
+                  return_lse: bool = False, out=None, workspace=None):
+    """The fp8 forward (ffpa_attn_fwd_fp8) on the current HIP stream: 16-bit q, k,
+    v in, quantised per head to e4m3 inside the call; output in q's dtype."""
+    import torch
+
+    B, Hq, Hkv, Nq, Nkv, D = _dims(q, k, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        o = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", q.shape, q.dtype, q.device)
+        o = out
+    lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device) if return_lse else None
+    ws_bytes = ffpa_attn_fwd_fp8_workspace_size(B, Hq, Hkv, Nq, Nkv, D)
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_contiguous() or \
+                workspace.device != q.device:
+            raise ValueError("workspace must be a contiguous tensor on q's device of "
+                             "ffpa_attn_fwd_fp8_workspace_size() bytes")
+        ws = workspace
+    else:
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(ffpa_attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr() if lse is not None else 0, B, Hq, Hkv, Nq, Nkv, D, scale,
+                             int(causal), _dtype_code(q), ws.data_ptr(), ws_bytes, stream))
+    return (o, lse) if return_lse else o
 
 
 def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None,

@@ -13,10 +13,12 @@
 #include "ffpa_attn.h"
 #include "bwd.hpp"
 #include "decode.hpp"
+#include "fwd_fp8.hpp"
 #include "fwd_prefill.hpp"
 #include "fwd_vt.hpp"
 #include "fwd_wide.hpp"
 #include "fwd_wide16.hpp"
+#include "instances.hpp"
 
 namespace {
 
@@ -100,6 +102,20 @@ WideLauncher wide_launcher(int D, int bf16, int shape, bool drop, int* rows) {
     *rows = ffpa::wide16_rows<DD, 2>();                                                                \
     return bf16 ? ffpa::launch_fwd_wide16<DD, true, 2> : ffpa::launch_fwd_wide16<DD, false, 2>;
     FFPA_CASE(832) FFPA_CASE(896) FFPA_CASE(960) FFPA_CASE(1024)
+#undef FFPA_CASE
+    default:
+      return nullptr;
+  }
+}
+
+using Fp8Launcher = hipError_t (*)(const ffpa::Fp8Args&, hipStream_t);
+
+Fp8Launcher fp8_launcher(int D, int bf16) {
+  switch (D) {
+#define FFPA_CASE(DD) \
+  case DD:            \
+    return bf16 ? ffpa::launch_fwd_fp8<DD, true> : ffpa::launch_fwd_fp8<DD, false>;
+    FFPA_CASE(128) FFPA_CASE(192) FFPA_CASE(256) FFPA_CASE(320) FFPA_CASE(384) FFPA_CASE(448) FFPA_CASE(512)
 #undef FFPA_CASE
     default:
       return nullptr;
@@ -508,6 +524,52 @@ int ffpa_attn_fwd_tune(const void* q, const void* k, const void* v, void* o, flo
   // o and lse end with the chosen variant's results
   return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, mask, mask_rows, accum_dtype, dtype,
                   workspace, workspace_bytes, best, stream);
+}
+
+size_t ffpa_attn_fwd_fp8_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1) return 0;
+  return ffpa::f8_workspace_bytes(B, Hq, Hkv, Nq, Nkv, D);
+}
+
+int ffpa_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                      int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  const int st = fwd_check_args(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, nullptr, 0,
+                                FFPA_ACC_F32, dtype);
+  if (st != FFPA_OK) return st;
+  Fp8Launcher launch = fp8_launcher(D, dtype == FFPA_BF16);
+  if (launch == nullptr) return fail(FFPA_ERR_UNSUPPORTED, "the fp8 forward is built for D = 128, 192, ..., 512");
+  if (!aligned16(workspace)) return fail(FFPA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  const size_t need = ffpa::f8_workspace_bytes(B, Hq, Hkv, Nq, Nkv, D);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(FFPA_ERR_WORKSPACE, "workspace smaller than ffpa_attn_fwd_fp8_workspace_size()");
+  ffpa::Fp8Args a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nkv = Nkv;
+  a.causal = causal;
+  a.scale_log2 = scale * ffpa::kLog2e;
+  a.nkt = (Nkv + ffpa::kF8Bc - 1) / ffpa::kF8Bc;
+  a.n_qtiles = (Nq + ffpa::kF8Rows - 1) / ffpa::kF8Rows;
+  const int64_t total = (int64_t)B * Hq * a.n_qtiles;
+  const int64_t amax_wg = (int64_t)B * Hq * ((Nq + 63) / 64) + 2 * (int64_t)B * Hkv * ((Nkv + 63) / 64);
+  const int64_t n16 = ((int64_t)B * Hq * Nq + (int64_t)B * Hkv * Nkv) * (D / 16);
+  if (total >= (int64_t(1) << 31) || amax_wg >= (int64_t(1) << 31) || (n16 + 255) / 256 >= (int64_t(1) << 31) ||
+      (int64_t)B * Hkv * a.nkt >= (int64_t(1) << 31) || (int64_t)a.nkt * ffpa::kF8Bc * D >= (int64_t(1) << 32))
+    return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
+  a.total_wg = (int)total;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  char* w = (char*)workspace;
+  a.amax = (float*)w;
+  w += ffpa::f8_amax_bytes(B, Hq);
+  a.q8 = (uint8_t*)w;
+  w += up((size_t)B * Hq * Nq * D);
+  a.k8 = (uint8_t*)w;
+  w += up((size_t)B * Hkv * Nkv * D);
+  a.vt8 = (uint8_t*)w;
+  const hipError_t e = launch(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return FFPA_OK;
 }
 
 void ffpa_attn_tune_reset(void) {

@@ -258,6 +258,37 @@ int ffpa_attn_fwd_tune(const void* q, const void* k, const void* v, void* o, flo
 void ffpa_attn_tune_reset(void);
 
 /*
+ * FP8 forward: S = Q K^T and O = P V on the fp8 (OCP e4m3) matrix cores of
+ * gfx950, fp32 accumulation. The pages list fp8 attention kernels next to the
+ * 16-bit ones ("FFPA Attention Benchmark", "FP8 and FP4") without stating
+ * their quantisation; the reading taken here:
+ *  - each head's Q, each kv head's K and V: one scale per head and tensor,
+ *    x8 = e4m3(x * (448 / amax)) with amax = max |x| over that head, the
+ *    product in fp32, rounded to nearest even (448 is e4m3's largest finite
+ *    value; an all-zero head gets codes 0);
+ *  - scores S = scale * (Q8 K8^T) * (amax_Q / 448) * (amax_K / 448), online
+ *    softmax in fp32 against a running reference m per row: over the keys in
+ *    tiles of 64 (in order), m rises to the tile's largest score when that
+ *    exceeds m by more than ln(2) / 2, and only then; P = exp(S - m) of the
+ *    tile (at most 2^0.5) is quantised as e4m3(256 P); the row sum takes the
+ *    unquantised P;
+ *  - O = (sum_j P8_j V8_j) (amax_V / 448) / (256 l), rounded to the output
+ *    type; lse = m + ln l (natural log, of the scores above).
+ * q, k, v, o, lse, sizes, scale, causal (top-left), dtype: as ffpa_attn_fwd
+ * (no mask; FFPA_ACC_F32 implied). Built for D a multiple of 64 in
+ * [128, 512] (else FFPA_ERR_UNSUPPORTED, checked after the argument checks of
+ * ffpa_attn_fwd). workspace: at least ffpa_attn_fwd_fp8_workspace_size(...)
+ * bytes, 16-byte aligned; the call writes there the per-head amax values, Q8,
+ * K8 and V8 transposed per tile of 64 keys. Kernels enqueued: amax clear,
+ * amax, quantisation of Q and K, of V, the attention.
+ */
+int ffpa_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nkv, int D, float scale, int causal, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+size_t ffpa_attn_fwd_fp8_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D);
+
+/*
  * Attention with dropout on the attention probabilities: the "dropout" case
  * of the forward and backward tables of "FFPA Attention Benchmark", section
  * "More Benchmark", which run it beside PyTorch SDPA. The pages fix neither
