@@ -552,7 +552,8 @@ int ffpa_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, floa
   a.nkt = (Nkv + ffpa::kF8Bc - 1) / ffpa::kF8Bc;
   a.n_qtiles = (Nq + ffpa::kF8Rows - 1) / ffpa::kF8Rows;
   const int64_t total = (int64_t)B * Hq * a.n_qtiles;
-  const int64_t amax_wg = (int64_t)B * Hq * ((Nq + 63) / 64) + 2 * (int64_t)B * Hkv * ((Nkv + 63) / 64);
+  constexpr int R = ffpa::kF8AmaxRows;
+  const int64_t amax_wg = (int64_t)B * Hq * ((Nq + R - 1) / R) + 2 * (int64_t)B * Hkv * ((Nkv + R - 1) / R);
   const int64_t n16 = ((int64_t)B * Hq * Nq + (int64_t)B * Hkv * Nkv) * (D / 16);
   if (total >= (int64_t(1) << 31) || amax_wg >= (int64_t(1) << 31) || (n16 + 255) / 256 >= (int64_t(1) << 31) ||
       (int64_t)B * Hkv * a.nkt >= (int64_t(1) << 31) || (int64_t)a.nkt * ffpa::kF8Bc * D >= (int64_t(1) << 32))

@@ -6,11 +6,14 @@
 //  - Q, K and V of each head are quantised with one scale per head and tensor:
 //    x8 = e4m3(x * (448 / amax)), amax = max |x| over the head (a 448-sized
 //    code is e4m3's largest finite value), rounded to nearest even;
-//  - P = 2^(s - m) is quantised as e4m3(256 P) against a running reference
+//  - P = 2^(s - m) is quantised as e4m3(64 P) against a running reference
 //    m per row: over the keys in tiles of 64, m rises to a tile's maximum
-//    score when that exceeds m by more than 0.5 (log2 units), and only then
-//    (so P <= 2^0.5 and 256 P < 448); the row sum l takes the unquantised P;
-//  - O = (sum_j P8_j V8_j) * (amax_V / 448) / (256 l), in fp32, then rounded
+//    score when that exceeds m by more than 2.5 (log2 units), and only then
+//    (so P <= 2^2.5 and 64 P < 448); the row sum l takes the unquantised P.
+//    The loose threshold keeps the O rescales rare (on N(0, 1) scores about
+//    one row in 100 rises after its first tile); 64 P keeps P >= 2^-12 in
+//    e4m3's normal range;
+//  - O = (sum_j P8_j V8_j) * (amax_V / 448) / (64 l), in fp32, then rounded
 //    to the 16-bit output type; lse as for the 16-bit kernels.
 // A pre-pass writes the quantised tensors into the workspace: Q8, K8 row-major
 // and V8 transposed per 64-key tile with the keys of a tile permuted (see
@@ -26,8 +29,9 @@ typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 constexpr int kF8Rows = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kF8Bc = 64;     // keys per staged tile
 constexpr float kF8Max = 448.f;
-constexpr float kF8PScale = 256.f;
-constexpr float kF8Tau = 0.5f;  // rescale threshold (log2 units)
+constexpr float kF8PScale = 64.f;
+constexpr float kF8PLog2 = 6.f;  // log2 of the P scale
+constexpr float kF8Tau = 2.5f;  // rescale threshold (log2 units)
 
 struct Fp8Args {
   const void* q;  // the 16-bit inputs (pre-pass)
@@ -78,13 +82,17 @@ __global__ __launch_bounds__(256) void f8_zero_kernel(float* amax, int n) {
   if (i < n) amax[i] = 0.f;
 }
 
-// max |x| per head: workgroup (t, head, slab of 64 rows) of tensor t (0 Q, 1 K,
-// 2 V), 8 elements per thread and step; atomicMax on the bits (non-negative
-// floats order as their bit patterns).
+// max |x| per head: workgroup (t, head, slab of kF8AmaxRows rows) of tensor t
+// (0 Q, 1 K, 2 V), four 16-byte loads in flight per thread; the workgroup's
+// max goes to the head's slot with one atomicMax on the bits (non-negative
+// floats order as their bit patterns). Slabs of 256 rows keep the atomics to
+// one per 256 rows: thousands of them on a few cache lines would serialise.
+constexpr int kF8AmaxRows = 256;
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void f8_amax_kernel(Fp8Args a) {
   using E = Elem<BF16>;
-  const int nq_slabs = (a.Nq + 63) / 64, nk_slabs = (a.Nkv + 63) / 64;
+  __shared__ float wmax[4];
+  const int nq_slabs = (a.Nq + kF8AmaxRows - 1) / kF8AmaxRows, nk_slabs = (a.Nkv + kF8AmaxRows - 1) / kF8AmaxRows;
   const int q_wg = a.B * a.Hq * nq_slabs, k_wg = a.B * a.Hkv * nk_slabs;
   int w = blockIdx.x, t = 0;
   if (w >= q_wg) {
@@ -95,20 +103,32 @@ __global__ __launch_bounds__(256) void f8_amax_kernel(Fp8Args a) {
   const int slabs = t == 0 ? nq_slabs : nk_slabs, rows = t == 0 ? a.Nq : a.Nkv;
   const int head = w / slabs, slab = w % slabs;
   const uint16_t* x = (const uint16_t*)(t == 0 ? a.q : t == 1 ? a.k : a.v) + (size_t)head * rows * D;
-  const int r0 = slab * 64, r1 = min(rows, r0 + 64);
+  const int r0 = slab * kF8AmaxRows, r1 = min(rows, r0 + kF8AmaxRows);
   const int n8 = (r1 - r0) * D / 8;
+  const uint16_t* x0 = x + (size_t)r0 * D;
   float m = 0.f;
-  for (int i = threadIdx.x; i < n8; i += 256) {
-    const u32x4 g = *(const u32x4*)(x + (size_t)r0 * D + 8 * i);
+  auto fold = [&](const u32x4& g) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       m = fmaxf(m, fabsf(E::to_f32((uint16_t)(g[e] & 0xffff))));
       m = fmaxf(m, fabsf(E::to_f32((uint16_t)(g[e] >> 16))));
     }
+  };
+  int i = threadIdx.x;
+  for (; i + 3 * 256 < n8; i += 4 * 256) {
+    u32x4 g[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) g[u] = *(const u32x4*)(x0 + 8 * (i + 256 * u));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fold(g[u]);
   }
+  for (; i < n8; i += 256) fold(*(const u32x4*)(x0 + 8 * i));
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-  if ((threadIdx.x & 63) == 0) {
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const int base = t == 0 ? 0 : t == 1 ? a.B * a.Hq : a.B * a.Hq + a.B * a.Hkv;
     atomicMax((unsigned int*)(a.amax + base + head), __float_as_uint(m));
   }
@@ -208,7 +228,7 @@ __device__ inline void mfma_f8_asm(f32x16& acc, u32x8 a, u32x8 b) {
 //   S^T (keys x queries, two blocks of 32 keys) = K8 Q8^T, A = K8 from LDS,
 //   B = Q8 from registers (loaded once);
 //   P = 2^(S - m) per query (a lane's query is lane % 32; its two lane halves
-//   hold different keys), quantised to e4m3 (256 P) in registers: exactly the
+//   hold different keys), quantised to e4m3 (64 P) in registers: exactly the
 //   B operand of O^T += V8^T P^T, whose A is the V8^T tile;
 //   O^T (d x queries) in AGPRs: a lane holds its own query, so the online
 //   softmax rescale is per lane.
@@ -228,7 +248,8 @@ void fwd_fp8_kernel(Fp8Args a) {
   constexpr int G = D / 16;    // 16-byte granules per K row
   constexpr int KT = kF8Bc * D;  // bytes of a K (or V^T) tile
   constexpr int NKC = D / 64;  // copy instructions per wave and tile, each tensor
-  constexpr int kAhead = 4;    // operand fragments read ahead of their MFMA
+  constexpr int kAhead = 4;    // K operand fragments read ahead of their MFMA
+  constexpr int kAheadV = D == 512 ? 3 : 4;  // V^T fragments (registers are short at 512)
 
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   FFPA_LDS char* smem = (FFPA_LDS char*)smem_raw;
@@ -276,14 +297,16 @@ void fwd_fp8_kernel(Fp8Args a) {
     const int vd = s >> 2, vg = (s & 3) ^ ((vd >> 2) & 3);
     voff[r] = (uint32_t)(vd * kF8Bc + 16 * vg);
   }
-  auto issue_tile = [&](int j) {
+  // K(j) and V^T(j) go to the buffer pair j % 2 (K at 0, V^T at KT)
+  auto issue_k = [&](int j) {
     FFPA_LDS char* kb = smem + (j & 1) * 2 * KT;
 #pragma unroll
-    for (int r = 0; r < NKC; ++r) {
-      const int n = wave + 4 * r;
-      dma16(Kr, koff[r] + (uint32_t)j * KT, kb + n * 1024);
-      dma16(Vr, voff[r] + (uint32_t)j * KT, kb + KT + n * 1024);
-    }
+    for (int r = 0; r < NKC; ++r) dma16(Kr, koff[r] + (uint32_t)j * KT, kb + (wave + 4 * r) * 1024);
+  };
+  auto issue_v = [&](int j) {
+    FFPA_LDS char* vb = smem + (j & 1) * 2 * KT + KT;
+#pragma unroll
+    for (int r = 0; r < NKC; ++r) dma16(Vr, voff[r] + (uint32_t)j * KT, vb + (wave + 4 * r) * 1024);
   };
 
   int n_tiles = (a.Nkv + kF8Bc - 1) / kF8Bc;
@@ -295,7 +318,7 @@ void fwd_fp8_kernel(Fp8Args a) {
   float m_ref = -INFINITY, l_run = 0.f;
 
   // LDS addresses of this lane's fragments, relative to a tile buffer
-  uint32_t kaddr[2][NST], vaddr[NDB];
+  uint32_t kaddr[2][NST];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -303,11 +326,9 @@ void fwd_fp8_kernel(Fp8Args a) {
       const int r = 32 * kb + l32, g = 4 * st + 2 * hi;
       kaddr[kb][st] = (uint32_t)(r * D + 16 * dense_pos(G, r, g));
     }
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int d = 32 * db + l32;
-    vaddr[db] = (uint32_t)(KT + d * kF8Bc + 16 * ((2 * hi) ^ ((d >> 2) & 3)));
-  }
+  // V^T row d = 32 db + l32 has the swizzle of l32 ((d / 4) % 4 = (l32 / 4) % 4):
+  // one base, d-block db at + 32 x 64 db bytes
+  const uint32_t vaddr0 = (uint32_t)(KT + l32 * kF8Bc + 16 * ((2 * hi) ^ ((l32 >> 2) & 3)));
   // the second granule of a fragment: logical g + 1 (g even), stored at
   // dense_pos(g + 1) = dense_pos(g) ^ 1 for both layouts (their swizzles flip
   // whole aligned pairs or leave bit 0 alone)
@@ -316,54 +337,79 @@ void fwd_fp8_kernel(Fp8Args a) {
     return u32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
   };
 
-  if (n_tiles > 0) issue_tile(0);
+  // The loop is pipelined over tiles: iteration j computes the scores
+  // S(j + 1) on the matrix cores while the VALU turns the scores of tile j
+  // into quantised P (exponentials at the MFMA slots), then the products
+  // O^T += V8^T(j) P8^T(j) while the VALU scales and masks S(j + 1) and takes
+  // its row max. K(j + 1) and V^T(j) must be in LDS at iteration j: the
+  // copies of K(j + 2) and V^T(j + 1) are issued at its top, into the
+  // buffers that K(j) and V^T(j - 1) have left.
+  float tv[32];             // scaled, masked scores of the tile the VALU works on
+  float mx = -INFINITY;     // their row max (lane half's keys, then both)
+  // scores of tile jn from s_acc, element pair c (2c, 2c + 1), into tv / mx
+  auto score_pair = [&](const f32x16* s_acc, int jn, bool edge, int c) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * c + e, kb = i >> 4, r = i & 15;
+      float x = s_acc[kb][r] * sc;
+      if (edge) {
+        const int key = jn * kF8Bc + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const bool dead = (key >= a.Nkv) | (a.causal & (key > my_q));
+        x = dead ? -INFINITY : x;
+      }
+      tv[i] = x;
+      mx = fmaxf(mx, x);
+    }
+  };
+  // only a tile that reaches past Nkv or past the wave's first query (causal)
+  // has keys to mask; the test is uniform over the wave
+  auto is_edge = [&](int jn) { return jn * kF8Bc + kF8Bc > a.Nkv || (a.causal && jn * kF8Bc + kF8Bc - 1 > qw); };
+  // S^T(jn) = K8(jn) Q8^T, the two 32-key blocks interleaved; `slot(u)` runs
+  // beside MFMA u (VALU work pinned there)
+  auto s_chain = [&](f32x16* s_acc, int jn, auto&& slot) {
+    const FFPA_LDS char* buf = smem + (jn & 1) * 2 * KT;
+    u32x8 kf[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) kf[u] = frag(buf, kaddr[u & 1][u >> 1]);
+#pragma unroll
+    for (int u = 0; u < 2 * NST; ++u) {
+      const u32x8 x = kf[u % kAhead];
+      if (u + kAhead < 2 * NST) kf[u % kAhead] = frag(buf, kaddr[(u + kAhead) & 1][(u + kAhead) >> 1]);
+      const int kb = u & 1, st = u >> 1;
+      if (st == 0) mfma_f8_asm<false, true, true>(s_acc[kb], x, qf[st]);
+      else if (u == 2 * NST - 1) mfma_f8_asm<false, false, false, true>(s_acc[kb], x, qf[st]);
+      else mfma_f8_asm<false>(s_acc[kb], x, qf[st]);
+      slot(u);
+    }
+    pin_after_pad(s_acc[0]);
+    pin_after_pad(s_acc[1]);
+  };
+
+  f32x16 s_acc[2];
+  if (n_tiles > 0) {
+    issue_k(0);
+    if (n_tiles > 1) issue_k(1);
+    issue_v(0);
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    barrier();
+    s_chain(s_acc, 0, [&](int) {});
+#pragma unroll
+    for (int c = 0; c < 16; ++c) score_pair(s_acc, 0, true, c);
+    mx = fmaxf(mx, swap_halves(mx));
+  }
   for (int j = 0; j < n_tiles; ++j) {
 #pragma unroll
     for (int d = 0; d < NDB; ++d) asm volatile("" : "+a"(o_acc[d]));
     wait_vmcnt<0>();
     wait_lgkm0();
-    barrier();  // tile j landed for every wave; buffer (j + 1) % 2 is free
-    if (j + 1 < n_tiles) issue_tile(j + 1);
-    const FFPA_LDS char* buf = smem + (j & 1) * 2 * KT;
+    barrier();  // K(j + 1) and V^T(j) landed everywhere; K(j), V^T(j - 1) read by all
+    if (j + 2 < n_tiles) issue_k(j + 2);
+    if (j + 1 < n_tiles) issue_v(j + 1);
 
-    // S^T for key blocks 0 and 1, steps interleaved (consecutive MFMAs write
-    // different accumulators)
-    f32x16 s_acc[2];
-    {
-      u32x8 kf[kAhead];
-#pragma unroll
-      for (int u = 0; u < kAhead; ++u) kf[u] = frag(buf, kaddr[u & 1][u >> 1]);
-#pragma unroll
-      for (int u = 0; u < 2 * NST; ++u) {
-        const u32x8 x = kf[u % kAhead];
-        if (u + kAhead < 2 * NST) kf[u % kAhead] = frag(buf, kaddr[(u + kAhead) & 1][(u + kAhead) >> 1]);
-        const int kb = u & 1, st = u >> 1;
-        if (st == 0) mfma_f8_asm<false, true, true>(s_acc[kb], x, qf[st]);
-        else if (u == 2 * NST - 1) mfma_f8_asm<false, false, false, true>(s_acc[kb], x, qf[st]);
-        else mfma_f8_asm<false>(s_acc[kb], x, qf[st]);
-      }
-      pin_after_pad(s_acc[0]);
-    }
-
-    // scores (log2 domain) and masks: register i of block kb holds key
-    // j0 + 32 kb + 8 (i / 4) + 4 h + i % 4 of the lane's query
-    const int j0 = j * kF8Bc;
-    float tv[32];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = j0 + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-        float x = s_acc[kb][i] * sc;
-        if (key >= a.Nkv || (a.causal && key > my_q)) x = -INFINITY;
-        tv[16 * kb + i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, swap_halves(mx));
     // a row's reference max rises to the tile's max (O and l follow) when
     // that passes it by more than tau, and only then: P stays below 2^tau,
-    // 256 P inside e4m3's range, and each row's reference depends on its own
+    // 64 P inside e4m3's range, and each row's reference depends on its own
     // scores alone (the ballot only skips the rescale when no row rises)
     const bool rise = mx > m_ref + kF8Tau;
     if (__builtin_amdgcn_ballot_w64(rise) != 0) {
@@ -377,41 +423,67 @@ void fwd_fp8_kernel(Fp8Args a) {
         asm volatile("" : "+a"(o_acc[d]));
       }
     }
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    float psum = 0.f;
+    // 64 P = 2^(t - (m - 6)): the P scale folded into the exponent; l_run
+    // sums 64 P (the 64 is taken out at the end)
+    static_assert(kF8PScale == 64.f && kF8PLog2 == 6.f, "P scale and its log2 go together");
+    const float m_use = (m_ref == -INFINITY ? 0.f : m_ref) - kF8PLog2;
+    float pv[32];
     u32x8 pf;
+    // exponentials of element pair c (2c, 2c + 1), packed by fours
+    auto exp_pair = [&](int c) {
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = exp2_fast(tv[4 * w + e] - m_use);
-        psum += p[e];
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * c + e;
+        asm volatile("" : "+v"(tv[i]));
+        pv[i] = exp2_fast(tv[i] - m_use);
+        l_run += pv[i];
       }
-      pf[w] = f8_pack4(p[0] * kF8PScale, p[1] * kF8PScale, p[2] * kF8PScale, p[3] * kF8PScale);
-    }
-    l_run += psum;
+      if (c & 1) {
+        const int w = c >> 1;
+        pf[w] = f8_pack4(pv[4 * w], pv[4 * w + 1], pv[4 * w + 2], pv[4 * w + 3]);
+        asm volatile("" : "+v"(pf[w]));
+      }
+    };
+    // the 16 pairs spread over the 2 NST MFMA slots of the next scores
+    auto exp_slot = [&](int u) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        if ((c * 2 * NST) / 16 == u) exp_pair(c);
+    };
+    // on the last tile the chain runs on a stale K buffer (no copy is in
+    // flight into it) and its scores are never used: one spare chain per
+    // workgroup instead of a branch in every slot
+    s_chain(s_acc, j + 1, exp_slot);
     asm volatile("" : "+v"(pf));
 
-    // O^T += V8^T P8^T over the d-blocks
-    {
-      u32x8 vf[kAhead];
+    // O^T += V8^T(j) P8^T(j) over the d-blocks, beside the scores of S(j + 1)
+    // (edge: it has keys to mask)
+    auto pv_phase = [&](bool edge) {
+      const FFPA_LDS char* buf = smem + (j & 1) * 2 * KT;
+      u32x8 vf[kAheadV];
 #pragma unroll
-      for (int u = 0; u < kAhead; ++u) vf[u] = frag(buf, vaddr[u]);
+      for (int u = 0; u < kAheadV; ++u) vf[u] = frag(buf, vaddr0 + 32 * kF8Bc * u);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const u32x8 x = vf[db % kAhead];
-        if (db + kAhead < NDB) vf[db % kAhead] = frag(buf, vaddr[db + kAhead]);
+        const u32x8 x = vf[db % kAheadV];
+        if (db + kAheadV < NDB) vf[db % kAheadV] = frag(buf, vaddr0 + 32 * kF8Bc * (db + kAheadV));
         if (db == 0) mfma_f8_asm<true, false, true>(o_acc[db], x, pf);
         else if (db == NDB - 1) mfma_f8_asm<true, false, false, true>(o_acc[db], x, pf);
         else mfma_f8_asm<true>(o_acc[db], x, pf);
+        // 32 scores over the NDB slots (NDB = D / 32 >= 4)
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if ((c * NDB) / 16 == db) score_pair(s_acc, j + 1, edge, c);
       }
-    }
+    };
+    mx = -INFINITY;
+    pv_phase(is_edge(j + 1));
+    mx = fmaxf(mx, swap_halves(mx));
   }
 
   // epilogue: both lane halves hold partial row sums of the lane's query
-  const float l_tot = l_run + swap_halves(l_run);
-  const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * dv / kF8PScale;
+  const float l_tot = l_run + swap_halves(l_run);  // 64 l
+  const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * dv;
   if (my_q < a.Nq) {
     typename E::scalar* orow = (typename E::scalar*)a.o + ((size_t)bh * a.Nq + my_q) * D;
 #pragma unroll
@@ -426,7 +498,7 @@ void fwd_fp8_kernel(Fp8Args a) {
       }
     }
     if (a.lse != nullptr && hi == 0)
-      a.lse[(size_t)bh * a.Nq + my_q] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+      a.lse[(size_t)bh * a.Nq + my_q] = l_tot > 0.f ? (m_ref + __log2f(l_tot) - kF8PLog2) * kLn2 : -INFINITY;
   }
 }
 
@@ -458,7 +530,8 @@ hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
   if (attr != hipSuccess) return attr;
   const int n_amax = a.B * a.Hq + 2 * a.B * a.Hkv;
   hipLaunchKernelGGL(f8_zero_kernel<D>, dim3((n_amax + 255) / 256), dim3(256), 0, stream, a.amax, n_amax);
-  const int amax_wg = a.B * a.Hq * ((a.Nq + 63) / 64) + 2 * a.B * a.Hkv * ((a.Nkv + 63) / 64);
+  const int amax_wg = a.B * a.Hq * ((a.Nq + kF8AmaxRows - 1) / kF8AmaxRows) +
+                      2 * a.B * a.Hkv * ((a.Nkv + kF8AmaxRows - 1) / kF8AmaxRows);
   hipLaunchKernelGGL((f8_amax_kernel<D, BF16>), dim3(amax_wg), dim3(256), 0, stream, a);
   const int64_t n16 = ((int64_t)a.B * a.Hq * a.Nq + (int64_t)a.B * a.Hkv * a.Nkv) * (D / 16);
   hipLaunchKernelGGL((f8_quant_qk_kernel<D, BF16>), dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream, a);

@@ -269,10 +269,10 @@ void ffpa_attn_tune_reset(void);
  *  - scores S = scale * (Q8 K8^T) * (amax_Q / 448) * (amax_K / 448), online
  *    softmax in fp32 against a running reference m per row: over the keys in
  *    tiles of 64 (in order), m rises to the tile's largest score when that
- *    exceeds m by more than ln(2) / 2, and only then; P = exp(S - m) of the
- *    tile (at most 2^0.5) is quantised as e4m3(256 P); the row sum takes the
+ *    exceeds m by more than 2.5 ln(2), and only then; P = exp(S - m) of the
+ *    tile (at most 2^2.5) is quantised as e4m3(64 P); the row sum takes the
  *    unquantised P;
- *  - O = (sum_j P8_j V8_j) (amax_V / 448) / (256 l), rounded to the output
+ *  - O = (sum_j P8_j V8_j) (amax_V / 448) / (64 l), rounded to the output
  *    type; lse = m + ln l (natural log, of the scores above).
  * q, k, v, o, lse, sizes, scale, causal (top-left), dtype: as ffpa_attn_fwd
  * (no mask; FFPA_ACC_F32 implied). Built for D a multiple of 64 in

@@ -15,12 +15,13 @@ taken (the same as the library's header states):
   and the product rounded to float32 first (an all-zero head: s = 1).
 * Scores S = scale * (Q8 K8^T) * (amax_Q / 448) * (amax_K / 448), with the
   causal mask (top-left) as in ``attention.py``.
-* P = exp(S - m) is quantised as e4m3(256 P) against a running reference m
+* P = exp(S - m) is quantised as e4m3(64 P) against a running reference m
   per row: going over the keys in blocks of 64, in order, m rises to a
-  block's largest score when that exceeds m by more than ln(2) / 2, and only
-  then (the partial O and l are rescaled by exp(m_old - m_new)); so P <= 2^0.5
-  and 256 P stays inside e4m3's range. The row sum l takes the unquantised P;
-  O = (sum of P8 V8) (amax_V / 448) / (256 l), and lse = m + ln l.
+  block's largest score when that exceeds m by more than 2.5 ln(2), and only
+  then (the partial O and l are rescaled by exp(m_old - m_new)); so P <= 2^2.5
+  and 64 P stays inside e4m3's range (64 x 2^2.5 < 448). The row sum l takes
+  the unquantised P; O = (sum of P8 V8) (amax_V / 448) / (64 l), and
+  lse = m + ln l.
 
 Everything after the quantisation of the inputs is float64.
 """
@@ -33,7 +34,7 @@ from .attention import to_f64
 __all__ = ["e4m3_round", "quantize_head", "attn_fwd_fp8"]
 
 E4M3_MAX = 448.0
-P_SCALE = 256.0
+P_SCALE = 64.0
 
 
 def e4m3_round(x) -> np.ndarray:
@@ -61,7 +62,7 @@ def quantize_head(x) -> tuple[np.ndarray, float]:
 
 
 BLOCK = 64  # keys per block of the running reference
-RISE = 0.5 * np.log(2.0)  # the reference rises when a block's max exceeds it by more
+RISE = 2.5 * np.log(2.0)  # the reference rises when a block's max exceeds it by more
 
 
 def attn_fwd_fp8(q, k, v, scale, causal=False):

@@ -3,8 +3,8 @@ against oracle/fp8.py, the quantised attention the header specifies.
 
 Both sides quantise Q, K and V identically (per-head amax in float32, the
 product in float32, e4m3 round to nearest even) and quantise P against the
-same per-row running reference (blocks of 64 keys, rise by more than ln 2 /
-2), so the kernel differs from the oracle only in its arithmetic: the
+same per-row running reference (blocks of 64 keys, rise by more than 2.5 ln 2),
+so the kernel differs from the oracle only in its arithmetic: the
 matrix core's sums of exact fp8 products, the fast exp2, and the decisions
 these move (a P on an e4m3 rounding tie, a block maximum at the rise
 threshold). Such a decision moves one quantised p by one e4m3 step, at most
@@ -114,16 +114,20 @@ def test_fp8_zero_query_and_zero_values(lib):
 
 
 def test_fp8_power_of_two_ramp_is_exact(lib):
-    """Scores c ln 2 with integer c whose block maxima rise by one from each
-    64-key block to the next (K on its e4m3 grid, Q = e_0, V on its grid): the
-    running reference rises at every tile by exactly ln 2, every quantised P
-    is an exact power of two, so O is the exact attention (to the output's
-    rounding) and lse = ln sum 2^c."""
-    B, H, Nq, N, D = 1, 2, 96, 512, 128
+    """Scores c ln 2 with integer c whose 64-key block maxima rise by 3 from
+    each block to the next (K[:, 0] = 16 c with a 448 pin in another column,
+    so K is its own e4m3 code; Q = e_0; scale = ln 2 / 16; V on its grid): the
+    running reference rises at every tile by exactly 3 ln 2 (past the 2.5 ln 2
+    threshold), every quantised P is an exact power of two, so O is the exact
+    attention (to the output's rounding and the matrix core's summation) and
+    lse = ln sum 2^c. The rows span several tiles and a ragged tail (Nkv is
+    not a multiple of 64; the last block is cut short)."""
+    B, H, Nq, N, D = 1, 2, 96, 300, 128
     rng = np.random.default_rng(11)
-    c = np.array([j // 64 - (j % 64) % 7 for j in range(N)], dtype=np.float64)
+    c = np.array([3 * (j // 64) - (j % 64) % 4 for j in range(N)], dtype=np.float64)
     k = np.zeros((B, H, N, D))
-    k[..., 0] = c
+    k[..., 0] = 16 * c
+    k[..., 0, 1] = 448.0
     q = np.zeros((B, H, Nq, D))
     q[..., 0] = 1.0
     codes = np.array([m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
@@ -132,7 +136,7 @@ def test_fp8_power_of_two_ramp_is_exact(lib):
     v[..., 0, 0] = 448 * 2.0 ** -5
     qt, kt, vt = (torch.from_numpy(x).to(torch.float16) for x in (q, k, v))
     assert np.array_equal(vt.double().numpy(), v) and np.array_equal(kt.double().numpy(), k)
-    scale = math.log(2.0)
+    scale = math.log(2.0) / 16
     o, lse = lib.attention_fp8(qt.cuda(), kt.cuda(), vt.cuda(), scale=scale, return_lse=True)
     torch.cuda.synchronize()
     ref, lref = attn_fwd(qt, kt, vt, scale)

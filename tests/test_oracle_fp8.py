@@ -5,7 +5,7 @@
   value, ties to the even code; known values; every code is a fixed point.
 * Per-head quantisation: the largest element maps to +-448 exactly, every
   code stays in range, the relative error of normal values is <= 2^-4.
-* Closed forms of the quantised attention: Q = 0 gives P = 1 (256 P exact),
+* Closed forms of the quantised attention: Q = 0 gives P = 1 (64 P exact),
   so O is the mean of the dequantised V and lse = ln Nkv; with V on the e4m3
   grid of its own scale (amax = 448 * 2^k) that mean is the plain mean of V.
   One key: O = V[0] (on the grid) and lse = the dequantised score.
@@ -13,9 +13,9 @@
   the quantised result is attention to within the fp8 rounding (relative L2
   about 5 %, gate 10 %), causal and GQA included.
 * The running reference: scores c ln 2 (integer c) whose block maxima rise by
-  ln 2 from block to block, with Q, K and V on their e4m3 grids, make every
-  quantised P and every rescale exact: the result must be the exact
-  attention to float64 rounding.
+  3 ln 2 from block to block (past the 2.5 ln 2 threshold), with Q, K and V
+  on their e4m3 grids, make every quantised P and every rescale exact: the
+  result must be the exact attention to float64 rounding.
 * Planted mistakes (a dropped K dequantisation factor, the P scale not taken
   out, ties rounded away from zero, the row sum over quantised P replaced by
   its square, O not rescaled when the reference rises) are rejected by these
@@ -142,21 +142,29 @@ def test_close_to_exact_attention(causal):
     assert np.abs(l8 - l).max() < 0.1
 
 
-def _rising_case(rng, n_blocks=8, D=16):
-    """Scores c ln 2 with integer c: in block b, c = b - (j % 7), so every
-    block's maximum is b and the reference rises by ln 2 at every block. K is
-    on the e4m3 grid of its own scale (amax 7: 448 / 7 = 64, and 64 c is an
-    e4m3 value for c in -6 .. 7), Q = e_0 exactly, V on its grid: each
-    quantised P = 2^(c - b) is exact and the rescales are exact powers of 2,
-    so the result is the exact attention to float64 rounding."""
-    N = 64 * n_blocks
-    c = np.array([j // 64 - (j % 64) % 7 for j in range(N)], dtype=np.float64)
+def ramp_scores(n_blocks=5):
+    """Integer c per key: in block b (64 keys), c = 3 b - (j % 4), so block b's
+    maximum is 3 b: the reference rises by 3 (past the 2.5 threshold) at every
+    block, and every c lies in -3 .. 12 (|16 c| <= 192 is an e4m3 value)."""
+    return np.array([3 * (j // 64) - (j % 64) % 4 for j in range(64 * n_blocks)], dtype=np.float64)
+
+
+def _rising_case(rng, n_blocks=5, D=16):
+    """Scores c ln 2 (ramp_scores): K[:, 0] = 16 c and K[0, 1] = 448 (so
+    amax_K = 448, the scale is 1 and K is its own code), Q = e_0 (code 448,
+    amax 1), scale = ln 2 / 16: the score is exactly c ln 2 up to the float64
+    rounding of the dequantisation. V on its grid: each quantised
+    64 P = 64 x 2^(c - 3 b) is an exact e4m3 value and each rescale an exact
+    power of 2, so the result is the exact attention to float64 rounding."""
+    c = ramp_scores(n_blocks)
+    N = c.size
     k = np.zeros((1, 1, N, D))
-    k[0, 0, :, 0] = c
+    k[0, 0, :, 0] = 16 * c
+    k[0, 0, 0, 1] = 448.0
     q = np.zeros((1, 1, 3, D))
     q[..., 0] = 1.0
     v = _grid_v(rng, (1, 1, N, D))
-    return q, k, v, math.log(2.0)
+    return q, k, v, math.log(2.0) / 16
 
 
 def test_rising_reference_is_exact_on_a_power_of_two_ramp():
