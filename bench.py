@@ -47,6 +47,7 @@ COUNTER_SOURCES = {
     "wide": KERNEL_SOURCES + (CSRC + "fwd_wide.hpp",),
     "bwd": (CSRC + "bwd.hpp", CSRC + "ffpa_common.hpp", CSRC + "fwd_vt.hpp", CSRC + "fwd_vt.hip"),
     "decode": (CSRC + "decode.hpp", CSRC + "ffpa_common.hpp"),
+    "fp8": (CSRC + "fwd_fp8.hpp", CSRC + "ffpa_common.hpp"),
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -320,7 +321,8 @@ def run_fp8(ffpa, W, name, steps, warmup):
             "kernels": "f8_zero + f8_amax + f8_quant_qk + f8_quant_vt + fwd_fp8_kernel",
             "workspace_bytes": ws_bytes,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4)}}
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4)},
+            "rocprof": recorded_counters("fp8:" + name)}
 
 
 def timed_call(w, accum="f32", variant=0) -> str:
@@ -482,21 +484,34 @@ def main(argv=None) -> int:
         print(json.dumps(run_decode(ffpa, W, args.steps, args.warmup)), flush=True)
         return 0
     paths = None
+
+    def done(section, name, rec):
+        # one progress line per measured path on stderr (stdout carries only
+        # the JSON line)
+        print(f"bench: {section} {name}: {rec['value']} {rec['unit']}", file=sys.stderr, flush=True)
+        return rec
+
     if not args.no_paths:
         # the backward first: its calls (~0.2 s of GPU work) also bring the
         # clock past its ramp before the headline's warm-up steps
-        paths = {"backward": run_backward(ffpa, W, "bwd", max(3, args.steps // 2), 5)}
+        paths = {"backward": done("backward", "bwd", run_backward(ffpa, W, "bwd", max(3, args.steps // 2), 5))}
     line = run_one(ffpa, W, args.workload, args.accum, args.steps, args.warmup,
                    not args.no_cpu_baseline, args.cpu_heads)
+    done("headline", args.workload, line)
     if paths is not None:
         for name in BWD_PATHS:
-            paths["backward" + name[3:]] = run_backward(ffpa, W, name, max(3, args.steps // 2), 3)
-        paths["decode"] = run_decode(ffpa, W, args.steps, max(args.warmup, 50))
-        paths["forward"] = {f"{n}:{a}": run_forward_path(ffpa, W, n, a, args.steps, args.warmup)
+            paths["backward" + name[3:]] = done("backward", name,
+                                                run_backward(ffpa, W, name, max(3, args.steps // 2), 3))
+        paths["decode"] = done("decode", "decode", run_decode(ffpa, W, args.steps, max(args.warmup, 50)))
+        paths["forward"] = {f"{n}:{a}": done("forward", f"{n}:{a}",
+                                             run_forward_path(ffpa, W, n, a, args.steps, args.warmup))
                             for n, a in FWD_PATHS}
-        paths["forward_tuned"] = {f"{n}:{a}": run_forward_path(ffpa, W, n, a, args.steps, args.warmup, tune=True)
+        paths["forward_tuned"] = {f"{n}:{a}": done("forward_tuned", f"{n}:{a}",
+                                                   run_forward_path(ffpa, W, n, a, args.steps, args.warmup,
+                                                                    tune=True))
                                   for n, a in TUNED_PATHS}
-        paths["forward_fp8"] = {n: run_fp8(ffpa, W, n, args.steps, args.warmup) for n in FP8_PATHS}
+        paths["forward_fp8"] = {n: done("forward_fp8", n, run_fp8(ffpa, W, n, args.steps, args.warmup))
+                                for n in FP8_PATHS}
         line["paths"] = paths
     print(json.dumps(line), flush=True)
     if args.copy_calibration:
