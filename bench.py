@@ -441,7 +441,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="self")
     ap.add_argument("--accum", default="f32", choices=["f32", "f16"])
-    ap.add_argument("--cpu-heads", type=int, default=2,
+    # 16 of the 32 heads: about 10 s of the oracle on a 16-core host
+    ap.add_argument("--cpu-heads", type=int, default=16,
                     help="(b, h) heads the oracle CPU baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", action="store_true", help="time every workload family")
