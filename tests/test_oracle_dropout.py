@@ -17,10 +17,10 @@ t = round(256 p)) is pinned by what mathematics and statistics fix:
 * planted mistakes (unscaled output, transposed mask, dP not masked, the
   scale applied to dV twice, the counter ignoring the head) are rejected.
 
-The Philox round function itself follows the published definition; no known-
-answer vector of it is printed on the pages, so its bit pattern is parity-
-unpinned beyond the statistics above (the HIP path implements the same
-definition independently and must agree with this oracle bit for bit).
+The Philox block function itself follows the published definition; the pages
+print no random numbers, so its bit pattern is pinned against rocRAND's
+Philox-4x32-10 in tests/test_oracle_philox.py (the HIP path implements the
+same definition independently and must agree with this oracle bit for bit).
 """
 import inspect
 import math
