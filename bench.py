@@ -501,8 +501,9 @@ def main(argv=None) -> int:
     done("headline", args.workload, line)
     if paths is not None:
         for name in BWD_PATHS:
+            # 5 warm-up calls: the first calls of a backward shape run measurably slower
             paths["backward" + name[3:]] = done("backward", name,
-                                                run_backward(ffpa, W, name, max(3, args.steps // 2), 3))
+                                                run_backward(ffpa, W, name, max(3, args.steps // 2), 5))
         paths["decode"] = done("decode", "decode", run_decode(ffpa, W, args.steps, max(args.warmup, 50)))
         paths["forward"] = {f"{n}:{a}": done("forward", f"{n}:{a}",
                                              run_forward_path(ffpa, W, n, a, args.steps, args.warmup))
