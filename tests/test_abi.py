@@ -269,3 +269,39 @@ def test_tune_validation():
     st, _, ms = ffpa.ffpa_attn_fwd_tune(P, P, P, P, P, 1, 2, 2, 8, 8, 640, 0.125, 0, 0, 0, 0, 0, 0, 0, 1, 0)
     assert st == ffpa.ERR_WORKSPACE and ms == [-1.0, -1.0, -1.0]
     ffpa.ffpa_attn_tune_reset()
+
+
+def fp8(**kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Nq=8, Nkv=8, D=128, scale=0.125,
+                causal=0, dtype=0, workspace=P, workspace_bytes=1 << 30, stream=0)
+    args.update(kw)
+    return ffpa.ffpa_attn_fwd_fp8(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), ffpa.ERR_INVALID_ARG),
+    (dict(Nq=0), ffpa.ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), ffpa.ERR_INVALID_ARG),
+    (dict(k=P + 8), ffpa.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), ffpa.ERR_INVALID_ARG),
+    (dict(dtype=7), ffpa.ERR_UNSUPPORTED),
+    (dict(D=64), ffpa.ERR_UNSUPPORTED),      # built for D = 128 .. 512, multiples of 64
+    (dict(D=160), ffpa.ERR_UNSUPPORTED),
+    (dict(D=576), ffpa.ERR_UNSUPPORTED),
+    (dict(workspace=P + 8), ffpa.ERR_INVALID_ARG),
+    (dict(workspace=0), ffpa.ERR_WORKSPACE),
+    (dict(workspace_bytes=1024), ffpa.ERR_WORKSPACE),
+])
+def test_fp8_validation(kw, code):
+    assert fp8(**kw) == code
+    assert ffpa.ffpa_last_error() != ""
+
+
+def test_fp8_workspace_size():
+    """amax (3 B Hq floats, 256-aligned), Q8, K8 and V8^T (keys padded to 64),
+    each 256-byte aligned; 0 for invalid sizes."""
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for B, Hq, Hkv, Nq, Nkv, D in ((1, 32, 32, 8192, 8192, 512), (2, 4, 1, 100, 130, 192), (1, 1, 1, 1, 1, 128)):
+        want = up(3 * B * Hq * 4) + up(B * Hq * Nq * D) + up(B * Hkv * Nkv * D) + up(B * Hkv * ((Nkv + 63) // 64) * 64 * D)
+        assert ffpa.ffpa_attn_fwd_fp8_workspace_size(B, Hq, Hkv, Nq, Nkv, D) == want
+    assert ffpa.ffpa_attn_fwd_fp8_workspace_size(1, 2, 2, 0, 8, 128) == 0
