@@ -423,12 +423,13 @@ FWD_PATHS = ([("self_bf16", "f32"), ("self", "f16"), ("self_bf16", "f16")] +
              [(n, "f32") for n in ("cross", "gqa", "causal", "nonaligned", "mask", "dropout")] +
              [(n + "_bf16", "f32") for n in ("cross", "gqa", "causal", "nonaligned", "mask", "dropout")] +
              [(f"dsweep{d}_{a}", a) for d in (320, 448, 512, 576, 768, 1024) for a in ("f32", "f16")] +
-             [("self16k", "f32"), ("self16k_bf16", "f32"), ("causal16k", "f32"), ("nonaligned16k", "f32")])
+             [("self16k", "f32"), ("self16k_bf16", "f32"), ("causal16k", "f32"), ("nonaligned16k", "f32")] +
+             [("d128_16k", "f32"), ("d128_32k", "f32")])
 # Forward workloads measured again after tuning (the variants differ most there)
 TUNED_PATHS = [("cross", "f32"), ("gqa", "f32"), ("dsweep576_f16", "f16"), ("dsweep768_f16", "f16"),
                ("dsweep1024_f16", "f16")]
 # 16-bit workloads timed again through the fp8 forward
-FP8_PATHS = ("self", "self_bf16", "causal", "dsweep320_f32")
+FP8_PATHS = ("self", "self_bf16", "causal", "dsweep320_f32", "d128_16k", "d128_32k")
 BWD_PATHS = ("bwd_causal", "bwd_cross", "bwd_decode", "bwd_gqa", "bwd_mask", "bwd_nonaligned", "bwd_dropout",
              "bwd_d1024", "bwd16k", "bwd16k_causal")
 

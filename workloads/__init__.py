@@ -114,6 +114,12 @@ WORKLOADS.update({
     "bwd_dropout": _w("bwd_dropout", 4, 1, 32, 32, 8192, 8192, 512, dtype="bf16", backward=True,
                       dropout_p=0.1),
 })
+# the shapes of the fp8 benchmark of "FFPA Attention Benchmark" ("FP8 and FP4":
+# D = 128 at N = 16K and 32K; B and H are not printed, B = 1 and H = 32 as above)
+WORKLOADS.update({
+    "d128_16k": _w("d128_16k", 7, 1, 32, 32, 16384, 16384, 128),
+    "d128_32k": _w("d128_32k", 7, 1, 32, 32, 32768, 32768, 128),
+})
 # bf16 variants of the variant family (same float32 draws as the fp16 ones)
 for _n in ("cross", "gqa", "causal", "nonaligned", "mask", "dropout"):
     WORKLOADS[f"{_n}_bf16"] = WORKLOADS[_n].replace(name=f"{_n}_bf16", dtype="bf16")
