@@ -157,9 +157,11 @@ def test_fp8_validation(lib):
         lib.attention_fp8(q, q, q)
 
 
-@pytest.mark.parametrize("name", ["self", "self_bf16"])
+@pytest.mark.parametrize("name", ["self", "self_bf16", "d128_16k"])
 def test_fp8_full_size(lib, name):
-    """The benchmark workload (B1 H32 N8192 D512): two whole heads."""
+    """The benchmark workloads (B1 H32 N8192 D512, and the pages' fp8 shape
+    B1 H32 D128 at N = 16K): two whole heads. (At 32K the oracle's score
+    matrix of one head alone takes 8 GiB of float64.)"""
     w = W.WORKLOADS[name]
     inp = W.make_inputs(w, device="cuda")
     o, lse = lib.attention_fp8(inp["q"], inp["k"], inp["v"], scale=w.scale, return_lse=True)

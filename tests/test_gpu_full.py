@@ -113,6 +113,13 @@ def test_16k_forward(lib, name, accum):
     _check_forward(lib, name, accum)
 
 
+@pytest.mark.parametrize("name", ["d128_16k", "d128_32k"])
+def test_d128_long_forward(lib, name):
+    """The fp8 benchmark's shapes through the 16-bit forward (B1 H32 D128 at
+    N = 16K and 32K): whole heads against the oracle."""
+    _check_forward(lib, name, "f32")
+
+
 def test_decode(lib):
     """Decode (one query row per head): 64 of the 512 heads, every one whole."""
     w = W.WORKLOADS["decode"]
