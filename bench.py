@@ -299,6 +299,8 @@ def run_fp8(ffpa, W, name, steps, warmup):
     import torch
 
     w = W.WORKLOADS[name]
+    if w.mask is not None or w.dropout_p:
+        raise ValueError(f"the fp8 forward takes no mask and no dropout: {name}")
     inp = W.make_inputs(w, device="cuda")
     q, k, v = inp["q"], inp["k"], inp["v"]
     o = torch.empty_like(q)
