@@ -683,13 +683,20 @@ static size_t bwd_ds_bytes_kvhead(int Hq, int Hkv, int Nq, int Nkv) {
 }
 
 // dS budget of the size query: the dK/dV and dQ passes run over chunks of kv
-// heads whose dS fits it (at least one kv head's group per chunk).
+// heads whose dS fits it (at least one kv head's group per chunk), and of
+// at least as many kv heads as give a chunk's dQ pass kBwdDqMinWg workgroups
+// (two per CU): with fewer, the causal rows' very different lengths leave
+// most CUs idle behind the longest (16K causal: 641 -> 722 TFLOP/s).
 constexpr size_t kBwdDsBudget = size_t(1) << 30;
+constexpr int64_t kBwdDqMinWg = 512;
 
-static int bwd_default_chunk(int B, int Hq, int Hkv, int Nq, int Nkv) {
+static int bwd_default_chunk(int B, int Hq, int Hkv, int Nq, int Nkv, int D) {
   const size_t per = bwd_ds_bytes_kvhead(Hq, Hkv, Nq, Nkv);
   const int64_t nkv = (int64_t)B * Hkv;
-  const int64_t fit = (int64_t)(kBwdDsBudget / per);
+  const int dq_rows = D <= 512 ? 128 : 64;  // query rows per dQ workgroup
+  const int64_t dq_wg_per_kv = (int64_t)(Hq / Hkv) * ((Nq + dq_rows - 1) / dq_rows);
+  const int64_t fit = std::max<int64_t>((int64_t)(kBwdDsBudget / per),
+                                        (kBwdDqMinWg + dq_wg_per_kv - 1) / dq_wg_per_kv);
   // equal chunks: the fewest that respect the budget, then the chunk size
   // that spreads the heads evenly over them
   const int64_t chunks = (nkv + std::max<int64_t>(fit, 1) - 1) / std::max<int64_t>(fit, 1);
@@ -699,7 +706,7 @@ static int bwd_default_chunk(int B, int Hq, int Hkv, int Nq, int Nkv) {
 size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {
   const size_t base = ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype);
   if (base == 0 || Hkv < 1 || Nkv < 1 || D < 1 || Hq % Hkv != 0) return base;
-  const int chunk = bwd_default_chunk(B, Hq, Hkv, Nq, Nkv);
+  const int chunk = bwd_default_chunk(B, Hq, Hkv, Nq, Nkv, D);
   return base + bwd_kt_bytes(B, Hkv, Nkv, D) + (size_t)chunk * bwd_ds_bytes_kvhead(Hq, Hkv, Nq, Nkv);
 }
 

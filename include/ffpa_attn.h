@@ -179,8 +179,10 @@ int ffpa_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, 
  *    many kv heads as the dS room holds, reusing it chunk after chunk;
  *  - with less, dQ recomputes S and dP.
  * ffpa_attn_bwd_workspace_size(...) gives the stored-dS path a dS buffer of at
- * most 1 GiB (or one kv head's group, if that is larger), in equal chunks:
- * at B = 1, Hq = Hkv = 32, N = 8192, D = 512 that is 8 heads of 128 MiB.
+ * most 1 GiB, or more where needed for one kv head's group or for a chunk
+ * whose dQ pass has at least 512 workgroups, in equal chunks: at B = 1,
+ * Hq = Hkv = 32, D = 512 that is 8 heads of 128 MiB at N = 8192 (1 GiB) and
+ * 4 heads of 512 MiB at N = 16384 (2 GiB).
  * Every path and chunk size gives the same gradients up to rounding order;
  * a given workspace size always gives the same bits. Kernels enqueued: the
  * delta pass, then [the K transpose, then per chunk: dK/dV, dQ] or

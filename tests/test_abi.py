@@ -134,14 +134,20 @@ def test_backward_workspace_sizes():
     # 8K: 128 MiB of dS per head, at most 1 GiB of it: 4 chunks of 8 heads
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 32, 8192, 8192, 512, 1) == (
         2 * 32 * 8192 * 4 + 32 * 512 * 8192 * 2 + 8 * 256 * 256 * 2048)
-    # 16K: 512 MiB per head, 2 per chunk; GQA 32/8: a kv head's group is 4 query heads
+    # 16K: 512 MiB per head; 2 would fit 1 GiB, but a chunk's dQ pass needs 512
+    # workgroups of 128 rows: 4 heads per chunk. GQA 32/8: a kv head's group is 4
+    # query heads (2 GiB, 512 dQ workgroups)
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 32, 16384, 16384, 512, 0) == (
-        2 * 32 * 16384 * 4 + 32 * 512 * 16384 * 2 + 2 * 512 * 512 * 2048)
+        2 * 32 * 16384 * 4 + 32 * 512 * 16384 * 2 + 4 * 512 * 512 * 2048)
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 8, 16384, 16384, 512, 0) == (
         2 * 32 * 16384 * 4 + 8 * 512 * 16384 * 2 + 1 * 4 * 512 * 512 * 2048)
-    # 33 heads of 128 MiB: 5 chunks of 7 (the fewest within 1 GiB, spread evenly)
+    # 33 heads of 128 MiB: chunks of up to 8 (1 GiB, and 512 dQ workgroups of 64
+    # rows), so 5 chunks, the heads spread evenly over them: 7 each
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 33, 33, 8192, 8192, 64, 0) == (
         2 * 33 * 8192 * 4 + 33 * 64 * 8192 * 2 + 7 * 256 * 256 * 2048)
+    # D = 1024: 64 dQ rows per workgroup, so 4 heads suffice; the 1 GiB budget's 8 win
+    assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 32, 8192, 8192, 1024, 1) == (
+        2 * 32 * 8192 * 4 + 32 * 1024 * 8192 * 2 + 8 * 256 * 256 * 2048)
 
 
 def fwd_noalloc(**kw):
