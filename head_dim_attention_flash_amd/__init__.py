@@ -23,7 +23,8 @@ __all__ = [
     "ffpa_attn_fwd_variant_workspace_size", "ffpa_attn_fwd_tune", "ffpa_attn_tune_reset", "tune_forward",
     "ffpa_attn_fwd_fp8", "ffpa_attn_fwd_fp8_workspace_size", "attention_fp8",
     "ffpa_attn_fwd_workspace_size",
-    "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min", "ffpa_last_error",
+    "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_stored",
+    "ffpa_attn_bwd_workspace_size_min", "ffpa_last_error",
     "ffpa_version", "attention",
     "attention_backward", "F16", "BF16", "ACC_F32", "ACC_F16", "LIB_PATH", "EXPORTED",
 ]
@@ -39,8 +40,8 @@ _STATUS = {1: "FFPA_ERR_INVALID_ARG", 2: "FFPA_ERR_UNSUPPORTED", 3: "FFPA_ERR_WO
 
 # Symbols declared in include/ffpa_attn.h.
 EXPORTED = ("ffpa_attn_fwd", "ffpa_attn_fwd_workspace_size", "ffpa_attn_fwd_noalloc", "ffpa_attn_bwd",
-            "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_min",
-            "ffpa_attn_fwd_dropout", "ffpa_attn_bwd_dropout", "ffpa_attn_fwd_variant",
+            "ffpa_attn_bwd_workspace_size", "ffpa_attn_bwd_workspace_size_stored",
+            "ffpa_attn_bwd_workspace_size_min", "ffpa_attn_fwd_dropout", "ffpa_attn_bwd_dropout", "ffpa_attn_fwd_variant",
             "ffpa_attn_fwd_variant_workspace_size", "ffpa_attn_fwd_tune", "ffpa_attn_tune_reset",
             "ffpa_attn_fwd_fp8", "ffpa_attn_fwd_fp8_workspace_size", "ffpa_last_error", "ffpa_version")
 
@@ -94,6 +95,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffpa_attn_fwd_workspace_size.restype = sz
     lib.ffpa_attn_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.ffpa_attn_bwd_workspace_size.restype = sz
+    lib.ffpa_attn_bwd_workspace_size_stored.argtypes = [i, i, i, i, i, i, i]
+    lib.ffpa_attn_bwd_workspace_size_stored.restype = sz
     lib.ffpa_attn_bwd_workspace_size_min.argtypes = [i, i, i, i, i, i, i]
     lib.ffpa_attn_bwd_workspace_size_min.restype = sz
     lib.ffpa_last_error.argtypes = []
@@ -123,6 +126,10 @@ def ffpa_attn_fwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype) -> int:
 
 def ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype) -> int:
     return load().ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dtype)
+
+
+def ffpa_attn_bwd_workspace_size_stored(B, Hq, Hkv, Nq, Nkv, D, dtype) -> int:
+    return load().ffpa_attn_bwd_workspace_size_stored(B, Hq, Hkv, Nq, Nkv, D, dtype)
 
 
 def ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype) -> int:
@@ -384,14 +391,15 @@ def attention_fp8(q, k, v, *, causal: bool = False, scale: Optional[float] = Non
 
 
 def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None,
-                       scale: Optional[float] = None, store_ds: bool = True,
+                       scale: Optional[float] = None, store_ds: Optional[bool] = None,
                        workspace_bytes: Optional[int] = None, dropout_p: float = 0.0,
                        seed: int = 0):
     """(dq, dk, dv) of attention on the current HIP stream; o, lse from ``attention``.
 
-    store_ds=True (default) gives the call ffpa_attn_bwd_workspace_size bytes:
-    the dK/dV pass keeps dS for the dQ pass, over chunks of kv heads whose dS
-    fits a bounded buffer. store_ds=False gives it the minimum
+    By default the call gets ffpa_attn_bwd_workspace_size bytes. store_ds=True
+    gives it ffpa_attn_bwd_workspace_size_stored bytes whatever Nq: the dK/dV
+    pass keeps dS for the dQ pass, over chunks of kv heads whose dS fits a
+    bounded buffer. store_ds=False gives it the minimum
     (ffpa_attn_bwd_workspace_size_min): dQ then recomputes S and dP.
     workspace_bytes overrides either size (at least the minimum; the library
     takes the stored-dS path when it holds K^T and one kv head's dS).
@@ -407,7 +415,8 @@ def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None
     mptr, mrows = _mask_args(mask, q, Nq, Nkv)
     dt = _dtype_code(q)
     if workspace_bytes is None:
-        size = ffpa_attn_bwd_workspace_size if store_ds else ffpa_attn_bwd_workspace_size_min
+        size = {None: ffpa_attn_bwd_workspace_size, True: ffpa_attn_bwd_workspace_size_stored,
+                False: ffpa_attn_bwd_workspace_size_min}[store_ds]
         workspace_bytes = size(B, Hq, Hkv, Nq, Nkv, D, dt)
     ws = torch.empty(max(workspace_bytes, 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream

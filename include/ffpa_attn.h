@@ -182,7 +182,10 @@ int ffpa_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, 
  * most 1 GiB, or more where needed for one kv head's group or for a chunk
  * whose dQ pass has at least 512 workgroups, in equal chunks: at B = 1,
  * Hq = Hkv = 32, D = 512 that is 8 heads of 128 MiB at N = 8192 (1 GiB) and
- * 4 heads of 512 MiB at N = 16384 (2 GiB).
+ * 4 heads of 512 MiB at N = 16384 (2 GiB) (ffpa_attn_bwd_workspace_size_stored).
+ * For Nq <= 64, ffpa_attn_bwd_workspace_size returns the minimum: one dQ
+ * workgroup per head then reads K and V once, which costs less than the
+ * transposed copy of K.
  * Every path and chunk size gives the same gradients up to rounding order;
  * a given workspace size always gives the same bits. Kernels enqueued: the
  * delta pass, then [the K transpose, then per chunk: dK/dV, dQ] or
@@ -198,8 +201,14 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
                   const void* mask, int mask_rows, int accum_dtype, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace for the stored-dS path with its default, bounded dS buffer. */
+/* Bytes of workspace the backward takes by default: that of the stored-dS
+ * path with its default, bounded dS buffer (ffpa_attn_bwd_workspace_size_stored),
+ * or for Nq <= 64 the minimum. */
 size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
+
+/* Bytes of workspace of the stored-dS path with its default, bounded dS
+ * buffer, whatever Nq. */
+size_t ffpa_attn_bwd_workspace_size_stored(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
 
 /* The least workspace ffpa_attn_bwd accepts (dQ then recomputes S and dP). */
 size_t ffpa_attn_bwd_workspace_size_min(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);

@@ -145,6 +145,20 @@ def test_backward_workspace_sizes():
     # rows), so 5 chunks, the heads spread evenly over them: 7 each
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 33, 33, 8192, 8192, 64, 0) == (
         2 * 33 * 8192 * 4 + 33 * 64 * 8192 * 2 + 7 * 256 * 256 * 2048)
+    # up to 64 query rows: the minimum (dQ recomputes; no K transpose)
+    for nq in (1, 64):
+        assert ffpa.ffpa_attn_bwd_workspace_size(16, 32, 32, nq, 8192, 512, 0) == \
+            ffpa.ffpa_attn_bwd_workspace_size_min(16, 32, 32, nq, 8192, 512, 0)
+    assert ffpa.ffpa_attn_bwd_workspace_size(1, 2, 2, 65, 100, 64, 0) > \
+        ffpa.ffpa_attn_bwd_workspace_size_min(1, 2, 2, 65, 100, 64, 0)
+    # the stored-dS size whatever Nq: K^T (Nkv padded to 128) and dS of both kv
+    # heads (32 x 32 blocks of 2048 bytes) on top of the minimum
+    for nq in (1, 64, 65):
+        assert ffpa.ffpa_attn_bwd_workspace_size_stored(1, 2, 2, nq, 100, 64, 0) == (
+            ffpa.ffpa_attn_bwd_workspace_size_min(1, 2, 2, nq, 100, 64, 0) + 2 * 128 * 64 * 2
+            + 2 * ((nq + 31) // 32) * 4 * 2048)
+    assert ffpa.ffpa_attn_bwd_workspace_size_stored(1, 32, 32, 8192, 8192, 512, 1) == \
+        ffpa.ffpa_attn_bwd_workspace_size(1, 32, 32, 8192, 8192, 512, 1)
     # D = 1024: 64 dQ rows per workgroup, so 4 heads suffice; the 1 GiB budget's 8 win
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 32, 32, 8192, 8192, 1024, 1) == (
         2 * 32 * 8192 * 4 + 32 * 1024 * 8192 * 2 + 8 * 256 * 256 * 2048)
