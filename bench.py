@@ -443,7 +443,8 @@ def main(argv=None) -> int:
     # 25 forward calls (~0.1 s at the headline size): the clock ramps up over the first ~10
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--workload", default="self")
-    ap.add_argument("--accum", default="f32", choices=["f32", "f16"])
+    ap.add_argument("--accum", default=None, choices=["f32", "f16"],
+                    help="output accumulator of the headline call (default: the workload's)")
     # 16 of the 32 heads: about 10 s of the oracle on a 16-core host
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="(b, h) heads the oracle CPU baseline runs on")
@@ -499,7 +500,8 @@ def main(argv=None) -> int:
         # the backward first: its calls (~0.2 s of GPU work) also bring the
         # clock past its ramp before the headline's warm-up steps
         paths = {"backward": done("backward", "bwd", run_backward(ffpa, W, "bwd", max(3, args.steps // 2), 5))}
-    line = run_one(ffpa, W, args.workload, args.accum, args.steps, args.warmup,
+    accum = args.accum or W.WORKLOADS[args.workload].accum
+    line = run_one(ffpa, W, args.workload, accum, args.steps, args.warmup,
                    not args.no_cpu_baseline, args.cpu_heads)
     done("headline", args.workload, line)
     if paths is not None:

@@ -97,6 +97,11 @@ void fwd_wide16_kernel(FwdArgs a) {
   // is odd); a group's MFMAs run (d0, t2 0), (d1, t2 0), (d0, t2 1), (d1, t2 1),
   // so that consecutive MFMAs write different accumulators
   constexpr int NSV = 2 * NDB;  // MFMA steps of the V phase
+  // each phase issues the other buffer's copies over its first half of MFMA
+  // steps (NH = 2: three quarters, 3 % faster at D = 1024; NH = 1 is no
+  // faster that way, and D = 768 then spills)
+  constexpr int KSPAN = NH == 2 ? 3 * NS / 4 : NS / 2;
+  constexpr int VSPAN = NH == 2 ? 3 * NSV / 4 : NSV / 2;
   static_assert(NS % 2 == 0, "two score chains of equal length");
 
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
@@ -234,7 +239,7 @@ void fwd_wide16_kernel(FwdArgs a) {
       for (int st = 0; st < NS; ++st) {
 #pragma unroll
         for (int r = 0; r < NVC; ++r)
-          if ((r * (NS / 2)) / NVC == st) vt_copy(j, r, vlo);
+          if ((r * KSPAN) / NVC == st) vt_copy(j, r, vlo);
         const u32x4 a0 = kf[st % kKAhead];
         if (st + kKAhead < NS) kf[st % kKAhead] = kread(st + kKAhead);
         f32x16& acc = (st & 1) ? s_odd : s_acc;
@@ -383,7 +388,7 @@ void fwd_wide16_kernel(FwdArgs a) {
         // zeros) or, causal, rows nobody reads: harmless, and branch-free
 #pragma unroll
         for (int r = 0; r < NKC; ++r)
-          if ((r * (NSV / 2)) / NKC == s) k_copy(j + 1, r);
+          if ((r * VSPAN) / NKC == s) k_copy(j + 1, r);
         int g, uu, t2;
         step_of(s, g, uu, t2);
         const u32x4 vbits = vf[s % kVAhead];
