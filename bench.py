@@ -335,6 +335,9 @@ def timed_call(w, accum="f32", variant=0) -> str:
     if w.D > 512:
         if variant == 0:
             variant = 1 if (accum != "f16" or w.dropout_p) else (2 if w.D <= 768 else 3)
+        if variant == 2 and w.D <= 640:
+            return ("fwd_vt_kernel (V transposed into the workspace) + "
+                    "fwd_prefill_kernel (fp16 accumulator, a wave holds all of D, 128 rows)")
         return ("fwd_vt_kernel (V transposed, blocks of 32 keys) + " +
                 {1: "fwd_wide_kernel (fp32 accumulator, 64 rows)",
                  2: "fwd_wide16_kernel (a wave holds all of D, 128 rows)",

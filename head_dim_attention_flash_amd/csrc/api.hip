@@ -58,6 +58,16 @@ FwdLauncher fwd_launcher(int D, int bf16, int acc16, bool vt, bool drop, size_t*
     FFPA_CASE(448)
     FFPA_CASE(512)
 #undef FFPA_CASE
+    // 576 and 640: the fp16 accumulator with V^T staged only (the one-part
+    // tile shape of the wide forward)
+#define FFPA_CASE(DD)                                                                                  \
+  case DD:                                                                                             \
+    *ring_bytes = ffpa::fwd_ring_bytes<DD>();                                                          \
+    if (!acc16 || !vt || drop) return nullptr;                                                         \
+    return bf16 ? ffpa::launch_fwd_prefill<DD, true, true, true> : ffpa::launch_fwd_prefill<DD, false, true, true>;
+    FFPA_CASE(576)
+    FFPA_CASE(640)
+#undef FFPA_CASE
     default:
       return nullptr;
   }
@@ -67,8 +77,9 @@ using WideLauncher = hipError_t (*)(const ffpa::FwdArgs&, hipStream_t);
 
 // The wide kernels (D > 512), by tile shape:
 //   kWideF32:   fwd_wide_kernel, fp32 output accumulator, 64 rows per workgroup;
-//   kWide16One: fwd_wide16_kernel, fp16 accumulator, a wave holds all of D,
-//               128 rows per workgroup (D <= 768 only);
+//   kWide16One: fp16 accumulator, a wave holds all of D, 128 rows per
+//               workgroup (D <= 768 only): fwd_wide16_kernel at 704 and 768,
+//               the prefill kernel (64-key tiles) at 576 and 640;
 //   kWide16Two: fwd_wide16_kernel, fp16 accumulator, a wave pair splits D,
 //               64 rows per workgroup.
 enum WideShape { kWideF32 = 1, kWide16One = 2, kWide16Two = 3 };
@@ -89,7 +100,19 @@ WideLauncher wide_launcher(int D, int bf16, int shape, bool drop, int* rows) {
     if (DD > 768) return nullptr;                                                                      \
     *rows = ffpa::wide16_rows<DD, 1>();                                                                \
     return bf16 ? ffpa::launch_fwd_wide16<DD, true, 1> : ffpa::launch_fwd_wide16<DD, false, 1>;
-    FFPA_CASE(576) FFPA_CASE(640) FFPA_CASE(704) FFPA_CASE(768)
+    FFPA_CASE(704) FFPA_CASE(768)
+#undef FFPA_CASE
+#define FFPA_CASE(DD)                                                                                  \
+  case DD:                                                                                             \
+    if (drop || shape == kWideF32) {                                                                   \
+      *rows = 64;                                                                                      \
+      if (drop) return bf16 ? ffpa::launch_fwd_wide<DD, true, true> : ffpa::launch_fwd_wide<DD, false, true>; \
+      return bf16 ? ffpa::launch_fwd_wide<DD, true> : ffpa::launch_fwd_wide<DD, false>;               \
+    }                                                                                                  \
+    if (shape != kWide16Two) return nullptr; /* kWide16One: the prefill kernel */                      \
+    *rows = ffpa::wide16_rows<DD, 2>();                                                                \
+    return bf16 ? ffpa::launch_fwd_wide16<DD, true, 2> : ffpa::launch_fwd_wide16<DD, false, 2>;
+    FFPA_CASE(576) FFPA_CASE(640)
 #undef FFPA_CASE
 #define FFPA_CASE(DD)                                                                                  \
   case DD:                                                                                             \
@@ -335,7 +358,11 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     return FFPA_OK;
   }
 
-  if (D > 512) {
+  // 576 and 640 with the fp16 accumulator, one part of D per wave: the
+  // prefill kernel (64-key tiles, V^T staged) serves that tile shape
+  const bool prefill_wide = (D == 576 || D == 640) && variant == kWide16One && !dropout &&
+                            accum_dtype == FFPA_ACC_F16;
+  if (D > 512 && !prefill_wide) {
     // head dimensions above 512
     int rows = 64;
     WideLauncher launch = wide_launcher(D, dtype == FFPA_BF16, variant, dropout, &rows);
@@ -366,7 +393,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   const bool vt = variant == 2;
   FwdLauncher launch = fwd_launcher(D, dtype == FFPA_BF16, accum_dtype == FFPA_ACC_F16, vt, dropout, &ring);
   if (launch == nullptr) return fail(FFPA_ERR_UNSUPPORTED, "this head dimension is not built yet");
-  size_t lds = ring + ffpa::kFwdFlagBytes;
+  // the restart flags: fp32 accumulation only
+  size_t lds = ring + (accum_dtype == FFPA_ACC_F16 ? 0 : ffpa::kFwdFlagBytes);
   // a key bias is staged in LDS when it fits beside the tiles; otherwise the
   // kernel reads it (like a per-query mask) from global memory
   const bool bias_lds = mask != nullptr && mask_rows == 1 &&

@@ -1,0 +1,8 @@
+// Instances of the forward prefill kernel for head dimension 640: the fp16
+// output accumulator with V staged from its transposed copy only.
+#include "fwd_prefill.hpp"
+
+namespace ffpa {
+template hipError_t launch_fwd_prefill<640, false, true, true>(const FwdArgs&, size_t, hipStream_t);
+template hipError_t launch_fwd_prefill<640, true, true, true>(const FwdArgs&, size_t, hipStream_t);
+}  // namespace ffpa

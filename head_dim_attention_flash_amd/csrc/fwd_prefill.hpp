@@ -1,5 +1,6 @@
 // Forward attention kernel, 32 query rows per wave (head dimensions that are
-// multiples of 64, up to 512).
+// multiples of 64, up to 512; and 576 and 640 with the fp16 output
+// accumulator and V staged from its transposed copy).
 //
 // What it computes: O = softmax(scale * Q K^T + mask) V and lse per row, the
 // "naive_math" definition of section 3 of the attention-kernel-profiler design
@@ -62,13 +63,28 @@ constexpr int kFwdBc = 64;                // keys per tile
 
 // Every staged row takes 1 KiB of LDS whatever D is (up to 512): one copy
 // instruction fills one row, the swizzle groups are all complete, and two
-// 64-row tiles still fit.
+// 64-row tiles still fit. Above 512 (576, 640) a row takes D x 2 bytes: the
+// two tiles then fill 144 or 160 KiB, and the epilogue stages each row in
+// whole groups of 16 granules.
 constexpr int kFwdRowBytes = 1024;
+template <int D>
+constexpr int fwd_row_bytes() {
+  return D * 2 > kFwdRowBytes ? D * 2 : kFwdRowBytes;
+}
+template <int D>
+constexpr int fwd_epi_pitch() {
+  return D * 2 > kFwdRowBytes ? (D / 8 + 15) / 16 * 256 : kFwdRowBytes;
+}
 
 // LDS bytes of the K and V tile buffers.
 template <int D>
 constexpr int fwd_ring_bytes() {
-  return 2 * kFwdBc * kFwdRowBytes;
+  return 2 * kFwdBc * fwd_row_bytes<D>();
+}
+// LDS bytes of the epilogue's staging (the 32 rows of each of the 4 waves)
+template <int D>
+constexpr int fwd_epi_bytes() {
+  return kFwdWaves * 32 * fwd_epi_pitch<D>();
 }
 // LDS bytes of the staged key bias (zero-padded to whole tiles).
 __host__ __device__ inline int fwd_bias_bytes(int nkv) { return ((nkv + kFwdBc - 1) / kFwdBc) * kFwdBc * 2; }
@@ -94,11 +110,15 @@ constexpr float kRescaleTau = 8.0f;  // fp16-accumulator path: move m_ref past t
 template <int D, bool BF16, bool ACC16, bool VT, bool DROP = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fwd_prefill_kernel(FwdArgs a) {
-  static_assert(D % 64 == 0 && D <= 512, "D must be a multiple of 64, at most 512");
+  // above 512 the fp32 O no longer fits beside Q, and only the transposed V
+  // layout (128-byte rows) keeps the V tile within the LDS
+  static_assert(D % 64 == 0 && (D <= 512 || ((D == 576 || D == 640) && ACC16 && VT)),
+                "D must be a multiple of 64, at most 512 (576, 640: fp16 accumulator, V^T staged)");
   static_assert(!(ACC16 && DROP), "dropout is built with fp32 accumulation");
   using E = Elem<BF16>;
   using V8 = typename E::vec8;
-  constexpr int ROWB = kFwdRowBytes;      // bytes per LDS row (D * 2 used)
+  constexpr int ROWB = fwd_row_bytes<D>();  // bytes per LDS row (D * 2 used)
+  constexpr int EPB = fwd_epi_pitch<D>();   // bytes per row staged by the epilogue
   constexpr int GPR = D / 8;              // 16-byte granules of data per row
   constexpr int TILEB = kFwdBc * ROWB;    // bytes per tile buffer
   constexpr int NDMA = kFwdBc / kFwdWaves;  // V copies per wave per tile without VT (one per row)
@@ -107,7 +127,7 @@ void fwd_prefill_kernel(FwdArgs a) {
   constexpr int NDB = D / 32;             // output d-blocks of 32
   constexpr int KB = 0, VB = TILEB;       // buffer offsets
   constexpr int kKAhead = 3;              // K-fragment read-ahead, in d-steps
-  constexpr int kVAhead = ACC16 ? 6 : 8;  // V-fragment read-ahead, in MFMAs
+  constexpr int kVAhead = ACC16 ? (D > 512 ? 4 : 6) : 8;  // V-fragment read-ahead, in MFMAs
   // fp32 accumulator d-blocks that share the AGPRs with the Q fragments; the
   // remaining blocks live in VGPRs
   constexpr int kOAgpr = (256 - D / 4) / 16 < NDB ? (256 - D / 4) / 16 : NDB;
@@ -917,10 +937,10 @@ void fwd_prefill_kernel(FwdArgs a) {
   // ===== epilogue: normalise, store O and lse
   // The accumulators hold O transposed (a lane has 4-element pieces of one
   // row), so the rows go through LDS first: each wave writes its 32 rows to a
-  // 32 KiB slice of the (now idle) tile buffers, then stores them as whole
-  // contiguous 1 KiB pieces. Written straight from the accumulators, a cache
-  // line of O would be filled by many partial writes and leave the L2 several
-  // times.
+  // slice of the (now idle) tile buffers (32 rows of EPB bytes), then stores
+  // them as one contiguous run of 32 D elements. Written straight from the
+  // accumulators, a cache line of O would be filled by many partial writes and
+  // leave the L2 several times.
   int le = threadIdx.x & 63;
   asm volatile("" : "+v"(le));  // derived afresh: no lane value lives across the loop
   const int hie = le >> 5, my_qe = qw + (le & 31);
@@ -935,7 +955,7 @@ void fwd_prefill_kernel(FwdArgs a) {
   }
   wait_lgkm0();
   barrier();  // every wave is done reading the tile buffers
-  FFPA_LDS char* ostage = smem + wave * 32 * ROWB;
+  FFPA_LDS char* ostage = smem + wave * 32 * EPB;
   {
     // row r = lane % 32 of the wave; granule g (8 elements) sits in slot
     // g ^ (r % 16), which puts 16 consecutive rows on distinct banks
@@ -961,7 +981,7 @@ void fwd_prefill_kernel(FwdArgs a) {
         }
         const u32x2 st = {E::pack2(x0, x1), E::pack2(x2, x3)};
         const int g = 4 * db + g4;  // elements 32 db + 8 g4 + 4 hi .. +3
-        *(FFPA_LDS u32x2*)(ostage + r * ROWB + ((g ^ (r & 15)) << 4) + 8 * hie) = st;
+        *(FFPA_LDS u32x2*)(ostage + r * EPB + ((g ^ (r & 15)) << 4) + 8 * hie) = st;
       }
     }
   }
@@ -974,7 +994,7 @@ void fwd_prefill_kernel(FwdArgs a) {
     for (int it = 0; it < GPR / 2; ++it) {
       const int c = it * 64 + le;  // granule index within the wave's rows
       const int r = c / GPR, g = c % GPR;
-      const u32x4 x = *(const FFPA_LDS u32x4*)(ostage + r * ROWB + ((g ^ (r & 15)) << 4));
+      const u32x4 x = *(const FFPA_LDS u32x4*)(ostage + r * EPB + ((g ^ (r & 15)) << 4));
       if (r < rows) *(u32x4*)(O + (size_t)c * 8) = x;
     }
   }
@@ -984,8 +1004,9 @@ void fwd_prefill_kernel(FwdArgs a) {
   }
 }
 
-// Host launcher. lds_bytes = tile buffers + key-bias bytes (the caller checks
-// <= 160 KiB). With VT the transposed copy of V is written into a.vt first.
+// Host launcher. lds_bytes = tile buffers + key-bias bytes [+ restart flags]
+// (the caller checks <= 160 KiB); above D = 512 the launch takes at least the
+// epilogue's staging, which is larger than the tiles. With VT the transposed copy of V is written into a.vt first.
 // The kernel's LDS limit is set before anything is enqueued, so a failure
 // there leaves the stream untouched.
 template <int D, bool BF16, bool ACC16, bool VT, bool DROP = false>
@@ -998,7 +1019,8 @@ hipError_t launch_fwd_prefill(const FwdArgs& a, size_t lds_bytes, hipStream_t st
     const hipError_t e = launch_fwd_vt(a.v, const_cast<void*>(a.vt), a.B * a.Hkv, a.Nkv, D, a.nkv_pad, stream);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3(a.total_wg), dim3(256), lds_bytes, stream, a);
+  const size_t lds = lds_bytes > (size_t)fwd_epi_bytes<D>() ? lds_bytes : (size_t)fwd_epi_bytes<D>();
+  hipLaunchKernelGGL(kern, dim3(a.total_wg), dim3(256), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -32,23 +32,33 @@ namespace ffpa {
 FFPA_X_PREFILL(64) FFPA_X_PREFILL(128) FFPA_X_PREFILL(192) FFPA_X_PREFILL(256)
 FFPA_X_PREFILL(320) FFPA_X_PREFILL(384) FFPA_X_PREFILL(448) FFPA_X_PREFILL(512)
 #undef FFPA_X_PREFILL
+// 576 and 640: the fp16 accumulator with V^T staged only
+#define FFPA_X_PREFILL16(D)                                                                           \
+  extern template hipError_t launch_fwd_prefill<D, false, true, true>(const FwdArgs&, size_t, hipStream_t); \
+  extern template hipError_t launch_fwd_prefill<D, true, true, true>(const FwdArgs&, size_t, hipStream_t);
+FFPA_X_PREFILL16(576) FFPA_X_PREFILL16(640)
+#undef FFPA_X_PREFILL16
 
 #define FFPA_X_WIDE(D)                                                                   \
   extern template hipError_t launch_fwd_wide<D, false>(const FwdArgs&, hipStream_t);       \
   extern template hipError_t launch_fwd_wide<D, true>(const FwdArgs&, hipStream_t);        \
   extern template hipError_t launch_fwd_wide<D, false, true>(const FwdArgs&, hipStream_t); \
-  extern template hipError_t launch_fwd_wide<D, true, true>(const FwdArgs&, hipStream_t);  \
-  extern template hipError_t launch_fwd_wide16<D, false>(const FwdArgs&, hipStream_t);     \
-  extern template hipError_t launch_fwd_wide16<D, true>(const FwdArgs&, hipStream_t);
+  extern template hipError_t launch_fwd_wide<D, true, true>(const FwdArgs&, hipStream_t);
+#define FFPA_X_WIDE_NH1(D)                                                                 \
+  extern template hipError_t launch_fwd_wide16<D, false, 1>(const FwdArgs&, hipStream_t); \
+  extern template hipError_t launch_fwd_wide16<D, true, 1>(const FwdArgs&, hipStream_t);
 #define FFPA_X_WIDE_NH2(D)                                                                 \
   extern template hipError_t launch_fwd_wide16<D, false, 2>(const FwdArgs&, hipStream_t); \
   extern template hipError_t launch_fwd_wide16<D, true, 2>(const FwdArgs&, hipStream_t);
 FFPA_X_WIDE(576) FFPA_X_WIDE(640) FFPA_X_WIDE(704) FFPA_X_WIDE(768)
 FFPA_X_WIDE(832) FFPA_X_WIDE(896) FFPA_X_WIDE(960) FFPA_X_WIDE(1024)
-// up to 768 the default wide16 tile has one wave per 32 rows; the two-wave
-// (NH = 2) shape is instantiated beside it (above 768 it is the default)
+// wide16: one wave per 32 rows of all of D at 704 and 768 (at 576 and 640
+// that shape is the prefill kernel's); a wave pair per 32 rows at every D
+FFPA_X_WIDE_NH1(704) FFPA_X_WIDE_NH1(768)
 FFPA_X_WIDE_NH2(576) FFPA_X_WIDE_NH2(640) FFPA_X_WIDE_NH2(704) FFPA_X_WIDE_NH2(768)
+FFPA_X_WIDE_NH2(832) FFPA_X_WIDE_NH2(896) FFPA_X_WIDE_NH2(960) FFPA_X_WIDE_NH2(1024)
 #undef FFPA_X_WIDE
+#undef FFPA_X_WIDE_NH1
 #undef FFPA_X_WIDE_NH2
 
 #define FFPA_X_BWD(D)                                                                  \

@@ -225,7 +225,8 @@ size_t ffpa_attn_bwd_workspace_size_min(int B, int Hq, int Hkv, int Nq, int Nkv,
  *   Nq > 1, D > 512:  1 = fp32 output accumulator, 64 query rows per
  *                     workgroup, D split across wave pairs; with
  *                     accum_dtype = FFPA_ACC_F16 also 2 = fp16 accumulator,
- *                     a wave holds all of D, 128 rows per workgroup (D <= 768)
+ *                     a wave holds all of D, 128 rows per workgroup (D <= 768;
+ *                     64-key tiles at D = 576 and 640, 32-key tiles above)
  *                     and 3 = fp16 accumulator, D split across wave pairs, 64
  *                     rows per workgroup;
  *   Nq = 1:           1, 2, 3 = the default number of key ranges per head
