@@ -112,6 +112,8 @@ CASES = [
     (1, 2, 2, 33, 64, 960),     # D above 512, two whole key tiles
     (1, 2, 2, 300, 250, 704),   # fp16 accumulation: three 128-row blocks, the last ragged
     (1, 4, 2, 129, 96, 576),    # fp16 accumulation: one row past a 128-row block
+    (1, 2, 2, 260, 200, 640),   # fp16 accumulation at 640: 64-key tiles fill the LDS
+    (1, 1, 1, 130, 8300, 576),  # the key bias no longer fits beside 64-key tiles at 576
 ]
 
 
