@@ -45,6 +45,7 @@ CSRC = "head_dim_attention_flash_amd/csrc/"
 COUNTER_SOURCES = {
     "fwd": KERNEL_SOURCES,
     "wide": KERNEL_SOURCES + (CSRC + "fwd_wide.hpp",),
+    "wide16": KERNEL_SOURCES + (CSRC + "fwd_wide.hpp", CSRC + "fwd_wide16.hpp"),
     "bwd": (CSRC + "bwd.hpp", CSRC + "ffpa_common.hpp", CSRC + "fwd_vt.hpp", CSRC + "fwd_vt.hip"),
     "decode": (CSRC + "decode.hpp", CSRC + "ffpa_common.hpp"),
     "fp8": (CSRC + "fwd_fp8.hpp", CSRC + "ffpa_common.hpp"),
