@@ -278,8 +278,9 @@ int fwd_check_args(const void* q, const void* k, const void* v, void* o, float* 
 // with (ffpa_attn_fwd_variant, ffpa_attn_fwd_tune). 0 = the default choice.
 //   Nq > 1, D <= 512: 1 = V staged as is, 2 = V from its transposed copy;
 //   Nq > 1, D > 512:  WideShape (1 = fp32 accumulator, 64 rows; 2 = fp16
-//                     accumulator, a wave holds all of D, 128 rows, D <= 768;
-//                     3 = fp16 accumulator, a wave pair splits D, 64 rows);
+//                     accumulator, a wave holds all of D, 128 rows, D <= 768,
+//                     the prefill kernel at 576 and 640; 3 = fp16
+//                     accumulator, a wave pair splits D, 64 rows);
 //   Nq = 1:           1, 2, 3 = the default number of key ranges per head
 //                     divided by 1, 2, 4.
 constexpr int kMaxVariant = 3;
