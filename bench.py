@@ -237,19 +237,39 @@ def run_backward(ffpa, W, name, steps, warmup):
 
     per = _time_calls(call, steps, warmup)
     mean_ms = sum(per) / len(per)
-    tflops = counted_flops(w.B, w.Hq, w.Nq, w.Nkv, w.D, w.causal, backward=True) / (mean_ms * 1e-3) / 1e12
+    flops = counted_flops(w.B, w.Hq, w.Nq, w.Nkv, w.D, w.causal, backward=True)
+    tflops = flops / (mean_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    nbytes = backward_bytes(w)
+    if flops / nbytes < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        # below the ridge point (few query rows per key, e.g. Nq = 1): the
+        # bound is HBM, against the bytes every call must move
+        gbs = nbytes / (mean_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(tflops / peak, 4)}
+    chosen = "stored dS" if ws_bytes > ffpa.ffpa_attn_bwd_workspace_size_min(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, dt) \
+        else "dQ recomputes"
     del inp, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return {"workload": f"{name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nkv={w.Nkv} D={w.D} {w.dtype} "
                         f"causal={w.causal} mask={w.mask}" + (f" dropout_p={w.dropout_p}" if w.dropout_p else ""),
             "value": round(tflops, 2), "unit": "TFLOPS (5 GEMMs counted)",
             "ms_per_call": round(mean_ms, 4),
-            "kernels": "prep + K^T copy + per chunk of kv heads: dK/dV (stores dS) + dQ from dS",
+            "kernels": ("prep + K^T copy + per chunk of kv heads: dK/dV (stores dS) + dQ from dS"
+                        if chosen == "stored dS" else "prep + dK/dV + dQ (recomputes S and dP)"),
             "workspace_bytes": ws_bytes,
-            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4)},
+            "roofline": roof,
             "rocprof": recorded_counters(name)}
+
+
+def backward_bytes(w) -> int:
+    """Algorithmic HBM bytes of one backward call: q, k, v, o, dO and lse read,
+    dq, dk, dv written once each."""
+    e = 2
+    return e * (4 * w.B * w.Hq * w.Nq * w.D + 4 * w.B * w.Hkv * w.Nkv * w.D) + 4 * w.B * w.Hq * w.Nq
 
 
 def decode_bytes(w) -> int:
