@@ -250,16 +250,21 @@ def run_backward(ffpa, W, name, steps, warmup):
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(tflops / peak, 4)}
-    chosen = "stored dS" if ws_bytes > ffpa.ffpa_attn_bwd_workspace_size_min(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, dt) \
-        else "dQ recomputes"
+    stored = ffpa.ffpa_attn_bwd_workspace_size_stored(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, dt)
+    minimum = ffpa.ffpa_attn_bwd_workspace_size_min(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, dt)
+    if ws_bytes >= stored:
+        kernels = "prep + K^T copy + per chunk of kv heads: dK/dV (stores dS) + dQ from dS"
+    elif w.Nq == 1 and ws_bytes > minimum and not w.dropout_p:
+        kernels = "decode backward (dK, dV and dQ partials per key range, vector ALUs) + dQ sum"
+    else:
+        kernels = "prep + dK/dV + dQ (recomputes S and dP)"
     del inp, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return {"workload": f"{name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Nq={w.Nq} Nkv={w.Nkv} D={w.D} {w.dtype} "
                         f"causal={w.causal} mask={w.mask}" + (f" dropout_p={w.dropout_p}" if w.dropout_p else ""),
             "value": round(tflops, 2), "unit": "TFLOPS (5 GEMMs counted)",
             "ms_per_call": round(mean_ms, 4),
-            "kernels": ("prep + K^T copy + per chunk of kv heads: dK/dV (stores dS) + dQ from dS"
-                        if chosen == "stored dS" else "prep + dK/dV + dQ (recomputes S and dP)"),
+            "kernels": kernels,
             "workspace_bytes": ws_bytes,
             "roofline": roof,
             "rocprof": recorded_counters(name)}

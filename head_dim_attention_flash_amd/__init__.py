@@ -396,7 +396,8 @@ def attention_backward(dout, q, k, v, o, lse, *, causal: bool = False, mask=None
                        seed: int = 0):
     """(dq, dk, dv) of attention on the current HIP stream; o, lse from ``attention``.
 
-    By default the call gets ffpa_attn_bwd_workspace_size bytes. store_ds=True
+    By default the call gets ffpa_attn_bwd_workspace_size bytes (for one query
+    row: the decode backward's, see include/ffpa_attn.h). store_ds=True
     gives it ffpa_attn_bwd_workspace_size_stored bytes whatever Nq: the dK/dV
     pass keeps dS for the dQ pass, over chunks of kv heads whose dS fits a
     bounded buffer. store_ds=False gives it the minimum

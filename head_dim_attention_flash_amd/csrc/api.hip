@@ -12,6 +12,7 @@
 
 #include "ffpa_attn.h"
 #include "bwd.hpp"
+#include "dec_bwd.hpp"
 #include "decode.hpp"
 #include "fwd_fp8.hpp"
 #include "fwd_prefill.hpp"
@@ -194,6 +195,42 @@ BwdLauncher bwd_launcher(int D, int bf16) {
     default:
       return nullptr;
   }
+}
+
+using DecBwdLauncher = hipError_t (*)(const ffpa::DecBwdArgs&, hipStream_t);
+
+// The decode backward (Nq = 1) by head dimension and group size G = Hq / Hkv:
+// built for D = 64 .. 1024 (step 64), G = 1, 2, 4 up to D = 512 and G = 1, 2
+// above; nullptr otherwise.
+template <int D>
+DecBwdLauncher dec_bwd_pick(int bf16, int G) {
+  if (G == 1) return bf16 ? ffpa::launch_dec_bwd<D, true, 1> : ffpa::launch_dec_bwd<D, false, 1>;
+  if (G == 2) return bf16 ? ffpa::launch_dec_bwd<D, true, 2> : ffpa::launch_dec_bwd<D, false, 2>;
+  if constexpr (D <= 512) {
+    if (G == 4) return bf16 ? ffpa::launch_dec_bwd<D, true, 4> : ffpa::launch_dec_bwd<D, false, 4>;
+  }
+  return nullptr;
+}
+
+DecBwdLauncher dec_bwd_launcher(int D, int bf16, int G) {
+  switch (D) {
+#define FFPA_CASE(DD) \
+  case DD:            \
+    return dec_bwd_pick<DD>(bf16, G);
+    FFPA_CASE(64) FFPA_CASE(128) FFPA_CASE(192) FFPA_CASE(256) FFPA_CASE(320) FFPA_CASE(384)
+    FFPA_CASE(448) FFPA_CASE(512) FFPA_CASE(576) FFPA_CASE(640) FFPA_CASE(704) FFPA_CASE(768)
+    FFPA_CASE(832) FFPA_CASE(896) FFPA_CASE(960) FFPA_CASE(1024)
+#undef FFPA_CASE
+    default:
+      return nullptr;
+  }
+}
+
+// Whether the decode backward serves this shape (the size query cannot know
+// about dropout; a call with dropout takes the other kernels).
+bool dec_bwd_built(int Nq, int Hq, int Hkv, int Nkv, int D) {
+  if (Nq != 1 || Hkv < 1 || Hq % Hkv != 0 || Nkv < 1) return false;
+  return dec_bwd_launcher(D, 0, Hq / Hkv) != nullptr;
 }
 
 int64_t bwd_nq_pad(int Nq) { return ((int64_t)Nq + ffpa::kBwdPad - 1) / ffpa::kBwdPad * ffpa::kBwdPad; }
@@ -740,10 +777,12 @@ size_t ffpa_attn_bwd_workspace_size_stored(int B, int Hq, int Hkv, int Nq, int N
 }
 
 size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {
+  const size_t base = ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  // one query row: the decode backward (dQ partials of each key range)
+  if (dec_bwd_built(Nq, Hq, Hkv, Nkv, D)) return std::max(base, ffpa::dec_bwd_bytes(B, Hq, Hkv, Nkv, D));
   // up to 64 query rows a head's dQ is one workgroup that reads K and V once:
-  // cheaper than the K transpose the stored-dS path needs (decode: 5.0 against
-  // 6.1 ms at B16 H32 Nkv 8192 D 512)
-  if (Nq <= 64) return ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  // cheaper than the K transpose the stored-dS path needs
+  if (Nq <= 64) return base;
   return ffpa_attn_bwd_workspace_size_stored(B, Hq, Hkv, Nq, Nkv, D, dtype);
 }
 
@@ -785,6 +824,31 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   BwdLauncher launch = bwd_launcher(D, dtype == FFPA_BF16);
   if (launch == nullptr)
     return fail(FFPA_ERR_UNSUPPORTED, "the backward is built for D = 64, 128, ..., 1024");
+
+  // one query row, no dropout, and room for the dQ partials but not for the
+  // stored-dS path: the decode backward (a stream over K and V on the vector
+  // ALUs; the dK/dV kernel's 32-row query tiles would be 31/32 empty)
+  if (!store_ds && !with_drop && dec_bwd_built(Nq, Hq, Hkv, Nkv, D) &&
+      workspace_bytes >= std::max(need, ffpa::dec_bwd_bytes(B, Hq, Hkv, Nkv, D))) {
+    DecBwdLauncher dlaunch = dec_bwd_launcher(D, dtype == FFPA_BF16, Hq / Hkv);
+    ffpa::DecBwdArgs d{};
+    d.q = q; d.k = k; d.v = v; d.o = o; d.dout = dout; d.lse = lse; d.mask = mask;
+    d.dq = dq; d.dk = dk; d.dv = dv;
+    d.part_dq = (float*)workspace;
+    d.B = B; d.Hq = Hq; d.Hkv = Hkv; d.Nkv = Nkv;
+    d.kv_end = dec_kv_end(Nkv, causal);
+    d.splits = ffpa::dec_bwd_splits(B, Hkv, Nkv);
+    d.keys_per_split = ffpa::dec_keys_per_split(Nkv, d.splits);
+    d.scale = scale;
+    d.scale_log2 = scale * ffpa::kLog2e;
+    const int64_t waves = (int64_t)B * Hkv * d.splits;
+    if (waves >= (int64_t(1) << 31) - 3 || (int64_t)B * Hq >= (int64_t(1) << 31) - 3)
+      return fail(FFPA_ERR_UNSUPPORTED, "grid too large");
+    d.n_waves = (int)waves;
+    const hipError_t e = dlaunch(d, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(FFPA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    return FFPA_OK;
+  }
 
   ffpa::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;

@@ -8,6 +8,7 @@
 #pragma once
 
 #include "bwd.hpp"
+#include "dec_bwd.hpp"
 #include "decode.hpp"
 #include "fwd_fp8.hpp"
 #include "fwd_prefill.hpp"
@@ -79,6 +80,19 @@ FFPA_X_DEC(608) FFPA_X_DEC(640) FFPA_X_DEC(672) FFPA_X_DEC(704) FFPA_X_DEC(736) 
 FFPA_X_DEC(800) FFPA_X_DEC(832) FFPA_X_DEC(864) FFPA_X_DEC(896) FFPA_X_DEC(928) FFPA_X_DEC(960)
 FFPA_X_DEC(992) FFPA_X_DEC(1024)
 #undef FFPA_X_DEC
+
+#define FFPA_X_DB(D, G)                                                                          \
+  extern template hipError_t launch_dec_bwd<D, false, G>(const DecBwdArgs&, hipStream_t); \
+  extern template hipError_t launch_dec_bwd<D, true, G>(const DecBwdArgs&, hipStream_t);
+#define FFPA_X_DB_LO(D) FFPA_X_DB(D, 1) FFPA_X_DB(D, 2) FFPA_X_DB(D, 4)
+#define FFPA_X_DB_HI(D) FFPA_X_DB(D, 1) FFPA_X_DB(D, 2)
+FFPA_X_DB_LO(64) FFPA_X_DB_LO(128) FFPA_X_DB_LO(192) FFPA_X_DB_LO(256)
+FFPA_X_DB_LO(320) FFPA_X_DB_LO(384) FFPA_X_DB_LO(448) FFPA_X_DB_LO(512)
+FFPA_X_DB_HI(576) FFPA_X_DB_HI(640) FFPA_X_DB_HI(704) FFPA_X_DB_HI(768)
+FFPA_X_DB_HI(832) FFPA_X_DB_HI(896) FFPA_X_DB_HI(960) FFPA_X_DB_HI(1024)
+#undef FFPA_X_DB_LO
+#undef FFPA_X_DB_HI
+#undef FFPA_X_DB
 
 #define FFPA_X_FP8(D)                                                                 \
   extern template hipError_t launch_fwd_fp8<D, false>(const Fp8Args&, hipStream_t); \

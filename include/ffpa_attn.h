@@ -177,19 +177,27 @@ int ffpa_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, 
  *    pass stores dS (bf16/fp16, per 32 x 32 block) and the dQ pass reads it
  *    back (one product instead of three). Both passes run over chunks of as
  *    many kv heads as the dS room holds, reusing it chunk after chunk;
+ *  - otherwise, for one query row (Nq = 1) without dropout and a group of
+ *    g = 1, 2 or 4 query heads per kv head (4 only up to D = 512), with at
+ *    least max(minimum, B * Hq * S * D * 4) bytes: the decode backward, a
+ *    stream over K and V on the vector ALUs that writes dK and dV once per
+ *    key and fp32 dQ partials of S key ranges per head (S: about 2048 waves
+ *    over the B * Hkv kv heads, ranges of at least 256 keys, at most 64),
+ *    which a second kernel adds in range order;
  *  - with less, dQ recomputes S and dP.
  * ffpa_attn_bwd_workspace_size(...) gives the stored-dS path a dS buffer of at
  * most 1 GiB, or more where needed for one kv head's group or for a chunk
  * whose dQ pass has at least 512 workgroups, in equal chunks: at B = 1,
  * Hq = Hkv = 32, D = 512 that is 8 heads of 128 MiB at N = 8192 (1 GiB) and
  * 4 heads of 512 MiB at N = 16384 (2 GiB) (ffpa_attn_bwd_workspace_size_stored).
- * For Nq <= 64, ffpa_attn_bwd_workspace_size returns the minimum: one dQ
+ * For Nq = 1 ffpa_attn_bwd_workspace_size returns the decode backward's
+ * size where that path is built, and for other Nq <= 64 the minimum: one dQ
  * workgroup per head then reads K and V once, which costs less than the
  * transposed copy of K.
  * Every path and chunk size gives the same gradients up to rounding order;
  * a given workspace size always gives the same bits. Kernels enqueued: the
  * delta pass, then [the K transpose, then per chunk: dK/dV, dQ] or
- * [dK/dV, dQ]. Built for D a multiple of 64 up to 1024, with either mask
+ * [dK/dV, dQ]; or the decode backward and its dQ sum. Built for D a multiple of 64 up to 1024, with either mask
  * shape; other valid shapes (D not a multiple of 64) return
  * FFPA_ERR_UNSUPPORTED.
  * The gradients are those of sum(dout * O) ("FFPA Attention Benchmark",
@@ -202,8 +210,9 @@ int ffpa_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace the backward takes by default: that of the stored-dS
- * path with its default, bounded dS buffer (ffpa_attn_bwd_workspace_size_stored),
- * or for Nq <= 64 the minimum. */
+ * path with its default, bounded dS buffer (ffpa_attn_bwd_workspace_size_stored);
+ * for Nq = 1 that of the decode backward where it is built; for other
+ * Nq <= 64 the minimum. */
 size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype);
 
 /* Bytes of workspace of the stored-dS path with its default, bounded dS

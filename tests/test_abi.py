@@ -145,10 +145,18 @@ def test_backward_workspace_sizes():
     # rows), so 5 chunks, the heads spread evenly over them: 7 each
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 33, 33, 8192, 8192, 64, 0) == (
         2 * 33 * 8192 * 4 + 33 * 64 * 8192 * 2 + 7 * 256 * 256 * 2048)
-    # up to 64 query rows: the minimum (dQ recomputes; no K transpose)
-    for nq in (1, 64):
-        assert ffpa.ffpa_attn_bwd_workspace_size(16, 32, 32, nq, 8192, 512, 0) == \
-            ffpa.ffpa_attn_bwd_workspace_size_min(16, 32, 32, nq, 8192, 512, 0)
+    # up to 64 query rows: the minimum (dQ recomputes; no K transpose) ...
+    assert ffpa.ffpa_attn_bwd_workspace_size(16, 32, 32, 64, 8192, 512, 0) == \
+        ffpa.ffpa_attn_bwd_workspace_size_min(16, 32, 32, 64, 8192, 512, 0)
+    # ... but one row takes the decode backward: fp32 dQ partials of 4 key
+    # ranges per head (2048 waves over 16 x 32 kv heads)
+    assert ffpa.ffpa_attn_bwd_workspace_size(16, 32, 32, 1, 8192, 512, 0) == 16 * 32 * 4 * 512 * 4
+    # a group of 8 query heads per kv head has no decode backward: the minimum
+    assert ffpa.ffpa_attn_bwd_workspace_size(1, 8, 1, 1, 8192, 512, 0) == \
+        ffpa.ffpa_attn_bwd_workspace_size_min(1, 8, 1, 1, 8192, 512, 0)
+    # and never less than the minimum (one short range, D = 64)
+    assert ffpa.ffpa_attn_bwd_workspace_size(1, 2, 2, 1, 100, 64, 0) == \
+        ffpa.ffpa_attn_bwd_workspace_size_min(1, 2, 2, 1, 100, 64, 0)
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 2, 2, 65, 100, 64, 0) > \
         ffpa.ffpa_attn_bwd_workspace_size_min(1, 2, 2, 65, 100, 64, 0)
     # the stored-dS size whatever Nq: K^T (Nkv padded to 128) and dS of both kv

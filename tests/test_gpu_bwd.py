@@ -106,8 +106,8 @@ def _run_case(lib, shape, dtype, causal, with_mask, seed, mask_rows=1, store_ds=
                                         store_ds=store_ds)
     torch.cuda.synchronize()
     rq, rk, rv = attn_bwd(q, k, v, do, scale, causal=causal, mask=m2)
-    label = (f"{shape}-{dtype}-{'causal' if causal else 'full'}-{'mask' if with_mask else 'nomask'}"
-             f"-{'stored dS' if store_ds else 'recomputed dS'}")
+    path = {True: "stored dS", False: "recomputed dS", None: "default workspace"}[store_ds]
+    label = f"{shape}-{dtype}-{'causal' if causal else 'full'}-{'mask' if with_mask else 'nomask'}-{path}"
     print(label, flush=True)
     bounds = (_rounding_bounds(q, k, v, do, scale, causal, m2, (rq, rk, rv), dtype)
               if dtype == "bf16" else {})
@@ -236,3 +236,33 @@ def test_backward_causal_few_heads_long_rows(lib, shape, store_ds):
     """Causal with few heads and long rows: the blocks of one head fill several
     XCD ranges, whose causal work order interleaves them."""
     _run_case(lib, shape, "fp16", True, False, 31, store_ds=store_ds)
+
+
+# One query row with the default workspace: the decode backward (dQ partials
+# per key range, dK and dV written once per key) where it is built (G = Hq /
+# Hkv up to 4 at D <= 512, up to 2 above), the minimal-workspace kernels
+# otherwise (G = 8 below).
+DECODE_CASES = [
+    # (B, Hq, Hkv, Nq, Nkv, D)
+    (1, 2, 2, 1, 70, 512),      # one key range, ragged
+    (2, 4, 2, 1, 1000, 320),    # G = 2, four ranges, the last one shorter
+    (1, 8, 2, 1, 4097, 128),    # G = 4, 17 ranges of 248 keys
+    (1, 2, 1, 1, 600, 1024),    # G = 2, two granules per lane
+    (1, 3, 3, 1, 517, 576),     # a lane's second granule only in lanes 0 .. 7
+    (3, 2, 2, 1, 33, 64),       # 8 lanes hold the row
+    (1, 8, 1, 1, 300, 128),     # G = 8: no decode backward, the minimal path
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_CASES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("variant", ["plain", "causal", "mask", "causal_mask"])
+def test_decode_backward_matches_oracle(lib, shape, dtype, variant):
+    B, Hq, Hkv, Nq, Nkv, D = shape
+    dt = lib.BF16 if dtype == "bf16" else lib.F16
+    size = lib.ffpa_attn_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D, dt)
+    if Hq // Hkv <= (4 if D <= 512 else 2):
+        # the default holds the dQ partials, not the stored-dS path's K^T and dS
+        assert lib.ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dt) <= size < \
+            lib.ffpa_attn_bwd_workspace_size_stored(B, Hq, Hkv, Nq, Nkv, D, dt)
+    _run_case(lib, shape, dtype, "causal" in variant, "mask" in variant, 500 + sum(shape), store_ds=None)
