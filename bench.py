@@ -48,6 +48,7 @@ COUNTER_SOURCES = {
     "wide16": KERNEL_SOURCES + (CSRC + "fwd_wide.hpp", CSRC + "fwd_wide16.hpp"),
     "bwd": (CSRC + "bwd.hpp", CSRC + "ffpa_common.hpp", CSRC + "fwd_vt.hpp", CSRC + "fwd_vt.hip"),
     "decode": (CSRC + "decode.hpp", CSRC + "ffpa_common.hpp"),
+    "dec_bwd": (CSRC + "dec_bwd.hpp", CSRC + "decode.hpp", CSRC + "ffpa_common.hpp"),
     "fp8": (CSRC + "fwd_fp8.hpp", CSRC + "ffpa_common.hpp"),
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
