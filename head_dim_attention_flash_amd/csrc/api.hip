@@ -778,6 +778,7 @@ size_t ffpa_attn_bwd_workspace_size_stored(int B, int Hq, int Hkv, int Nq, int N
 
 size_t ffpa_attn_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nkv, int D, int dtype) {
   const size_t base = ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dtype);
+  if (base == 0) return 0;  // no valid problem (B, Hq or Nq below 1)
   // one query row: the decode backward (dQ partials of each key range)
   if (dec_bwd_built(Nq, Hq, Hkv, Nkv, D)) return std::max(base, ffpa::dec_bwd_bytes(B, Hq, Hkv, Nkv, D));
   // up to 64 query rows a head's dQ is one workgroup that reads K and V once:

@@ -154,6 +154,9 @@ def test_backward_workspace_sizes():
     # a group of 8 query heads per kv head has no decode backward: the minimum
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 8, 1, 1, 8192, 512, 0) == \
         ffpa.ffpa_attn_bwd_workspace_size_min(1, 8, 1, 1, 8192, 512, 0)
+    # sizes of no valid problem are 0 (and compute nothing that divides by them)
+    for dims in ((0, 2, 2, 1, 100, 64), (1, 0, 2, 1, 100, 64), (1, 2, 2, 0, 100, 64), (-1, 2, 2, 1, 100, 64)):
+        assert ffpa.ffpa_attn_bwd_workspace_size(*dims, 0) == 0
     # and never less than the minimum (one short range, D = 64)
     assert ffpa.ffpa_attn_bwd_workspace_size(1, 2, 2, 1, 100, 64, 0) == \
         ffpa.ffpa_attn_bwd_workspace_size_min(1, 2, 2, 1, 100, 64, 0)
