@@ -266,3 +266,20 @@ def test_decode_backward_matches_oracle(lib, shape, dtype, variant):
         assert lib.ffpa_attn_bwd_workspace_size_min(B, Hq, Hkv, Nq, Nkv, D, dt) <= size < \
             lib.ffpa_attn_bwd_workspace_size_stored(B, Hq, Hkv, Nq, Nkv, D, dt)
     _run_case(lib, shape, dtype, "causal" in variant, "mask" in variant, 500 + sum(shape), store_ds=None)
+
+
+def test_decode_backward_deterministic_and_zero_dout(lib):
+    """The decode backward gives the same bits on every call (dQ partials are
+    summed in range order), and zero gradients for dO = 0."""
+    B, Hq, Hkv, Nq, Nkv, D = 2, 8, 4, 1, 3000, 512
+    q, k, v, do, _ = _inputs(81, B, Hq, Hkv, Nq, Nkv, D, "bf16", False)
+    q, k, v, do = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = lib.attention(q, k, v, return_lse=True)
+    r1 = lib.attention_backward(do, q, k, v, o, lse)
+    r2 = lib.attention_backward(do, q, k, v, o, lse)
+    z = lib.attention_backward(torch.zeros_like(do), q, k, v, o, lse)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(r1, r2):
+        assert torch.equal(a_, b_)
+    for t in z:
+        assert torch.count_nonzero(t).item() == 0
