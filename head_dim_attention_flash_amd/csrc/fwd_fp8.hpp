@@ -159,34 +159,50 @@ __global__ __launch_bounds__(256) void f8_quant_qk_kernel(Fp8Args a) {
 }
 
 // V8^T: workgroup per (kv head, tile of 64 keys); the tile's 16-bit rows go
-// through LDS (64 x D), then each thread writes 16 positions of a V^T row.
+// through LDS (64 x D), then each thread writes 16 positions of two V^T rows.
 // Keys at or past Nkv are written as 0.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void f8_quant_vt_kernel(Fp8Args a) {
   using E = Elem<BF16>;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  uint16_t* tile = (uint16_t*)smem_raw;  // [64][D]
+  // the tile [64 keys][D], 16-byte granule g of key row r stored at granule
+  // g ^ swz(r): the four rows a wave reads at once (keys r, r + 4, r + 32,
+  // r + 36 of the position order) then sit in distinct 32-byte bank windows
+  char* tile = smem_raw;
+  auto swz = [](int r) { return 2 * (((r >> 2) & 1) | (((r >> 5) & 1) << 1)); };
   const int head = blockIdx.x / a.nkt, kt = blockIdx.x % a.nkt;
   const uint16_t* v = (const uint16_t*)a.v + ((size_t)head * a.Nkv + (size_t)kt * kF8Bc) * D;
   const int nrows = min(kF8Bc, a.Nkv - kt * kF8Bc);
   for (int i = threadIdx.x; i < kF8Bc * D / 8; i += 256) {
-    const int r = i / (D / 8);
-    u32x4 g = {0u, 0u, 0u, 0u};
-    if (r < nrows) g = *(const u32x4*)(v + 8 * (size_t)i);
-    *(u32x4*)(tile + 8 * i) = g;
+    const int r = i / (D / 8), g = i % (D / 8);
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (r < nrows) x = *(const u32x4*)(v + 8 * (size_t)i);
+    *(u32x4*)(tile + r * (2 * D) + ((g ^ swz(r)) << 4)) = x;
   }
   __syncthreads();
   const float s = f8_qscale(a.amax[a.B * a.Hq + a.B * a.Hkv + head]);
   uint8_t* out = a.vt8 + ((size_t)head * a.nkt + kt) * D * kF8Bc;
-  for (int i = threadIdx.x; i < D * 4; i += 256) {
-    const int d = i >> 2, p0 = 16 * (i & 3);
-    float f[16];
+  // each thread: columns 2 c2 and 2 c2 + 1 (one 4-byte read per key) at
+  // positions p0 .. p0 + 15, i.e. 16 bytes of two rows of V8^T
+  for (int i = threadIdx.x; i < D * 2; i += 256) {
+    const int c2 = i >> 2, p0 = 16 * (i & 3);
+    const int g = c2 >> 2, within = 4 * (c2 & 3);  // granule of the pair, its byte offset
+    float f0[16], f1[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) f[e] = E::to_f32(tile[f8_key_of_pos(p0 + e) * D + d]) * s;
-    u32x4 w;
+    for (int e = 0; e < 16; ++e) {
+      const int r = f8_key_of_pos(p0 + e);
+      const uint32_t w = *(const uint32_t*)(tile + r * (2 * D) + ((g ^ swz(r)) << 4) + within);
+      f0[e] = E::to_f32((uint16_t)(w & 0xffff)) * s;
+      f1[e] = E::to_f32((uint16_t)(w >> 16)) * s;
+    }
+    u32x4 w0, w1;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) w[c] = f8_pack4(f[4 * c], f[4 * c + 1], f[4 * c + 2], f[4 * c + 3]);
-    *(u32x4*)(out + (size_t)d * kF8Bc + p0) = w;
+    for (int c = 0; c < 4; ++c) {
+      w0[c] = f8_pack4(f0[4 * c], f0[4 * c + 1], f0[4 * c + 2], f0[4 * c + 3]);
+      w1[c] = f8_pack4(f1[4 * c], f1[4 * c + 1], f1[4 * c + 2], f1[4 * c + 3]);
+    }
+    *(u32x4*)(out + (size_t)(2 * c2) * kF8Bc + p0) = w0;
+    *(u32x4*)(out + (size_t)(2 * c2 + 1) * kF8Bc + p0) = w1;
   }
 }
 
