@@ -18,7 +18,7 @@ The backward of the same problem has dV[target] = the sum of dO over the
 queries that attend it, dV = 0 on every other key, and dQ, dK = 0 up to the
 rounding of dP - delta (dS = P (dP - delta) vanishes when P is one-hot);
 with bf16 operands P keeps 2^-115 on the other keys, so their dV is ~1e-33
-rather than 0."""
+rather than 0. The decode backward (one query row) is checked the same way."""
 import math
 
 import pytest
@@ -117,4 +117,33 @@ def test_backward_at_the_size_limit(lib):
     assert dv[0, 0][mask].abs().max().item() <= 1e-30
     dk_max, dq_max = dk.abs().max().item(), dq.abs().max().item()
     print(f"backward D=1024: max|dK| = {dk_max:.3e}, max|dQ| = {dq_max:.3e}", flush=True)
+    assert dk_max <= 5e-2 and dq_max <= 1e-2
+
+
+def test_decode_backward_at_the_size_limit(lib):
+    """One query row per head at the largest Nkv: the decode backward's key
+    ranges and row offsets span the whole 2^31-element slice."""
+    D = 1024
+    print(f"case limit decode backward D={D} Nkv={D_LIMITS[D]}", flush=True)
+    q, k, v, targets, qi = _problem(D, Hq=8, Nq=1, dtype=torch.bfloat16)
+    o, lse = lib.attention(q, k, v, scale=1.0, return_lse=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(98)
+    dout = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    dq, dk, dv = lib.attention_backward(dout, q, k, v, o, lse, scale=1.0)
+    torch.cuda.synchronize()
+    t_idx = torch.tensor(targets, device="cuda")
+    want = torch.zeros(len(targets), D, device="cuda")
+    want.index_add_(0, qi.reshape(-1), dout[0].reshape(-1, D).float())
+    err = (dv[0, 0, t_idx].float() - want).abs().max().item()
+    scale_ref = want.abs().max().item()
+    print(f"decode backward D=1024: max|dV[target] - sum dO| = {err:.3e} (max |sum| {scale_ref:.2f})", flush=True)
+    assert err <= 1e-2 + 2.0 ** -8 * scale_ref
+    mask = torch.ones(dv.shape[2], dtype=torch.bool, device="cuda")
+    mask[t_idx] = False
+    # P of the other keys is e^-80 in fp32 (the decode backward keeps P in
+    # fp32): their dV is ~1e-35
+    assert dv[0, 0][mask].abs().max().item() <= 1e-30
+    dk_max, dq_max = dk.abs().max().item(), dq.abs().max().item()
+    print(f"decode backward D=1024: max|dK| = {dk_max:.3e}, max|dQ| = {dq_max:.3e}", flush=True)
     assert dk_max <= 5e-2 and dq_max <= 1e-2
