@@ -250,6 +250,7 @@ DECODE_CASES = [
     (1, 2, 1, 1, 600, 1024),    # G = 2, two granules per lane
     (1, 3, 3, 1, 517, 576),     # a lane's second granule only in lanes 0 .. 7
     (3, 2, 2, 1, 33, 64),       # 8 lanes hold the row
+    (1, 2, 2, 1, 1, 256),       # one key: dV = dO, dK = dQ = 0
     (1, 8, 1, 1, 300, 128),     # G = 8: no decode backward, the minimal path
 ]
 
@@ -282,4 +283,19 @@ def test_decode_backward_deterministic_and_zero_dout(lib):
     for a_, b_ in zip(r1, r2):
         assert torch.equal(a_, b_)
     for t in z:
+        assert torch.count_nonzero(t).item() == 0
+
+
+
+def test_decode_backward_fully_masked_row(lib):
+    """A row that sees no key (every bias -inf) has lse = -inf and no gradient."""
+    B, Hq, Hkv, Nq, Nkv, D = 1, 4, 2, 1, 300, 128
+    q, k, v, do, _ = _inputs(82, B, Hq, Hkv, Nq, Nkv, D, "fp16", False)
+    q, k, v, do = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    mask = torch.full((1, 1, 1, Nkv), float("-inf"), dtype=torch.float16, device="cuda")
+    o, lse = lib.attention(q, k, v, mask=mask, return_lse=True)
+    dq, dk, dv = lib.attention_backward(do, q, k, v, o, lse, mask=mask)
+    torch.cuda.synchronize()
+    assert torch.isinf(lse).all() and (lse < 0).all()
+    for t in (dq, dk, dv):
         assert torch.count_nonzero(t).item() == 0
