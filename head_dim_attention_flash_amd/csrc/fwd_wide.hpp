@@ -151,6 +151,10 @@ void fwd_wide_kernel(FwdArgs a) {
   // issued in one burst, they held the wave's MFMAs back while the copy
   // instructions queued.
   constexpr int NKC = SG / 4, NVC = D / 64;  // copies per wave per tile: K, V^T
+  // each phase issues the other buffer's copies over the first half of its
+  // steps; above D = 768 over three quarters (1.4 % faster at D = 1024, no
+  // faster at 576 and 768)
+  constexpr int SPAN_NUM = D > 768 ? 3 : 2, SPAN_DEN = 4;
 
   // K fragment (A of S^T) for k-step st = 8 a + c: key row l % 32, granule 2 st + l / 32
   auto k_bases = [&](int ln, uint32_t* kx) {
@@ -219,7 +223,7 @@ void fwd_wide_kernel(FwdArgs a) {
       for (int st = 0; st < NS; ++st) {
 #pragma unroll
         for (int r = 0; r < NVC; ++r)
-          if ((r * (NS / 2)) / NVC == st) vt_copy(j, r, vlo);
+          if ((r * (SPAN_NUM * NS / SPAN_DEN)) / NVC == st) vt_copy(j, r, vlo);
         const u32x4 a0 = kf[st % kKAhead];
         if (st + kKAhead < NS) kf[st % kKAhead] = kread(st + kKAhead);
         f32x16& acc = (st & 1) ? s_odd : s_acc;
@@ -346,7 +350,7 @@ void fwd_wide_kernel(FwdArgs a) {
         // zeros) or, causal, rows nobody reads: harmless, and branch-free
 #pragma unroll
         for (int r = 0; r < NKC; ++r)
-          if ((r * (NSV / 2)) / NKC == st) k_copy(j + 1, r, lnc);
+          if ((r * (SPAN_NUM * NSV / SPAN_DEN)) / NKC == st) k_copy(j + 1, r, lnc);
         const int db = st % NDB, t2 = st / NDB;
         const u32x4 vbits = vf[st % kVAhead];
         if (st + kVAhead < NSV) vf[st % kVAhead] = vread(st + kVAhead);
