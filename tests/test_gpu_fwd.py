@@ -147,7 +147,7 @@ def test_forward_matches_oracle(lib, shape, dtype, accum, variant):
     _compare(o, lse, q, k, v, scale, causal, mask, dtype, accum, f"{shape}-{dtype}-{accum}-{variant}")
 
 
-@pytest.mark.parametrize("D", [64, 320, 512, 704, 1024])
+@pytest.mark.parametrize("D", [64, 320, 512, 576, 640, 704, 1024])
 @pytest.mark.parametrize("accum", ["f32", "f16"])
 def test_zero_query_gives_mean_and_log_n(lib, D, accum):
     _, k, v, _ = _inputs(7, 1, 2, 2, 8, 300, D, "fp16")
@@ -158,7 +158,7 @@ def test_zero_query_gives_mean_and_log_n(lib, D, accum):
     assert np.abs(to_f64(lse) - math.log(300)).max() <= 1e-5
 
 
-@pytest.mark.parametrize("D", [320, 768, 960])
+@pytest.mark.parametrize("D", [320, 576, 640, 768, 960])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("accum", ["f32", "f16"])
 def test_single_key_returns_v0_exactly(lib, D, dtype, accum):
@@ -180,20 +180,23 @@ def test_causal_row0_is_v0_exactly(lib, dtype):
     assert torch.equal(o[:, :, 0].cpu(), v.repeat_interleave(2, dim=1)[:, :, 0])
 
 
-def test_fully_masked_rows_give_zero_and_neg_inf(lib):
-    q, k, v, _ = _inputs(10, 1, 2, 2, 70, 90, 320, "fp16")
+@pytest.mark.parametrize("D,accum", [(320, "f32"), (576, "f16"), (768, "f16"), (1024, "f32")])
+def test_fully_masked_rows_give_zero_and_neg_inf(lib, D, accum):
+    q, k, v, _ = _inputs(10, 1, 2, 2, 70, 90, D, "fp16")
     mask = torch.full((1, 90), float("-inf"), dtype=torch.float16)
-    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), mask=mask.cuda())
+    o, lse = _run(lib, q.cuda(), k.cuda(), v.cuda(), mask=mask.cuda(), accum=accum)
     assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
 
 
-def test_mask_equals_deleting_keys(lib):
-    q, k, v, _ = _inputs(11, 1, 2, 2, 96, 200, 512, "fp16")
+@pytest.mark.parametrize("D,accum", [(512, "f32"), (640, "f16"), (1024, "f16")])
+def test_mask_equals_deleting_keys(lib, D, accum):
+    q, k, v, _ = _inputs(11, 1, 2, 2, 96, 200, D, "fp16")
     keep = torch.ones(200, dtype=torch.bool)
     keep[torch.randperm(200, generator=torch.Generator().manual_seed(1))[:37]] = False
     mask = torch.where(keep, 0.0, float("-inf")).to(torch.float16)[None]
-    o1, l1 = _run(lib, q.cuda(), k.cuda(), v.cuda(), mask=mask.cuda())
-    o2, l2 = _run(lib, q.cuda(), k[:, :, keep].contiguous().cuda(), v[:, :, keep].contiguous().cuda())
+    o1, l1 = _run(lib, q.cuda(), k.cuda(), v.cuda(), mask=mask.cuda(), accum=accum)
+    o2, l2 = _run(lib, q.cuda(), k[:, :, keep].contiguous().cuda(), v[:, :, keep].contiguous().cuda(),
+                  accum=accum)
     assert (o1 - o2).abs().max().item() <= 2e-3
     assert (l1 - l2).abs().max().item() <= 1e-4
 
@@ -292,7 +295,7 @@ def test_query_mask_equals_deleting_keys_per_row(lib, shape):
         assert np.abs(to_f64(lse[:, :, r:r + 1]) - lo).max() <= 2e-3
 
 
-@pytest.mark.parametrize("D", [320, 768])
+@pytest.mark.parametrize("D", [320, 576, 768, 1024])
 def test_bf16_inputs_with_the_fp16_accumulator(lib, D):
     """bf16 inputs with FFPA_ACC_F16 accumulate O in fp16 (the reading of
     "fp16 accumulation" the header documents). Inside fp16's range the result
